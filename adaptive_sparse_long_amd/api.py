@@ -1,0 +1,211 @@
+"""Python binding of libdash.so over torch tensors.
+
+torch provides device memory and the current HIP stream; every step of the
+computation runs in the library's kernels. Each function checks that tensors
+are contiguous, on the GPU and of the expected dtype, allocates the outputs,
+and passes raw pointers to the C entry point of the same name (include/dash.h).
+
+Method (DashAttention README page, "How it works"): ``summarize`` builds one
+key summary per chunk with head_cls, ``route`` runs alpha-entmax chunk routing,
+``sparse_attn_prefill`` / ``sparse_attn_decode`` run the prior-induced sparse
+softmax over the routed chunks. ``entmax_attn`` is the dense alpha-entmax
+attention with block skipping of the AdaSplash README page.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "Params",
+    "summarize",
+    "workspace_size",
+    "route",
+    "sparse_attn_prefill",
+    "sparse_attn_decode",
+    "entmax_attn",
+    "prefill",
+    "decode_step",
+]
+
+CHUNK = 64
+
+
+@dataclass(frozen=True)
+class Params:
+    """The wrapper arguments of "Core API" plus the entmax alpha / iteration count."""
+
+    chunk_size: int = 64
+    alpha: float = 1.5
+    n_iter: int = 10
+    scaling_factor: float = 1.0
+    causal: bool = True
+    estimate_diagonal: bool = True
+
+    def c(self) -> _lib.DashParams:
+        return _lib.params(self.chunk_size, self.alpha, self.n_iter, self.scaling_factor, self.causal, self.estimate_diagonal)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.DASH_BF16
+    if t.dtype == torch.float32:
+        return _lib.DASH_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def summarize(K, head_cls, S, n_tokens=None, seqlens=None, chunk_begin=0, chunk_end=None, params: Params = Params()):
+    """Chunk summaries S[b, h, c] for c in [chunk_begin, chunk_end) ("How it works" 1)."""
+    lib = _lib.load()
+    _need(K, "K", dim=4)
+    _need(head_cls, "head_cls", K.dtype, 2)
+    _need(S, "S", torch.float32, 4)
+    B, Hkv, Lmax, d = K.shape
+    if seqlens is not None:
+        _need(seqlens, "seqlens", torch.int32, 1)
+    n_tokens = Lmax if n_tokens is None else int(n_tokens)
+    if chunk_end is None:
+        chunk_end = -(-n_tokens // CHUNK)
+    st = lib.dash_summarize(_p(K), _p(head_cls), _p(S), _dt(K), B, Hkv, Lmax, d, n_tokens, _p(seqlens),
+                            int(chunk_begin), int(chunk_end), S.shape[2], params.c(), _stream(K.device))
+    _lib.check(st, "dash_summarize")
+    return S
+
+
+def workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode: bool, params: Params = Params()) -> int:
+    return int(_lib.load().dash_workspace_size(B, Hq, Hkv, Nq, Lmax, d, int(decode), params.c()))
+
+
+def route(Q, K, head_cls, S, params: Params = Params(), seqlens=None, with_bits=True, workspace=None):
+    """Chunk routing ("How it works" 2). Returns (tau, active_bits or None, workspace)."""
+    lib = _lib.load()
+    _need(Q, "Q", dim=4)
+    _need(K, "K", Q.dtype, 4)
+    _need(head_cls, "head_cls", Q.dtype, 2)
+    _need(S, "S", torch.float32, 4)
+    B, Hq, Nq, d = Q.shape
+    Hkv, Lmax = K.shape[1], K.shape[2]
+    decode = seqlens is not None
+    if decode:
+        _need(seqlens, "seqlens", torch.int32, 1)
+    n_slots = -(-(Lmax if decode else Nq) // CHUNK)
+    words = -(-n_slots // 32)
+    ws_bytes = workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode, params)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
+    tau = torch.empty(B, Hq, Nq, dtype=torch.float32, device=Q.device)
+    bits = torch.empty(B, Hq, Nq, words, dtype=torch.int32, device=Q.device) if with_bits else None
+    st = lib.dash_route(_p(Q), _p(K), _p(head_cls), _p(S), _dt(Q), B, Hq, Hkv, Nq, Lmax, d, S.shape[2],
+                        _p(seqlens), params.c(), _p(tau), _p(bits), words, _p(workspace),
+                        workspace.numel(), _stream(Q.device))
+    _lib.check(st, "dash_route")
+    return tau, bits, workspace
+
+
+def sparse_attn_prefill(Q, K, V, workspace, params: Params = Params(), out=None):
+    """Prior-induced sparse softmax over the routed chunks ("How it works" 3)."""
+    lib = _lib.load()
+    _need(Q, "Q", dim=4)
+    _need(K, "K", Q.dtype, 4)
+    _need(V, "V", Q.dtype, 4)
+    B, Hq, N, d = Q.shape
+    Hkv, Lmax = K.shape[1], K.shape[2]
+    out = torch.empty_like(Q) if out is None else out
+    st = lib.dash_sparse_attn_prefill(_p(Q), _p(K), _p(V), _dt(Q), B, Hq, Hkv, N, Lmax, d, params.c(),
+                                      _p(out), _p(workspace), workspace.numel(), _stream(Q.device))
+    _lib.check(st, "dash_sparse_attn_prefill")
+    return out
+
+
+def sparse_attn_decode(q, Kc, Vc, seqlens, workspace, params: Params = Params(), out=None):
+    """Sparse attention of one new token per sequence over the routed cache chunks."""
+    lib = _lib.load()
+    _need(q, "q", dim=4)
+    _need(Kc, "Kc", q.dtype, 4)
+    _need(Vc, "Vc", q.dtype, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, _, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    out = torch.empty_like(q) if out is None else out
+    st = lib.dash_sparse_attn_decode(_p(q), _p(Kc), _p(Vc), _dt(q), B, Hq, Hkv, _p(seqlens), Lmax, d,
+                                     params.c(), _p(out), _p(workspace), workspace.numel(), _stream(q.device))
+    _lib.check(st, "dash_sparse_attn_decode")
+    return out
+
+
+def entmax_attn(Q, K, V, alpha=1.5, n_iter=10, causal=True, varlen=None, with_mask=True):
+    """Dense alpha-entmax attention with a per-tile block mask (AdaSplash "Usage")."""
+    lib = _lib.load()
+    _need(Q, "Q", dim=4)
+    _need(K, "K", Q.dtype, 4)
+    _need(V, "V", Q.dtype, 4)
+    B, H, N, d = Q.shape
+    if varlen is not None:
+        _need(varlen, "varlen", torch.int32, 1)
+    nT = -(-N // 64)
+    out = torch.empty_like(Q)
+    tau = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
+    mask = torch.empty(B, H, nT, -(-nT // 32), dtype=torch.int32, device=Q.device) if with_mask else None
+    st = lib.entmax_attn(_p(Q), _p(K), _p(V), _dt(Q), B, H, N, d, _p(varlen), float(alpha), int(n_iter),
+                         int(bool(causal)), _p(out), _p(tau), _p(mask), _stream(Q.device))
+    _lib.check(st, "entmax_attn")
+    return out, tau, mask
+
+
+def prefill(Q, K, V, head_cls, params: Params = Params(), with_bits=True, workspace=None, S=None):
+    """Whole prefill: summaries of every chunk, routing, sparse attention.
+
+    Returns (O, tau, active_bits, S, workspace); S is the float32 summary cache."""
+    B, Hkv, N, d = K.shape
+    n_c = -(-N // CHUNK)
+    if S is None:
+        S = torch.empty(B, Hkv, n_c, d, dtype=torch.float32, device=K.device)
+    summarize(K, head_cls, S, n_tokens=N, chunk_begin=0, chunk_end=n_c if not params.causal else N // CHUNK,
+              params=params)
+    tau, bits, workspace = route(Q, K, head_cls, S, params, with_bits=with_bits, workspace=workspace)
+    O = sparse_attn_prefill(Q, K, V, workspace, params)
+    return O, tau, bits, S, workspace
+
+
+def decode_step(q, Kc, Vc, head_cls, S, seqlens, params: Params = Params(), lengths=None, with_bits=True,
+                workspace=None):
+    """One decode step for new tokens already written at position seqlens[b] - 1.
+
+    Routes against the summary cache, attends over the routed chunks, then
+    appends the summary of every chunk this token completed. ``lengths`` holds
+    the same lengths on the host (ints); it only selects which chunk indices to
+    append, so no device-to-host copy is needed. Returns (O, tau, bits, workspace).
+    """
+    tau, bits, workspace = route(q, Kc, head_cls, S, params, seqlens=seqlens, with_bits=with_bits, workspace=workspace)
+    O = sparse_attn_decode(q, Kc, Vc, seqlens, workspace, params)
+    if lengths is not None:
+        done = sorted({int(n) // CHUNK - 1 for n in lengths if int(n) % CHUNK == 0})
+        for c in done:
+            summarize(Kc, head_cls, S, seqlens=seqlens, chunk_begin=c, chunk_end=c + 1, params=params)
+    return O, tau, bits, workspace

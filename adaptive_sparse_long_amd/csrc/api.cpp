@@ -1,0 +1,232 @@
+// api.cpp -- the C ABI of libdash.so (declared in include/dash.h): argument
+// validation on the host, workspace sizing, and kernel launches on the caller's
+// stream. Nothing here allocates device memory or synchronises the host.
+#include "dash.h"
+
+#include <math.h>
+
+#include "kernels.hpp"
+
+using namespace dash;
+
+namespace {
+
+bool finite_gt1(float a) { return isfinite(a) && a > 1.f; }
+
+dash_status check_params(const dash_params& p) {
+  if (p.chunk_size <= 0) return DASH_ERR_INVALID_ARG;
+  if (!finite_gt1(p.alpha) || p.n_iter < 1 || !isfinite(p.scaling_factor)) return DASH_ERR_INVALID_ARG;
+  if ((p.causal != 0 && p.causal != 1) || (p.estimate_diagonal != 0 && p.estimate_diagonal != 1))
+    return DASH_ERR_INVALID_ARG;
+  if (p.chunk_size != kChunk) return DASH_ERR_UNSUPPORTED;
+  return DASH_OK;
+}
+
+bool gqa_ok(int Hq, int Hkv) { return Hq > 0 && Hkv > 0 && Hq % Hkv == 0; }
+bool g_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+dash_status from_hip(hipError_t e) { return e == hipSuccess ? DASH_OK : DASH_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+void dash_default_params(dash_params* p) {
+  if (!p) return;
+  p->chunk_size = 64;
+  p->alpha = 1.5f;
+  p->n_iter = 10;
+  p->scaling_factor = 1.0f;
+  p->causal = 1;
+  p->estimate_diagonal = 1;
+}
+
+const char* dash_status_string(dash_status s) {
+  switch (s) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARG: return "invalid argument";
+    case DASH_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DASH_ERR_WORKSPACE: return "workspace too small";
+    case DASH_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_dtype dt, int B,
+                           int Hkv, int Lmax, int d, int n_tokens, const int* seqlens,
+                           int chunk_begin, int chunk_end, int s_cap, dash_params p,
+                           hipStream_t stream) {
+  if (!K || !head_cls || !S) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || d <= 0 || s_cap <= 0) return DASH_ERR_INVALID_ARG;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > s_cap) return DASH_ERR_INVALID_ARG;
+  if (!seqlens && (n_tokens <= 0 || n_tokens > Lmax)) return DASH_ERR_INVALID_ARG;
+  if (p.chunk_size <= 0) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (p.chunk_size != kChunk || dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if ((long long)chunk_end * kChunk > (long long)Lmax + kChunk - 1) return DASH_ERR_INVALID_ARG;
+  if (chunk_end == chunk_begin) return DASH_OK;
+  SummarizeArgs a{K, head_cls, S, B, Hkv, Lmax, d, n_tokens, seqlens, chunk_begin, chunk_end,
+                  s_cap, kChunk, 1.f / sqrtf((float)d)};
+  return from_hip(launch_summarize(a, stream));
+}
+
+size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int decode,
+                           dash_params p) {
+  if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
+  if (decode) return decode_layout(B, Hq, Hkv, Lmax, d).total;
+  if (Nq <= 0 || Nq > Lmax) return 0;
+  return prefill_layout(B, Hq, Nq, p.causal != 0).total;
+}
+
+dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
+                       dash_dtype dt, int B, int Hq, int Hkv, int Nq, int Lmax, int d, int s_cap,
+                       const int* seqlens, dash_params p, float* tau, uint32_t* active_bits,
+                       int bits_words, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!Q || !K || !head_cls || !S || !tau || !workspace) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || Nq <= 0 || Lmax <= 0 || d <= 0 || s_cap <= 0 || !gqa_ok(Hq, Hkv))
+    return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  dash_status st = check_params(p);
+  if (st != DASH_OK) return st;
+  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  const int g = Hq / Hkv;
+  const bool decode = seqlens != nullptr;
+  RouteArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.cls = static_cast<const uint16_t*>(head_cls);
+  a.S = S;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = g; a.Nq = Nq; a.Lmax = Lmax; a.d = d; a.s_cap = s_cap;
+  a.seqlens = seqlens;
+  a.alpha = p.alpha;
+  a.beta = 1.f / (p.alpha - 1.f);
+  a.inv_sqrt_d = 1.f / sqrtf((float)d);
+  a.zscale = p.scaling_factor * a.inv_sqrt_d;
+  a.n_iter = p.n_iter;
+  a.causal = p.causal;
+  a.est = p.causal ? p.estimate_diagonal : 0;
+  a.tau = tau;
+  a.bits = active_bits;
+  a.bits_words = bits_words;
+  char* ws = static_cast<char*>(workspace);
+  if (decode) {
+    if (Nq != 1 || p.causal != 1) return DASH_ERR_INVALID_ARG;
+    if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete || !g_supported(g)) return DASH_ERR_UNSUPPORTED;
+    if (s_cap < (Lmax - 1) / kChunk) return DASH_ERR_INVALID_ARG;
+    const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, d);
+    if (active_bits && bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+    if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
+    a.n_slots = L.n_slots;
+    a.z = reinterpret_cast<float*>(ws + L.off_z);
+    a.counts = reinterpret_cast<int*>(ws + L.off_counts);
+    a.lists = reinterpret_cast<int*>(ws + L.off_lists);
+    a.bias = reinterpret_cast<float*>(ws + L.off_bias);
+    return from_hip(launch_route_decode(a, stream));
+  }
+  if (Nq > Lmax) return DASH_ERR_INVALID_ARG;
+  const PrefillLayout L = prefill_layout(B, Hq, Nq, p.causal != 0);
+  if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  const int need_cap = p.causal ? Nq / kChunk : L.n_slots;
+  if (s_cap < need_cap) return DASH_ERR_INVALID_ARG;
+  if (active_bits && bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
+  a.n_tiles = L.n_tiles;
+  a.n_slots = L.n_slots;
+  a.per_head = L.per_head;
+  a.counts = reinterpret_cast<int*>(ws + L.off_counts);
+  a.lists = reinterpret_cast<int*>(ws + L.off_lists);
+  a.bias = reinterpret_cast<float*>(ws + L.off_bias);
+  return from_hip(launch_route_prefill(a, stream));
+}
+
+dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V, dash_dtype dt,
+                                     int B, int Hq, int Hkv, int N, int Lmax, int d,
+                                     dash_params p, void* O, const void* workspace,
+                                     size_t ws_bytes, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !workspace) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || N <= 0 || Lmax <= 0 || N > Lmax || d <= 0 || !gqa_ok(Hq, Hkv))
+    return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  dash_status st = check_params(p);
+  if (st != DASH_OK) return st;
+  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  const PrefillLayout L = prefill_layout(B, Hq, N, p.causal != 0);
+  if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
+  const char* ws = static_cast<const char*>(workspace);
+  PrefillAttnArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.O = static_cast<uint16_t*>(O);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = Hq / Hkv; a.N = N; a.Lmax = Lmax;
+  a.causal = p.causal;
+  a.scale_log2 = kLog2e / sqrtf((float)d);
+  a.n_tiles = L.n_tiles;
+  a.n_slots = L.n_slots;
+  a.per_head = L.per_head;
+  a.counts = reinterpret_cast<const int*>(ws + L.off_counts);
+  a.lists = reinterpret_cast<const int*>(ws + L.off_lists);
+  a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
+  return from_hip(launch_sparse_prefill(a, stream));
+}
+
+dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* Vc, dash_dtype dt,
+                                    int B, int Hq, int Hkv, const int* seqlens, int Lmax, int d,
+                                    dash_params p, void* O, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!Q || !Kc || !Vc || !O || !workspace || !seqlens) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || Lmax <= 0 || d <= 0 || !gqa_ok(Hq, Hkv)) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  dash_status st = check_params(p);
+  if (st != DASH_OK) return st;
+  if (p.causal != 1) return DASH_ERR_INVALID_ARG;
+  const int g = Hq / Hkv;
+  if (dt != DASH_BF16 || d != 128 || !g_supported(g)) return DASH_ERR_UNSUPPORTED;
+  if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete) return DASH_ERR_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, d);
+  if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  DecodeAttnArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(Kc);
+  a.V = static_cast<const uint16_t*>(Vc);
+  a.O = static_cast<uint16_t*>(O);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = g; a.Lmax = Lmax;
+  a.seqlens = seqlens;
+  a.scale_log2 = kLog2e / sqrtf((float)d);
+  a.n_slots = L.n_slots;
+  a.n_splits = L.n_splits;
+  a.counts = reinterpret_cast<const int*>(ws + L.off_counts);
+  a.lists = reinterpret_cast<const int*>(ws + L.off_lists);
+  a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
+  a.part = reinterpret_cast<float*>(ws + L.off_part);
+  return from_hip(launch_sparse_decode(a, stream));
+}
+
+dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype dt, int B, int H,
+                        int Nmax, int d, const int* varlen, float alpha, int n_iter, int causal,
+                        void* O, float* tau, uint32_t* block_mask, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !tau) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nmax <= 0 || d <= 0) return DASH_ERR_INVALID_ARG;
+  if (!finite_gt1(alpha) || n_iter < 1 || (causal != 0 && causal != 1)) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DASH_ERR_UNSUPPORTED;
+  const int nT = (Nmax + 63) / 64;
+  if (nT > kEntmaxMaxTiles) return DASH_ERR_UNSUPPORTED;
+  EntmaxAttnArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.O = O;
+  a.B = B; a.H = H; a.N = Nmax; a.d = d;
+  a.varlen = varlen;
+  a.alpha = alpha;
+  a.beta = 1.f / (alpha - 1.f);
+  a.scale = (alpha - 1.f) / sqrtf((float)d);
+  a.n_iter = n_iter;
+  a.causal = causal;
+  a.tau = tau;
+  a.mask = block_mask;
+  a.mask_words = (nT + 31) / 32;
+  return from_hip(launch_entmax_attn(a, dt == DASH_BF16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,171 @@
+// kernels.hpp -- launch arguments, workspace layouts and launcher declarations
+// shared by the HIP kernels and the host API (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "cdna4.hpp"
+
+namespace dash {
+
+// Query rows per prefill workgroup (four wavefronts of 32 rows) and keys per chunk.
+constexpr int kTileRows = 128;
+constexpr int kChunk = 64;
+// Routed chunks handled by one decode split (one workgroup, four wavefronts).
+constexpr int kDecodeSplit = 16;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Prefill work lists, per (b, query head): for each 128-row tile, the union of
+// the chunks routed to any of its rows (ascending), and for each listed chunk
+// the 128 rows' log2 routing weights (-inf: chunk not attended by that row).
+// Causal tile t can only list chunks 0 .. 2t+1, so tiles are packed in a
+// triangle: tile t starts at slot t*(t+1). Non-causal tiles hold n_slots each.
+// ---------------------------------------------------------------------------
+struct PrefillLayout {
+  int n_tiles = 0;
+  int n_slots = 0;        // chunk slots = ceil(N / 64)
+  long long per_head = 0; // list slots per (b, head)
+  size_t off_counts = 0, off_lists = 0, off_bias = 0, total = 0;
+};
+
+__host__ __device__ inline long long prefill_tile_offset(int tile, int n_slots, bool causal) {
+  return causal ? (long long)tile * (tile + 1) : (long long)tile * n_slots;
+}
+__host__ __device__ inline int prefill_tile_cap(int tile, int n_slots, bool causal) {
+  return causal ? min(n_slots, 2 * tile + 2) : n_slots;
+}
+
+inline PrefillLayout prefill_layout(int B, int Hq, int N, bool causal) {
+  PrefillLayout L;
+  L.n_tiles = (N + kTileRows - 1) / kTileRows;
+  L.n_slots = (N + kChunk - 1) / kChunk;
+  const int t = L.n_tiles - 1;
+  L.per_head = prefill_tile_offset(t, L.n_slots, causal) + prefill_tile_cap(t, L.n_slots, causal);
+  const size_t heads = (size_t)B * Hq;
+  L.off_counts = 0;
+  L.off_lists = align256(heads * L.n_tiles * sizeof(int));
+  L.off_bias = L.off_lists + align256(heads * (size_t)L.per_head * sizeof(int));
+  L.total = L.off_bias + align256(heads * (size_t)L.per_head * kTileRows * sizeof(float));
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Decode workspace, per (b, kv head) group of g query heads: routing scores of
+// every query head, the union list of routed chunks, g log2 weights per listed
+// chunk, and per-split partial results (max, sum, unnormalised output).
+// ---------------------------------------------------------------------------
+struct DecodeLayout {
+  int n_slots = 0;   // ceil(Lmax / 64): chunk slots, own chunk included
+  int n_splits = 0;  // ceil(n_slots / kDecodeSplit)
+  int g = 0;
+  size_t off_z = 0, off_counts = 0, off_lists = 0, off_bias = 0, off_part = 0, total = 0;
+};
+
+inline DecodeLayout decode_layout(int B, int Hq, int Hkv, int Lmax, int d) {
+  DecodeLayout L;
+  L.g = Hq / Hkv;
+  L.n_slots = (Lmax + kChunk - 1) / kChunk;
+  L.n_splits = (L.n_slots + kDecodeSplit - 1) / kDecodeSplit;
+  const size_t groups = (size_t)B * Hkv;
+  L.off_z = 0;
+  L.off_counts = align256((size_t)B * Hq * L.n_slots * sizeof(float));
+  L.off_lists = L.off_counts + align256(groups * sizeof(int));
+  L.off_bias = L.off_lists + align256(groups * L.n_slots * sizeof(int));
+  L.off_part = L.off_bias + align256(groups * L.n_slots * L.g * sizeof(float));
+  L.total = L.off_part + align256(groups * L.n_splits * L.g * (size_t)(d + 2) * sizeof(float));
+  return L;
+}
+
+// --------------------------------------------------------------------------- args
+struct SummarizeArgs {
+  const void* K;
+  const void* cls;
+  float* S;
+  int B, Hkv, Lmax, d, n_tokens;
+  const int* seqlens;
+  int chunk_begin, chunk_end, s_cap, C;
+  float inv_sqrt_d;
+};
+
+struct RouteArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* cls;
+  const float* S;
+  int B, Hq, Hkv, g, Nq, Lmax, d, s_cap;
+  const int* seqlens;
+  float alpha, beta, zscale, inv_sqrt_d;
+  int n_iter, causal, est;
+  float* tau;
+  uint32_t* bits;
+  int bits_words;
+  // prefill lists
+  int n_tiles, n_slots;
+  long long per_head;
+  int* counts;
+  int* lists;
+  float* bias;
+  // decode scratch
+  float* z;
+};
+
+struct PrefillAttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  int B, Hq, Hkv, g, N, Lmax, causal;
+  float scale_log2;
+  int n_tiles, n_slots;
+  long long per_head;
+  const int* counts;
+  const int* lists;
+  const float* bias;
+};
+
+struct DecodeAttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  int B, Hq, Hkv, g, Lmax;
+  const int* seqlens;
+  float scale_log2;
+  int n_slots, n_splits;
+  const int* counts;
+  const int* lists;
+  const float* bias;
+  float* part;
+};
+
+struct EntmaxAttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int B, H, N, d;
+  const int* varlen;
+  float alpha, beta, scale;  // scale = (alpha - 1) / sqrt(d)
+  int n_iter, causal;
+  float* tau;
+  uint32_t* mask;
+  int mask_words;
+};
+
+hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
+hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_route_decode(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream);
+hipError_t launch_sparse_decode(const DecodeAttnArgs& a, hipStream_t stream);
+hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t stream);
+
+// Limits of the current kernels (checked by the host API).
+constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
+constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
+constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
+
+}  // namespace dash

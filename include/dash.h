@@ -1,0 +1,197 @@
+/*
+ * dash.h -- C ABI of libdash.so: hierarchical adaptive sparse attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow two pages:
+ *   - "DashAttention: Differentiable and Adaptive Sparse Hierarchical Attention"
+ *     (README page), sections "Usage", "How it works" (items 1-3 and the
+ *     prefill/decoding paragraph) and "Core API";
+ *   - "AdaSplash: Adaptive Sparse Flash Attention" (README page), sections
+ *     "Usage" (Triton Entmax; AdaSplash with Block Masking) and "Key Features"
+ *     (varlen, alpha, causal masking).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a device pointer owned by the caller (for example
+ *     a torch tensor's data_ptr()). The library never allocates device memory
+ *     and keeps no state between calls except cached device properties, so
+ *     calls are thread safe; calls that share a workspace must be ordered by
+ *     the caller (same stream).
+ *   - Tensors are contiguous row-major. q/k/v use [batch, heads, seq, head_dim]
+ *     ("Usage" of both pages); head_cls is [kv_heads, head_dim].
+ *   - Work is enqueued on `stream` (NULL = the null stream); nothing
+ *     synchronises the host. Outputs are valid once the stream reaches them.
+ *   - All argument checks run on the host before any HIP call, so a bad call
+ *     returns an error code, writes nothing and launches nothing. No C++
+ *     exception crosses this boundary.
+ *   - Status codes: DASH_ERR_INVALID_ARG for null pointers, non-positive sizes,
+ *     Hq not a multiple of Hkv, alpha <= 1, n_iter < 1 and inconsistent sizes;
+ *     DASH_ERR_UNSUPPORTED for a head_dim, dtype, chunk size or length outside
+ *     what the kernels are built for; DASH_ERR_WORKSPACE when ws_bytes is below
+ *     the matching *_workspace_size(); DASH_ERR_HIP when a launch fails.
+ *
+ * Notation: B batch, Hq query heads, Hkv KV heads (Hq % Hkv == 0, query head h
+ * reads KV head h / (Hq / Hkv): the "enable_gqa" behaviour of "Core API"),
+ * d head_dim, C chunk_size, alpha > 1, u = (alpha - 1) * score.
+ */
+#ifndef DASH_H_
+#define DASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = 1,
+  DASH_ERR_UNSUPPORTED = 2,
+  DASH_ERR_WORKSPACE = 3,
+  DASH_ERR_HIP = 4
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+/* Arguments of the DashAttention wrapper ("Core API": chunk_size,
+ * estimate_diagonal, scaling_factor) plus the entmax alpha and iteration
+ * count of the AdaSplash "Usage" section. Passed by value. */
+typedef struct {
+  int chunk_size;        /* C; the kernels are built for 64 */
+  float alpha;           /* entmax alpha for chunk routing, > 1 (default 1.5) */
+  int n_iter;            /* maximum Halley/bisection steps for tau (default 10) */
+  float scaling_factor;  /* multiplies the routing scores (default 1.0) */
+  int causal;            /* 1: query i sees keys j <= i; 0: all keys */
+  int estimate_diagonal; /* causal only. 1: the query's own, still incomplete
+                            chunk is routed like the others, scored against the
+                            summary of its tokens seen so far; 0: it is not
+                            routed and always attended with weight 1 */
+} dash_params;
+
+/* Fills p with the defaults of "Core API": C = 64, alpha = 1.5, n_iter = 10,
+ * scaling_factor = 1, causal = 1, estimate_diagonal = 1. */
+void dash_default_params(dash_params* p);
+
+/* ---------------------------------------------------------------------------
+ * dash_summarize -- stage 1, "Local chunk summarization" ("How it works" 1):
+ * one key summary per KV chunk built with head_cls. For every (b, kv head h)
+ * and chunk c in [chunk_begin, chunk_end):
+ *     a_j = softmax_j(<k_j, head_cls[h]> / sqrt(d)) over the chunk's tokens,
+ *     S[b, h, c, :] = sum_j a_j k_j          (float32)
+ * Chunk c holds tokens [c*C, min((c+1)*C, n_b)) where n_b = seqlens[b] if
+ * seqlens is given, else n_tokens. A chunk with no token in a batch entry is
+ * skipped; with seqlens given, only chunks complete in that entry
+ * ((c+1)*C <= seqlens[b]) are written -- the decode-time "append newly
+ * completed chunks" of the prefill/decoding paragraph.
+ *   K        [B, Hkv, Lmax, d]   dtype dt
+ *   head_cls [Hkv, d]            dtype dt
+ *   S        [B, Hkv, s_cap, d]  float32, chunk_end <= s_cap
+ *   seqlens  [B] int32 on the device, or NULL
+ * --------------------------------------------------------------------------- */
+dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_dtype dt,
+                           int B, int Hkv, int Lmax, int d, int n_tokens,
+                           const int* seqlens, int chunk_begin, int chunk_end, int s_cap,
+                           dash_params p, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dash_route -- stage 2, "Entmax block routing" ("How it works" 2): routing
+ * scores z = scaling_factor * <q_i, s_c> / sqrt(d) against every candidate
+ * chunk summary, alpha-entmax over them with the threshold tau found by
+ * safeguarded Halley steps with bisection (AdaSplash "Usage": Triton Entmax),
+ * the routed set (the support) and the prior pi_c = (u_c - tau)_+^(1/(alpha-1)).
+ *
+ * Candidates of query row i with chunk c_i = i / C:
+ *   causal:     complete chunks c < c_i, plus (estimate_diagonal) c_i scored
+ *               against the summary of tokens [c_i*C, i] computed on the fly;
+ *               without estimate_diagonal c_i is attended with weight 1.
+ *   non-causal: every chunk; S must then also hold the partial last chunk.
+ *
+ * Two modes:
+ *   prefill (seqlens == NULL): rows i = 0 .. Nq-1 of Q [B, Hq, Nq, d];
+ *       keys K [B, Hkv, Lmax, d] with Nq <= Lmax, n_tokens = Nq.
+ *   decode  (seqlens != NULL): Nq must be 1; Q [B, Hq, 1, d] is the new token
+ *       at position t_b = seqlens[b] - 1, whose key/value are already in the
+ *       caches; causal must be 1.
+ * S [B, Hkv, s_cap, d] float32 holds the chunk summaries (dash_summarize).
+ *
+ * Outputs
+ *   tau         [B, Hq, Nq] float32, in u units; +inf for a row without any
+ *               candidate (causal, estimate_diagonal = 0, first chunk).
+ *   active_bits [B, Hq, Nq, bits_words] uint32 or NULL; bit c % 32 of word
+ *               c / 32 is set iff chunk c is attended by the row (the kernel
+ *               form of "return_active_blocks", "Usage"/"Core API").
+ *               bits_words >= ceil(ceil(Lmax / C) / 32).
+ *   workspace   the routed work lists and log2 priors read by the matching
+ *               dash_sparse_attn_* call; size from dash_workspace_size().
+ * --------------------------------------------------------------------------- */
+dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
+                       dash_dtype dt, int B, int Hq, int Hkv, int Nq, int Lmax, int d,
+                       int s_cap, const int* seqlens, dash_params p, float* tau,
+                       uint32_t* active_bits, int bits_words, void* workspace,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace that dash_route and dash_sparse_attn_* need for these
+ * sizes (decode = 1 for the seqlens mode). 0 for invalid sizes. */
+size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int decode,
+                           dash_params p);
+
+/* ---------------------------------------------------------------------------
+ * dash_sparse_attn_prefill -- stage 3, "Prior-induced sparse softmax" ("How it
+ * works" 3) over rows 0 .. N-1:
+ *   O_i = sum_j softmax_j(<q_i, k_j> / sqrt(d) + log w_{i, c(j)}) v_j
+ * over the tokens j of the chunks routed to row i (j <= i when causal), w the
+ * routing prior (1 for an always-attended own chunk). Reads the work lists
+ * that dash_route (prefill mode, same sizes and params) left in `workspace`.
+ *   Q [B, Hq, N, d], K/V [B, Hkv, Lmax, d], O [B, Hq, N, d], all dtype dt.
+ * --------------------------------------------------------------------------- */
+dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V,
+                                     dash_dtype dt, int B, int Hq, int Hkv, int N, int Lmax,
+                                     int d, dash_params p, void* O, const void* workspace,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dash_sparse_attn_decode -- stage 3 for one new token per sequence, reading
+ * only the routed chunks of the caches (prefill/decoding paragraph of "How it
+ * works": decoding reuses the chunk-summary cache). Query row t_b =
+ * seqlens[b] - 1. Split over the routed chunk list, then merged.
+ *   Q [B, Hq, 1, d], Kc/Vc [B, Hkv, Lmax, d], O [B, Hq, 1, d], dtype dt.
+ * Reads the lists that dash_route (decode mode) left in `workspace` and uses
+ * the rest of it for per-split partial results.
+ * --------------------------------------------------------------------------- */
+dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* Vc,
+                                    dash_dtype dt, int B, int Hq, int Hkv,
+                                    const int* seqlens, int Lmax, int d, dash_params p,
+                                    void* O, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * entmax_attn -- dense alpha-entmax attention with block skipping (AdaSplash
+ * "Usage": AdaSplash with Block Masking; "Key Features"). For each (b, h) and
+ * row i < len_b (len_b = varlen[b], or Nmax when varlen is NULL):
+ *   s_ij = <q_i, k_j> / sqrt(d) over j < len_b (and j <= i when causal),
+ *   tau_i : sum_j ((alpha-1) s_ij - tau_i)_+^(1/(alpha-1)) = 1,
+ *   O_i = sum_j ((alpha-1) s_ij - tau_i)_+^(1/(alpha-1)) v_j.
+ * Rows i >= len_b get O = 0 and tau = 0.
+ *   Q/K/V/O    [B, H, Nmax, d] dtype dt (DASH_F32 or DASH_BF16)
+ *   varlen     [B] int32 on the device, 1 <= varlen[b] <= Nmax, or NULL
+ *   tau        [B, H, Nmax] float32, in u units
+ *   block_mask [B, H, nT, ceil(nT / 32)] uint32 or NULL, nT = ceil(Nmax / 64):
+ *              bit J % 32 of word J / 32 of row-tile I is set iff the 64 x 64
+ *              tile (I, J) holds a non-zero weight ("binary mask per block").
+ *              Tiles that are all zero are skipped in the output pass.
+ * n_iter bounds the tau iterations (Halley + bisection, "Triton Entmax").
+ * --------------------------------------------------------------------------- */
+dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype dt, int B,
+                        int H, int Nmax, int d, const int* varlen, float alpha, int n_iter,
+                        int causal, void* O, float* tau, uint32_t* block_mask,
+                        hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* dash_status_string(dash_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H_ */

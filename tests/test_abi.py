@@ -1,0 +1,123 @@
+"""The C ABI library loads without a GPU, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call.
+
+Only argument combinations that fail validation are passed here (plus the pure
+host helpers), so nothing is launched: these tests need no GPU.
+"""
+
+import ctypes
+
+import pytest
+
+from adaptive_sparse_long_amd import _lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    names = _lib.header_symbols()
+    assert set(names) == {
+        "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
+        "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
+    }
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_params_and_status_strings(lib):
+    p = _lib.DashParams()
+    lib.dash_default_params(ctypes.byref(p))
+    assert (p.chunk_size, p.alpha, p.n_iter, p.scaling_factor, p.causal, p.estimate_diagonal) == (64, 1.5, 10, 1.0, 1, 1)
+    assert lib.dash_status_string(0) == b"ok"
+    assert lib.dash_status_string(3) == b"workspace too small"
+    assert lib.dash_status_string(99) == b"unknown status"
+
+
+def _p(**kw):
+    return _lib.params(**kw)
+
+
+def test_workspace_size(lib):
+    p = _p()
+    assert lib.dash_workspace_size(1, 32, 8, 4096, 4096, 128, 0, p) > 0
+    assert lib.dash_workspace_size(16, 32, 8, 1, 131073, 128, 1, p) > 0
+    assert lib.dash_workspace_size(1, 6, 4, 128, 128, 128, 0, p) == 0  # Hq % Hkv
+    assert lib.dash_workspace_size(1, 4, 4, 200, 100, 128, 0, p) == 0  # Nq > Lmax
+    assert lib.dash_workspace_size(1, 4, 4, 100, 100, 128, 0, _p(chunk_size=32)) == 0
+    # causal tiles are packed in a triangle: smaller than the rectangle
+    assert lib.dash_workspace_size(1, 4, 4, 4096, 4096, 128, 0, p) < lib.dash_workspace_size(
+        1, 4, 4, 4096, 4096, 128, 0, _p(causal=False))
+
+
+def _summ(lib, K=FAKE, cls=FAKE, S=FAKE, dt=1, B=1, Hkv=1, Lmax=128, d=128, n=128, seqlens=NULL, c0=0, c1=2, cap=2, p=None):
+    return lib.dash_summarize(K, cls, S, dt, B, Hkv, Lmax, d, n, seqlens, c0, c1, cap, p or _p(), NULL)
+
+
+def test_summarize_validation(lib):
+    assert _summ(lib, K=NULL) == INVALID
+    assert _summ(lib, B=0) == INVALID
+    assert _summ(lib, c1=3, cap=2) == INVALID       # chunk_end beyond the cache
+    assert _summ(lib, n=0) == INVALID
+    assert _summ(lib, n=200, Lmax=128) == INVALID
+    assert _summ(lib, d=64) == UNSUPPORTED
+    assert _summ(lib, dt=0) == UNSUPPORTED
+    assert _summ(lib, dt=7) == INVALID
+    assert _summ(lib, p=_p(chunk_size=32)) == UNSUPPORTED
+    assert _summ(lib, c0=1, c1=1) == OK             # empty range: nothing to do, nothing launched
+
+
+def _route(lib, Q=FAKE, K=FAKE, cls=FAKE, S=FAKE, dt=1, B=1, Hq=4, Hkv=1, Nq=256, Lmax=256, d=128, cap=4,
+           seqlens=NULL, p=None, tau=FAKE, bits=NULL, words=1, ws=FAKE, ws_bytes=0):
+    return lib.dash_route(Q, K, cls, S, dt, B, Hq, Hkv, Nq, Lmax, d, cap, seqlens, p or _p(), tau, bits, words,
+                          ws, ws_bytes, NULL)
+
+
+def test_route_validation(lib):
+    assert _route(lib, Q=NULL) == INVALID
+    assert _route(lib, tau=NULL) == INVALID
+    assert _route(lib, Hq=6, Hkv=4) == INVALID
+    assert _route(lib, p=_p(alpha=1.0)) == INVALID
+    assert _route(lib, p=_p(alpha=float("nan"))) == INVALID
+    assert _route(lib, p=_p(n_iter=0)) == INVALID
+    assert _route(lib, d=64) == UNSUPPORTED
+    assert _route(lib, dt=0) == UNSUPPORTED
+    assert _route(lib, p=_p(chunk_size=128)) == UNSUPPORTED
+    assert _route(lib, Nq=300, Lmax=256) == INVALID
+    assert _route(lib, Nq=40000, Lmax=40000, cap=700) == UNSUPPORTED   # > 512 chunk slots in prefill
+    assert _route(lib, cap=2) == INVALID                             # summary cache too small
+    assert _route(lib, bits=FAKE, words=0) == INVALID
+    assert _route(lib, ws_bytes=16) == WORKSPACE
+    # decode mode
+    assert _route(lib, seqlens=FAKE, Nq=2) == INVALID
+    assert _route(lib, seqlens=FAKE, Nq=1, p=_p(causal=False)) == INVALID
+    assert _route(lib, seqlens=FAKE, Nq=1, Hq=12, Hkv=4) == UNSUPPORTED  # g = 3
+    assert _route(lib, seqlens=FAKE, Nq=1, Lmax=300000, cap=5000) == UNSUPPORTED
+    assert _route(lib, seqlens=FAKE, Nq=1, ws_bytes=16) == WORKSPACE
+
+
+def test_attention_validation(lib):
+    p = _p()
+    f = lib.dash_sparse_attn_prefill
+    assert f(NULL, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 128, p, FAKE, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 128, 128, p, FAKE, FAKE, 0, NULL) == INVALID
+    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 64, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 128, p, FAKE, FAKE, 8, NULL) == WORKSPACE
+    g = lib.dash_sparse_attn_decode
+    assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, NULL, 256, 128, p, FAKE, FAKE, 0, NULL) == INVALID
+    assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 128, _p(causal=False), FAKE, FAKE, 0, NULL) == INVALID
+    assert g(FAKE, FAKE, FAKE, 1, 1, 48, 1, FAKE, 256, 128, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 128, p, FAKE, FAKE, 8, NULL) == WORKSPACE
+    e = lib.entmax_attn
+    assert e(NULL, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == INVALID
+    assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.0, 10, 1, FAKE, FAKE, NULL, NULL) == INVALID
+    assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.5, 0, 1, FAKE, FAKE, NULL, NULL) == INVALID
+    assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.5, 10, 2, FAKE, FAKE, NULL, NULL) == INVALID
+    assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 96, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == UNSUPPORTED
+    assert e(FAKE, FAKE, FAKE, 1, 1, 1, 70000, 64, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == UNSUPPORTED

@@ -1,0 +1,112 @@
+"""GPU parity of dense alpha-entmax attention with block skipping (entmax_attn)
+against the float64 CPU oracle, through the C ABI: float32 (1e-4) and bfloat16
+(2e-2) outputs, tau within 1e-4, block masks equal except for tiles decided only
+by entries within 1e-4 of tau; varlen, causal and non-causal, head_dim 64/128,
+the three tau solver specialisations, and the full varlen workload on sampled
+rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adaptive_sparse_long_amd import api
+from adaptive_sparse_long_amd.workloads import WORKLOADS, dense_entmax_inputs
+
+from _helpers import MARGIN, TOL_BF16, TOL_F32, assert_close, f64, tau_close, unpack_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _mask_ok(gpu_mask, q, k, tau_ref, L, alpha, causal, where):
+    """Compare one (b, h) block mask with the oracle's, tile by tile."""
+    N = q.shape[0]
+    nT = -(-N // 64)
+    d = q.shape[1]
+    u = (alpha - 1.0) * (q[:L] @ k[:L].T) / np.sqrt(d)
+    if causal:
+        u = np.where(np.arange(L)[None, :] <= np.arange(L)[:, None], u, -np.inf)
+    umt = u - tau_ref[:L, None]
+    g = unpack_bits(gpu_mask, nT)
+    for I in range(nT):
+        for J in range(nT):
+            blk = umt[I * 64 : min(L, I * 64 + 64), J * 64 : min(L, J * 64 + 64)]
+            ref = bool(blk.size) and bool((blk > 0).any())
+            if g[I, J] != ref:
+                near = blk.size and np.all((blk <= 0) | (blk < MARGIN)) and np.any(np.abs(blk) < MARGIN)
+                assert near, f"{where}: mask tile ({I},{J}) gpu={g[I, J]} oracle={ref}"
+
+
+def check_entmax(Q, K, V, alpha, causal, varlen=None, rows_of=None, where=""):
+    O, tau, mask = api.entmax_attn(Q, K, V, alpha=alpha, causal=causal, varlen=varlen)
+    torch.cuda.synchronize()
+    B, H, N, d = Q.shape
+    tol = TOL_F32 if Q.dtype == torch.float32 else TOL_BF16
+    lens = varlen.cpu().numpy() if varlen is not None else np.full(B, N)
+    O_, tau_, mask_ = f64(O), f64(tau), mask.cpu().numpy()
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(H):
+            q, k, v = f64(Q[b, h]), f64(K[b, h]), f64(V[b, h])
+            rows = np.arange(L) if rows_of is None else np.asarray(rows_of(b, h, L))
+            o_ref, t_ref, _ = oracle.entmax_attention_rows(q[rows], rows, k, v, L, alpha, causal)
+            assert_close(O_[b, h, rows], o_ref, tol, f"{where} O b{b} h{h}")
+            tau_close(tau_[b, h, rows], t_ref, f"{where} b{b} h{h}")
+            if rows_of is None:
+                assert np.all(O_[b, h, L:] == 0) and np.all(tau_[b, h, L:] == 0), f"{where}: padded rows"
+                _mask_ok(mask_[b, h], q, k, t_ref, L, alpha, causal, f"{where} b{b} h{h}")
+    return O, tau, mask
+
+
+def test_dense_entmax_128_f32():
+    w = WORKLOADS["dense_entmax_128"]
+    q, k, v, _ = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype="f32", device="cuda")
+    check_entmax(q, k, v, w.alpha, w.causal, where="f32 128")
+
+
+@pytest.mark.parametrize(
+    "B,H,N,d,alpha,causal,lens,scale,dtype",
+    [
+        (3, 2, 700, 64, 2.0, False, [700, 129, 65], 2.0, "bf16"),
+        (1, 2, 300, 64, 1.5, True, None, 1.0, "bf16"),
+        (2, 1, 200, 128, 1.5, False, [200, 77], 1.0, "bf16"),
+        (1, 1, 200, 64, 1.333, True, None, 1.0, "bf16"),
+        (2, 2, 190, 64, 2.0, True, [190, 1], 1.0, "f32"),
+        (1, 1, 256, 128, 1.5, False, None, 1.0, "f32"),
+    ],
+)
+def test_entmax_small(B, H, N, d, alpha, causal, lens, scale, dtype):
+    q, k, v, _ = dense_entmax_inputs(B, H, N, d, 50 + N, dtype=dtype, scale=scale, device="cuda")
+    varlen = torch.tensor(lens, dtype=torch.int32, device="cuda") if lens else None
+    check_entmax(q, k, v, alpha, causal, varlen, where=f"{dtype} N{N} a{alpha}")
+
+
+def test_entmax_deterministic():
+    q, k, v, _ = dense_entmax_inputs(2, 2, 900, 64, 4, dtype="bf16", scale=2.0, device="cuda")
+    a = api.entmax_attn(q, k, v, alpha=2.0, causal=False)
+    b = api.entmax_attn(q, k, v, alpha=2.0, causal=False)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_varlen_workload_sampled():
+    w = WORKLOADS["varlen_entmax"]
+    q, k, v, lens = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype=w.dtype, scale=w.scale,
+                                        varlen_range=w.varlen_range, device="cuda")
+    rng = np.random.default_rng(w.seed)
+
+    def rows_of(b, h, L):
+        if h not in (0, 7):
+            return np.array([], dtype=int)
+        return np.unique(np.concatenate([[0, 63, 64, L - 1], rng.integers(0, L, 10)]))
+
+    O, tau, mask = check_entmax(q, k, v, w.alpha, w.causal, lens, rows_of=rows_of, where="varlen")
+    # sparsity of the block mask is what makes block skipping pay
+    lens_ = lens.cpu().numpy()
+    nT = -(-w.N // 64)
+    m = mask.cpu().numpy()
+    for b in range(w.B):
+        t = -(-int(lens_[b]) // 64)
+        bits = unpack_bits(m[b, 0], nT)
+        assert bits[:t, :t].mean() < 0.5
+        assert not bits[t:].any() and not bits[:, t:].any()
