@@ -455,7 +455,7 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
       const float pq = sum16(dot8_bf16(kv, wq));
       const float pc = sum16(dot8_bf16(kv, wc));
       if (sub == 0) {
-        s_qk[w][key] = pq * a.inv_sqrt_d;
+        s_qk[w][key] = pq;  // raw q.k: the 1/sqrt(d) is inside zscale
         s_lc[w][key] = val ? pc * a.inv_sqrt_d : -INFINITY;
       }
     }

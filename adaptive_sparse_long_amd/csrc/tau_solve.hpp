@@ -72,7 +72,7 @@ __device__ __forceinline__ float tau_step(float tau, float f0, float f1, float f
   }
   const float den = 2.f * fp * fp - f * fpp;
   float nt = (den != 0.f) ? tau - 2.f * f * fp / den : 0.5f * (lo + hi);
-  if (!(nt > lo && nt < hi)) nt = 0.5f * (lo + hi);
+  if (!(nt >= lo && nt <= hi)) nt = 0.5f * (lo + hi);  // closed: a step that stays put is kept
   return nt;
 }
 

@@ -1,0 +1,391 @@
+"""Benchmark of the hierarchical adaptive sparse attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is the whole prefill of the 32K-token workload: chunk summaries,
+routing (scores, alpha-entmax tau, routed lists and priors) and sparse
+attention, 32 query heads over 8 KV heads, head_dim 128, bf16, chunk 64, causal,
+alpha 1.5, own chunk always attended, 1% needle keys scaled by 4 (synthetic,
+seeded). ``value`` is tokens/s of that step. The same run also times one decode
+step at 131072 cached tokens for a batch of 16 (routing against the summary
+cache plus split-KV attention over the routed chunks) and the varlen dense
+alpha-entmax attention workload; their figures are reported under "decode" and
+"entmax". Inputs are resident in HBM before timing starts. Kernel durations
+for the roofline come from HIP events recorded on the launch stream.
+
+Prints one JSON line on stdout.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from adaptive_sparse_long_amd import api  # noqa: E402
+from adaptive_sparse_long_amd.workloads import (  # noqa: E402
+    WORKLOADS,
+    decode_inputs,
+    dense_entmax_inputs,
+    routed_prefill_inputs,
+)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+C = 64
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def popcount32(x: torch.Tensor) -> torch.Tensor:
+    x = x.to(torch.int64) & 0xFFFFFFFF
+    x = x - ((x >> 1) & 0x55555555)
+    x = (x & 0x33333333) + ((x >> 2) & 0x33333333)
+    x = (x + (x >> 4)) & 0x0F0F0F0F
+    return ((x * 0x01010101) & 0xFFFFFFFF) >> 24
+
+
+class Timer:
+    """HIP events on the current (launch) stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+# --------------------------------------------------------------------------- prefill
+def prefill_flops(bits: torch.Tensor, N: int, d: int):
+    """Algorithmic flops (per row: 4 d x visible tokens of its routed chunks) and
+    executed flops (per 32-row wavefront block: 4 d x 32 x 64 per chunk that any
+    of its rows routed and that is not in its future)."""
+    B, Hq, _, W = bits.shape
+    n_slots = -(-N // C)
+    c = torch.arange(n_slots, device=bits.device)
+    on = ((bits[..., c // 32] >> (c % 32)) & 1).bool()  # [B, Hq, N, n_slots]
+    i = torch.arange(N, device=bits.device)
+    vis = torch.clamp(i[:, None] + 1 - c[None, :] * C, 0, C)  # causal visible tokens per (row, chunk)
+    alg = 4.0 * d * float((on * vis).sum())
+    rows = (N + 31) // 32
+    pad = rows * 32 - N
+    onp = torch.nn.functional.pad(on, (0, 0, 0, pad)).view(B, Hq, rows, 32, n_slots).any(dim=3)
+    own = torch.arange(rows, device=bits.device) * 32 // C
+    not_future = c[None, :] <= own[:, None]
+    execd = 4.0 * d * 32 * C * float((onp & not_future).sum())
+    dense = 2.0 * 2.0 * d * (N * (N + 1) / 2.0) * B * Hq
+    per_row = float(on.sum()) / (B * Hq * N)
+    return alg, execd, dense, per_row
+
+
+def bench_prefill(w, steps, warmup):
+    dev = torch.device("cuda")
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device=dev)
+    p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    n_c = -(-w.N // C)
+    S = torch.empty(w.B, w.Hkv, n_c, w.d, dtype=torch.float32, device=dev)
+    ws = torch.empty(api.workspace_size(w.B, w.Hq, w.Hkv, w.N, w.N, w.d, False, p), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(Q)
+    n_sum = w.N // C if w.causal else n_c
+    t_sum, t_route, t_attn = Timer(), Timer(), Timer()
+
+    def step(timed):
+        e = t_sum.start() if timed else None
+        api.summarize(K, cls, S, n_tokens=w.N, chunk_begin=0, chunk_end=n_sum, params=p)
+        if timed:
+            t_sum.stop(e)
+            e = t_route.start()
+        tau, bits, _ = api.route(Q, K, cls, S, p, with_bits=False, workspace=ws)
+        if timed:
+            t_route.stop(e)
+            e = t_attn.start()
+        api.sparse_attn_prefill(Q, K, V, ws, p, out=O)
+        if timed:
+            t_attn.stop(e)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    # work counts (outside the timed region)
+    _, bits, _ = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
+    alg, execd, dense, per_row = prefill_flops(bits, w.N, w.d)
+    ms_attn = t_attn.mean_ms()
+    res = {
+        "wall_ms": wall * 1e3,
+        "ms_summarize": t_sum.mean_ms(),
+        "ms_route": t_route.mean_ms(),
+        "ms_attention": ms_attn,
+        "alg_flops": alg,
+        "exec_flops": execd,
+        "dense_causal_flops": dense,
+        "active_chunk_frac_per_row": per_row,
+    }
+    del Q, K, V, S, ws, O, bits
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- decode
+def bench_decode(w, steps, warmup):
+    dev = torch.device("cuda")
+    q, Kc, Vc, cls, seqlens = decode_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, device=dev)
+    p = api.Params(alpha=w.alpha, estimate_diagonal=w.estimate_diagonal)
+    Lmax = Kc.shape[2]
+    S = torch.zeros(w.B, w.Hkv, -(-Lmax // C), w.d, dtype=torch.float32, device=dev)
+    api.summarize(Kc, cls, S, seqlens=seqlens, chunk_begin=0, chunk_end=Lmax // C, params=p)
+    ws = torch.empty(api.workspace_size(w.B, w.Hq, w.Hkv, 1, Lmax, w.d, True, p), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(q)
+    lengths = [int(x) for x in seqlens.cpu()]
+    # Infinity Cache (256 MB) holds the whole summary cache; evict it between steps
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    t_route, t_attn, t_step = Timer(), Timer(), Timer()
+
+    def step(timed):
+        e = t_step.start() if timed else None
+        e1 = t_route.start() if timed else None
+        api.route(q, Kc, cls, S, p, seqlens=seqlens, with_bits=False, workspace=ws)
+        if timed:
+            t_route.stop(e1)
+            e1 = t_attn.start()
+        api.sparse_attn_decode(q, Kc, Vc, seqlens, ws, p, out=O)
+        if timed:
+            t_attn.stop(e1)
+        done = sorted({n // C - 1 for n in lengths if n % C == 0})
+        for c in done:
+            api.summarize(Kc, cls, S, seqlens=seqlens, chunk_begin=c, chunk_end=c + 1, params=p)
+        if timed:
+            t_step.stop(e)
+
+    for _ in range(warmup):
+        flush.zero_()
+        step(False)
+    for _ in range(steps):
+        flush.zero_()
+        step(True)
+    torch.cuda.synchronize()
+    # chunks each (b, kv head) group read: union of its g heads' routed chunks
+    _, bits, _ = api.route(q, Kc, cls, S, p, seqlens=seqlens, with_bits=True, workspace=ws)
+    g = w.Hq // w.Hkv
+    union = bits.view(w.B, w.Hkv, g, -1)
+    acc = union[:, :, 0]
+    for j in range(1, g):
+        acc = acc | union[:, :, j]
+    counts = popcount32(acc).sum(dim=-1).flatten().cpu().numpy()
+    n_keys = w.N + 1
+    kv_bytes = 0.0
+    last_chunk = (n_keys - 1) // C
+    for cnt in counts:
+        # every listed chunk is full except the own (last) chunk, which has n_keys - last_chunk*C tokens
+        kv_bytes += ((cnt - 1) * C + (n_keys - last_chunk * C)) * w.d * 2 * 2
+    s_bytes = w.B * w.Hkv * (n_keys - 1) // C * w.d * 4
+    res = {
+        "us_per_step": t_step.mean_ms() * 1e3,
+        "us_route": t_route.mean_ms() * 1e3,
+        "us_attention": t_attn.mean_ms() * 1e3,
+        "kv_bytes": kv_bytes,
+        "summary_bytes": float(s_bytes),
+        "dense_kv_bytes": float(w.B * w.Hkv * n_keys * w.d * 2 * 2),
+        "union_chunk_frac": float(np.mean(counts)) / (last_chunk + 1),
+    }
+    del q, Kc, Vc, S, ws, O, flush
+    torch.cuda.empty_cache()
+    return res
+
+
+# --------------------------------------------------------------------------- entmax
+def bench_entmax(w, steps, warmup):
+    dev = torch.device("cuda")
+    q, k, v, lens = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype=w.dtype, scale=w.scale,
+                                        varlen_range=w.varlen_range, device=dev)
+    t = Timer()
+    for _ in range(warmup):
+        api.entmax_attn(q, k, v, alpha=w.alpha, causal=w.causal, varlen=lens)
+    for _ in range(steps):
+        e = t.start()
+        O, tau, mask = api.entmax_attn(q, k, v, alpha=w.alpha, causal=w.causal, varlen=lens)
+        t.stop(e)
+    ms = t.mean_ms()
+    L = lens.cpu().numpy().astype(np.float64)
+    qk_flops = float(np.sum(2.0 * L * L * w.d) * w.Hq)
+    nT = -(-w.N // 64)
+    c = torch.arange(nT, device=dev)
+    on = ((mask[..., c // 32] >> (c % 32)) & 1).bool()
+    tiles_on = float(on.sum())
+    tiles_all = float(np.sum(np.ceil(L / 64) ** 2) * w.Hq)
+    return {
+        "ms": ms,
+        "tokens_per_s": float(L.sum()) / (ms / 1e3),
+        "qk_flops": qk_flops,
+        "tflops_qk_pass": qk_flops / (ms / 1e3) / 1e12,
+        "nonnull_tile_frac": tiles_on / tiles_all,
+    }
+
+
+# --------------------------------------------------------------------------- CPU oracle
+def cpu_baseline(w, budget_s=20.0):
+    """The float64 oracle on host cores, on a random sample of query rows of the
+    prefill workload (all of their routing, and their attention), scaled to
+    tokens/s: one token is one row in each of the Hq query heads."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cpu")
+    op = oracle.DashParams(chunk_size=C, alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    rng = np.random.default_rng(w.seed)
+    g = w.Hq // w.Hkv
+    rows_done = 0
+    t0 = time.perf_counter()
+    summ_cache = {}
+    while time.perf_counter() - t0 < budget_s:
+        h = int(rng.integers(0, w.Hq))
+        hk = h // g
+        if hk not in summ_cache:
+            keys = K[0, hk].double().numpy()
+            summ_cache[hk] = (keys, V[0, hk].double().numpy(), cls[hk].double().numpy(),
+                              oracle.chunk_summaries(keys, cls[hk].double().numpy(), C, w.N))
+        keys, vals, clsv, summ = summ_cache[hk]
+        rows = np.sort(rng.integers(0, w.N, 16))
+        oracle.dash_rows(Q[0, h, rows].double().numpy(), rows, keys, vals, clsv, w.N, op, summ)
+        rows_done += rows.size
+    el = time.perf_counter() - t0
+    return {
+        "value": (rows_done / w.Hq) / el,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_done} random query rows (uniform positions, random heads) of the 32K prefill "
+                  f"workload incl. summaries of the KV heads touched, {el:.1f} s; tokens/s = rows / {w.Hq} / s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-entmax", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes "
+              "in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wp = WORKLOADS["routed_prefill_32k"]
+    log(f"prefill {wp.name}: steps={args.steps} warmup={args.warmup}")
+    pre = bench_prefill(wp, args.steps, args.warmup)
+    log(f"prefill done: {pre['wall_ms']:.3f} ms/step")
+    ms_step = pre["ms_summarize"] + pre["ms_route"] + pre["ms_attention"]
+    value = wp.N / (ms_step / 1e3)
+    ach = pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12
+    roof = {
+        "kernel": "k_sparse_prefill",
+        "bound": "mfma",
+        "achieved": ach,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": ach / PEAK_BF16_TFLOPS,
+        "traffic": None,
+        "executed_tflops": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
+        "executed_frac": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "alg_flops_per_launch": pre["alg_flops"],
+        "exec_flops_per_launch": pre["exec_flops"],
+        "ms_per_launch": pre["ms_attention"],
+    }
+    out = {
+        "metric": "sparse prefill tokens/s at 32K + decode us/step at 128K; % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wp.name,
+            "batch": wp.B, "q_heads": wp.Hq, "kv_heads": wp.Hkv, "seq_len": wp.N, "head_dim": wp.d,
+            "chunk_size": wp.chunk_size, "alpha": wp.alpha, "causal": wp.causal,
+            "estimate_diagonal": wp.estimate_diagonal, "needles": "1% keys x4", "seed": wp.seed,
+        },
+        "prefill": {
+            "ms_summarize": pre["ms_summarize"], "ms_route": pre["ms_route"], "ms_attention": pre["ms_attention"],
+            "wall_ms_per_step": pre["wall_ms"],
+            "active_chunk_frac_per_row": pre["active_chunk_frac_per_row"],
+            "exec_over_alg": pre["exec_flops"] / pre["alg_flops"],
+            "alg_over_dense": pre["alg_flops"] / pre["dense_causal_flops"],
+            "dense_equiv_tflops": pre["dense_causal_flops"] / (ms_step / 1e3) / 1e12,
+        },
+        "roofline": roof,
+    }
+    if not args.no_decode:
+        wd = WORKLOADS["decode_128k"]
+        log("decode 128k")
+        dec = bench_decode(wd, max(args.steps, 20), args.warmup)
+        gbs = (dec["kv_bytes"]) / (dec["us_attention"] / 1e6) / 1e9
+        step_bytes = dec["kv_bytes"] + dec["summary_bytes"]
+        out["decode"] = {
+            "workload": wd.name,
+            "us_per_step": dec["us_per_step"],
+            "us_route": dec["us_route"],
+            "us_attention": dec["us_attention"],
+            "union_chunk_frac": dec["union_chunk_frac"],
+            "step_GBps": step_bytes / (dec["us_per_step"] / 1e6) / 1e9,
+            "roofline": {
+                "kernel": "k_sparse_decode", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dec["kv_bytes"],
+            },
+        }
+    if not args.no_entmax:
+        we = WORKLOADS["varlen_entmax"]
+        log("entmax varlen")
+        ent = bench_entmax(we, args.steps, args.warmup)
+        out["entmax"] = {"workload": we.name, **ent,
+                         "roofline": {"kernel": "k_entmax_attn", "bound": "mfma", "achieved": ent["tflops_qk_pass"],
+                                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": ent["tflops_qk_pass"] / PEAK_BF16_TFLOPS}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
