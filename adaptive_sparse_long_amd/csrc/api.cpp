@@ -75,7 +75,7 @@ size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int 
   if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
   if (decode) return decode_layout(B, Hq, Hkv, Lmax, d).total;
   if (Nq <= 0 || Nq > Lmax) return 0;
-  return prefill_layout(B, Hq, Nq, p.causal != 0).total;
+  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0).total;
 }
 
 dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
@@ -124,7 +124,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
     return from_hip(launch_route_decode(a, stream));
   }
   if (Nq > Lmax) return DASH_ERR_INVALID_ARG;
-  const PrefillLayout L = prefill_layout(B, Hq, Nq, p.causal != 0);
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0);
   if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
   const int need_cap = p.causal ? Nq / kChunk : L.n_slots;
   if (s_cap < need_cap) return DASH_ERR_INVALID_ARG;
@@ -136,6 +136,8 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.counts = reinterpret_cast<int*>(ws + L.off_counts);
   a.lists = reinterpret_cast<int*>(ws + L.off_lists);
   a.bias = reinterpret_cast<float*>(ws + L.off_bias);
+  a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
+  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
   return from_hip(launch_route_prefill(a, stream));
 }
 
@@ -150,7 +152,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
   if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
-  const PrefillLayout L = prefill_layout(B, Hq, N, p.causal != 0);
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0);
   if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   const char* ws = static_cast<const char*>(workspace);

@@ -32,6 +32,12 @@ constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxi
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// v_exp_f32 / v_log_f32 (base 2) without the denormal range fix-ups of exp2f /
+// log2f: results below 2^-126 flush to zero, which is harmless for attention
+// weights and priors.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

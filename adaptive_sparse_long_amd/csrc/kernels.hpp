@@ -29,7 +29,7 @@ struct PrefillLayout {
   int n_tiles = 0;
   int n_slots = 0;        // chunk slots = ceil(N / 64)
   long long per_head = 0; // list slots per (b, head)
-  size_t off_counts = 0, off_lists = 0, off_bias = 0, total = 0;
+  size_t off_counts = 0, off_lists = 0, off_bias = 0, off_split = 0, total = 0;
 };
 
 __host__ __device__ inline long long prefill_tile_offset(int tile, int n_slots, bool causal) {
@@ -39,7 +39,8 @@ __host__ __device__ inline int prefill_tile_cap(int tile, int n_slots, bool caus
   return causal ? min(n_slots, 2 * tile + 2) : n_slots;
 }
 
-inline PrefillLayout prefill_layout(int B, int Hq, int N, bool causal) {
+// off_split: the summaries split into bf16 high and low parts, [B, Hkv, n_slots, d] each.
+inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool causal) {
   PrefillLayout L;
   L.n_tiles = (N + kTileRows - 1) / kTileRows;
   L.n_slots = (N + kChunk - 1) / kChunk;
@@ -49,7 +50,8 @@ inline PrefillLayout prefill_layout(int B, int Hq, int N, bool causal) {
   L.off_counts = 0;
   L.off_lists = align256(heads * L.n_tiles * sizeof(int));
   L.off_bias = L.off_lists + align256(heads * (size_t)L.per_head * sizeof(int));
-  L.total = L.off_bias + align256(heads * (size_t)L.per_head * kTileRows * sizeof(float));
+  L.off_split = L.off_bias + align256(heads * (size_t)L.per_head * kTileRows * sizeof(float));
+  L.total = L.off_split + align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
   return L;
 }
 
@@ -109,6 +111,9 @@ struct RouteArgs {
   int* counts;
   int* lists;
   float* bias;
+  // summaries split into bf16 high / low parts (prefill), [B, Hkv, n_slots, d] each
+  uint16_t* s_hi;
+  uint16_t* s_lo;
   // decode scratch
   float* z;
 };

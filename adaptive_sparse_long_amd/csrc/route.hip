@@ -64,6 +64,12 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 32;                // k-steps of the 16x16x32 MFMA
   constexpr int NW = (NB * 16 + 31) / 32;   // union words
+  // Split summaries of 64 chunks per stage, shared by the eight wavefronts:
+  // per chunk 128 high parts, 128 low parts and 8 bf16 of padding (a chunk
+  // stride of 132 dwords keeps eight consecutive lanes on distinct LDS banks).
+  constexpr int SROW = 2 * D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sS[2][64 * SROW];
+  __shared__ uint32_t s_wu[8][NW];          // per-wavefront union words
   __shared__ uint32_t s_union[NW];
   __shared__ int s_pre[NW + 1];
 
@@ -83,52 +89,95 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   const bool est = causal && a.est != 0;
   const int n_slots = a.n_slots;
   // complete-chunk candidates of this wavefront's rows
-  const int ncomp = causal ? cw : n_slots;
+  const int ncomp = wave_valid ? (causal ? cw : n_slots) : 0;
   const int nblk = (ncomp + 15) / 16;
   const int ncand = ncomp + (est ? 1 : 0);
-
-  if (threadIdx.x < NW) s_union[threadIdx.x] = 0u;
-
   const size_t bh = (size_t)b * a.Hq + h;
-  const uint16_t* Qb = a.Q + bh * (size_t)N * D;
-  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap * D;
+  const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
 
   // ---- q as A operand: row i0 + col, dims 32 s + 8 grp .. +7
   bf16x8 qa[NS];
   {
-    const int qi = i0 + col;
+    const int qi = min(i0 + col, N - 1);
+    const uint16_t* qp = a.Q + (bh * N + qi) * (size_t)D + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qa[s] = as_bf16x8(qi < N ? ldg16(Qb + (size_t)qi * D + 32 * s + 8 * grp) : zero4());
+    for (int s = 0; s < NS; ++s) qa[s] = as_bf16x8(ldg16(qp + 32 * s));
   }
 
-  // ---- routing scores in u units: u[blk][r] for chunk blk*16 + col, row grp*4 + r
+  // ---- routing scores in u units, u[blk][r]: chunk blk*16 + col, row grp*4 + r.
+  // Groups of four blocks (64 chunks) pass through LDS: all 512 threads load a
+  // group once (the next group's loads in flight while the current one is
+  // multiplied), then every wavefront reads its B operands from LDS.
   const float uscale = (a.alpha - 1.f) * a.zscale;
   float u[NB][4];
+  const int last_row = min(tile * kTileRows + kTileRows, N) - 1;
+  const int ncomp_wg = causal ? last_row / kChunk : n_slots;  // most chunks any wavefront scores
+  const int ngrp = (ncomp_wg + 63) / 64;
+  const int tid = threadIdx.x;
+  u32x4 gl[4];
+  auto load_grp = [&](int gi) {
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    if (wave_valid && blk < nblk) {
-      const int c = blk * 16 + col;
-      const bool cval = c < ncomp;
-      const float* sp = Sb + (size_t)c * D + 8 * grp;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 512 * k;  // 2048 segments of 16 bytes
+      const int ch = idx >> 5;        // chunk within the group
+      const int part = idx & 31;      // 0..15 high, 16..31 low
+      const int c = min(gi * 64 + ch, max(ncomp_wg - 1, 0));
+      const uint16_t* src = (part < 16 ? a.s_hi : a.s_lo) + sbase + (size_t)c * D + 8 * (part & 15);
+      gl[k] = ldg16(src);
+    }
+  };
+  auto store_grp = [&](int stage) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-        if (cval) {
-          x0 = *reinterpret_cast<const f32x4*>(sp + 32 * s);
-          x1 = *reinterpret_cast<const f32x4*>(sp + 32 * s + 4);
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 512 * k;
+      const int ch = idx >> 5;
+      const int part = idx & 31;
+      *reinterpret_cast<u32x4*>(&sS[stage][ch * SROW + (part < 16 ? 0 : D) + 8 * (part & 15)]) = gl[k];
+    }
+  };
+  if (ngrp > 0) {
+    load_grp(0);
+    store_grp(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int gi = 0; gi < (NB + 3) / 4; ++gi) {
+    if (gi < ngrp) {  // uniform over the workgroup
+      const bool more = gi + 1 < ngrp;
+      if (more) load_grp(gi + 1);
+      const uint16_t* base = &sS[gi & 1][col * SROW + 8 * grp];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int blk = gi * 4 + j;
+        if (blk < NB) {
+          if (blk < nblk) {
+            const uint16_t* bp = base + j * 16 * SROW;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              acc = mfma16x16x32(qa[s], *reinterpret_cast<const bf16x8*>(bp + 32 * s), acc);
+              acc = mfma16x16x32(qa[s], *reinterpret_cast<const bf16x8*>(bp + D + 32 * s), acc);
+            }
+            const bool cval = blk * 16 + col < ncomp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u[blk][r] = cval ? acc[r] * uscale : -INFINITY;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
+          }
         }
-        bf16x8 hi, lo;
-        split_hi_lo(x0, x1, hi, lo);
-        acc = mfma16x16x32(qa[s], hi, acc);
-        acc = mfma16x16x32(qa[s], lo, acc);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) u[blk][r] = cval ? acc[r] * uscale : -INFINITY;
+      if (more) store_grp((gi + 1) & 1);
+      __syncthreads();
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const int blk = gi * 4 + j;
+        if (blk < NB) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
+        }
+      }
     }
   }
 
@@ -149,13 +198,12 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     float lc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int key = kb * 16 + col;
-      const bool kval = cw * kChunk + key < N;
+      const int key = min(kb * 16 + col, N - 1 - cw * kChunk);  // stays inside the sequence
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       float part = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u32x4 kv = kval ? ldg16(kp + (size_t)key * D + 32 * s + 8 * grp) : zero4();
+        u32x4 kv = ldg16(kp + (size_t)key * D + 32 * s + 8 * grp);
         acc = mfma16x16x32(qa[s], as_bf16x8(kv), acc);
         part += dot8_bf16(kv, wc[s]);
       }
@@ -167,21 +215,16 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       const int pi = i0 + grp * 4 + r - cw * kChunk;  // position of the row in its chunk
       float mloc = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        if (kb * 16 + col <= pi) mloc = fmaxf(mloc, lc[kb]);
+      for (int kb = 0; kb < 4; ++kb) mloc = kb * 16 + col <= pi ? fmaxf(mloc, lc[kb]) : mloc;
       const float M = max16(mloc);
       float num = 0.f, den = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        if (kb * 16 + col <= pi) {
-          const float e = exp2f((lc[kb] - M) * kLog2e);
-          num = fmaf(e, qk[kb][r], num);
-          den += e;
-        }
+        const float e = kb * 16 + col <= pi ? fast_exp2((lc[kb] - M) * kLog2e) : 0.f;
+        num = fmaf(e, qk[kb][r], num);
+        den += e;
       }
-      num = sum16(num);
-      den = sum16(den);
-      ud[r] = (num / den) * uscale;
+      ud[r] = (sum16(num) / sum16(den)) * uscale;
     }
   }
 
@@ -189,7 +232,10 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   float tau[4];
   bool row_ok[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) row_ok[r] = wave_valid && (i0 + grp * 4 + r < N);
+  for (int r = 0; r < 4; ++r) {
+    row_ok[r] = wave_valid && (i0 + grp * 4 + r < N);
+    tau[r] = INFINITY;
+  }
   if (wave_valid && ncand > 0) {
     float lo[4], hi[4];
 #pragma unroll
@@ -202,11 +248,19 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       hi[r] = tau_upper(m, ncand, a.alpha);
       tau[r] = lo[r];
     }
+    // Only values above max u - 1 can carry weight (tau >= max u - 1): blocks
+    // holding none of them are left out of the iterations.
+    uint32_t live = 0u;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
+      live |= wave_any(any) ? (1u << blk) : 0u;
+    }
     for (int it = 0; it < a.n_iter; ++it) {
       float f0[4] = {0.f, 0.f, 0.f, 0.f}, f1[4] = {0.f, 0.f, 0.f, 0.f}, f2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        if (blk < nblk) {
+        if ((live >> blk) & 1u) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
         }
@@ -224,9 +278,6 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       }
       if (wave_all(conv)) break;
     }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) tau[r] = INFINITY;
   }
 
   // ---- tau output: lanes 0, 16, 32, 48 hold rows grp*4 .. +3
@@ -236,59 +287,76 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       if (row_ok[r]) a.tau[bh * (size_t)N + i0 + grp * 4 + r] = tau[r];
   }
 
-  // ---- routed flags and log2 weights
+  // ---- own chunk: routed (estimate) or always attended with weight 1
   bool dact[4];
   float lwd[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float td = ud[r] - tau[r];
     dact[r] = row_ok[r] && (est ? (td > 0.f) : causal);
-    lwd[r] = est ? ((row_ok[r] && td > 0.f) ? log2_prior<KIND>(td, a.beta) : -INFINITY)
-                 : (row_ok[r] ? 0.f : -INFINITY);
+    lwd[r] = !row_ok[r] ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   }
 
-  // ---- union of routed chunks over the 128 rows, and the per-row bitmask
-  // output (lanes 0..15 write row i0 + lane). Ballots run with all lanes active.
-  __syncthreads();  // s_union cleared
-  unsigned long long md[4];
+  // ---- this wavefront's union of routed chunks, one 16-bit half word per block
+  uint32_t wu[NW];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) md[r] = __ballot(dact[r]);
-  const bool write_bits = a.bits != nullptr && wave_valid && lane < 16 && i0 + lane < N;
-  const int rg = lane >> 2, rr = lane & 3;  // D-layout owner of row `lane`
-  const bool dl = ((rr == 0 ? md[0] : rr == 1 ? md[1] : rr == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
-  uint32_t* bdst = a.bits + ((bh * (size_t)N) + i0 + lane) * (size_t)a.bits_words;
+  for (int wd = 0; wd < NW; ++wd) wu[wd] = 0u;
 #pragma unroll
-  for (int wd = 0; wd < NW; ++wd) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int blk = 2 * wd + half;
-      if (blk < NB) {
-        unsigned long long mb[4];
-        bool any = false;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool act = row_ok[r] && (u[blk][r] - tau[r] > 0.f);
-          mb[r] = __ballot(act);
-          any = any || act;
-        }
-        const unsigned long long ma = __ballot(any);
-        const uint32_t m16 = (uint32_t)((ma | (ma >> 16) | (ma >> 32) | (ma >> 48)) & 0xffffull);
-        if (lane == 0 && m16) atomicOr(&s_union[blk >> 1], m16 << (16 * (blk & 1)));
-        const unsigned long long mr = rr == 0 ? mb[0] : rr == 1 ? mb[1] : rr == 2 ? mb[2] : mb[3];
-        word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
-      }
+  for (int blk = 0; blk < NB; ++blk) {
+    if (blk < nblk) {
+      const bool any = (row_ok[0] && u[blk][0] > tau[0]) || (row_ok[1] && u[blk][1] > tau[1]) ||
+                       (row_ok[2] && u[blk][2] > tau[2]) || (row_ok[3] && u[blk][3] > tau[3]);
+      const unsigned long long ma = __ballot(any);
+      const uint32_t m16 = (uint32_t)((ma | (ma >> 16) | (ma >> 32) | (ma >> 48)) & 0xffffull);
+      wu[blk >> 1] |= m16 << (16 * (blk & 1));
     }
-    if (causal && dl && (cw >> 5) == wd) word |= 1u << (cw & 31);
-    if (write_bits && wd < a.bits_words) bdst[wd] = word;
   }
-  if (write_bits)
-    for (int wd = NW; wd < a.bits_words; ++wd) bdst[wd] = 0u;
-  if (causal && wave_valid) {
-    const bool anyd = (md[0] | md[1] | md[2] | md[3]) != 0ull;
-    if (lane == 0 && anyd) atomicOr(&s_union[cw >> 5], 1u << (cw & 31));
+  if (causal && wave_any(dact[0] || dact[1] || dact[2] || dact[3])) {
+#pragma unroll
+    for (int wd = 0; wd < NW; ++wd) wu[wd] |= (cw >> 5) == wd ? (1u << (cw & 31)) : 0u;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int wd = 0; wd < NW; ++wd) s_wu[w][wd] = wu[wd];
   }
 
+  // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
+  if (a.bits != nullptr) {
+    unsigned long long md[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) md[r] = __ballot(dact[r]);
+    const bool write_bits = wave_valid && lane < 16 && i0 + lane < N;
+    const int rg = lane >> 2, rr = lane & 3;  // D-layout owner of row `lane`
+    const bool dl = ((rr == 0 ? md[0] : rr == 1 ? md[1] : rr == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
+    uint32_t* bdst = a.bits + ((bh * (size_t)N) + min(i0 + lane, N - 1)) * (size_t)a.bits_words;
+#pragma unroll
+    for (int wd = 0; wd < NW; ++wd) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int blk = 2 * wd + half;
+        if (blk < NB) {
+          unsigned long long mb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
+          const unsigned long long mr = rr == 0 ? mb[0] : rr == 1 ? mb[1] : rr == 2 ? mb[2] : mb[3];
+          word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
+        }
+      }
+      if (causal && dl && (cw >> 5) == wd) word |= 1u << (cw & 31);
+      if (write_bits && wd < a.bits_words) bdst[wd] = word;
+    }
+    if (write_bits)
+      for (int wd = NW; wd < a.bits_words; ++wd) bdst[wd] = 0u;
+  }
+
+  __syncthreads();
+  if (threadIdx.x < NW) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) v |= s_wu[ww][threadIdx.x];
+    s_union[threadIdx.x] = v;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     int acc = 0;
@@ -313,36 +381,53 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
 
   // ---- log2 weights of this wavefront's 16 rows for every listed chunk
-  if (wave_valid) {
-    float* bias = a.bias + toff * kTileRows + w * 16;
+  // (-inf where a row did not route the chunk, and for rows past N)
+  float* bias = a.bias + toff * kTileRows + w * 16 + grp * 4;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const int c = blk * 16 + col;
-      const uint32_t word = s_union[c >> 5];
-      if (((word >> (c & 31)) & 1u) && !(causal && c == cw)) {
-        const int pos = s_pre[c >> 5] + __popc(word & ((1u << (c & 31)) - 1u));
-        f32x4 v;
+  for (int blk = 0; blk < NB; ++blk) {
+    const uint32_t word = s_union[blk >> 1];
+    const int bit = 16 * (blk & 1) + col;
+    const int c = blk * 16 + col;
+    if (((word >> bit) & 1u) && !(causal && c == cw)) {
+      const int pos = s_pre[blk >> 1] + __popc(word & ((1u << bit) - 1u));
+      f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float t = u[blk][r] - tau[r];
-          v[r] = (row_ok[r] && t > 0.f) ? log2_prior<KIND>(t, a.beta) : -INFINITY;
-        }
-        *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows + grp * 4) = v;
+      for (int r = 0; r < 4; ++r) {
+        const float t = u[blk][r] - tau[r];
+        v[r] = (row_ok[r] && t > 0.f) ? log2_prior<KIND>(t, a.beta) : -INFINITY;
       }
+      *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows) = v;
     }
-    if (causal && col == 0) {
-      const uint32_t word = s_union[cw >> 5];
-      if ((word >> (cw & 31)) & 1u) {
-        const int pos = s_pre[cw >> 5] + __popc(word & ((1u << (cw & 31)) - 1u));
-        f32x4 v = {lwd[0], lwd[1], lwd[2], lwd[3]};
-        *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows + grp * 4) = v;
-      }
+  }
+  if (causal && col == 0) {
+    const uint32_t word = s_union[cw >> 5];
+    if ((word >> (cw & 31)) & 1u) {
+      const int pos = s_pre[cw >> 5] + __popc(word & ((1u << (cw & 31)) - 1u));
+      f32x4 v = {lwd[0], lwd[1], lwd[2], lwd[3]};
+      *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows) = v;
     }
-  } else {
-    // rows past N: every listed chunk gets -inf so the attention pass skips them
-    float* bias = a.bias + toff * kTileRows + w * 16;
-    const int cnt = s_pre[NW];
-    for (int pos = lane; pos < cnt * 16; pos += kWave) bias[(size_t)(pos >> 4) * kTileRows + (pos & 15)] = -INFINITY;
+  }
+}
+
+// Split the float32 summaries of the chunks the prefill routing reads into bf16
+// high parts and bf16 low parts (x - high), once per call.
+__global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need) {
+  constexpr int D = 128;
+  const size_t per_bh = (size_t)n_need * (D / 8);
+  const size_t total = (size_t)a.B * a.Hkv * per_bh;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t bh = i / per_bh;
+    const size_t rem = i % per_bh;
+    const size_t c = rem / (D / 8);
+    const int e8 = (int)(rem % (D / 8)) * 8;
+    const float* src = a.S + (bh * a.s_cap + c) * D + e8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    bf16x8 hi, lo;
+    split_hi_lo(x0, x1, hi, lo);
+    const size_t dst = (bh * a.n_slots + c) * D + e8;
+    *reinterpret_cast<bf16x8*>(a.s_hi + dst) = hi;
+    *reinterpret_cast<bf16x8*>(a.s_lo + dst) = lo;
   }
 }
 
@@ -463,7 +548,7 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
     const float lcv = s_lc[w][lane];
     const float qkv = s_qk[w][lane];
     const float M = wave_max(lcv);
-    const float e = (lcv > -INFINITY) ? exp2f((lcv - M) * kLog2e) : 0.f;
+    const float e = (lcv > -INFINITY) ? fast_exp2((lcv - M) * kLog2e) : 0.f;
     const float num = wave_sum(e * qkv);
     const float den = wave_sum(e);
     ud = (num / den) * a.zscale * am1;
@@ -568,6 +653,12 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
 // ============================================================================
 template <int KIND>
 static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
+  const int n_need = a.causal ? a.Nq / kChunk : a.n_slots;
+  if (n_need > 0) {
+    const size_t work = (size_t)a.B * a.Hkv * n_need * 16;
+    const int blocks = (int)((work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096);
+    hipLaunchKernelGGL(k_split_summaries, dim3(blocks), dim3(256), 0, stream, a, n_need);
+  }
   dim3 grid(a.n_tiles, a.Hq, a.B);
   const int nb = (a.n_slots + 15) / 16;
 #define DASH_RP(NBV)                                                                   \

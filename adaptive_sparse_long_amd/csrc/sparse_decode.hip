@@ -131,12 +131,12 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
       }
       mx = max16(mx);
       const float m_new = fmaxf(m_run[q], mx);
-      const float al = exp2f(m_run[q] - m_new);
+      const float al = fast_exp2(m_run[q] - m_new);
       m_run[q] = m_new;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float p = exp2f(x[kb] - m_new);
+        const float p = fast_exp2(x[kb] - m_new);
         ls += p;
         if (my_valid[q]) sP[w][(kb * 16 + col) * G + my_head[q]] = p;
       }
@@ -201,47 +201,47 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
     float M = kNegBig;
     for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, sM[ww][hh]);
     float o = 0.f;
-    for (int ww = 0; ww < 4; ++ww) o += sO[ww][hh][dd] * exp2f(sM[ww][hh] - M);
+    for (int ww = 0; ww < 4; ++ww) o += sO[ww][hh][dd] * fast_exp2(sM[ww][hh] - M);
     part[hh * (D + 2) + 2 + dd] = o;
     if (dd == 0) {
       float L = 0.f;
-      for (int ww = 0; ww < 4; ++ww) L += sL[ww][hh] * exp2f(sM[ww][hh] - M);
+      for (int ww = 0; ww < 4; ++ww) L += sL[ww][hh] * fast_exp2(sM[ww][hh] - M);
       part[hh * (D + 2)] = M;
       part[hh * (D + 2) + 1] = L;
     }
   }
 }
 
-// Merge the split partials of one (b, kv head) in split order and store O.
+// Merge the split partials of one (b, query head) in split order and store O:
+// one workgroup per head, one thread per dim.
 template <int G>
-__global__ __launch_bounds__(256) void k_decode_combine(DecodeAttnArgs a) {
+__global__ __launch_bounds__(128) void k_decode_combine(DecodeAttnArgs a) {
   constexpr int D = 128;
-  const int grp_id = blockIdx.x;
+  const int grp_id = blockIdx.x / G;
+  const int hh = blockIdx.x % G;
   const int b = grp_id / a.Hkv;
   const int hk = grp_id % a.Hkv;
+  const int dd = threadIdx.x;
   const int count = a.counts[grp_id];
   const int ns = (count + kDecodeSplit - 1) / kDecodeSplit;
-  const float* part = a.part + (size_t)grp_id * a.n_splits * G * (D + 2);
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int hh = i / D, dd = i % D;
-    float M = kNegBig;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, part[(s * G + hh) * (D + 2)]);
-    float L = 0.f, o = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float* p = part + (s * G + hh) * (D + 2);
-      const float e = exp2f(p[0] - M);
-      L = fmaf(p[1], e, L);
-      o = fmaf(p[2 + dd], e, o);
-    }
-    const float r = o / L;
-    a.O[((size_t)b * a.Hq + hk * G + hh) * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)r);
+  const float* part = a.part + (size_t)grp_id * a.n_splits * G * (D + 2) + hh * (D + 2);
+  constexpr int kStride = G * (D + 2);
+  float M = kNegBig;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * kStride]);
+  float L = 0.f, o = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* p = part + s * kStride;
+    const float e = fast_exp2(p[0] - M);
+    L = fmaf(p[1], e, L);
+    o = fmaf(p[2 + dd], e, o);
   }
+  a.O[((size_t)b * a.Hq + hk * G + hh) * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(o / L));
 }
 
 template <int G>
 static hipError_t decode_g(const DecodeAttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(k_sparse_decode<G>, dim3(a.n_splits, a.B * a.Hkv), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(k_decode_combine<G>, dim3(a.B * a.Hkv), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_decode_combine<G>, dim3(a.B * a.Hkv * G), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

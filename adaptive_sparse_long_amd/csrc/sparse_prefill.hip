@@ -98,14 +98,16 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   const int n_keys = N;
 
   u32x4 kr[4], vr[4];
+  // Keys past the sequence end are read from its last row instead (a valid
+  // address); their scores are masked, so their weights are exactly zero.
   auto load_chunk = [&](int c) {
     const int base = c * kChunk;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = base + k_row + 16 * r;
-      kr[r] = key < n_keys ? ldg16(Kb + (size_t)key * D + k_col) : u32x4{0, 0, 0, 0};
-      const int vkey = base + 4 * v_kg + r;
-      vr[r] = vkey < n_keys ? ldg16(Vb + (size_t)vkey * D + 8 * v_dg) : u32x4{0, 0, 0, 0};
+      const int key = min(base + k_row + 16 * r, n_keys - 1);
+      kr[r] = ldg16(Kb + (size_t)key * D + k_col);
+      const int vkey = min(base + 4 * v_kg + r, n_keys - 1);
+      vr[r] = ldg16(Vb + (size_t)vkey * D + 8 * v_dg);
     }
   };
   auto store_chunk = [&](int buf) {
@@ -165,37 +167,42 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
         s0 = mfma32x32x16(a0, qb[s], s0);
         s1 = mfma32x32x16(a1, qb[s], s1);
       }
-      // ---- bias, masks, online softmax (lane owns query qi; keys of block kb:
-      //      kb*32 + 8*(r/4) + 4*hi32 + r%4)
-      const bool diag = causal && c == cw;
-      const bool tail = !causal && (c + 1) * kChunk > n_keys;
-      float mx = kNegBig;
+      // ---- masks (own chunk: causal; non-causal last chunk: sequence end), only
+      //      in these uniform branches. Lane owns query qi; block kb holds keys
+      //      c*64 + 32 kb + 8 (r/4) + 4 hi32 + r%4.
+      if (causal && c == cw) {
+        const int lim = qi - c * kChunk;  // keys 0 .. lim of this chunk are visible
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
-        float x0 = fmaf(s0[r], sc, bias);
-        float x1 = fmaf(s1[r], sc, bias);
-        if (diag) {
-          if (c * kChunk + kk > qi) x0 = -INFINITY;
-          if (c * kChunk + 32 + kk > qi) x1 = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+          s0[r] = kk <= lim ? s0[r] : -INFINITY;
+          s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
         }
-        if (tail) {
-          if (c * kChunk + kk >= n_keys) x0 = -INFINITY;
-          if (c * kChunk + 32 + kk >= n_keys) x1 = -INFINITY;
+      } else if (!causal && (c + 1) * kChunk > n_keys) {
+        const int lim = n_keys - 1 - c * kChunk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+          s0[r] = kk <= lim ? s0[r] : -INFINITY;
+          s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
         }
-        s0[r] = x0;
-        s1[r] = x1;
-        mx = fmaxf(mx, fmaxf(x0, x1));
       }
-      mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+      // ---- online softmax in the exp2 domain. The row's bias is constant over
+      //      the chunk and the scale is positive, so the max is taken on raw
+      //      scores and each weight costs one fma and one v_exp.
+      float smax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, fmaxf(s0[r], s1[r]));
+      smax = max_xor32(smax);
+      const float m_new = fmaxf(m_run, fmaf(smax, sc, bias));
+      const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
+      const float off = bias - m_new;
       float ls = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2f(s0[r] - m_new);
-        s1[r] = exp2f(s1[r] - m_new);
+        s0[r] = fast_exp2(fmaf(s0[r], sc, off));
+        s1[r] = fast_exp2(fmaf(s1[r], sc, off));
         ls += s0[r] + s1[r];
       }
       l_run = fmaf(l_run, alpha, ls);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int it = 0; it < kMaxIt; ++it) {
-    float a = exp2f((logit[it] - mx) * kLog2e);  // 0 for masked rows
+    float a = fast_exp2((logit[it] - mx) * kLog2e);  // 0 for masked rows
     den += a;
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] = fmaf(a, bf16lo(kv[it][e]), acc[2 * e]);

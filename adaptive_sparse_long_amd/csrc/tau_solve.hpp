@@ -36,10 +36,10 @@ __device__ __forceinline__ void tau_terms(float u, float tau, float beta, float&
     f1 += (t > 0.f) ? 1.f : 0.f;
   } else {
     if (t > 0.f) {
-      const float lg = __log2f(t);
-      f0 += exp2f(beta * lg);
-      f1 += exp2f((beta - 1.f) * lg);
-      f2 += exp2f((beta - 2.f) * lg);
+      const float lg = fast_log2(t);
+      f0 += fast_exp2(beta * lg);
+      f1 += fast_exp2((beta - 1.f) * lg);
+      f2 += fast_exp2((beta - 2.f) * lg);
     }
   }
 }
@@ -83,7 +83,7 @@ __device__ __forceinline__ bool tau_converged(float old_tau, float new_tau) {
 // log2 of the prior max(t, 0)^beta for t > 0.
 template <int KIND>
 __device__ __forceinline__ float log2_prior(float t, float beta) {
-  const float lg = __log2f(t);
+  const float lg = fast_log2(t);
   if constexpr (KIND == 2) return 2.f * lg;
   else if constexpr (KIND == 1) return lg;
   else return beta * lg;
@@ -95,12 +95,12 @@ __device__ __forceinline__ float prior_of(float t, float beta) {
   const float p = fmaxf(t, 0.f);
   if constexpr (KIND == 2) return p * p;
   else if constexpr (KIND == 1) return p;
-  else return (t > 0.f) ? exp2f(beta * __log2f(t)) : 0.f;
+  else return (t > 0.f) ? fast_exp2(beta * fast_log2(t)) : 0.f;
 }
 
 // Right end of the bracket: max u - n^-(alpha - 1).
 __device__ __forceinline__ float tau_upper(float mx, int n, float alpha) {
-  return mx - exp2f(-(alpha - 1.f) * __log2f((float)n));
+  return mx - fast_exp2(-(alpha - 1.f) * fast_log2((float)n));
 }
 
 }  // namespace dash
