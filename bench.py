@@ -42,6 +42,14 @@ from adaptive_sparse_long_amd.workloads import (  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 C = 64
+CSRC = os.path.join(ROOT, "adaptive_sparse_long_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Sources each kernel's code depends on (a changed source voids its measured traffic).
+KERNEL_SOURCES = {
+    "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_entmax_attn": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+}
 
 
 def log(msg):
@@ -54,6 +62,42 @@ def popcount32(x: torch.Tensor) -> torch.Tensor:
     x = (x & 0x33333333) + ((x >> 2) & 0x33333333)
     x = (x + (x >> 4)) & 0x0F0F0F0F
     return ((x * 0x01010101) & 0xFFFFFFFF) >> 24
+
+
+def source_sha(kernel: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed PMC profile (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the plain-copy calibration), or None if the kernel source has
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def calibrate_copy(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling the PMC byte counters."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {reps} x {nbytes} bytes")
 
 
 class Timer:
@@ -298,6 +342,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-entmax", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes "
@@ -305,6 +351,8 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.calibrate_copy:
+        calibrate_copy()
     wp = WORKLOADS["routed_prefill_32k"]
     log(f"prefill {wp.name}: steps={args.steps} warmup={args.warmup}")
     pre = bench_prefill(wp, args.steps, args.warmup)
@@ -319,7 +367,7 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": ach / PEAK_BF16_TFLOPS,
-        "traffic": None,
+        "traffic": measured_traffic("k_sparse_prefill"),
         "executed_tflops": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
         "executed_frac": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "alg_flops_per_launch": pre["alg_flops"],
@@ -370,7 +418,8 @@ def main():
             "step_GBps": step_bytes / (dec["us_per_step"] / 1e6) / 1e9,
             "roofline": {
                 "kernel": "k_sparse_decode", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": dec["kv_bytes"],
+                "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("k_sparse_decode"),
+                "bytes_per_launch": dec["kv_bytes"],
             },
         }
     if not args.no_entmax:
@@ -380,7 +429,8 @@ def main():
         out["entmax"] = {"workload": we.name, **ent,
                          "roofline": {"kernel": "k_entmax_attn", "bound": "mfma", "achieved": ent["tflops_qk_pass"],
                                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": ent["tflops_qk_pass"] / PEAK_BF16_TFLOPS}}
+                                      "frac": ent["tflops_qk_pass"] / PEAK_BF16_TFLOPS,
+                                      "traffic": measured_traffic("k_entmax_attn")}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(wp)
