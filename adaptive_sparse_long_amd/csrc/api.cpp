@@ -27,6 +27,17 @@ bool g_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 dash_status from_hip(hipError_t e) { return e == hipSuccess ? DASH_OK : DASH_ERR_HIP; }
 
+// Compute units of the current device (sizes persistent grids).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+// Pool slots are addressed with 32 bits.
+bool prefill_pool_fits(int B, int Hq, int N) { return (long long)B * Hq * N * kCmSlots < (1ll << 32); }
+
 }  // namespace
 
 extern "C" {
@@ -125,7 +136,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   }
   if (Nq > Lmax) return DASH_ERR_INVALID_ARG;
   const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0);
-  if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (L.n_slots > kRoutePrefillMaxSlots || !prefill_pool_fits(B, Hq, Nq)) return DASH_ERR_UNSUPPORTED;
   const int need_cap = p.causal ? Nq / kChunk : L.n_slots;
   if (s_cap < need_cap) return DASH_ERR_INVALID_ARG;
   if (active_bits && bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
@@ -136,6 +147,18 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.counts = reinterpret_cast<int*>(ws + L.off_counts);
   a.lists = reinterpret_cast<int*>(ws + L.off_lists);
   a.bias = reinterpret_cast<float*>(ws + L.off_bias);
+  a.ccounts = reinterpret_cast<int*>(ws + L.off_ccounts);
+  a.clists = reinterpret_cast<int*>(ws + L.off_clists);
+  a.cw = reinterpret_cast<float*>(ws + L.off_cw);
+  a.ck = reinterpret_cast<uint16_t*>(ws + L.off_ck);
+  a.cbase = reinterpret_cast<int*>(ws + L.off_cbase);
+  a.cmp = reinterpret_cast<int*>(ws + L.off_cmp);
+  a.n_bhc = L.n_bhc;
+  a.pool = reinterpret_cast<unsigned long long*>(ws + L.off_pool);
+  a.pool_cap = L.pool_cap;
+  a.tbase = reinterpret_cast<uint32_t*>(ws + L.off_tbase);
+  a.rslot = reinterpret_cast<uint32_t*>(ws + L.off_rslot);
+  a.cmcnt = reinterpret_cast<uint16_t*>(ws + L.off_cmcnt);
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
   a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
   return from_hip(launch_route_prefill(a, stream));
@@ -143,7 +166,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
 
 dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V, dash_dtype dt,
                                      int B, int Hq, int Hkv, int N, int Lmax, int d,
-                                     dash_params p, void* O, const void* workspace,
+                                     dash_params p, void* O, void* workspace,
                                      size_t ws_bytes, hipStream_t stream) {
   if (!Q || !K || !V || !O || !workspace) return DASH_ERR_INVALID_ARG;
   if (B <= 0 || N <= 0 || Lmax <= 0 || N > Lmax || d <= 0 || !gqa_ok(Hq, Hkv))
@@ -153,9 +176,9 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   if (st != DASH_OK) return st;
   if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0);
-  if (L.n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (L.n_slots > kRoutePrefillMaxSlots || !prefill_pool_fits(B, Hq, N)) return DASH_ERR_UNSUPPORTED;
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
-  const char* ws = static_cast<const char*>(workspace);
+  char* ws = static_cast<char*>(workspace);
   PrefillAttnArgs a{};
   a.Q = static_cast<const uint16_t*>(Q);
   a.K = static_cast<const uint16_t*>(K);
@@ -170,6 +193,25 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.counts = reinterpret_cast<const int*>(ws + L.off_counts);
   a.lists = reinterpret_cast<const int*>(ws + L.off_lists);
   a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
+  a.ccounts = reinterpret_cast<const int*>(ws + L.off_ccounts);
+  a.clists = reinterpret_cast<const int*>(ws + L.off_clists);
+  a.cw = reinterpret_cast<const float*>(ws + L.off_cw);
+  a.ck = reinterpret_cast<const uint16_t*>(ws + L.off_ck);
+  a.cbase = reinterpret_cast<const int*>(ws + L.off_cbase);
+  a.cmp = reinterpret_cast<const int*>(ws + L.off_cmp);
+  a.cs = reinterpret_cast<int*>(ws + L.off_cs);
+  a.nitems = reinterpret_cast<int*>(ws + L.off_nitems);
+  a.items = reinterpret_cast<int2*>(ws + L.off_items);
+  a.recs = reinterpret_cast<int4*>(ws + L.off_recs);
+  a.n_bhc = L.n_bhc;
+  a.max_items = L.max_items;
+  a.pool_cap = L.pool_cap;
+  a.n_cu = device_cus();
+  a.tbase = reinterpret_cast<const uint32_t*>(ws + L.off_tbase);
+  a.rslot = reinterpret_cast<const uint32_t*>(ws + L.off_rslot);
+  a.cmcnt = reinterpret_cast<const uint16_t*>(ws + L.off_cmcnt);
+  a.pml = reinterpret_cast<float2*>(ws + L.off_pml);
+  a.po = reinterpret_cast<uint16_t*>(ws + L.off_po);
   return from_hip(launch_sparse_prefill(a, stream));
 }
 

@@ -62,6 +62,15 @@ __device__ __forceinline__ float round_bf16(float a) {
   return __uint_as_float(((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a)) << 16);
 }
 
+// --- fp16 <-> float (partial results) ----------------------------------------
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)a);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)b);
+  return lo | (hi << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)); }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+
 // --- cross-lane moves -------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

@@ -15,21 +15,49 @@ constexpr int kTileRows = 128;
 constexpr int kChunk = 64;
 // Routed chunks handled by one decode split (one workgroup, four wavefronts).
 constexpr int kDecodeSplit = 16;
+// Partial-result pool of the chunk-major kernel: kCmSlots slots per query row
+// on average. Every routed past chunk of a row is attended by the chunk-major
+// kernel into a slot of its own; the row's own chunk by the row-major kernel,
+// which merges the partials. A tile whose rows find the pool exhausted has all
+// its chunks attended row-major instead.
+constexpr int kCmSlots = 16;
+// Chunk-major work item: up to kCmBlocks blocks of 32 (row, chunk) pairs of one
+// (b, kv head, chunk).
+constexpr int kCmBlocks = 16;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
-// Prefill work lists, per (b, query head): for each 128-row tile, the union of
-// the chunks routed to any of its rows (ascending), and for each listed chunk
-// the 128 rows' log2 routing weights (-inf: chunk not attended by that row).
+// Prefill work lists, per (b, query head) and 128-row tile, each an ascending
+// list of chunk ids with, per listed chunk, one entry for each of the tile's
+// 128 rows:
+//   row-major list ("rm"): the row's own chunk (and, in a tile without pool
+//     slots, every routed chunk); entry = log2 weight (-inf: not attended);
+//   chunk-major list ("cm"): routed past chunks; entry = log2 weight and the
+//     partial slot it fills, as an offset from the tile's first slot.
 // Causal tile t can only list chunks 0 .. 2t+1, so tiles are packed in a
 // triangle: tile t starts at slot t*(t+1). Non-causal tiles hold n_slots each.
+// Per chunk-major list entry: the offset of its pairs among all pairs of its
+// chunk (cbase). Per (b, kv head, chunk) "bhc": the number of its pairs (cmp,
+// counted by the routing) and their start in the chunk-sorted pair records
+// (cs). Work items list (bhc, first block); recs hold one pair each.
+// Per tile: its first pool slot (tbase). Per row: its first slot (rslot) and
+// number of partials (cmcnt). Per slot: (max, sum) in float32 and the output
+// normalised by the sum in fp16, in the order [lane half][32-dim block][8
+// dims] that the kernels hold it in. pool: the slot allocation counter.
 // ---------------------------------------------------------------------------
 struct PrefillLayout {
   int n_tiles = 0;
   int n_slots = 0;        // chunk slots = ceil(N / 64)
   long long per_head = 0; // list slots per (b, head)
-  size_t off_counts = 0, off_lists = 0, off_bias = 0, off_split = 0, total = 0;
+  int n_bhc = 0;          // B * Hkv * n_slots
+  long long max_items = 0;
+  size_t off_counts = 0, off_lists = 0, off_bias = 0;          // row-major list
+  size_t off_ccounts = 0, off_clists = 0, off_cw = 0, off_ck = 0, off_cbase = 0;  // chunk-major list
+  size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0;  // chunk-major pairs
+  size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_pml = 0, off_po = 0;  // partials
+  long long pool_cap = 0;
+  size_t off_split = 0, total = 0;
 };
 
 __host__ __device__ inline long long prefill_tile_offset(int tile, int n_slots, bool causal) {
@@ -47,11 +75,34 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   const int t = L.n_tiles - 1;
   L.per_head = prefill_tile_offset(t, L.n_slots, causal) + prefill_tile_cap(t, L.n_slots, causal);
   const size_t heads = (size_t)B * Hq;
-  L.off_counts = 0;
-  L.off_lists = align256(heads * L.n_tiles * sizeof(int));
-  L.off_bias = L.off_lists + align256(heads * (size_t)L.per_head * sizeof(int));
-  L.off_split = L.off_bias + align256(heads * (size_t)L.per_head * kTileRows * sizeof(float));
-  L.total = L.off_split + align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
+  const size_t entries = heads * (size_t)L.per_head * kTileRows;
+  const size_t rows = heads * (size_t)N;
+  const size_t pairs = rows * kCmSlots;
+  L.pool_cap = (long long)pairs;
+  L.n_bhc = B * Hkv * L.n_slots;
+  L.max_items = (long long)((pairs + 32 * kCmBlocks - 1) / (32 * kCmBlocks)) + L.n_bhc;
+  size_t o = 0;
+  L.off_counts = o;  o += align256(heads * L.n_tiles * sizeof(int));
+  L.off_lists = o;   o += align256(heads * (size_t)L.per_head * sizeof(int));
+  L.off_bias = o;    o += align256(entries * sizeof(float));
+  L.off_ccounts = o; o += align256(heads * L.n_tiles * sizeof(int));
+  L.off_clists = o;  o += align256(heads * (size_t)L.per_head * sizeof(int));
+  L.off_cw = o;      o += align256(entries * sizeof(float));
+  L.off_ck = o;      o += align256(entries * sizeof(uint16_t));
+  L.off_cbase = o;   o += align256(heads * (size_t)L.per_head * sizeof(int));
+  L.off_cmp = o;     o += align256((size_t)L.n_bhc * sizeof(int));
+  L.off_cs = o;      o += align256((size_t)L.n_bhc * sizeof(int));
+  L.off_nitems = o;  o += align256(sizeof(int));
+  L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
+  L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
+  L.off_pool = o;    o += align256(sizeof(unsigned long long));
+  L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
+  L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
+  L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
+  L.off_pml = o;     o += align256(pairs * 2 * sizeof(float));
+  L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
+  L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
+  L.total = o;
   return L;
 }
 
@@ -105,12 +156,24 @@ struct RouteArgs {
   float* tau;
   uint32_t* bits;
   int bits_words;
-  // prefill lists
+  // prefill lists (row-major and chunk-major, see PrefillLayout)
   int n_tiles, n_slots;
   long long per_head;
   int* counts;
   int* lists;
   float* bias;
+  int* ccounts;
+  int* clists;
+  float* cw;
+  uint16_t* ck;
+  int* cbase;
+  int* cmp;  // zeroed by the summary split, counted by the routing
+  int n_bhc;
+  unsigned long long* pool;  // zeroed by the summary split
+  long long pool_cap;
+  uint32_t* tbase;
+  uint32_t* rslot;
+  uint16_t* cmcnt;
   // summaries split into bf16 high / low parts (prefill), [B, Hkv, n_slots, d] each
   uint16_t* s_hi;
   uint16_t* s_lo;
@@ -130,6 +193,25 @@ struct PrefillAttnArgs {
   const int* counts;
   const int* lists;
   const float* bias;
+  // chunk-major part
+  const int* ccounts;
+  const int* clists;
+  const float* cw;
+  const uint16_t* ck;
+  const int* cbase;
+  const int* cmp;
+  int* cs;
+  int* nitems;
+  int2* items;
+  int4* recs;
+  int n_bhc;
+  long long max_items, pool_cap;
+  int n_cu;
+  const uint32_t* tbase;
+  const uint32_t* rslot;
+  const uint16_t* cmcnt;
+  float2* pml;
+  uint16_t* po;
 };
 
 struct DecodeAttnArgs {
@@ -164,7 +246,7 @@ struct EntmaxAttnArgs {
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_route_decode(const RouteArgs& a, hipStream_t stream);
-hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream);
+hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream);  // plan, scatter, chunk-major, row-major + merge
 hipError_t launch_sparse_decode(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t stream);
 

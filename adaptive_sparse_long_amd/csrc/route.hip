@@ -20,6 +20,8 @@
 // KV head at once), then one workgroup per (b, kv head) solves tau for its g
 // query heads (one wavefront each, 32+ candidates per lane), takes the union of
 // their routed chunks and writes the list with g log2 priors per chunk.
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "tau_solve.hpp"
 
@@ -69,9 +71,14 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   // stride of 132 dwords keeps eight consecutive lanes on distinct LDS banks).
   constexpr int SROW = 2 * D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][64 * SROW];
-  __shared__ uint32_t s_wu[8][NW];          // per-wavefront union words
-  __shared__ uint32_t s_union[NW];
-  __shared__ int s_pre[NW + 1];
+  __shared__ uint32_t s_wu[8][NW];          // per-wavefront union words, row-major list
+  __shared__ uint32_t s_wc[8][NW];          // per-wavefront union words, chunk-major list
+  __shared__ uint32_t s_union[NW], s_cunion[NW];
+  __shared__ int s_pre[NW + 1], s_cpre[NW + 1];
+  __shared__ int s_ecnt[NW * 32];  // chunk-major entries: rows taking the chunk ...
+  __shared__ int s_cl[NW * 32];    // ... and the chunk
+  __shared__ int s_wtot[8];        // routed past chunks of each wavefront's rows
+  __shared__ long long s_tbase;    // the tile's first pool slot, -1: none
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -94,6 +101,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   const int ncand = ncomp + (est ? 1 : 0);
   const size_t bh = (size_t)b * a.Hq + h;
   const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
+  for (int e = threadIdx.x; e < NW * 32; e += blockDim.x) s_ecnt[e] = 0;
 
   // ---- q as A operand: row i0 + col, dims 32 s + 8 grp .. +7
   bf16x8 qa[NS];
@@ -297,27 +305,94 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     lwd[r] = !row_ok[r] ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   }
 
-  // ---- this wavefront's union of routed chunks, one 16-bit half word per block
-  uint32_t wu[NW];
-#pragma unroll
-  for (int wd = 0; wd < NW; ++wd) wu[wd] = 0u;
+  auto seg_of = [&](unsigned long long m) { return (uint32_t)(m >> (16 * grp)) & 0xffffu; };
+  const uint32_t below = (1u << col) - 1u;
+
+  // ---- pool slots: one per attended chunk (routed past chunks, then the own
+  // chunk) of every row of the tile, taken with one atomic; the slots of a row
+  // are consecutive, in chunk order. Rows are numbered (wavefront, row group,
+  // r) inside the tile.
+  int nrt[4] = {0, 0, 0, 0};  // routed past chunks
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
     if (blk < nblk) {
-      const bool any = (row_ok[0] && u[blk][0] > tau[0]) || (row_ok[1] && u[blk][1] > tau[1]) ||
-                       (row_ok[2] && u[blk][2] > tau[2]) || (row_ok[3] && u[blk][3] > tau[3]);
-      const unsigned long long ma = __ballot(any);
-      const uint32_t m16 = (uint32_t)((ma | (ma >> 16) | (ma >> 32) | (ma >> 48)) & 0xffffull);
-      wu[blk >> 1] |= m16 << (16 * (blk & 1));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nrt[r] += __popc(seg_of(__ballot(row_ok[r] && u[blk][r] > tau[r])));
+    }
+  }
+  int nsl[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) nsl[r] = nrt[r] + (dact[r] ? 1 : 0);
+  const int grp_tot = nsl[0] + nsl[1] + nsl[2] + nsl[3];
+  const int g0 = __builtin_amdgcn_readlane(grp_tot, 0), g1 = __builtin_amdgcn_readlane(grp_tot, 16);
+  const int g2 = __builtin_amdgcn_readlane(grp_tot, 32), g3 = __builtin_amdgcn_readlane(grp_tot, 48);
+  const int grp_pre = (grp > 0 ? g0 : 0) + (grp > 1 ? g1 : 0) + (grp > 2 ? g2 : 0);
+  if (lane == 0) s_wtot[w] = g0 + g1 + g2 + g3;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) tot += s_wtot[ww];
+    long long base = -1;
+    if (tot > 0) {
+      const unsigned long long got = atomicAdd(a.pool, (unsigned long long)tot);
+      base = got + (unsigned long long)tot <= (unsigned long long)a.pool_cap ? (long long)got : -1;
+    }
+    s_tbase = base;
+    a.tbase[bh * a.n_tiles + tile] = base >= 0 ? (uint32_t)base : 0u;
+  }
+  __syncthreads();
+  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  int wpre = 0;
+#pragma unroll
+  for (int ww = 0; ww < 8; ++ww) wpre += ww < w ? s_wtot[ww] : 0;
+  int roff[4];  // first slot of each row, from the tile's first slot
+  roff[0] = wpre + grp_pre;
+#pragma unroll
+  for (int r = 1; r < 4; ++r) roff[r] = roff[r - 1] + nsl[r - 1];
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row_ok[r]) {
+        const size_t ri = bh * (size_t)N + i0 + grp * 4 + r;
+        a.cmcnt[ri] = pooled ? (uint16_t)nsl[r] : (uint16_t)0;
+        a.rslot[ri] = pooled ? (uint32_t)(s_tbase + roff[r]) : 0u;
+      }
+  }
+
+  // pass 1: this wavefront's union of chunk-major and of row-major chunks
+  uint32_t wcm[NW], wrm[NW];
+#pragma unroll
+  for (int wd = 0; wd < NW; ++wd) {
+    wcm[wd] = 0u;
+    wrm[wd] = 0u;
+  }
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    if (blk < nblk) {
+      bool any = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) any = any || (row_ok[r] && u[blk][r] > tau[r]);
+      const unsigned long long mk = __ballot(any);
+      const uint32_t wbits = (uint32_t)((mk | (mk >> 16) | (mk >> 32) | (mk >> 48)) & 0xffffull) << (16 * (blk & 1));
+      if (pooled) wcm[blk >> 1] |= wbits;
+      else wrm[blk >> 1] |= wbits;
     }
   }
   if (causal && wave_any(dact[0] || dact[1] || dact[2] || dact[3])) {
 #pragma unroll
-    for (int wd = 0; wd < NW; ++wd) wu[wd] |= (cw >> 5) == wd ? (1u << (cw & 31)) : 0u;
+    for (int wd = 0; wd < NW; ++wd) {
+      const uint32_t own = (cw >> 5) == wd ? (1u << (cw & 31)) : 0u;
+      if (pooled) wcm[wd] |= own;
+      else wrm[wd] |= own;
+    }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int wd = 0; wd < NW; ++wd) s_wu[w][wd] = wu[wd];
+    for (int wd = 0; wd < NW; ++wd) {
+      s_wu[w][wd] = wrm[wd];
+      s_wc[w][wd] = wcm[wd];
+    }
   }
 
   // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
@@ -351,68 +426,132 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
 
   __syncthreads();
-  if (threadIdx.x < NW) {
+  if (threadIdx.x < 2 * NW) {
+    const int wd = threadIdx.x % NW;
     uint32_t v = 0;
+    if (threadIdx.x < NW) {
 #pragma unroll
-    for (int ww = 0; ww < 8; ++ww) v |= s_wu[ww][threadIdx.x];
-    s_union[threadIdx.x] = v;
+      for (int ww = 0; ww < 8; ++ww) v |= s_wu[ww][wd];
+      s_union[wd] = v;
+    } else {
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) v |= s_wc[ww][wd];
+      s_cunion[wd] = v;
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 || threadIdx.x == kWave) {
+    const bool cm = threadIdx.x != 0;
+    const uint32_t* un = cm ? s_cunion : s_union;
+    int* pre = cm ? s_cpre : s_pre;
     int acc = 0;
     for (int wd = 0; wd < NW; ++wd) {
-      s_pre[wd] = acc;
-      acc += __popc(s_union[wd]);
+      pre[wd] = acc;
+      acc += __popc(un[wd]);
     }
-    s_pre[NW] = acc;
-    a.counts[bh * a.n_tiles + tile] = acc;
+    pre[NW] = acc;
+    (cm ? a.ccounts : a.counts)[bh * a.n_tiles + tile] = acc;
   }
   __syncthreads();
 
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, n_slots, causal);
-  if (threadIdx.x < NW) {
-    uint32_t bits = s_union[threadIdx.x];
-    int pos = s_pre[threadIdx.x];
+  if (threadIdx.x < 2 * NW) {
+    const bool cm = threadIdx.x >= NW;
+    const int wd = threadIdx.x % NW;
+    uint32_t bits = cm ? s_cunion[wd] : s_union[wd];
+    int pos = cm ? s_cpre[wd] : s_pre[wd];
+    int* lst = (cm ? a.clists : a.lists) + toff;
     while (bits) {
       const int bpos = __ffs(bits) - 1;
-      a.lists[toff + pos++] = threadIdx.x * 32 + bpos;
+      if (cm) s_cl[pos] = wd * 32 + bpos;
+      lst[pos++] = wd * 32 + bpos;
       bits &= bits - 1u;
     }
   }
 
-  // ---- log2 weights of this wavefront's 16 rows for every listed chunk
-  // (-inf where a row did not route the chunk, and for rows past N)
-  float* bias = a.bias + toff * kTileRows + w * 16 + grp * 4;
+  // ---- pass 2: entries of this wavefront's 16 rows for every listed chunk
+  // (-inf where a row does not take the chunk through that list, and for rows
+  // past N); a chunk-major entry also names the row's slot for the chunk (the
+  // row's first slot plus the chunk's rank among the row's routed chunks)
+  const size_t ebase = (size_t)toff * kTileRows + w * 16 + grp * 4;
+  int run[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int blk = 0; blk < NB; ++blk) {
-    const uint32_t word = s_union[blk >> 1];
+    const uint32_t wr = s_union[blk >> 1];
+    const uint32_t wc = s_cunion[blk >> 1];
     const int bit = 16 * (blk & 1) + col;
     const int c = blk * 16 + col;
-    if (((word >> bit) & 1u) && !(causal && c == cw)) {
-      const int pos = s_pre[blk >> 1] + __popc(word & ((1u << bit) - 1u));
-      f32x4 v;
+    const bool own = causal && c == cw;  // written below
+    const bool in_rm = ((wr >> bit) & 1u) && !own;
+    const bool in_cm = ((wc >> bit) & 1u) && !own;
+    if (wave_any(in_rm || in_cm)) {
+      f32x4 vrm, vcm;
+      uint32_t koff[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float t = u[blk][r] - tau[r];
-        v[r] = (row_ok[r] && t > 0.f) ? log2_prior<KIND>(t, a.beta) : -INFINITY;
+        const bool act = row_ok[r] && t > 0.f;
+        const uint32_t seg = seg_of(__ballot(act));
+        const int rank = run[r] + __popc(seg & below);
+        run[r] += __popc(seg);
+        const float lw = act ? log2_prior<KIND>(t, a.beta) : -INFINITY;
+        vrm[r] = pooled ? -INFINITY : lw;
+        vcm[r] = pooled ? lw : -INFINITY;
+        koff[r] = (uint32_t)(roff[r] + rank) & 0xffffu;
       }
-      *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows) = v;
+      if (in_rm) {
+        const int pos = s_pre[blk >> 1] + __popc(wr & ((1u << bit) - 1u));
+        *reinterpret_cast<f32x4*>(a.bias + ebase + (size_t)pos * kTileRows) = vrm;
+      }
+      // rows of this wavefront taking chunk c through the chunk-major list
+      int ncm = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ncm += vcm[r] > -INFINITY ? 1 : 0;
+      const int ntot = (int)sum_xor32(sum_xor16((float)ncm));
+      if (in_cm) {
+        const int pos = s_cpre[blk >> 1] + __popc(wc & ((1u << bit) - 1u));
+        *reinterpret_cast<f32x4*>(a.cw + ebase + (size_t)pos * kTileRows) = vcm;
+        *reinterpret_cast<u32x2*>(a.ck + ebase + (size_t)pos * kTileRows) = u32x2{koff[0] | (koff[1] << 16), koff[2] | (koff[3] << 16)};
+        if (grp == 0 && ntot > 0) atomicAdd(&s_ecnt[pos], ntot);
+      }
     }
   }
+  // the own chunk's entries of this wavefront's rows (slot: after the past chunks)
   if (causal && col == 0) {
-    const uint32_t word = s_union[cw >> 5];
+    const uint32_t word = (pooled ? s_cunion : s_union)[cw >> 5];
     if ((word >> (cw & 31)) & 1u) {
-      const int pos = s_pre[cw >> 5] + __popc(word & ((1u << (cw & 31)) - 1u));
+      const int pos = (pooled ? s_cpre : s_pre)[cw >> 5] + __popc(word & ((1u << (cw & 31)) - 1u));
       f32x4 v = {lwd[0], lwd[1], lwd[2], lwd[3]};
-      *reinterpret_cast<f32x4*>(bias + (size_t)pos * kTileRows) = v;
+      if (pooled) {
+        *reinterpret_cast<f32x4*>(a.cw + ebase + (size_t)pos * kTileRows) = v;
+        uint32_t ko[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ko[r] = (uint32_t)(roff[r] + nrt[r]) & 0xffffu;
+        *reinterpret_cast<u32x2*>(a.ck + ebase + (size_t)pos * kTileRows) = u32x2{ko[0] | (ko[1] << 16), ko[2] | (ko[3] << 16)};
+        const int nd = (dact[0] ? 1 : 0) + (dact[1] ? 1 : 0) + (dact[2] ? 1 : 0) + (dact[3] ? 1 : 0);
+        if (nd > 0) atomicAdd(&s_ecnt[pos], nd);
+      } else {
+        *reinterpret_cast<f32x4*>(a.bias + ebase + (size_t)pos * kTileRows) = v;
+      }
     }
   }
+
+  // ---- reserve each chunk-major entry's pairs among all pairs of its chunk
+  __syncthreads();
+  const int ncm_entries = s_cpre[NW];
+  int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
+  for (int e = threadIdx.x; e < ncm_entries; e += blockDim.x)
+    a.cbase[toff + e] = atomicAdd(&cmp[s_cl[e]], s_ecnt[e]);
 }
 
 // Split the float32 summaries of the chunks the prefill routing reads into bf16
-// high parts and bf16 low parts (x - high), once per call.
+// high parts and bf16 low parts (x - high), once per call; also clears the
+// per-chunk pair counters and the pool slot counter.
 __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need) {
   constexpr int D = 128;
+  // the per-chunk pair counters the routing adds to start from zero
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_bhc; i += gridDim.x * blockDim.x) a.cmp[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.pool = 0ull;
   const size_t per_bh = (size_t)n_need * (D / 8);
   const size_t total = (size_t)a.B * a.Hkv * per_bh;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
@@ -463,15 +602,18 @@ __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
     }
   }
   const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap * D;
+  f32x4 sva[2][4];  // both passes' loads issued before any arithmetic
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int c = min(c0 + pass * 8 + (lane >> 3), ncomp - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sva[pass][k] = *reinterpret_cast<const f32x4*>(Sb + (size_t)c * D + 32 * k + 4 * sub);
+  }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int c = c0 + pass * 8 + (lane >> 3);
     const bool val = c < ncomp;
-    f32x4 sv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      sv[k] = val ? *reinterpret_cast<const f32x4*>(Sb + (size_t)c * D + 32 * k + 4 * sub)
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4* sv = sva[pass];
     float mine = 0.f;
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -654,9 +796,9 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
 template <int KIND>
 static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
   const int n_need = a.causal ? a.Nq / kChunk : a.n_slots;
-  if (n_need > 0) {
-    const size_t work = (size_t)a.B * a.Hkv * n_need * 16;
-    const int blocks = (int)((work + 255) / 256 < 4096 ? (work + 255) / 256 : 4096);
+  {
+    const size_t work = std::max((size_t)a.B * a.Hkv * n_need * 16, (size_t)a.n_bhc);
+    const int blocks = (int)std::min<size_t>((work + 255) / 256, 4096);
     hipLaunchKernelGGL(k_split_summaries, dim3(blocks), dim3(256), 0, stream, a, n_need);
   }
   dim3 grid(a.n_tiles, a.Hq, a.B);

@@ -226,14 +226,30 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeAttnArgs a) {
   const int ns = (count + kDecodeSplit - 1) / kDecodeSplit;
   const float* part = a.part + (size_t)grp_id * a.n_splits * G * (D + 2) + hh * (D + 2);
   constexpr int kStride = G * (D + 2);
-  float M = kNegBig;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * kStride]);
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* p = part + s * kStride;
-    const float e = fast_exp2(p[0] - M);
-    L = fmaf(p[1], e, L);
-    o = fmaf(p[2 + dd], e, o);
+  // one pass with a running max; eight splits' loads in flight per step
+  float M = kNegBig, L = 0.f, o = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float pm[8], pl[8], po[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float* p = part + min(s0 + j, ns - 1) * kStride;
+      pm[j] = s0 + j < ns ? p[0] : kNegBig;
+      pl[j] = p[1];
+      po[j] = p[2 + dd];
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, pm[j]);
+    const float a = fast_exp2(M - Mn);
+    L *= a;
+    o *= a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = s0 + j < ns ? fast_exp2(pm[j] - Mn) : 0.f;
+      L = fmaf(pl[j], e, L);
+      o = fmaf(po[j], e, o);
+    }
+    M = Mn;
   }
   a.O[((size_t)b * a.Hq + hk * G + hh) * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(o / L));
 }

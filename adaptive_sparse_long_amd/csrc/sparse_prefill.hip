@@ -22,6 +22,8 @@
 // rows routed, so executed work follows 32-row unions, not 128-row ones.
 // Workgroups are issued longest-tile first, and the g query heads sharing a KV
 // head are placed on the same XCD so their chunk reads share that XCD's L2.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace dash {
@@ -52,217 +54,575 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
 
-  // ---- work unit: (tile, b, kv head), heaviest tiles first; the g heads of a
-  // unit get workgroup ids that are equal modulo 8 (same XCD)
+  // ---- work units (tile, b, kv head) x g query heads, walked by a persistent
+  // grid whose size is a multiple of 8; the g heads of a unit get work ids that
+  // are equal modulo 8 (same XCD)
   const int g = a.g;
   const int n_units = a.n_tiles * a.B * a.Hkv;
-  const int idx = blockIdx.x;
-  const int grp8 = idx / (8 * g);
-  const int rem = idx % (8 * g);
-  const int gh = rem / 8;
-  const int unit = grp8 * 8 + rem % 8;
-  if (unit >= n_units) return;
-  const int tile = a.n_tiles - 1 - unit / (a.B * a.Hkv);
-  const int bhk = unit % (a.B * a.Hkv);
-  const int b = bhk / a.Hkv;
-  const int hk = bhk % a.Hkv;
-  const int h = hk * g + gh;
-  const size_t bh = (size_t)b * a.Hq + h;
-  const int N = a.N;
-  const bool causal = a.causal != 0;
+  const int n_work = ((n_units + 7) / 8) * 8 * g;
+  for (int idx = blockIdx.x; idx < n_work; idx += gridDim.x) {
+    const int grp8 = idx / (8 * g);
+    const int rem = idx % (8 * g);
+    const int gh = rem / 8;
+    const int unit = grp8 * 8 + rem % 8;
+    if (unit >= n_units) continue;
+    const int tile = unit / (a.B * a.Hkv);
+    const int bhk = unit % (a.B * a.Hkv);
+    const int b = bhk / a.Hkv;
+    const int hk = bhk % a.Hkv;
+    const int h = hk * g + gh;
+    const size_t bh = (size_t)b * a.Hq + h;
+    const int N = a.N;
+    const bool causal = a.causal != 0;
 
-  const int count = a.counts[bh * a.n_tiles + tile];
-  const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, causal);
-  const int* list = a.lists + toff;
-  const float* biasp = a.bias + toff * kTileRows + w * 32 + (lane & 31);
+    const int count = a.counts[bh * a.n_tiles + tile];
+    if (count == 0) continue;  // every chunk of the tile went chunk-major
+    const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, causal);
+    const int* list = a.lists + toff;
+    const float* biasp = a.bias + toff * kTileRows + w * 32 + (lane & 31);
 
-  const int row0 = tile * kTileRows + w * 32;
-  const int cw = row0 / kChunk;
-  const int qi = row0 + (lane & 31);
-  const int hi32 = lane >> 5;
+    const int row0 = tile * kTileRows + w * 32;
+    const int cw = row0 / kChunk;
+    const int qi = row0 + (lane & 31);
+    const int hi32 = lane >> 5;
 
-  // Q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
-  bf16x8 qb[NS];
-  {
-    const uint16_t* qp = a.Q + (bh * N + qi) * (size_t)D + 8 * hi32;
+    // Q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
+    bf16x8 qb[NS];
+    {
+      const uint16_t* qp = a.Q + (bh * N + qi) * (size_t)D + 8 * hi32;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qb[s] = as_bf16x8(qi < N ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0});
-  }
-
-  const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-  const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-  // staging roles: K rows t/16 + 16 r at dims (t%16)*8; V keys 4 (t%16) + r at dims 8 (t/16)
-  const int k_row = tid >> 4, k_col = (tid & 15) * 8;
-  const int v_kg = tid & 15, v_dg = tid >> 4;
-  const int n_keys = N;
-
-  u32x4 kr[4], vr[4];
-  // Keys past the sequence end are read from its last row instead (a valid
-  // address); their scores are masked, so their weights are exactly zero.
-  auto load_chunk = [&](int c) {
-    const int base = c * kChunk;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = min(base + k_row + 16 * r, n_keys - 1);
-      kr[r] = ldg16(Kb + (size_t)key * D + k_col);
-      const int vkey = min(base + 4 * v_kg + r, n_keys - 1);
-      vr[r] = ldg16(Vb + (size_t)vkey * D + 8 * v_dg);
+      for (int s = 0; s < NS; ++s)
+        qb[s] = as_bf16x8(qi < N ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0});
     }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 16 * r) * KROW + k_col]) = kr[r];
-    uint16_t* vt = &sV[buf][(8 * v_dg) * VROW + 4 * v_kg];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims 8 v_dg + 2e (low halves) and + 2e + 1 (high halves), keys 4 v_kg .. +3
-      u32x2 lo2 = {perm_lo(vr[0][e], vr[1][e]), perm_lo(vr[2][e], vr[3][e])};
-      u32x2 hi2 = {perm_hi(vr[0][e], vr[1][e]), perm_hi(vr[2][e], vr[3][e])};
-      *reinterpret_cast<u32x2*>(vt + (2 * e) * VROW) = lo2;
-      *reinterpret_cast<u32x2*>(vt + (2 * e + 1) * VROW) = hi2;
-    }
-  };
 
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
-  const float sc = a.scale_log2;
+    const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+    const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+    // staging roles: K rows t/16 + 16 r at dims (t%16)*8; V keys 4 (t%16) + r at dims 8 (t/16)
+    const int k_row = tid >> 4, k_col = (tid & 15) * 8;
+    const int v_kg = tid & 15, v_dg = tid >> 4;
+    const int n_keys = N;
 
-  float bias_next = 0.f;
-  if (count > 0) {
-    load_chunk(list[0]);
-    bias_next = biasp[0];
-    store_chunk(0);
-  }
-  __syncthreads();
+    u32x4 kr[4], vr[4];
+    // Keys past the sequence end are read from its last row instead (a valid
+    // address); their scores are masked, so their weights are exactly zero.
+    auto load_chunk = [&](int c) {
+      const int base = c * kChunk;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = min(base + k_row + 16 * r, n_keys - 1);
+        kr[r] = ldg16(Kb + (size_t)key * D + k_col);
+        const int vkey = min(base + 4 * v_kg + r, n_keys - 1);
+        vr[r] = ldg16(Vb + (size_t)vkey * D + 8 * v_dg);
+      }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 16 * r) * KROW + k_col]) = kr[r];
+      uint16_t* vt = &sV[buf][(8 * v_dg) * VROW + 4 * v_kg];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // dims 8 v_dg + 2e (low halves) and + 2e + 1 (high halves), keys 4 v_kg .. +3
+        u32x2 lo2 = {perm_lo(vr[0][e], vr[1][e]), perm_lo(vr[2][e], vr[3][e])};
+        u32x2 hi2 = {perm_hi(vr[0][e], vr[1][e]), perm_hi(vr[2][e], vr[3][e])};
+        *reinterpret_cast<u32x2*>(vt + (2 * e) * VROW) = lo2;
+        *reinterpret_cast<u32x2*>(vt + (2 * e + 1) * VROW) = hi2;
+      }
+    };
 
-  for (int it = 0; it < count; ++it) {
-    const int buf = it & 1;
-    const int c = list[it];
-    const float bias = bias_next;
-    const bool more = it + 1 < count;
-    if (more) {
-      load_chunk(list[it + 1]);
-      bias_next = biasp[(size_t)(it + 1) * kTileRows];
-    }
-    const bool skip = (causal && c > cw) || wave_all(bias == -INFINITY);
-    if (!skip) {
-      // ---- S^T = K Q^T
-      f32x16 s0, s1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = 0.f;
-        s1[r] = 0.f;
-      }
-      const uint16_t* ka = &sK[buf][(lane & 31) * KROW + 8 * hi32];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ka + 16 * s);
-        bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ka + 32 * KROW + 16 * s);
-        s0 = mfma32x32x16(a0, qb[s], s0);
-        s1 = mfma32x32x16(a1, qb[s], s1);
-      }
-      // ---- masks (own chunk: causal; non-causal last chunk: sequence end), only
-      //      in these uniform branches. Lane owns query qi; block kb holds keys
-      //      c*64 + 32 kb + 8 (r/4) + 4 hi32 + r%4.
-      if (causal && c == cw) {
-        const int lim = qi - c * kChunk;  // keys 0 .. lim of this chunk are visible
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
-          s0[r] = kk <= lim ? s0[r] : -INFINITY;
-          s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
-        }
-      } else if (!causal && (c + 1) * kChunk > n_keys) {
-        const int lim = n_keys - 1 - c * kChunk;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
-          s0[r] = kk <= lim ? s0[r] : -INFINITY;
-          s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
-        }
-      }
-      // ---- online softmax in the exp2 domain. The row's bias is constant over
-      //      the chunk and the scale is positive, so the max is taken on raw
-      //      scores and each weight costs one fma and one v_exp.
-      float smax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, fmaxf(s0[r], s1[r]));
-      smax = max_xor32(smax);
-      const float m_new = fmaxf(m_run, fmaf(smax, sc, bias));
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      const float off = bias - m_new;
-      float ls = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = fast_exp2(fmaf(s0[r], sc, off));
-        s1[r] = fast_exp2(fmaf(s1[r], sc, off));
-        ls += s0[r] + s1[r];
-      }
-      l_run = fmaf(l_run, alpha, ls);
-      if (wave_any(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      // ---- P^T as B operands: k-step (kb, hh) takes registers 8 hh .. 8 hh + 7
-      bf16x8 pb[4];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 p0, p1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p0[e] = pack_bf16x2(s0[8 * hh + 2 * e], s0[8 * hh + 2 * e + 1]);
-          p1[e] = pack_bf16x2(s1[8 * hh + 2 * e], s1[8 * hh + 2 * e + 1]);
-        }
-        pb[hh] = as_bf16x8(p0);
-        pb[2 + hh] = as_bf16x8(p1);
-      }
-      // ---- O^T += V^T P^T; V^T row = dim, keys kb*32 + 16 hh + 4 hi32 + {0..3, 8..11}
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vrow = &sV[buf][(32 * db + (lane & 31)) * VROW + 4 * hi32];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int k0 = (ks >> 1) * 32 + (ks & 1) * 16;
-          u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
-          u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
-          u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = mfma32x32x16(as_bf16x8(va), pb[ks], o[db]);
-        }
-      }
-    }
-    if (more) store_chunk(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- normalise and store O (lane: query qi, dims 32 db + 8 (r/4) + 4 hi32 + r%4)
-  const float l_tot = sum_xor32(l_run);
-  if (qi < N) {
-    const float inv = 1.f / l_tot;
-    uint16_t* op = a.O + (bh * N + qi) * (size_t)D + 4 * hi32;
+    f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        u32x2 v = {pack_bf16x2(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv),
-                   pack_bf16x2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * q4) = v;
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    float m_run = kNegBig, l_run = 0.f;
+    const float sc = a.scale_log2;
+
+    float bias_next = 0.f;
+    if (count > 0) {
+      load_chunk(list[0]);
+      bias_next = biasp[0];
+      store_chunk(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < count; ++it) {
+      const int buf = it & 1;
+      const int c = list[it];
+      const float bias = bias_next;
+      const bool more = it + 1 < count;
+      if (more) {
+        load_chunk(list[it + 1]);
+        bias_next = biasp[(size_t)(it + 1) * kTileRows];
       }
+      const bool skip = (causal && c > cw) || wave_all(bias == -INFINITY);
+      if (!skip) {
+        // ---- S^T = K Q^T
+        f32x16 s0, s1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = 0.f;
+          s1[r] = 0.f;
+        }
+        const uint16_t* ka = &sK[buf][(lane & 31) * KROW + 8 * hi32];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ka + 16 * s);
+          bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ka + 32 * KROW + 16 * s);
+          s0 = mfma32x32x16(a0, qb[s], s0);
+          s1 = mfma32x32x16(a1, qb[s], s1);
+        }
+        // ---- masks (own chunk: causal; non-causal last chunk: sequence end), only
+        //      in these uniform branches. Lane owns query qi; block kb holds keys
+        //      c*64 + 32 kb + 8 (r/4) + 4 hi32 + r%4.
+        if (causal && c == cw) {
+          const int lim = qi - c * kChunk;  // keys 0 .. lim of this chunk are visible
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+            s0[r] = kk <= lim ? s0[r] : -INFINITY;
+            s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
+          }
+        } else if (!causal && (c + 1) * kChunk > n_keys) {
+          const int lim = n_keys - 1 - c * kChunk;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+            s0[r] = kk <= lim ? s0[r] : -INFINITY;
+            s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
+          }
+        }
+        // ---- online softmax in the exp2 domain. The row's bias is constant over
+        //      the chunk and the scale is positive, so the max is taken on raw
+        //      scores and each weight costs one fma and one v_exp.
+        float smax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, fmaxf(s0[r], s1[r]));
+        smax = max_xor32(smax);
+        const float m_new = fmaxf(m_run, fmaf(smax, sc, bias));
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        const float off = bias - m_new;
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = fast_exp2(fmaf(s0[r], sc, off));
+          s1[r] = fast_exp2(fmaf(s1[r], sc, off));
+          ls += s0[r] + s1[r];
+        }
+        l_run = fmaf(l_run, alpha, ls);
+        if (wave_any(alpha != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+        // ---- P^T as B operands: k-step (kb, hh) takes registers 8 hh .. 8 hh + 7
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          u32x4 p0, p1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p0[e] = pack_bf16x2(s0[8 * hh + 2 * e], s0[8 * hh + 2 * e + 1]);
+            p1[e] = pack_bf16x2(s1[8 * hh + 2 * e], s1[8 * hh + 2 * e + 1]);
+          }
+          pb[hh] = as_bf16x8(p0);
+          pb[2 + hh] = as_bf16x8(p1);
+        }
+        // ---- O^T += V^T P^T; V^T row = dim, keys kb*32 + 16 hh + 4 hi32 + {0..3, 8..11}
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint16_t* vrow = &sV[buf][(32 * db + (lane & 31)) * VROW + 4 * hi32];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = (ks >> 1) * 32 + (ks & 1) * 16;
+            u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
+            u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+            u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+            o[db] = mfma32x32x16(as_bf16x8(va), pb[ks], o[db]);
+          }
+        }
+      }
+      if (more) store_chunk(buf ^ 1);
+      __syncthreads();
+    }
+
+    // ---- normalise and store O (lane: query qi, dims 32 db + 8 (r/4) + 4 hi32 + r%4)
+    const float l_tot = sum_xor32(l_run);
+    if (qi < N) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = a.O + (bh * N + qi) * (size_t)D + 4 * hi32;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 v = {pack_bf16x2(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv),
+                     pack_bf16x2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * q4) = v;
+        }
+    }
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunk-major part. Every (query head, row) pair that routed a past chunk c
+// (in a tile that got pool slots) is attended against c alone, 32 pairs per
+// MFMA block, and leaves a partial result in its pool slot:
+//   1. k_cm_plan (one workgroup): prefix sums of the per-chunk pair counts that
+//      the routing left give every (b, kv head, chunk) its start among all
+//      pairs, and its blocks are cut into work items of up to kCmBlocks blocks;
+//   2. k_cm_scatter: every chunk-major list entry copies its pairs into the
+//      chunk-sorted records (row and head in group, pool slot, log2 weight);
+//   3. k_prefill_cm: a persistent grid walks the work items in (b, kv head,
+//      chunk) order; per item the K and V of its chunk are staged once in LDS
+//      and each wavefront attends whole blocks of 32 pairs, gathering their
+//      query rows from Q.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kCmWgPerCu = 3;  // resident chunk-major workgroups per CU
+
+// Exclusive prefix sum over a 1024-thread workgroup; returns the total.
+// s_tmp holds 16 ints and may be reused once the call returns.
+__device__ int block_excl_scan_1024(int v, int* s_tmp, int& excl) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    x += lane >= off ? y : 0;
+  }
+  if (lane == kWave - 1) s_tmp[w] = x;
+  __syncthreads();
+  int wpre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int t = s_tmp[k];
+    wpre += k < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  excl = wpre + x - v;
+  return tot;
+}
+}  // namespace
+
+__global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
+  __shared__ int s_tmp[2][16];
+  int carry_p = 0, carry_i = 0;
+  for (int base = 0; base < a.n_bhc; base += 1024) {
+    const int idx = base + threadIdx.x;
+    const int P = idx < a.n_bhc ? a.cmp[idx] : 0;
+    const int ni = ((P + 31) / 32 + kCmBlocks - 1) / kCmBlocks;
+    int ep, ei;
+    const int tp = block_excl_scan_1024(P, s_tmp[0], ep);
+    const int ti = block_excl_scan_1024(ni, s_tmp[1], ei);
+    if (idx < a.n_bhc) {
+      a.cs[idx] = carry_p + ep;
+      for (int j = 0; j < ni; ++j) {
+        const long long it = (long long)carry_i + ei + j;
+        if (it < a.max_items) a.items[it] = make_int2(idx, j * kCmBlocks);
+      }
+    }
+    carry_p += tp;
+    carry_i += ti;
+  }
+  if (threadIdx.x == 0) *a.nitems = carry_i;
+}
+
+// One workgroup per (tile, query head, b); one wavefront per list entry.
+__global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = a.g;
+  const int hk = h / g;
+  const int hh = h % g;
+  const size_t bh = (size_t)b * a.Hq + h;
+  const int cnt = a.ccounts[bh * a.n_tiles + tile];
+  const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, a.causal != 0);
+  const int* cs = a.cs + ((size_t)b * a.Hkv + hk) * a.n_slots;
+  const uint32_t tb = cnt > 0 ? a.tbase[bh * a.n_tiles + tile] : 0u;
+  for (int e = w; e < cnt; e += 4) {
+    const int c = a.clists[toff + e];
+    const long long dst0 = (long long)cs[c] + a.cbase[toff + e];
+    const size_t ent = (size_t)(toff + e) * kTileRows;
+    int run = 0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rt = half * kWave + lane;
+      const int row = tile * kTileRows + rt;
+      const float wv = a.cw[ent + rt];
+      const bool take = wv > -INFINITY && row < a.N;
+      const unsigned long long m = __ballot(take);
+      if (take) {
+        const long long dst = dst0 + run + __popcll(m & ((1ull << lane) - 1ull));
+        if (dst < a.pool_cap)
+          a.recs[dst] = make_int4(row * g + hh, (int)(tb + a.ck[ent + rt]), __float_as_int(wv), 0);
+      }
+      run += __popcll(m);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int KROW = D + KPAD;
+  constexpr int VROW = kChunk + VPAD;
+  constexpr int NBW = kCmBlocks / 4;  // blocks of an item per wavefront
+  static_assert(D == 128, "staging is laid out for head_dim 128");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int g = a.g;
+  const int N = a.N;
+  const float sc = a.scale_log2;
+  const int hi32 = lane >> 5;
+  const bool causal = a.causal != 0;
+  const int nitems = (int)min((long long)*a.nitems, a.max_items);
+
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int2 it = a.items[item];
+    const int bhc = it.x;
+    const int c = bhc % a.n_slots;
+    const int bhk = bhc / a.n_slots;
+    const int b = bhk / a.Hkv;
+    const int hk = bhk % a.Hkv;
+    const int P = a.cmp[bhc];
+    const size_t start = (size_t)a.cs[bhc];
+    const int k1 = min(it.y + kCmBlocks, (P + 31) / 32);
+    // this wavefront's blocks: it.y + w + 4 i, i < nb
+    const int nb = max(0, (k1 - (it.y + w) + 3) / 4);
+
+    // ---- the pair records of this wavefront's blocks; lane j % 32 takes pair
+    // 32 k + j % 32 of block k (lanes past the block's end repeat its last pair)
+    int4 rec[NBW];
+    int cnt[NBW];
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const int k = it.y + w + 4 * i;
+      cnt[i] = i < nb ? min(32, P - 32 * k) : 0;
+      if (i < nb) rec[i] = a.recs[start + 32 * k + min(lane & 31, cnt[i] - 1)];
+    }
+    // a record names a row of the sequence (row * g + head in group) and a pool slot
+    auto valid_of = [&](const int4& r, int n) {
+      return (lane & 31) < n && r.x >= 0 && r.x < N * g && (long long)(uint32_t)r.y < a.pool_cap;
+    };
+    auto load_q = [&](const int4& r, int n, bf16x8 (&qb)[NS]) {
+      const int qh = valid_of(r, n) ? r.x : 0;
+      const int row = qh / g;
+      const size_t bh = (size_t)b * a.Hq + hk * g + (qh - row * g);
+      const uint16_t* qp = a.Q + (bh * N + row) * (size_t)D + 8 * hi32;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
+    };
+
+    // ---- stage K (row-major) and V (transposed) of chunk c; keys past the
+    // sequence end read its last row (masked below). The first block's query
+    // rows are fetched meanwhile.
+    __syncthreads();  // the previous item's LDS reads are done
+    bf16x8 qbuf[2][NS];
+    {
+      const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+      const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+      const int k_row = tid >> 4, k_col = (tid & 15) * 8;
+      const int v_kg = tid & 15, v_dg = tid >> 4;
+      u32x4 kr[4], vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kr[r] = ldg16(Kb + (size_t)min(c * kChunk + k_row + 16 * r, N - 1) * D + k_col);
+        vr[r] = ldg16(Vb + (size_t)min(c * kChunk + 4 * v_kg + r, N - 1) * D + 8 * v_dg);
+      }
+      if (nb > 0) load_q(rec[0], cnt[0], qbuf[0]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&sK[(k_row + 16 * r) * KROW + k_col]) = kr[r];
+      uint16_t* vt = &sV[(8 * v_dg) * VROW + 4 * v_kg];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x2 lo2 = {perm_lo(vr[0][e], vr[1][e]), perm_lo(vr[2][e], vr[3][e])};
+        u32x2 hi2 = {perm_hi(vr[0][e], vr[1][e]), perm_hi(vr[2][e], vr[3][e])};
+        *reinterpret_cast<u32x2*>(vt + (2 * e) * VROW) = lo2;
+        *reinterpret_cast<u32x2*>(vt + (2 * e + 1) * VROW) = hi2;
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      if (i < nb) {
+        // the next block's query rows are in flight while this one is computed
+        if (i + 1 < NBW && i + 1 < nb) load_q(rec[i + 1], cnt[i + 1], qbuf[(i + 1) & 1]);
+        const bf16x8 (&qb)[NS] = qbuf[i & 1];
+        const bool valid = valid_of(rec[i], cnt[i]);
+        const int qh = valid ? rec[i].x : 0;
+        const int row = qh / g;
+        const float bias = valid ? __int_as_float(rec[i].z) : -INFINITY;
+
+        // ---- S^T = K Q^T (lane: query row, registers: keys)
+        f32x16 s0, s1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = 0.f;
+          s1[r] = 0.f;
+        }
+        const uint16_t* ka = &sK[(lane & 31) * KROW + 8 * hi32];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          s0 = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ka + 16 * s), qb[s], s0);
+          s1 = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ka + 32 * KROW + 16 * s), qb[s], s1);
+          if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);  // bounds the operands in flight
+        }
+        // keys of the chunk visible to the row: up to the row itself (causal: the
+        // own chunk is the only one that reaches past it) and the sequence end
+        const int lim = min(causal ? row - c * kChunk : kChunk - 1, N - 1 - c * kChunk);
+        if (wave_any(lim < kChunk - 1)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+            s0[r] = kk <= lim ? s0[r] : -INFINITY;
+            s1[r] = kk + 32 <= lim ? s1[r] : -INFINITY;
+          }
+        }
+        // ---- softmax over the chunk in the exp2 domain, with the row's bias
+        float smax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, fmaxf(s0[r], s1[r]));
+        smax = max_xor32(smax);
+        const bool live = valid && smax > -INFINITY;
+        const float m = live ? fmaf(smax, sc, bias) : 0.f;
+        const float off = live ? bias - m : -INFINITY;
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = fast_exp2(fmaf(s0[r], sc, off));
+          s1[r] = fast_exp2(fmaf(s1[r], sc, off));
+          ls += s0[r] + s1[r];
+        }
+        const float l = sum_xor32(ls);
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hh2 = 0; hh2 < 2; ++hh2) {
+          u32x4 p0, p1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            p0[q] = pack_bf16x2(s0[8 * hh2 + 2 * q], s0[8 * hh2 + 2 * q + 1]);
+            p1[q] = pack_bf16x2(s1[8 * hh2 + 2 * q], s1[8 * hh2 + 2 * q + 1]);
+          }
+          pb[hh2] = as_bf16x8(p0);
+          pb[2 + hh2] = as_bf16x8(p1);
+        }
+        // ---- partial result of the pair: (max, sum), and O^T = V^T P^T over the
+        // sum, each 32-dim block stored as soon as it is done
+        const size_t slot = (uint32_t)rec[i].y;
+        if (valid && hi32 == 0) a.pml[slot] = make_float2(m, l);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* op = a.po + slot * D + 64 * hi32;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          f32x16 o;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] = 0.f;
+          const uint16_t* vrow = &sV[(32 * db + (lane & 31)) * VROW + 4 * hi32];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int k0 = (ks >> 1) * 32 + (ks & 1) * 16;
+            u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
+            u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+            o = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (valid) {
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              u32x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = pack_f16x2(o[8 * qq + 2 * e] * inv, o[8 * qq + 2 * e + 1] * inv);
+              *reinterpret_cast<u32x4*>(op + 16 * db + 8 * qq) = v;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: every row with partial results (the rows of tiles that got pool
+// slots) combines them with the exact online-softmax merge (each side rescaled
+// to the larger max) and writes its output row. 16 lanes per row, each owning
+// 8 of the 128 fp16 values of a slot; the next slot's loads are in flight
+// while one is merged.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
+  constexpr int D = 128;
+  const size_t rows = (size_t)a.B * a.Hq * a.N;
+  const size_t ri = (size_t)blockIdx.x * 16 + threadIdx.x / 16;
+  const int p = threadIdx.x & 15;
+  if (ri >= rows) return;
+  const int n = a.cmcnt[ri];
+  if (n == 0) return;  // the row was attended row-major
+  const size_t s0 = a.rslot[ri];
+  float m = kNegBig, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+  auto load_slot = [&](int k, u32x4& v, float2& ml) {
+    ml = a.pml[s0 + k];
+    v = ldg16(a.po + (s0 + k) * D + 8 * p);
+  };
+  auto merge_slot = [&](const u32x4& v, float2 ml) {
+    const float M = fmaxf(m, ml.x);
+    const float al = fast_exp2(m - M);
+    const float be = ml.y * fast_exp2(ml.x - M);
+    m = M;
+    l = fmaf(l, al, be);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(acc[2 * e], al, be * f16lo(v[e]));
+      acc[2 * e + 1] = fmaf(acc[2 * e + 1], al, be * f16hi(v[e]));
+    }
+  };
+  u32x4 va, vb;
+  float2 ma, mb;
+  load_slot(0, va, ma);
+  for (int k = 0; k < n; k += 2) {
+    if (k + 1 < n) load_slot(k + 1, vb, mb);
+    merge_slot(va, ma);
+    if (k + 1 < n) {
+      if (k + 2 < n) load_slot(k + 2, va, ma);
+      merge_slot(vb, mb);
+    }
+  }
+  // values 8p .. 8p+7 of a slot: lane half hi = p / 8, 32-dim block db = (p % 8) / 2,
+  // registers 8 (p % 2) + j, i.e. dims 32 db + 16 (p % 2) + 8 (j / 4) + 4 hi + j % 4
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int hi = p >> 3, db = (p & 7) >> 1, qq = p & 1;
+  uint16_t* op = a.O + ri * D + 32 * db + 16 * qq + 4 * hi;
+  *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(op + 8) = u32x2{pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+}
+
 hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_cm_plan, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(k_cm_scatter, dim3(a.n_tiles, a.Hq, a.B), dim3(256), 0, stream, a);
+  const long long cm_grid = std::min<long long>(a.max_items, (long long)a.n_cu * kCmWgPerCu);
+  hipLaunchKernelGGL(k_prefill_cm<128>, dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
+  const long long rows = (long long)a.B * a.Hq * a.N;
+  hipLaunchKernelGGL(k_prefill_merge, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  // row-major fallback for tiles without pool slots (a persistent grid that
+  // skips every other tile)
   const int n_units = a.n_tiles * a.B * a.Hkv;
-  const int grid = ((n_units + 7) / 8) * 8 * a.g;
-  hipLaunchKernelGGL(k_sparse_prefill<128>, dim3(grid), dim3(256), 0, stream, a);
+  const int n_work = ((n_units + 7) / 8) * 8 * a.g;
+  const int rm_grid = std::min(n_work, ((a.n_cu * 2 + 7) / 8) * 8);
+  hipLaunchKernelGGL(k_sparse_prefill<128>, dim3(rm_grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -142,12 +142,16 @@ size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int 
  *   O_i = sum_j softmax_j(<q_i, k_j> / sqrt(d) + log w_{i, c(j)}) v_j
  * over the tokens j of the chunks routed to row i (j <= i when causal), w the
  * routing prior (1 for an always-attended own chunk). Reads the work lists
- * that dash_route (prefill mode, same sizes and params) left in `workspace`.
+ * that dash_route (prefill mode, same sizes and params) left in `workspace`
+ * and uses the rest of it for per-(row, chunk) partial results: a row's first
+ * routed past chunks are attended chunk by chunk (all rows that routed a chunk
+ * share one pass over it), the rest row by row, and the partials are merged
+ * (the online-softmax merge is exact in any order).
  *   Q [B, Hq, N, d], K/V [B, Hkv, Lmax, d], O [B, Hq, N, d], all dtype dt.
  * --------------------------------------------------------------------------- */
 dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V,
                                      dash_dtype dt, int B, int Hq, int Hkv, int N, int Lmax,
-                                     int d, dash_params p, void* O, const void* workspace,
+                                     int d, dash_params p, void* O, void* workspace,
                                      size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------

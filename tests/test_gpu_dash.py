@@ -99,6 +99,19 @@ def test_prefill_zero_scaling_is_dense_causal():
     assert_close(f64(O), ref.double().numpy(), TOL_BF16, "dense causal")
 
 
+def test_prefill_pool_exhausted_falls_back_to_row_major():
+    """Uniform routing over 4096 causal keys needs about twice the partial-result
+    pool (16 slots per row): tiles that find it exhausted attend all their
+    chunks row-major, the others chunk-major; both must give dense causal
+    attention."""
+    Q, K, V, cls = _inputs(1, 2, 1, 4096, 17, None)
+    O, tau, bits, _, _ = api.prefill(Q, K, V, cls, api.Params(scaling_factor=0.0))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q.float().cpu(), K.float().cpu().repeat_interleave(2, 1), V.float().cpu().repeat_interleave(2, 1),
+        is_causal=True)
+    assert_close(f64(O), ref.double().numpy(), TOL_BF16, "dense causal, pool exhausted")
+
+
 def test_prefill_deterministic():
     Q, K, V, cls = _inputs(1, 8, 2, 1536, 5)
     p = api.Params()
