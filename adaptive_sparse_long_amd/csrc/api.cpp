@@ -210,7 +210,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.tbase = reinterpret_cast<const uint32_t*>(ws + L.off_tbase);
   a.rslot = reinterpret_cast<const uint32_t*>(ws + L.off_rslot);
   a.cmcnt = reinterpret_cast<const uint16_t*>(ws + L.off_cmcnt);
-  a.pml = reinterpret_cast<float2*>(ws + L.off_pml);
+  a.plse = reinterpret_cast<float*>(ws + L.off_plse);
   a.po = reinterpret_cast<uint16_t*>(ws + L.off_po);
   return from_hip(launch_sparse_prefill(a, stream));
 }

@@ -42,9 +42,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // counted by the routing) and their start in the chunk-sorted pair records
 // (cs). Work items list (bhc, first block); recs hold one pair each.
 // Per tile: its first pool slot (tbase). Per row: its first slot (rslot) and
-// number of partials (cmcnt). Per slot: (max, sum) in float32 and the output
-// normalised by the sum in fp16, in the order [lane half][32-dim block][8
-// dims] that the kernels hold it in. pool: the slot allocation counter.
+// number of partials (cmcnt); a row's slots follow its attended chunks in
+// ascending order. pool: the slot allocation counter. Per slot: the log2 of
+// the partial's sum of exp2 weights (its max included) in float32 and its
+// output normalised by that sum in fp16, dims in natural order.
 // ---------------------------------------------------------------------------
 struct PrefillLayout {
   int n_tiles = 0;
@@ -55,7 +56,7 @@ struct PrefillLayout {
   size_t off_counts = 0, off_lists = 0, off_bias = 0;          // row-major list
   size_t off_ccounts = 0, off_clists = 0, off_cw = 0, off_ck = 0, off_cbase = 0;  // chunk-major list
   size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0;  // chunk-major pairs
-  size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_pml = 0, off_po = 0;  // partials
+  size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_plse = 0, off_po = 0;  // partials
   long long pool_cap = 0;
   size_t off_split = 0, total = 0;
 };
@@ -99,7 +100,7 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
-  L.off_pml = o;     o += align256(pairs * 2 * sizeof(float));
+  L.off_plse = o;    o += align256(pairs * sizeof(float));
   L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
   L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
   L.total = o;
@@ -210,7 +211,7 @@ struct PrefillAttnArgs {
   const uint32_t* tbase;
   const uint32_t* rslot;
   const uint16_t* cmcnt;
-  float2* pml;
+  float* plse;
   uint16_t* po;
 };
 

@@ -331,8 +331,11 @@ __global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
   if (threadIdx.x == 0) *a.nitems = carry_i;
 }
 
-// One workgroup per (tile, query head, b); one wavefront per list entry.
+// One workgroup per (tile, query head, b). The destinations of up to 256 list
+// entries are looked up at once (one per thread, into LDS); then each
+// wavefront copies two entries at a time, the loads of both in flight together.
 __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
+  __shared__ long long s_dst[256];
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int tile = blockIdx.x;
@@ -343,27 +346,49 @@ __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
   const int hh = h % g;
   const size_t bh = (size_t)b * a.Hq + h;
   const int cnt = a.ccounts[bh * a.n_tiles + tile];
+  if (cnt == 0) return;
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, a.causal != 0);
   const int* cs = a.cs + ((size_t)b * a.Hkv + hk) * a.n_slots;
-  const uint32_t tb = cnt > 0 ? a.tbase[bh * a.n_tiles + tile] : 0u;
-  for (int e = w; e < cnt; e += 4) {
-    const int c = a.clists[toff + e];
-    const long long dst0 = (long long)cs[c] + a.cbase[toff + e];
-    const size_t ent = (size_t)(toff + e) * kTileRows;
-    int run = 0;
+  const uint32_t tb = a.tbase[bh * a.n_tiles + tile];
+  for (int e0 = 0; e0 < cnt; e0 += 256) {
+    const int ne = min(256, cnt - e0);
+    __syncthreads();  // the previous batch's destinations are read
+    if ((int)threadIdx.x < ne) {
+      const int c = a.clists[toff + e0 + threadIdx.x];
+      s_dst[threadIdx.x] = (long long)cs[c] + a.cbase[toff + e0 + threadIdx.x];
+    }
+    __syncthreads();
+    for (int j = w; j < ne; j += 8) {
+      const int j2 = min(j + 4, ne - 1);  // the second entry (j itself when there is none)
+      const size_t ea = (size_t)(toff + e0 + j) * kTileRows;
+      const size_t eb = (size_t)(toff + e0 + j2) * kTileRows;
+      float wv[2][2];
+      uint32_t kv[2][2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int rt = half * kWave + lane;
-      const int row = tile * kTileRows + rt;
-      const float wv = a.cw[ent + rt];
-      const bool take = wv > -INFINITY && row < a.N;
-      const unsigned long long m = __ballot(take);
-      if (take) {
-        const long long dst = dst0 + run + __popcll(m & ((1ull << lane) - 1ull));
-        if (dst < a.pool_cap)
-          a.recs[dst] = make_int4(row * g + hh, (int)(tb + a.ck[ent + rt]), __float_as_int(wv), 0);
+      for (int half = 0; half < 2; ++half) {
+        wv[0][half] = a.cw[ea + half * kWave + lane];
+        kv[0][half] = a.ck[ea + half * kWave + lane];
+        wv[1][half] = a.cw[eb + half * kWave + lane];
+        kv[1][half] = a.ck[eb + half * kWave + lane];
       }
-      run += __popcll(m);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (x == 1 && j2 == j) break;
+        const long long dst0 = s_dst[x == 0 ? j : j2];
+        int run = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int row = tile * kTileRows + half * kWave + lane;
+          const bool take = wv[x][half] > -INFINITY && row < a.N;
+          const unsigned long long m = __ballot(take);
+          if (take) {
+            const long long dst = dst0 + run + __popcll(m & ((1ull << lane) - 1ull));
+            if (dst < a.pool_cap)
+              a.recs[dst] = make_int4(row * g + hh, (int)(tb + kv[x][half]), __float_as_int(wv[x][half]), 0);
+          }
+          run += __popcll(m);
+        }
+      }
     }
   }
 }
@@ -375,9 +400,11 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
   constexpr int KROW = D + KPAD;
   constexpr int VROW = kChunk + VPAD;
   constexpr int NBW = kCmBlocks / 4;  // blocks of an item per wavefront
+  constexpr int OROW = 64 + 8;        // output staging: 64 dims of a row, padded
   static_assert(D == 128, "staging is laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sO[4][32 * OROW];  // per wavefront
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -405,13 +432,10 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
     // ---- the pair records of this wavefront's blocks; lane j % 32 takes pair
     // 32 k + j % 32 of block k (lanes past the block's end repeat its last pair)
     int4 rec[NBW];
-    int cnt[NBW];
+    auto cnt_of = [&](int i) { return min(32, P - 32 * (it.y + w + 4 * i)); };  // pairs of block i
 #pragma unroll
-    for (int i = 0; i < NBW; ++i) {
-      const int k = it.y + w + 4 * i;
-      cnt[i] = i < nb ? min(32, P - 32 * k) : 0;
-      if (i < nb) rec[i] = a.recs[start + 32 * k + min(lane & 31, cnt[i] - 1)];
-    }
+    for (int i = 0; i < NBW; ++i)
+      if (i < nb) rec[i] = a.recs[start + 32 * (it.y + w + 4 * i) + min(lane & 31, cnt_of(i) - 1)];
     // a record names a row of the sequence (row * g + head in group) and a pool slot
     auto valid_of = [&](const int4& r, int n) {
       return (lane & 31) < n && r.x >= 0 && r.x < N * g && (long long)(uint32_t)r.y < a.pool_cap;
@@ -441,7 +465,7 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
         kr[r] = ldg16(Kb + (size_t)min(c * kChunk + k_row + 16 * r, N - 1) * D + k_col);
         vr[r] = ldg16(Vb + (size_t)min(c * kChunk + 4 * v_kg + r, N - 1) * D + 8 * v_dg);
       }
-      if (nb > 0) load_q(rec[0], cnt[0], qbuf[0]);
+      if (nb > 0) load_q(rec[0], cnt_of(0), qbuf[0]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&sK[(k_row + 16 * r) * KROW + k_col]) = kr[r];
       uint16_t* vt = &sV[(8 * v_dg) * VROW + 4 * v_kg];
@@ -459,9 +483,10 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
     for (int i = 0; i < NBW; ++i) {
       if (i < nb) {
         // the next block's query rows are in flight while this one is computed
-        if (i + 1 < NBW && i + 1 < nb) load_q(rec[i + 1], cnt[i + 1], qbuf[(i + 1) & 1]);
+        if (i + 1 < NBW && i + 1 < nb) load_q(rec[i + 1], cnt_of(i + 1), qbuf[(i + 1) & 1]);
         const bf16x8 (&qb)[NS] = qbuf[i & 1];
-        const bool valid = valid_of(rec[i], cnt[i]);
+        const int cnt_i = cnt_of(i);
+        const bool valid = valid_of(rec[i], cnt_i);
         const int qh = valid ? rec[i].x : 0;
         const int row = qh / g;
         const float bias = valid ? __int_as_float(rec[i].z) : -INFINITY;
@@ -519,35 +544,49 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
           pb[hh2] = as_bf16x8(p0);
           pb[2 + hh2] = as_bf16x8(p1);
         }
-        // ---- partial result of the pair: (max, sum), and O^T = V^T P^T over the
-        // sum, each 32-dim block stored as soon as it is done
-        const size_t slot = (uint32_t)rec[i].y;
-        if (valid && hi32 == 0) a.pml[slot] = make_float2(m, l);
+        // ---- partial result of the pair, stored in its pool slot: log2 of its
+        // sum of exp2 weights, and O^T = V^T P^T over that sum in natural dim
+        // order. Each 64-dim half passes through this wavefront's LDS rows, so
+        // that every store instruction writes whole 128-byte lines.
+        const uint32_t slot = valid ? (uint32_t)rec[i].y : 0u;
+        if (valid && hi32 == 0) a.plse[slot] = l > 0.f ? m + fast_log2(l) : -INFINITY;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* op = a.po + slot * D + 64 * hi32;
+        uint16_t* so = sO[w];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          f32x16 o;
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[r] = 0.f;
-          const uint16_t* vrow = &sV[(32 * db + (lane & 31)) * VROW + 4 * hi32];
+          for (int d2 = 0; d2 < 2; ++d2) {
+            f32x16 o;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int k0 = (ks >> 1) * 32 + (ks & 1) * 16;
-            u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
-            u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
-            o = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          if (valid) {
+            for (int r = 0; r < 16; ++r) o[r] = 0.f;
+            const uint16_t* vrow = &sV[(32 * (2 * half + d2) + (lane & 31)) * VROW + 4 * hi32];
 #pragma unroll
-            for (int qq = 0; qq < 2; ++qq) {
-              u32x4 v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = pack_f16x2(o[8 * qq + 2 * e] * inv, o[8 * qq + 2 * e + 1] * inv);
-              *reinterpret_cast<u32x4*>(op + 16 * db + 8 * qq) = v;
+            for (int ks = 0; ks < 4; ++ks) {
+              const int k0 = (ks >> 1) * 32 + (ks & 1) * 16;
+              u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + k0);
+              u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + k0 + 8);
+              o = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[ks], o);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            // row lane % 32, dims 32 d2 + 8 q4 + 4 hi32 + {0..3} of this half
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              *reinterpret_cast<u32x2*>(so + (lane & 31) * OROW + 32 * d2 + 8 * q4 + 4 * hi32) =
+                  u32x2{pack_f16x2(o[4 * q4] * inv, o[4 * q4 + 1] * inv), pack_f16x2(o[4 * q4 + 2] * inv, o[4 * q4 + 3] * inv)};
           }
+          wave_lds_fence();
+          // 32 rows x 128 bytes: eight lanes per row, eight rows per pass; the
+          // slot of row rr is held by lane rr
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = lane + kWave * u;
+            const int rr = t >> 3, c16 = t & 7;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(so + rr * OROW + 8 * c16);
+            const int vr = __shfl((int)valid, rr);
+            const size_t sr = (uint32_t)__shfl((int)slot, rr);
+            if (vr) *reinterpret_cast<u32x4*>(a.po + sr * D + 64 * half + 8 * c16) = v;
+          }
+          wave_lds_fence();
         }
       }
     }
@@ -556,58 +595,62 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
 
 // ---------------------------------------------------------------------------
 // Merge: every row with partial results (the rows of tiles that got pool
-// slots) combines them with the exact online-softmax merge (each side rescaled
-// to the larger max) and writes its output row. 16 lanes per row, each owning
-// 8 of the 128 fp16 values of a slot; the next slot's loads are in flight
-// while one is merged.
+// slots) combines them, in the order of its slots (consecutive, so rows stream
+// through memory), weighting each by 2^(its log2 sum - the largest one), and
+// writes its output row. Eight lanes per row, lane p owning dims 16p .. 16p+15;
+// the loads of up to four partials are in flight together.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   constexpr int D = 128;
+  constexpr int NP = 4;  // partials loaded together
   const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t ri = (size_t)blockIdx.x * 16 + threadIdx.x / 16;
-  const int p = threadIdx.x & 15;
+  const size_t ri = (size_t)blockIdx.x * 32 + threadIdx.x / 8;
+  const int p = threadIdx.x & 7;
   if (ri >= rows) return;
   const int n = a.cmcnt[ri];
   if (n == 0) return;  // the row was attended row-major
   const size_t s0 = a.rslot[ri];
+  if ((long long)(s0 + n) > a.pool_cap) return;
   float m = kNegBig, l = 0.f;
-  float acc[8];
+  float acc[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-  auto load_slot = [&](int k, u32x4& v, float2& ml) {
-    ml = a.pml[s0 + k];
-    v = ldg16(a.po + (s0 + k) * D + 8 * p);
-  };
-  auto merge_slot = [&](const u32x4& v, float2 ml) {
-    const float M = fmaxf(m, ml.x);
-    const float al = fast_exp2(m - M);
-    const float be = ml.y * fast_exp2(ml.x - M);
-    m = M;
-    l = fmaf(l, al, be);
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  for (int k0 = 0; k0 < n; k0 += NP) {
+    float lse[NP];
+    u32x4 v[NP][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] = fmaf(acc[2 * e], al, be * f16lo(v[e]));
-      acc[2 * e + 1] = fmaf(acc[2 * e + 1], al, be * f16hi(v[e]));
+    for (int x = 0; x < NP; ++x) {
+      const size_t sl = s0 + min(k0 + x, n - 1);
+      lse[x] = a.plse[sl];
+      v[x][0] = ldg16(a.po + sl * D + 16 * p);
+      v[x][1] = ldg16(a.po + sl * D + 16 * p + 8);
     }
-  };
-  u32x4 va, vb;
-  float2 ma, mb;
-  load_slot(0, va, ma);
-  for (int k = 0; k < n; k += 2) {
-    if (k + 1 < n) load_slot(k + 1, vb, mb);
-    merge_slot(va, ma);
-    if (k + 1 < n) {
-      if (k + 2 < n) load_slot(k + 2, va, ma);
-      merge_slot(vb, mb);
+#pragma unroll
+    for (int x = 0; x < NP; ++x) {
+      if (k0 + x < n && lse[x] > -INFINITY) {
+        const float M = fmaxf(m, lse[x]);
+        const float al = fast_exp2(m - M);
+        const float be = fast_exp2(lse[x] - M);
+        m = M;
+        l = fmaf(l, al, be);
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[8 * hv + 2 * e] = fmaf(acc[8 * hv + 2 * e], al, be * f16lo(v[x][hv][e]));
+            acc[8 * hv + 2 * e + 1] = fmaf(acc[8 * hv + 2 * e + 1], al, be * f16hi(v[x][hv][e]));
+          }
+      }
     }
   }
-  // values 8p .. 8p+7 of a slot: lane half hi = p / 8, 32-dim block db = (p % 8) / 2,
-  // registers 8 (p % 2) + j, i.e. dims 32 db + 16 (p % 2) + 8 (j / 4) + 4 hi + j % 4
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int hi = p >> 3, db = (p & 7) >> 1, qq = p & 1;
-  uint16_t* op = a.O + ri * D + 32 * db + 16 * qq + 4 * hi;
-  *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(op + 8) = u32x2{pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e] * inv, acc[8 * hv + 2 * e + 1] * inv);
+    *reinterpret_cast<u32x4*>(a.O + ri * D + 16 * p + 8 * hv) = out;
+  }
 }
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
@@ -616,7 +659,7 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
   const long long cm_grid = std::min<long long>(a.max_items, (long long)a.n_cu * kCmWgPerCu);
   hipLaunchKernelGGL(k_prefill_cm<128>, dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
   const long long rows = (long long)a.B * a.Hq * a.N;
-  hipLaunchKernelGGL(k_prefill_merge, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_prefill_merge, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, a);
   // row-major fallback for tiles without pool slots (a persistent grid that
   // skips every other tile)
   const int n_units = a.n_tiles * a.B * a.Hkv;
