@@ -149,8 +149,8 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.bias = reinterpret_cast<float*>(ws + L.off_bias);
   a.ccounts = reinterpret_cast<int*>(ws + L.off_ccounts);
   a.clists = reinterpret_cast<int*>(ws + L.off_clists);
-  a.cw = reinterpret_cast<float*>(ws + L.off_cw);
-  a.ck = reinterpret_cast<uint16_t*>(ws + L.off_ck);
+  a.ceo = reinterpret_cast<int2*>(ws + L.off_ceo);
+  a.trec = reinterpret_cast<int4*>(ws + L.off_trec);
   a.cbase = reinterpret_cast<int*>(ws + L.off_cbase);
   a.cmp = reinterpret_cast<int*>(ws + L.off_cmp);
   a.n_bhc = L.n_bhc;
@@ -195,8 +195,8 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
   a.ccounts = reinterpret_cast<const int*>(ws + L.off_ccounts);
   a.clists = reinterpret_cast<const int*>(ws + L.off_clists);
-  a.cw = reinterpret_cast<const float*>(ws + L.off_cw);
-  a.ck = reinterpret_cast<const uint16_t*>(ws + L.off_ck);
+  a.ceo = reinterpret_cast<const int2*>(ws + L.off_ceo);
+  a.trec = reinterpret_cast<const int4*>(ws + L.off_trec);
   a.cbase = reinterpret_cast<const int*>(ws + L.off_cbase);
   a.cmp = reinterpret_cast<const int*>(ws + L.off_cmp);
   a.cs = reinterpret_cast<int*>(ws + L.off_cs);

@@ -136,6 +136,33 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Exclusive prefix sum of v over a workgroup of NWAVES wavefronts; returns the
+// total. Every thread of the workgroup calls it; s_tmp holds NWAVES ints and
+// may be reused once it returns.
+template <int NWAVES>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int& excl) {
+  const int lane = __lane_id();
+  const int w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    x += lane >= off ? y : 0;
+  }
+  if (lane == kWave - 1) s_tmp[w] = x;
+  __syncthreads();
+  int wpre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < NWAVES; ++k) {
+    const int t = s_tmp[k];
+    wpre += k < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  excl = wpre + x - v;
+  return tot;
+}
+
 // Number of workgroups the blockIdx -> XCD round robin spreads over.
 constexpr int kNumXcd = 8;
 

@@ -29,12 +29,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
 // Prefill work lists, per (b, query head) and 128-row tile, each an ascending
-// list of chunk ids with, per listed chunk, one entry for each of the tile's
-// 128 rows:
-//   row-major list ("rm"): the row's own chunk (and, in a tile without pool
-//     slots, every routed chunk); entry = log2 weight (-inf: not attended);
-//   chunk-major list ("cm"): routed past chunks; entry = log2 weight and the
-//     partial slot it fills, as an offset from the tile's first slot.
+// list of chunk ids:
+//   row-major list ("rm", tiles without pool slots): every attended chunk, with
+//     one log2 weight per row of the tile (-inf: not attended by that row);
+//   chunk-major list ("cm", tiles with pool slots): every attended chunk, with
+//     the (row, chunk) pair records of the rows attending it -- (row * g + head
+//     in group, pool slot, log2 weight) -- grouped by chunk in the tile's own
+//     pool range (trec, at [tbase + first, + count) for list entry e, (first,
+//     count) in ceo).
 // Causal tile t can only list chunks 0 .. 2t+1, so tiles are packed in a
 // triangle: tile t starts at slot t*(t+1). Non-causal tiles hold n_slots each.
 // Per chunk-major list entry: the offset of its pairs among all pairs of its
@@ -54,8 +56,8 @@ struct PrefillLayout {
   int n_bhc = 0;          // B * Hkv * n_slots
   long long max_items = 0;
   size_t off_counts = 0, off_lists = 0, off_bias = 0;          // row-major list
-  size_t off_ccounts = 0, off_clists = 0, off_cw = 0, off_ck = 0, off_cbase = 0;  // chunk-major list
-  size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0;  // chunk-major pairs
+  size_t off_ccounts = 0, off_clists = 0, off_ceo = 0, off_cbase = 0;  // chunk-major list
+  size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0, off_trec = 0;  // chunk-major pairs
   size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_plse = 0, off_po = 0;  // partials
   long long pool_cap = 0;
   size_t off_split = 0, total = 0;
@@ -88,14 +90,14 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_bias = o;    o += align256(entries * sizeof(float));
   L.off_ccounts = o; o += align256(heads * L.n_tiles * sizeof(int));
   L.off_clists = o;  o += align256(heads * (size_t)L.per_head * sizeof(int));
-  L.off_cw = o;      o += align256(entries * sizeof(float));
-  L.off_ck = o;      o += align256(entries * sizeof(uint16_t));
+  L.off_ceo = o;     o += align256(heads * (size_t)L.per_head * 2 * sizeof(int));
   L.off_cbase = o;   o += align256(heads * (size_t)L.per_head * sizeof(int));
   L.off_cmp = o;     o += align256((size_t)L.n_bhc * sizeof(int));
   L.off_cs = o;      o += align256((size_t)L.n_bhc * sizeof(int));
   L.off_nitems = o;  o += align256(sizeof(int));
   L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
   L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
+  L.off_trec = o;    o += align256(pairs * 4 * sizeof(int));
   L.off_pool = o;    o += align256(sizeof(unsigned long long));
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
@@ -165,8 +167,8 @@ struct RouteArgs {
   float* bias;
   int* ccounts;
   int* clists;
-  float* cw;
-  uint16_t* ck;
+  int2* ceo;
+  int4* trec;
   int* cbase;
   int* cmp;  // zeroed by the summary split, counted by the routing
   int n_bhc;
@@ -197,8 +199,8 @@ struct PrefillAttnArgs {
   // chunk-major part
   const int* ccounts;
   const int* clists;
-  const float* cw;
-  const uint16_t* ck;
+  const int2* ceo;
+  const int4* trec;
   const int* cbase;
   const int* cmp;
   int* cs;
@@ -253,6 +255,7 @@ hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t st
 
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
+constexpr int kRouteCap = 64;                // routing candidates per row held in LDS
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 

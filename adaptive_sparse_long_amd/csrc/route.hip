@@ -71,13 +71,14 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   // stride of 132 dwords keeps eight consecutive lanes on distinct LDS banks).
   constexpr int SROW = 2 * D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sS[2][64 * SROW];
-  __shared__ uint32_t s_wu[8][NW];          // per-wavefront union words, row-major list
-  __shared__ uint32_t s_wc[8][NW];          // per-wavefront union words, chunk-major list
-  __shared__ uint32_t s_union[NW], s_cunion[NW];
+  __shared__ uint32_t s_union[NW], s_cunion[NW];  // attended chunks: row-major, chunk-major list
   __shared__ int s_pre[NW + 1], s_cpre[NW + 1];
-  __shared__ int s_ecnt[NW * 32];  // chunk-major entries: rows taking the chunk ...
-  __shared__ int s_cl[NW * 32];    // ... and the chunk
-  __shared__ int s_wtot[8];        // routed past chunks of each wavefront's rows
+  __shared__ int s_ecnt[NW * 32];  // chunk-major entries: rows taking the chunk,
+  __shared__ int s_cl[NW * 32];    // the chunk,
+  __shared__ int s_eoff[NW * 32];  // first record in the tile's pool range,
+  __shared__ int s_efill[NW * 32]; // records written so far
+  __shared__ int s_wtot[8];        // attended chunks of each wavefront's rows
+  __shared__ int s_tmp[8];
   __shared__ long long s_tbase;    // the tile's first pool slot, -1: none
 
   const int lane = lane_id();
@@ -101,7 +102,14 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   const int ncand = ncomp + (est ? 1 : 0);
   const size_t bh = (size_t)b * a.Hq + h;
   const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
-  for (int e = threadIdx.x; e < NW * 32; e += blockDim.x) s_ecnt[e] = 0;
+  for (int e = threadIdx.x; e < NW * 32; e += blockDim.x) {
+    s_ecnt[e] = 0;
+    s_efill[e] = 0;
+  }
+  if (threadIdx.x < NW) {
+    s_union[threadIdx.x] = 0u;
+    s_cunion[threadIdx.x] = 0u;
+  }
 
   // ---- q as A operand: row i0 + col, dims 32 s + 8 grp .. +7
   bf16x8 qa[NS];
@@ -236,7 +244,12 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     }
   }
 
-  // ---- tau per row (all 16 lanes of a row group hold the same values)
+  // ---- tau per row (all 16 lanes of a row group hold the same values). Only
+  // scores above max u - 1 can carry weight (tau >= max u - 1): each row's
+  // candidates, usually a handful, are gathered in ascending chunk order into
+  // an LDS list (in the summary staging, no longer read) and tau iterates over
+  // the list. A wavefront with a row of more than kRouteCap candidates
+  // iterates over all its blocks instead.
   float tau[4];
   bool row_ok[4];
 #pragma unroll
@@ -244,47 +257,101 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     row_ok[r] = wave_valid && (i0 + grp * 4 + r < N);
     tau[r] = INFINITY;
   }
+  auto seg_of = [&](unsigned long long m) { return (uint32_t)(m >> (16 * grp)) & 0xffffu; };
+  const uint32_t below = (1u << col) - 1u;
+  constexpr int NJ = kRouteCap / 16;  // list entries per lane and row: positions col + 16 j
+  float* const s_cu = reinterpret_cast<float*>(&sS[0][0]) + (size_t)w * 16 * kRouteCap;
+  uint16_t* const s_cc =
+      reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(&sS[0][0]) + 8 * 16 * kRouteCap) + (size_t)w * 16 * kRouteCap;
+  float cv[4][NJ];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) cv[r][j] = -INFINITY;
+  bool ovf = false;
   if (wave_valid && ncand > 0) {
-    float lo[4], hi[4];
+    float mx[4], lo[4], hi[4];
+    int nc[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float m = -INFINITY;
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) m = fmaxf(m, u[blk][r]);
-      m = fmaxf(max16(m), ud[r]);
-      lo[r] = m - 1.f;
-      hi[r] = tau_upper(m, ncand, a.alpha);
+      mx[r] = fmaxf(max16(m), ud[r]);
+      lo[r] = mx[r] - 1.f;
       tau[r] = lo[r];
     }
-    // Only values above max u - 1 can carry weight (tau >= max u - 1): blocks
-    // holding none of them are left out of the iterations.
-    uint32_t live = 0u;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
-      const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
-      live |= wave_any(any) ? (1u << blk) : 0u;
-    }
-    for (int it = 0; it < a.n_iter; ++it) {
-      float f0[4] = {0.f, 0.f, 0.f, 0.f}, f1[4] = {0.f, 0.f, 0.f, 0.f}, f2[4] = {0.f, 0.f, 0.f, 0.f};
+      if (blk < nblk) {
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        if ((live >> blk) & 1u) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
+        for (int r = 0; r < 4; ++r) {
+          const bool cnd = u[blk][r] > lo[r];
+          const uint32_t seg = seg_of(__ballot(cnd));
+          const int pos = nc[r] + __popc(seg & below);
+          if (cnd && pos < kRouteCap) {
+            s_cu[(grp * 4 + r) * kRouteCap + pos] = u[blk][r];
+            s_cc[(grp * 4 + r) * kRouteCap + pos] = (uint16_t)(blk * 16 + col);
+          }
+          nc[r] += __popc(seg);
         }
       }
-      bool conv = true;
+    }
+    ovf = wave_any(nc[0] > kRouteCap || nc[1] > kRouteCap || nc[2] > kRouteCap || nc[3] > kRouteCap);
+    wave_lds_fence();
+    // tau <= max - n^-(alpha-1) with n the values above tau, all among the candidates
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        f0[r] = sum16(f0[r]);
-        f1[r] = sum16(f1[r]);
-        if (KIND != 1) f2[r] = sum16(f2[r]);
-        if (est) tau_terms<KIND>(ud[r], tau[r], a.beta, f0[r], f1[r], f2[r]);
-        const float nt = tau_step<KIND>(tau[r], f0[r], f1[r], f2[r], a.beta, lo[r], hi[r]);
-        conv = conv && tau_converged(tau[r], nt);
-        tau[r] = nt;
+    for (int r = 0; r < 4; ++r)
+      hi[r] = tau_upper(mx[r], max(1, ovf ? ncand : nc[r] + ((est && ud[r] > lo[r]) ? 1 : 0)), a.alpha);
+    auto solve = [&](auto&& terms) {
+      for (int it = 0; it < a.n_iter; ++it) {
+        float f0[4] = {0.f, 0.f, 0.f, 0.f}, f1[4] = {0.f, 0.f, 0.f, 0.f}, f2[4] = {0.f, 0.f, 0.f, 0.f};
+        terms(f0, f1, f2);
+        bool conv = true;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f0[r] = sum16(f0[r]);
+          f1[r] = sum16(f1[r]);
+          if (KIND != 1) f2[r] = sum16(f2[r]);
+          if (est) tau_terms<KIND>(ud[r], tau[r], a.beta, f0[r], f1[r], f2[r]);
+          const float nt = tau_step<KIND>(tau[r], f0[r], f1[r], f2[r], a.beta, lo[r], hi[r]);
+          conv = conv && tau_converged(tau[r], nt);
+          tau[r] = nt;
+        }
+        if (wave_all(conv)) break;
       }
-      if (wave_all(conv)) break;
+    };
+    if (!ovf) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int pos = col + 16 * j;
+          cv[r][j] = pos < nc[r] ? s_cu[(grp * 4 + r) * kRouteCap + pos] : -INFINITY;
+        }
+      solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tau_terms<KIND>(cv[r][j], tau[r], a.beta, f0[r], f1[r], f2[r]);
+      });
+    } else {
+      // blocks holding none of the candidates are left out of the iterations
+      uint32_t live = 0u;
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
+        live |= wave_any(any) ? (1u << blk) : 0u;
+      }
+      solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+          if ((live >> blk) & 1u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
+          }
+        }
+      });
     }
   }
 
@@ -305,24 +372,83 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     lwd[r] = !row_ok[r] ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   }
 
-  auto seg_of = [&](unsigned long long m) { return (uint32_t)(m >> (16 * grp)) & 0xffffu; };
-  const uint32_t below = (1u << col) - 1u;
+  // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
+  if (a.bits != nullptr) {
+    unsigned long long md[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) md[r] = __ballot(dact[r]);
+    const bool write_bits = wave_valid && lane < 16 && i0 + lane < N;
+    const int rg = lane >> 2, rr = lane & 3;  // D-layout owner of row `lane`
+    const bool dl = ((rr == 0 ? md[0] : rr == 1 ? md[1] : rr == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
+    uint32_t* bdst = a.bits + ((bh * (size_t)N) + min(i0 + lane, N - 1)) * (size_t)a.bits_words;
+#pragma unroll
+    for (int wd = 0; wd < NW; ++wd) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int blk = 2 * wd + half;
+        if (blk < NB) {
+          unsigned long long mb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
+          const unsigned long long mr = rr == 0 ? mb[0] : rr == 1 ? mb[1] : rr == 2 ? mb[2] : mb[3];
+          word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
+        }
+      }
+      if (causal && dl && (cw >> 5) == wd) word |= 1u << (cw & 31);
+      if (write_bits && wd < a.bits_words) bdst[wd] = word;
+    }
+    if (write_bits)
+      for (int wd = NW; wd < a.bits_words; ++wd) bdst[wd] = 0u;
+  }
+
+  // ---- the routed past chunks of this lane's rows, in ascending chunk order
+  // per row (from the candidate list, or from all blocks): fn(r, chunk, rank,
+  // u) for each; afterwards run[r] holds the row's count. Called by the whole
+  // wavefront.
+  int run[4];
+  auto for_each_routed = [&](auto&& fn) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) run[r] = 0;
+    if (!ovf) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool act = row_ok[r] && cv[r][j] > tau[r];
+          const uint32_t seg = seg_of(__ballot(act));
+          const int rank = run[r] + __popc(seg & below);
+          run[r] += __popc(seg);
+          if (act) fn(r, (int)s_cc[(grp * 4 + r) * kRouteCap + col + 16 * j], rank, cv[r][j]);
+        }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        if (blk < nblk) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool act = row_ok[r] && u[blk][r] > tau[r];
+            const uint32_t seg = seg_of(__ballot(act));
+            const int rank = run[r] + __popc(seg & below);
+            run[r] += __popc(seg);
+            if (act) fn(r, blk * 16 + col, rank, u[blk][r]);
+          }
+        }
+      }
+    }
+  };
 
   // ---- pool slots: one per attended chunk (routed past chunks, then the own
   // chunk) of every row of the tile, taken with one atomic; the slots of a row
   // are consecutive, in chunk order. Rows are numbered (wavefront, row group,
   // r) inside the tile.
-  int nrt[4] = {0, 0, 0, 0};  // routed past chunks
+  for_each_routed([](int, int, int, float) {});
+  int nrt[4], nsl[4];
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    if (blk < nblk) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) nrt[r] += __popc(seg_of(__ballot(row_ok[r] && u[blk][r] > tau[r])));
-    }
+  for (int r = 0; r < 4; ++r) {
+    nrt[r] = run[r];
+    nsl[r] = nrt[r] + (dact[r] ? 1 : 0);
   }
-  int nsl[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) nsl[r] = nrt[r] + (dact[r] ? 1 : 0);
   const int grp_tot = nsl[0] + nsl[1] + nsl[2] + nsl[3];
   const int g0 = __builtin_amdgcn_readlane(grp_tot, 0), g1 = __builtin_amdgcn_readlane(grp_tot, 16);
   const int g2 = __builtin_amdgcn_readlane(grp_tot, 32), g3 = __builtin_amdgcn_readlane(grp_tot, 48);
@@ -360,100 +486,25 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       }
   }
 
-  // pass 1: this wavefront's union of chunk-major and of row-major chunks
-  uint32_t wcm[NW], wrm[NW];
-#pragma unroll
-  for (int wd = 0; wd < NW; ++wd) {
-    wcm[wd] = 0u;
-    wrm[wd] = 0u;
-  }
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    if (blk < nblk) {
-      bool any = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) any = any || (row_ok[r] && u[blk][r] > tau[r]);
-      const unsigned long long mk = __ballot(any);
-      const uint32_t wbits = (uint32_t)((mk | (mk >> 16) | (mk >> 32) | (mk >> 48)) & 0xffffull) << (16 * (blk & 1));
-      if (pooled) wcm[blk >> 1] |= wbits;
-      else wrm[blk >> 1] |= wbits;
-    }
-  }
-  if (causal && wave_any(dact[0] || dact[1] || dact[2] || dact[3])) {
-#pragma unroll
-    for (int wd = 0; wd < NW; ++wd) {
-      const uint32_t own = (cw >> 5) == wd ? (1u << (cw & 31)) : 0u;
-      if (pooled) wcm[wd] |= own;
-      else wrm[wd] |= own;
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int wd = 0; wd < NW; ++wd) {
-      s_wu[w][wd] = wrm[wd];
-      s_wc[w][wd] = wcm[wd];
-    }
-  }
-
-  // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
-  if (a.bits != nullptr) {
-    unsigned long long md[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) md[r] = __ballot(dact[r]);
-    const bool write_bits = wave_valid && lane < 16 && i0 + lane < N;
-    const int rg = lane >> 2, rr = lane & 3;  // D-layout owner of row `lane`
-    const bool dl = ((rr == 0 ? md[0] : rr == 1 ? md[1] : rr == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
-    uint32_t* bdst = a.bits + ((bh * (size_t)N) + min(i0 + lane, N - 1)) * (size_t)a.bits_words;
-#pragma unroll
-    for (int wd = 0; wd < NW; ++wd) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int blk = 2 * wd + half;
-        if (blk < NB) {
-          unsigned long long mb[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
-          const unsigned long long mr = rr == 0 ? mb[0] : rr == 1 ? mb[1] : rr == 2 ? mb[2] : mb[3];
-          word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
-        }
-      }
-      if (causal && dl && (cw >> 5) == wd) word |= 1u << (cw & 31);
-      if (write_bits && wd < a.bits_words) bdst[wd] = word;
-    }
-    if (write_bits)
-      for (int wd = NW; wd < a.bits_words; ++wd) bdst[wd] = 0u;
-  }
-
-  __syncthreads();
-  if (threadIdx.x < 2 * NW) {
-    const int wd = threadIdx.x % NW;
-    uint32_t v = 0;
-    if (threadIdx.x < NW) {
-#pragma unroll
-      for (int ww = 0; ww < 8; ++ww) v |= s_wu[ww][wd];
-      s_union[wd] = v;
-    } else {
-#pragma unroll
-      for (int ww = 0; ww < 8; ++ww) v |= s_wc[ww][wd];
-      s_cunion[wd] = v;
-    }
-  }
+  // ---- the tile's attended chunks: chunk-major list if pooled, else row-major
+  uint32_t* const un = pooled ? s_cunion : s_union;
+  for_each_routed([&](int, int c, int, float) { atomicOr(&un[c >> 5], 1u << (c & 31)); });
+  const bool own_any = causal && col == 0 && (dact[0] || dact[1] || dact[2] || dact[3]);
+  if (own_any) atomicOr(&un[cw >> 5], 1u << (cw & 31));
   __syncthreads();
   if (threadIdx.x == 0 || threadIdx.x == kWave) {
     const bool cm = threadIdx.x != 0;
-    const uint32_t* un = cm ? s_cunion : s_union;
+    const uint32_t* u2 = cm ? s_cunion : s_union;
     int* pre = cm ? s_cpre : s_pre;
     int acc = 0;
     for (int wd = 0; wd < NW; ++wd) {
       pre[wd] = acc;
-      acc += __popc(un[wd]);
+      acc += __popc(u2[wd]);
     }
     pre[NW] = acc;
     (cm ? a.ccounts : a.counts)[bh * a.n_tiles + tile] = acc;
   }
   __syncthreads();
-
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, n_slots, causal);
   if (threadIdx.x < 2 * NW) {
     const bool cm = threadIdx.x >= NW;
@@ -468,80 +519,61 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       bits &= bits - 1u;
     }
   }
+  // list position of chunk c
+  const int* const pre = pooled ? s_cpre : s_pre;
+  auto epos = [&](int c) { return pre[c >> 5] + __popc(un[c >> 5] & ((1u << (c & 31)) - 1u)); };
+  const int hh = h % a.g;
 
-  // ---- pass 2: entries of this wavefront's 16 rows for every listed chunk
-  // (-inf where a row does not take the chunk through that list, and for rows
-  // past N); a chunk-major entry also names the row's slot for the chunk (the
-  // row's first slot plus the chunk's rank among the row's routed chunks)
-  const size_t ebase = (size_t)toff * kTileRows + w * 16 + grp * 4;
-  int run[4] = {0, 0, 0, 0};
+  if (pooled) {
+    // ---- pair records, grouped by chunk in the tile's pool range: count the
+    // rows of every entry, place the entries, then write the records
+    for_each_routed([&](int, int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    const uint32_t wr = s_union[blk >> 1];
-    const uint32_t wc = s_cunion[blk >> 1];
-    const int bit = 16 * (blk & 1) + col;
-    const int c = blk * 16 + col;
-    const bool own = causal && c == cw;  // written below
-    const bool in_rm = ((wr >> bit) & 1u) && !own;
-    const bool in_cm = ((wc >> bit) & 1u) && !own;
-    if (wave_any(in_rm || in_cm)) {
-      f32x4 vrm, vcm;
-      uint32_t koff[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float t = u[blk][r] - tau[r];
-        const bool act = row_ok[r] && t > 0.f;
-        const uint32_t seg = seg_of(__ballot(act));
-        const int rank = run[r] + __popc(seg & below);
-        run[r] += __popc(seg);
-        const float lw = act ? log2_prior<KIND>(t, a.beta) : -INFINITY;
-        vrm[r] = pooled ? -INFINITY : lw;
-        vcm[r] = pooled ? lw : -INFINITY;
-        koff[r] = (uint32_t)(roff[r] + rank) & 0xffffu;
-      }
-      if (in_rm) {
-        const int pos = s_pre[blk >> 1] + __popc(wr & ((1u << bit) - 1u));
-        *reinterpret_cast<f32x4*>(a.bias + ebase + (size_t)pos * kTileRows) = vrm;
-      }
-      // rows of this wavefront taking chunk c through the chunk-major list
-      int ncm = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ncm += vcm[r] > -INFINITY ? 1 : 0;
-      const int ntot = (int)sum_xor32(sum_xor16((float)ncm));
-      if (in_cm) {
-        const int pos = s_cpre[blk >> 1] + __popc(wc & ((1u << bit) - 1u));
-        *reinterpret_cast<f32x4*>(a.cw + ebase + (size_t)pos * kTileRows) = vcm;
-        *reinterpret_cast<u32x2*>(a.ck + ebase + (size_t)pos * kTileRows) = u32x2{koff[0] | (koff[1] << 16), koff[2] | (koff[3] << 16)};
-        if (grp == 0 && ntot > 0) atomicAdd(&s_ecnt[pos], ntot);
-      }
+    for (int r = 0; r < 4; ++r)
+      if (causal && col == 0 && dact[r]) atomicAdd(&s_ecnt[epos(cw)], 1);
+    __syncthreads();
+    const int ne = s_cpre[NW];
+    int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
+    int first = 0;
+    const int cnt_e = (int)threadIdx.x < ne ? s_ecnt[threadIdx.x] : 0;
+    block_excl_scan<8>(cnt_e, s_tmp, first);
+    if ((int)threadIdx.x < ne) {
+      s_eoff[threadIdx.x] = first;
+      a.ceo[toff + threadIdx.x] = make_int2(first, cnt_e);
+      // the entry's pairs among all pairs of its chunk
+      a.cbase[toff + threadIdx.x] = atomicAdd(&cmp[s_cl[threadIdx.x]], cnt_e);
     }
-  }
-  // the own chunk's entries of this wavefront's rows (slot: after the past chunks)
-  if (causal && col == 0) {
-    const uint32_t word = (pooled ? s_cunion : s_union)[cw >> 5];
-    if ((word >> (cw & 31)) & 1u) {
-      const int pos = (pooled ? s_cpre : s_pre)[cw >> 5] + __popc(word & ((1u << (cw & 31)) - 1u));
-      f32x4 v = {lwd[0], lwd[1], lwd[2], lwd[3]};
-      if (pooled) {
-        *reinterpret_cast<f32x4*>(a.cw + ebase + (size_t)pos * kTileRows) = v;
-        uint32_t ko[4];
+    __syncthreads();
+    const long long tb = s_tbase;
+    for_each_routed([&](int r, int c, int rank, float uu) {
+      const int e = epos(c);
+      const int j = atomicAdd(&s_efill[e], 1);
+      const int row = i0 + grp * 4 + r;
+      a.trec[tb + s_eoff[e] + j] = make_int4(row * a.g + hh, (int)(tb + roff[r] + rank),
+                                             __float_as_int(log2_prior<KIND>(uu - tau[r], a.beta)), 0);
+    });
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ko[r] = (uint32_t)(roff[r] + nrt[r]) & 0xffffu;
-        *reinterpret_cast<u32x2*>(a.ck + ebase + (size_t)pos * kTileRows) = u32x2{ko[0] | (ko[1] << 16), ko[2] | (ko[3] << 16)};
-        const int nd = (dact[0] ? 1 : 0) + (dact[1] ? 1 : 0) + (dact[2] ? 1 : 0) + (dact[3] ? 1 : 0);
-        if (nd > 0) atomicAdd(&s_ecnt[pos], nd);
-      } else {
-        *reinterpret_cast<f32x4*>(a.bias + ebase + (size_t)pos * kTileRows) = v;
+    for (int r = 0; r < 4; ++r)
+      if (causal && col == 0 && dact[r]) {
+        const int e = epos(cw);
+        const int j = atomicAdd(&s_efill[e], 1);
+        const int row = i0 + grp * 4 + r;
+        a.trec[tb + s_eoff[e] + j] = make_int4(row * a.g + hh, (int)(tb + roff[r] + nrt[r]), __float_as_int(lwd[r]), 0);
       }
-    }
+  } else {
+    // ---- row-major list: -inf for every (entry, row) of this wavefront, then
+    // the log2 weights of the attended pairs
+    const int ne = s_pre[NW];
+    float* const bw = a.bias + (size_t)toff * kTileRows + w * 16;
+    for (int x = lane; x < ne * 16; x += kWave) bw[(size_t)(x >> 4) * kTileRows + (x & 15)] = -INFINITY;
+    __syncthreads();  // the fills are done before any weight lands on them
+    for_each_routed([&](int r, int c, int, float uu) {
+      bw[(size_t)epos(c) * kTileRows + grp * 4 + r] = log2_prior<KIND>(uu - tau[r], a.beta);
+    });
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (causal && col == 0 && dact[r]) bw[(size_t)epos(cw) * kTileRows + grp * 4 + r] = lwd[r];
   }
-
-  // ---- reserve each chunk-major entry's pairs among all pairs of its chunk
-  __syncthreads();
-  const int ncm_entries = s_cpre[NW];
-  int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
-  for (int e = threadIdx.x; e < ncm_entries; e += blockDim.x)
-    a.cbase[toff + e] = atomicAdd(&cmp[s_cl[e]], s_ecnt[e]);
 }
 
 // Split the float32 summaries of the chunks the prefill routing reads into bf16

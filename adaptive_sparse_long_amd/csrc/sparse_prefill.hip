@@ -281,31 +281,6 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kCmWgPerCu = 3;  // resident chunk-major workgroups per CU
-
-// Exclusive prefix sum over a 1024-thread workgroup; returns the total.
-// s_tmp holds 16 ints and may be reused once the call returns.
-__device__ int block_excl_scan_1024(int v, int* s_tmp, int& excl) {
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    x += lane >= off ? y : 0;
-  }
-  if (lane == kWave - 1) s_tmp[w] = x;
-  __syncthreads();
-  int wpre = 0, tot = 0;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int t = s_tmp[k];
-    wpre += k < w ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  excl = wpre + x - v;
-  return tot;
-}
 }  // namespace
 
 __global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
@@ -316,8 +291,8 @@ __global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
     const int P = idx < a.n_bhc ? a.cmp[idx] : 0;
     const int ni = ((P + 31) / 32 + kCmBlocks - 1) / kCmBlocks;
     int ep, ei;
-    const int tp = block_excl_scan_1024(P, s_tmp[0], ep);
-    const int ti = block_excl_scan_1024(ni, s_tmp[1], ei);
+    const int tp = block_excl_scan<16>(P, s_tmp[0], ep);
+    const int ti = block_excl_scan<16>(ni, s_tmp[1], ei);
     if (idx < a.n_bhc) {
       a.cs[idx] = carry_p + ep;
       for (int j = 0; j < ni; ++j) {
@@ -331,65 +306,40 @@ __global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
   if (threadIdx.x == 0) *a.nitems = carry_i;
 }
 
-// One workgroup per (tile, query head, b). The destinations of up to 256 list
-// entries are looked up at once (one per thread, into LDS); then each
-// wavefront copies two entries at a time, the loads of both in flight together.
+// One workgroup per (tile, query head, b): copies the tile's pair records,
+// grouped by chunk in its pool range, to their places among the chunk-sorted
+// records (each group after the pairs that other tiles reserved before it in
+// the same chunk). Thread q copies record q; its group is found by binary
+// search over the groups' first records.
 __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
-  __shared__ long long s_dst[256];
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  __shared__ int s_first[kRoutePrefillMaxSlots];
+  __shared__ long long s_dst[kRoutePrefillMaxSlots];  // destination of record q: s_dst[group] + q
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int g = a.g;
-  const int hk = h / g;
-  const int hh = h % g;
   const size_t bh = (size_t)b * a.Hq + h;
-  const int cnt = a.ccounts[bh * a.n_tiles + tile];
+  const int cnt = min(a.ccounts[bh * a.n_tiles + tile], kRoutePrefillMaxSlots);
   if (cnt == 0) return;
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, a.causal != 0);
-  const int* cs = a.cs + ((size_t)b * a.Hkv + hk) * a.n_slots;
-  const uint32_t tb = a.tbase[bh * a.n_tiles + tile];
-  for (int e0 = 0; e0 < cnt; e0 += 256) {
-    const int ne = min(256, cnt - e0);
-    __syncthreads();  // the previous batch's destinations are read
-    if ((int)threadIdx.x < ne) {
-      const int c = a.clists[toff + e0 + threadIdx.x];
-      s_dst[threadIdx.x] = (long long)cs[c] + a.cbase[toff + e0 + threadIdx.x];
+  const int* cs = a.cs + ((size_t)b * a.Hkv + h / a.g) * a.n_slots;
+  const long long tb = a.tbase[bh * a.n_tiles + tile];
+  for (int e = threadIdx.x; e < cnt; e += blockDim.x) {
+    const int2 fe = a.ceo[toff + e];
+    s_first[e] = fe.x;
+    s_dst[e] = (long long)cs[a.clists[toff + e]] + a.cbase[toff + e] - fe.x;
+  }
+  __syncthreads();
+  const int2 last = a.ceo[toff + cnt - 1];
+  const int total = last.x + last.y;
+  for (int q = threadIdx.x; q < total; q += blockDim.x) {
+    int lo = 0, hi = cnt - 1;  // the last group starting at or before q
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= q) lo = mid;
+      else hi = mid - 1;
     }
-    __syncthreads();
-    for (int j = w; j < ne; j += 8) {
-      const int j2 = min(j + 4, ne - 1);  // the second entry (j itself when there is none)
-      const size_t ea = (size_t)(toff + e0 + j) * kTileRows;
-      const size_t eb = (size_t)(toff + e0 + j2) * kTileRows;
-      float wv[2][2];
-      uint32_t kv[2][2];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        wv[0][half] = a.cw[ea + half * kWave + lane];
-        kv[0][half] = a.ck[ea + half * kWave + lane];
-        wv[1][half] = a.cw[eb + half * kWave + lane];
-        kv[1][half] = a.ck[eb + half * kWave + lane];
-      }
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        if (x == 1 && j2 == j) break;
-        const long long dst0 = s_dst[x == 0 ? j : j2];
-        int run = 0;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int row = tile * kTileRows + half * kWave + lane;
-          const bool take = wv[x][half] > -INFINITY && row < a.N;
-          const unsigned long long m = __ballot(take);
-          if (take) {
-            const long long dst = dst0 + run + __popcll(m & ((1ull << lane) - 1ull));
-            if (dst < a.pool_cap)
-              a.recs[dst] = make_int4(row * g + hh, (int)(tb + kv[x][half]), __float_as_int(wv[x][half]), 0);
-          }
-          run += __popcll(m);
-        }
-      }
-    }
+    const long long dst = s_dst[lo] + q;
+    if (dst >= 0 && dst < a.pool_cap && tb + q < a.pool_cap) a.recs[dst] = a.trec[tb + q];
   }
 }
 
