@@ -197,9 +197,9 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.clists = reinterpret_cast<const int*>(ws + L.off_clists);
   a.ceo = reinterpret_cast<const int2*>(ws + L.off_ceo);
   a.trec = reinterpret_cast<const int4*>(ws + L.off_trec);
-  a.cbase = reinterpret_cast<const int*>(ws + L.off_cbase);
   a.cmp = reinterpret_cast<const int*>(ws + L.off_cmp);
   a.cs = reinterpret_cast<int*>(ws + L.off_cs);
+  a.cbase = reinterpret_cast<const int*>(ws + L.off_cbase);
   a.nitems = reinterpret_cast<int*>(ws + L.off_nitems);
   a.items = reinterpret_cast<int2*>(ws + L.off_items);
   a.recs = reinterpret_cast<int4*>(ws + L.off_recs);

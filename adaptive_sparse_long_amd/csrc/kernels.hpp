@@ -24,6 +24,9 @@ constexpr int kCmSlots = 16;
 // Chunk-major work item: up to kCmBlocks blocks of 32 (row, chunk) pairs of one
 // (b, kv head, chunk).
 constexpr int kCmBlocks = 16;
+// The partial-result pool is split into kPools equal parts, each with its own
+// allocation counter (workgroup id modulo kPools picks the part).
+constexpr int kPools = 8;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -40,8 +43,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Causal tile t can only list chunks 0 .. 2t+1, so tiles are packed in a
 // triangle: tile t starts at slot t*(t+1). Non-causal tiles hold n_slots each.
 // Per chunk-major list entry: the offset of its pairs among all pairs of its
-// chunk (cbase). Per (b, kv head, chunk) "bhc": the number of its pairs (cmp,
-// counted by the routing) and their start in the chunk-sorted pair records
+// chunk (cbase, reserved by the routing). Per (b, kv head, chunk) "bhc": the
+// number of its pairs (cmp) and their start in the chunk-sorted pair records
 // (cs). Work items list (bhc, first block); recs hold one pair each.
 // Per tile: its first pool slot (tbase). Per row: its first slot (rslot) and
 // number of partials (cmcnt); a row's slots follow its attended chunks in
@@ -98,7 +101,7 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
   L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
   L.off_trec = o;    o += align256(pairs * 4 * sizeof(int));
-  L.off_pool = o;    o += align256(sizeof(unsigned long long));
+  L.off_pool = o;    o += align256(kPools * sizeof(unsigned long long));
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
@@ -172,7 +175,7 @@ struct RouteArgs {
   int* cbase;
   int* cmp;  // zeroed by the summary split, counted by the routing
   int n_bhc;
-  unsigned long long* pool;  // zeroed by the summary split
+  unsigned long long* pool;  // kPools counters, zeroed by the summary split
   long long pool_cap;
   uint32_t* tbase;
   uint32_t* rslot;
@@ -255,7 +258,7 @@ hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t st
 
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
-constexpr int kRouteCap = 64;                // routing candidates per row held in LDS
+constexpr int kRouteCap = 128;               // routing candidates per row held in LDS
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 

@@ -70,7 +70,13 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   // per chunk 128 high parts, 128 low parts and 8 bf16 of padding (a chunk
   // stride of 132 dwords keeps eight consecutive lanes on distinct LDS banks).
   constexpr int SROW = 2 * D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sS[2][64 * SROW];
+  // After the scores the same LDS holds the per-row candidate lists: per
+  // wavefront 16 rows of LROW scores (float) and LROW chunk ids (uint16).
+  constexpr int LROW = kRouteCap + 4;
+  constexpr int kStageHalves = 2 * 64 * SROW;
+  constexpr int kListHalves = 8 * 16 * LROW * 3;
+  __shared__ __attribute__((aligned(16))) uint16_t s_big[kStageHalves > kListHalves ? kStageHalves : kListHalves];
+  uint16_t (*const sS)[64 * SROW] = reinterpret_cast<uint16_t (*)[64 * SROW]>(s_big);
   __shared__ uint32_t s_union[NW], s_cunion[NW];  // attended chunks: row-major, chunk-major list
   __shared__ int s_pre[NW + 1], s_cpre[NW + 1];
   __shared__ int s_ecnt[NW * 32];  // chunk-major entries: rows taking the chunk,
@@ -174,9 +180,15 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
               acc = mfma16x16x32(qa[s], *reinterpret_cast<const bf16x8*>(bp + 32 * s), acc);
               acc = mfma16x16x32(qa[s], *reinterpret_cast<const bf16x8*>(bp + D + 32 * s), acc);
             }
-            const bool cval = blk * 16 + col < ncomp;
+            // the summaries are pre-scaled: acc is u. Only the last block can
+            // hold columns past the candidates.
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u[blk][r] = cval ? acc[r] * uscale : -INFINITY;
+            for (int r = 0; r < 4; ++r) u[blk][r] = acc[r];
+            if (blk == nblk - 1) {
+              const bool cval = blk * 16 + col < ncomp;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) u[blk][r] = cval ? u[blk][r] : -INFINITY;
+            }
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
@@ -244,115 +256,138 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     }
   }
 
-  // ---- tau per row (all 16 lanes of a row group hold the same values). Only
-  // scores above max u - 1 can carry weight (tau >= max u - 1): each row's
-  // candidates, usually a handful, are gathered in ascending chunk order into
-  // an LDS list (in the summary staging, no longer read) and tau iterates over
-  // the list. A wavefront with a row of more than kRouteCap candidates
-  // iterates over all its blocks instead.
-  float tau[4];
+  // ---- tau per row. Only scores above max u - 1 can carry weight (tau >=
+  // max u - 1): each row's candidates, usually a handful, are gathered in
+  // ascending chunk order into an LDS list (in the summary staging, no longer
+  // read). A wavefront whose lists all fit solves tau and emits its rows' work
+  // in a row layout, four lanes per row; a wavefront with a row of more than
+  // kRouteCap candidates solves tau and emits from all its blocks.
   bool row_ok[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    row_ok[r] = wave_valid && (i0 + grp * 4 + r < N);
-    tau[r] = INFINITY;
-  }
+  for (int r = 0; r < 4; ++r) row_ok[r] = wave_valid && (i0 + grp * 4 + r < N);
   auto seg_of = [&](unsigned long long m) { return (uint32_t)(m >> (16 * grp)) & 0xffffu; };
   const uint32_t below = (1u << col) - 1u;
-  constexpr int NJ = kRouteCap / 16;  // list entries per lane and row: positions col + 16 j
-  float* const s_cu = reinterpret_cast<float*>(&sS[0][0]) + (size_t)w * 16 * kRouteCap;
-  uint16_t* const s_cc =
-      reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(&sS[0][0]) + 8 * 16 * kRouteCap) + (size_t)w * 16 * kRouteCap;
-  float cv[4][NJ];
+  float* const s_cu = reinterpret_cast<float*>(s_big) + (size_t)w * 16 * LROW;
+  uint16_t* const s_cc = s_big + 2 * 8 * 16 * LROW + (size_t)w * 16 * LROW;
+  float mx[4], lo[4];
+  int nc[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 4; ++r) {
+    float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) cv[r][j] = -INFINITY;
-  bool ovf = false;
-  if (wave_valid && ncand > 0) {
-    float mx[4], lo[4], hi[4];
-    int nc[4] = {0, 0, 0, 0};
+    for (int blk = 0; blk < NB; ++blk) m = fmaxf(m, u[blk][r]);
+    mx[r] = fmaxf(max16(m), ud[r]);  // -inf: no candidate at all
+    lo[r] = mx[r] - 1.f;
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float m = -INFINITY;
+  for (int blk = 0; blk < NB; ++blk) {
+    if (blk < nblk) {
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) m = fmaxf(m, u[blk][r]);
-      mx[r] = fmaxf(max16(m), ud[r]);
-      lo[r] = mx[r] - 1.f;
-      tau[r] = lo[r];
-    }
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      if (blk < nblk) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool cnd = u[blk][r] > lo[r];
-          const uint32_t seg = seg_of(__ballot(cnd));
+      for (int r = 0; r < 4; ++r) {
+        const bool cnd = u[blk][r] > lo[r];
+        const unsigned long long m = __ballot(cnd);
+        if (m != 0ull) {
+          const uint32_t seg = seg_of(m);
           const int pos = nc[r] + __popc(seg & below);
           if (cnd && pos < kRouteCap) {
-            s_cu[(grp * 4 + r) * kRouteCap + pos] = u[blk][r];
-            s_cc[(grp * 4 + r) * kRouteCap + pos] = (uint16_t)(blk * 16 + col);
+            s_cu[(grp * 4 + r) * LROW + pos] = u[blk][r];
+            s_cc[(grp * 4 + r) * LROW + pos] = (uint16_t)(blk * 16 + col);
           }
           nc[r] += __popc(seg);
         }
       }
     }
-    ovf = wave_any(nc[0] > kRouteCap || nc[1] > kRouteCap || nc[2] > kRouteCap || nc[3] > kRouteCap);
-    wave_lds_fence();
-    // tau <= max - n^-(alpha-1) with n the values above tau, all among the candidates
+  }
+  const bool ovf = wave_any(nc[0] > kRouteCap || nc[1] > kRouteCap || nc[2] > kRouteCap || nc[3] > kRouteCap);
+  wave_lds_fence();
+
+  // row layout: lanes 4 rr .. 4 rr + 3 hold row i0 + rr, lane sub the list
+  // positions 4 k + sub
+  const int rr = lane >> 2, sub = lane & 3;
+  auto to_row = [&](const float (&x)[4]) {
+    float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      hi[r] = tau_upper(mx[r], max(1, ovf ? ncand : nc[r] + ((est && ud[r] > lo[r]) ? 1 : 0)), a.alpha);
-    auto solve = [&](auto&& terms) {
-      for (int it = 0; it < a.n_iter; ++it) {
-        float f0[4] = {0.f, 0.f, 0.f, 0.f}, f1[4] = {0.f, 0.f, 0.f, 0.f}, f2[4] = {0.f, 0.f, 0.f, 0.f};
-        terms(f0, f1, f2);
-        bool conv = true;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          f0[r] = sum16(f0[r]);
-          f1[r] = sum16(f1[r]);
-          if (KIND != 1) f2[r] = sum16(f2[r]);
-          if (est) tau_terms<KIND>(ud[r], tau[r], a.beta, f0[r], f1[r], f2[r]);
-          const float nt = tau_step<KIND>(tau[r], f0[r], f1[r], f2[r], a.beta, lo[r], hi[r]);
-          conv = conv && tau_converged(tau[r], nt);
-          tau[r] = nt;
-        }
-        if (wave_all(conv)) break;
-      }
-    };
-    if (!ovf) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int pos = col + 16 * j;
-          cv[r][j] = pos < nc[r] ? s_cu[(grp * 4 + r) * kRouteCap + pos] : -INFINITY;
-        }
-      solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tau_terms<KIND>(cv[r][j], tau[r], a.beta, f0[r], f1[r], f2[r]);
-      });
-    } else {
-      // blocks holding none of the candidates are left out of the iterations
-      uint32_t live = 0u;
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
-        live |= wave_any(any) ? (1u << blk) : 0u;
-      }
-      solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-          if ((live >> blk) & 1u) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
-          }
-        }
-      });
+    for (int r = 0; r < 4; ++r) {
+      const float t = __shfl(x[r], (rr >> 2) * 16);
+      v = (rr & 3) == r ? t : v;
     }
+    return v;
+  };
+  float ncf[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ncf[r] = (float)nc[r];
+  const float mx_r = to_row(mx), ud_r = to_row(ud);
+  const int nc_r = (int)to_row(ncf);
+  const bool row_ok_r = wave_valid && i0 + rr < N;
+  int kmax = 0;  // list steps of the wavefront (its longest list / 4)
+  auto cand = [&](int k) {  // list position 4 k + sub of the lane's row, -inf past its end
+    const int p = 4 * k + sub;
+    return p < nc_r ? s_cu[rr * LROW + p] : -INFINITY;
+  };
+  float tau_r = INFINITY;
+  float tau[4];
+  auto solve = [&](auto&& terms, float (&t)[4], float (&lo4)[4], float (&hi4)[4], auto&& reduce, int nrows) {
+    for (int it = 0; it < a.n_iter; ++it) {
+      float f0[4] = {0.f, 0.f, 0.f, 0.f}, f1[4] = {0.f, 0.f, 0.f, 0.f}, f2[4] = {0.f, 0.f, 0.f, 0.f};
+      terms(f0, f1, f2);
+      bool conv = true;
+      for (int r = 0; r < nrows; ++r) {
+        f0[r] = reduce(f0[r]);
+        f1[r] = reduce(f1[r]);
+        if (KIND != 1) f2[r] = reduce(f2[r]);
+        const float udr = nrows == 1 ? ud_r : ud[r];
+        if (est) tau_terms<KIND>(udr, t[r], a.beta, f0[r], f1[r], f2[r]);
+        const float nt = tau_step<KIND>(t[r], f0[r], f1[r], f2[r], a.beta, lo4[r], hi4[r]);
+        conv = conv && (tau_converged(t[r], nt) || !(t[r] > -INFINITY));
+        t[r] = nt;
+      }
+      if (wave_all(conv)) break;
+    }
+  };
+  if (!ovf) {
+    kmax = (int)wave_max((float)((min(nc_r, kRouteCap) + 3) >> 2));
+    // tau <= max - n^-(alpha-1), n the values above tau: all among the candidates
+    float t1[4] = {mx_r - 1.f, 0.f, 0.f, 0.f};
+    float lo1[4] = {mx_r - 1.f, 0.f, 0.f, 0.f};
+    float hi1[4] = {tau_upper(mx_r, max(1, nc_r + ((est && ud_r > mx_r - 1.f) ? 1 : 0)), a.alpha), 0.f, 0.f, 0.f};
+    solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
+            for (int k = 0; k < kmax; ++k) tau_terms<KIND>(cand(k), t1[0], a.beta, f0[0], f1[0], f2[0]);
+          },
+          t1, lo1, hi1,
+          [](float x) {  // sum over the row's four lanes
+            const float y = x + dpp_f<kDppXor1>(x);
+            return y + dpp_f<kDppXor2>(y);
+          },
+          1);
+    tau_r = mx_r > -INFINITY ? t1[0] : INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tau[r] = __shfl(tau_r, (grp * 4 + r) * 4);
+  } else {
+    float hi[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = tau_upper(mx[r], max(ncand, 1), a.alpha);
+      tau[r] = lo[r];
+    }
+    // blocks holding none of the candidates are left out of the iterations
+    uint32_t live = 0u;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
+      live |= wave_any(any) ? (1u << blk) : 0u;
+    }
+    solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+              if ((live >> blk) & 1u) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
+              }
+            }
+          },
+          tau, lo, hi, [](float x) { return sum16(x); }, 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tau[r] = mx[r] > -INFINITY ? tau[r] : INFINITY;
   }
 
   // ---- tau output: lanes 0, 16, 32, 48 hold rows grp*4 .. +3
@@ -371,6 +406,9 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     dact[r] = row_ok[r] && (est ? (td > 0.f) : causal);
     lwd[r] = !row_ok[r] ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   }
+  const float td_r = ud_r - tau_r;
+  const bool dact_r = row_ok_r && (est ? (td_r > 0.f) : causal);
+  const float lwd_r = !row_ok_r ? -INFINITY : (est ? (td_r > 0.f ? log2_prior<KIND>(td_r, a.beta) : -INFINITY) : 0.f);
 
   // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
   if (a.bits != nullptr) {
@@ -378,8 +416,8 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) md[r] = __ballot(dact[r]);
     const bool write_bits = wave_valid && lane < 16 && i0 + lane < N;
-    const int rg = lane >> 2, rr = lane & 3;  // D-layout owner of row `lane`
-    const bool dl = ((rr == 0 ? md[0] : rr == 1 ? md[1] : rr == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
+    const int rg = lane >> 2, r4 = lane & 3;  // D-layout owner of row `lane`
+    const bool dl = ((r4 == 0 ? md[0] : r4 == 1 ? md[1] : r4 == 2 ? md[2] : md[3]) >> (16 * rg)) & 1ull;
     uint32_t* bdst = a.bits + ((bh * (size_t)N) + min(i0 + lane, N - 1)) * (size_t)a.bits_words;
 #pragma unroll
     for (int wd = 0; wd < NW; ++wd) {
@@ -391,7 +429,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
           unsigned long long mb[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
-          const unsigned long long mr = rr == 0 ? mb[0] : rr == 1 ? mb[1] : rr == 2 ? mb[2] : mb[3];
+          const unsigned long long mr = r4 == 0 ? mb[0] : r4 == 1 ? mb[1] : r4 == 2 ? mb[2] : mb[3];
           word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
         }
       }
@@ -402,37 +440,39 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       for (int wd = NW; wd < a.bits_words; ++wd) bdst[wd] = 0u;
   }
 
-  // ---- the routed past chunks of this lane's rows, in ascending chunk order
-  // per row (from the candidate list, or from all blocks): fn(r, chunk, rank,
-  // u) for each; afterwards run[r] holds the row's count. Called by the whole
-  // wavefront.
-  int run[4];
-  auto for_each_routed = [&](auto&& fn) {
+  // ---- the routed past chunks of the wavefront's rows, in ascending chunk
+  // order per row, from the lists (row layout) or from all blocks (block
+  // layout, wavefronts with an overflowing list). Called by the whole
+  // wavefront; afterwards the running counts hold each row's number of routed
+  // past chunks.
+  //   row layout: fn(chunk, rank, u) for this lane's row rr;
+  int run_r = 0;
+  auto for_each_routed_row = [&](auto&& fn) {
+    run_r = 0;
+    for (int k = 0; k < kmax; ++k) {
+      const float uk = cand(k);
+      const bool act = row_ok_r && uk > tau_r;
+      const uint32_t q = (uint32_t)(__ballot(act) >> (4 * rr)) & 0xfu;
+      const int rank = run_r + __popc(q & ((1u << sub) - 1u));
+      run_r += __popc(q);
+      if (act) fn((int)s_cc[rr * LROW + 4 * k + sub], rank, uk);
+    }
+  };
+  //   block layout: fn(r, chunk, rank, u) for this lane's rows grp*4 + r.
+  int run4[4] = {0, 0, 0, 0};
+  auto for_each_routed_blk = [&](auto&& fn) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) run[r] = 0;
-    if (!ovf) {
+    for (int r = 0; r < 4; ++r) run4[r] = 0;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+    for (int blk = 0; blk < NB; ++blk) {
+      if (blk < nblk) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool act = row_ok[r] && cv[r][j] > tau[r];
+          const bool act = row_ok[r] && u[blk][r] > tau[r];
           const uint32_t seg = seg_of(__ballot(act));
-          const int rank = run[r] + __popc(seg & below);
-          run[r] += __popc(seg);
-          if (act) fn(r, (int)s_cc[(grp * 4 + r) * kRouteCap + col + 16 * j], rank, cv[r][j]);
-        }
-    } else {
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        if (blk < nblk) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool act = row_ok[r] && u[blk][r] > tau[r];
-            const uint32_t seg = seg_of(__ballot(act));
-            const int rank = run[r] + __popc(seg & below);
-            run[r] += __popc(seg);
-            if (act) fn(r, blk * 16 + col, rank, u[blk][r]);
-          }
+          const int rank = run4[r] + __popc(seg & below);
+          run4[r] += __popc(seg);
+          if (act) fn(r, blk * 16 + col, rank, u[blk][r]);
         }
       }
     }
@@ -440,20 +480,34 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 
   // ---- pool slots: one per attended chunk (routed past chunks, then the own
   // chunk) of every row of the tile, taken with one atomic; the slots of a row
-  // are consecutive, in chunk order. Rows are numbered (wavefront, row group,
-  // r) inside the tile.
-  for_each_routed([](int, int, int, float) {});
-  int nrt[4], nsl[4];
+  // are consecutive, in chunk order. Rows are numbered (wavefront, row in
+  // wavefront) inside the tile.
+  int nsl_r = 0, row_pre = 0;          // row layout: slots of the row, slots of the rows before it
+  int nsl4[4] = {0, 0, 0, 0}, pre4[4] = {0, 0, 0, 0};  // block layout
+  if (!ovf) {
+    for_each_routed_row([](int, int, float) {});
+    nsl_r = run_r + (dact_r ? 1 : 0);
+    int x = sub == 0 ? nsl_r : 0;
+    const int x0 = x;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    nrt[r] = run[r];
-    nsl[r] = nrt[r] + (dact[r] ? 1 : 0);
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      x += lane >= off ? y : 0;
+    }
+    row_pre = __shfl(x - x0, 4 * rr);
+    if (lane == kWave - 1) s_wtot[w] = x;
+  } else {
+    for_each_routed_blk([](int, int, int, float) {});
+#pragma unroll
+    for (int r = 0; r < 4; ++r) nsl4[r] = run4[r] + (dact[r] ? 1 : 0);
+    const int grp_tot = nsl4[0] + nsl4[1] + nsl4[2] + nsl4[3];
+    const int g0 = __builtin_amdgcn_readlane(grp_tot, 0), g1 = __builtin_amdgcn_readlane(grp_tot, 16);
+    const int g2 = __builtin_amdgcn_readlane(grp_tot, 32), g3 = __builtin_amdgcn_readlane(grp_tot, 48);
+    pre4[0] = (grp > 0 ? g0 : 0) + (grp > 1 ? g1 : 0) + (grp > 2 ? g2 : 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) pre4[r] = pre4[r - 1] + nsl4[r - 1];
+    if (lane == 0) s_wtot[w] = g0 + g1 + g2 + g3;
   }
-  const int grp_tot = nsl[0] + nsl[1] + nsl[2] + nsl[3];
-  const int g0 = __builtin_amdgcn_readlane(grp_tot, 0), g1 = __builtin_amdgcn_readlane(grp_tot, 16);
-  const int g2 = __builtin_amdgcn_readlane(grp_tot, 32), g3 = __builtin_amdgcn_readlane(grp_tot, 48);
-  const int grp_pre = (grp > 0 ? g0 : 0) + (grp > 1 ? g1 : 0) + (grp > 2 ? g2 : 0);
-  if (lane == 0) s_wtot[w] = g0 + g1 + g2 + g3;
   __syncthreads();
   if (threadIdx.x == 0) {
     int tot = 0;
@@ -461,36 +515,45 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     for (int ww = 0; ww < 8; ++ww) tot += s_wtot[ww];
     long long base = -1;
     if (tot > 0) {
-      const unsigned long long got = atomicAdd(a.pool, (unsigned long long)tot);
-      base = got + (unsigned long long)tot <= (unsigned long long)a.pool_cap ? (long long)got : -1;
+      // the workgroup's part of the pool
+      const int part = (int)((blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z)) % kPools);
+      const unsigned long long cap = (unsigned long long)a.pool_cap / kPools;
+      const unsigned long long got = atomicAdd(&a.pool[part], (unsigned long long)tot);
+      base = got + (unsigned long long)tot <= cap ? (long long)(part * cap + got) : -1;
     }
     s_tbase = base;
     a.tbase[bh * a.n_tiles + tile] = base >= 0 ? (uint32_t)base : 0u;
   }
   __syncthreads();
   const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  const long long tb = s_tbase;
   int wpre = 0;
 #pragma unroll
   for (int ww = 0; ww < 8; ++ww) wpre += ww < w ? s_wtot[ww] : 0;
-  int roff[4];  // first slot of each row, from the tile's first slot
-  roff[0] = wpre + grp_pre;
-#pragma unroll
-  for (int r = 1; r < 4; ++r) roff[r] = roff[r - 1] + nsl[r - 1];
-  if (col == 0) {
+  if (!ovf) {
+    if (sub == 0 && row_ok_r) {
+      const size_t ri = bh * (size_t)N + i0 + rr;
+      a.cmcnt[ri] = pooled ? (uint16_t)nsl_r : (uint16_t)0;
+      a.rslot[ri] = pooled ? (uint32_t)(tb + wpre + row_pre) : 0u;
+    }
+  } else if (col == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (row_ok[r]) {
         const size_t ri = bh * (size_t)N + i0 + grp * 4 + r;
-        a.cmcnt[ri] = pooled ? (uint16_t)nsl[r] : (uint16_t)0;
-        a.rslot[ri] = pooled ? (uint32_t)(s_tbase + roff[r]) : 0u;
+        a.cmcnt[ri] = pooled ? (uint16_t)nsl4[r] : (uint16_t)0;
+        a.rslot[ri] = pooled ? (uint32_t)(tb + wpre + pre4[r]) : 0u;
       }
   }
 
   // ---- the tile's attended chunks: chunk-major list if pooled, else row-major
   uint32_t* const un = pooled ? s_cunion : s_union;
-  for_each_routed([&](int, int c, int, float) { atomicOr(&un[c >> 5], 1u << (c & 31)); });
-  const bool own_any = causal && col == 0 && (dact[0] || dact[1] || dact[2] || dact[3]);
-  if (own_any) atomicOr(&un[cw >> 5], 1u << (cw & 31));
+  if (!ovf && pooled) {
+    for_each_routed_row([&](int c, int, float) { atomicOr(&un[c >> 5], 1u << (c & 31)); });
+  } else {
+    for_each_routed_blk([&](int, int c, int, float) { atomicOr(&un[c >> 5], 1u << (c & 31)); });
+  }
+  if (causal && col == 0 && (dact[0] || dact[1] || dact[2] || dact[3])) atomicOr(&un[cw >> 5], 1u << (cw & 31));
   __syncthreads();
   if (threadIdx.x == 0 || threadIdx.x == kWave) {
     const bool cm = threadIdx.x != 0;
@@ -527,10 +590,15 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   if (pooled) {
     // ---- pair records, grouped by chunk in the tile's pool range: count the
     // rows of every entry, place the entries, then write the records
-    for_each_routed([&](int, int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
+    if (!ovf) {
+      for_each_routed_row([&](int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
+      if (causal && sub == 0 && dact_r) atomicAdd(&s_ecnt[epos(cw)], 1);
+    } else {
+      for_each_routed_blk([&](int, int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (causal && col == 0 && dact[r]) atomicAdd(&s_ecnt[epos(cw)], 1);
+      for (int r = 0; r < 4; ++r)
+        if (causal && col == 0 && dact[r]) atomicAdd(&s_ecnt[epos(cw)], 1);
+    }
     __syncthreads();
     const int ne = s_cpre[NW];
     int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
@@ -544,22 +612,24 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       a.cbase[toff + threadIdx.x] = atomicAdd(&cmp[s_cl[threadIdx.x]], cnt_e);
     }
     __syncthreads();
-    const long long tb = s_tbase;
-    for_each_routed([&](int r, int c, int rank, float uu) {
-      const int e = epos(c);
+    auto put = [&](int e, int row, long long slot, float lw) {
       const int j = atomicAdd(&s_efill[e], 1);
-      const int row = i0 + grp * 4 + r;
-      a.trec[tb + s_eoff[e] + j] = make_int4(row * a.g + hh, (int)(tb + roff[r] + rank),
-                                             __float_as_int(log2_prior<KIND>(uu - tau[r], a.beta)), 0);
-    });
+      a.trec[tb + s_eoff[e] + j] = make_int4(row * a.g + hh, (int)slot, __float_as_int(lw), 0);
+    };
+    if (!ovf) {
+      const long long s0 = tb + wpre + row_pre;
+      for_each_routed_row([&](int c, int rank, float uu) {
+        put(epos(c), i0 + rr, s0 + rank, log2_prior<KIND>(uu - tau_r, a.beta));
+      });
+      if (causal && sub == 0 && dact_r) put(epos(cw), i0 + rr, s0 + (nsl_r - 1), lwd_r);
+    } else {
+      for_each_routed_blk([&](int r, int c, int rank, float uu) {
+        put(epos(c), i0 + grp * 4 + r, tb + wpre + pre4[r] + rank, log2_prior<KIND>(uu - tau[r], a.beta));
+      });
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (causal && col == 0 && dact[r]) {
-        const int e = epos(cw);
-        const int j = atomicAdd(&s_efill[e], 1);
-        const int row = i0 + grp * 4 + r;
-        a.trec[tb + s_eoff[e] + j] = make_int4(row * a.g + hh, (int)(tb + roff[r] + nrt[r]), __float_as_int(lwd[r]), 0);
-      }
+      for (int r = 0; r < 4; ++r)
+        if (causal && col == 0 && dact[r]) put(epos(cw), i0 + grp * 4 + r, tb + wpre + pre4[r] + (nsl4[r] - 1), lwd[r]);
+    }
   } else {
     // ---- row-major list: -inf for every (entry, row) of this wavefront, then
     // the log2 weights of the attended pairs
@@ -567,7 +637,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     float* const bw = a.bias + (size_t)toff * kTileRows + w * 16;
     for (int x = lane; x < ne * 16; x += kWave) bw[(size_t)(x >> 4) * kTileRows + (x & 15)] = -INFINITY;
     __syncthreads();  // the fills are done before any weight lands on them
-    for_each_routed([&](int r, int c, int, float uu) {
+    for_each_routed_blk([&](int r, int c, int, float uu) {
       bw[(size_t)epos(c) * kTileRows + grp * 4 + r] = log2_prior<KIND>(uu - tau[r], a.beta);
     });
 #pragma unroll
@@ -576,14 +646,16 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
 }
 
-// Split the float32 summaries of the chunks the prefill routing reads into bf16
-// high parts and bf16 low parts (x - high), once per call; also clears the
-// per-chunk pair counters and the pool slot counter.
+// Scale the float32 summaries of the chunks the prefill routing reads into u
+// units ((alpha - 1) * scaling_factor / sqrt(d)) and split them into bf16 high
+// parts and bf16 low parts (x - high), once per call; also clears the
+// per-chunk pair counters and the pool slot counters.
 __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need) {
   constexpr int D = 128;
   // the per-chunk pair counters the routing adds to start from zero
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_bhc; i += gridDim.x * blockDim.x) a.cmp[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.pool = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x < kPools) a.pool[threadIdx.x] = 0ull;
+  const float uscale = (a.alpha - 1.f) * a.zscale;
   const size_t per_bh = (size_t)n_need * (D / 8);
   const size_t total = (size_t)a.B * a.Hkv * per_bh;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
@@ -592,8 +664,13 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
     const size_t c = rem / (D / 8);
     const int e8 = (int)(rem % (D / 8)) * 8;
     const float* src = a.S + (bh * a.s_cap + c) * D + e8;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+    f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x0[e] *= uscale;
+      x1[e] *= uscale;
+    }
     bf16x8 hi, lo;
     split_hi_lo(x0, x1, hi, lo);
     const size_t dst = (bh * a.n_slots + c) * D + e8;

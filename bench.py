@@ -41,12 +41,16 @@ from adaptive_sparse_long_amd.workloads import (  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+# fp32 VALU issue without packed-fp32 instructions: 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz = 39.3e12 lane-operations/s (FMA counted once)
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 C = 64
 CSRC = os.path.join(ROOT, "adaptive_sparse_long_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources each kernel's code depends on (a changed source voids its measured traffic).
 KERNEL_SOURCES = {
-    "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_route_prefill": ["route.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_prefill_cm": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_attn": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
@@ -122,10 +126,14 @@ class Timer:
 
 
 # --------------------------------------------------------------------------- prefill
-def prefill_flops(bits: torch.Tensor, N: int, d: int):
-    """Algorithmic flops (per row: 4 d x visible tokens of its routed chunks) and
-    executed flops (per 32-row wavefront block: 4 d x 32 x 64 per chunk that any
-    of its rows routed and that is not in its future)."""
+def prefill_work(bits: torch.Tensor, N: int, d: int):
+    """Work counts of one prefill from the routed-chunk bits:
+    alg: attention flops, 4 d per (row, visible key of a routed chunk);
+    pair: MFMA flops of the chunk-major pass, 4 d x 64 keys per (row, routed
+      chunk) pair (the own chunk is masked inside its 64 keys);
+    dense: causal dense attention flops;
+    scores: routing scores, one per (row, complete past chunk) (causal);
+    per_row: routed chunks per row."""
     B, Hq, _, W = bits.shape
     n_slots = -(-N // C)
     c = torch.arange(n_slots, device=bits.device)
@@ -133,15 +141,11 @@ def prefill_flops(bits: torch.Tensor, N: int, d: int):
     i = torch.arange(N, device=bits.device)
     vis = torch.clamp(i[:, None] + 1 - c[None, :] * C, 0, C)  # causal visible tokens per (row, chunk)
     alg = 4.0 * d * float((on * vis).sum())
-    rows = (N + 31) // 32
-    pad = rows * 32 - N
-    onp = torch.nn.functional.pad(on, (0, 0, 0, pad)).view(B, Hq, rows, 32, n_slots).any(dim=3)
-    own = torch.arange(rows, device=bits.device) * 32 // C
-    not_future = c[None, :] <= own[:, None]
-    execd = 4.0 * d * 32 * C * float((onp & not_future).sum())
+    pairs = float(on.sum())
+    pair = 4.0 * d * C * pairs
     dense = 2.0 * 2.0 * d * (N * (N + 1) / 2.0) * B * Hq
-    per_row = float(on.sum()) / (B * Hq * N)
-    return alg, execd, dense, per_row
+    scores = float(B * Hq * sum(r // C for r in range(N)))
+    return alg, pair, dense, scores, pairs / (B * Hq * N)
 
 
 def bench_prefill(w, steps, warmup):
@@ -179,17 +183,17 @@ def bench_prefill(w, steps, warmup):
     wall = (time.perf_counter() - t0) / steps
     # work counts (outside the timed region)
     _, bits, _ = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
-    alg, execd, dense, per_row = prefill_flops(bits, w.N, w.d)
-    ms_attn = t_attn.mean_ms()
+    alg, pair, dense, scores, per_row = prefill_work(bits, w.N, w.d)
     res = {
         "wall_ms": wall * 1e3,
         "ms_summarize": t_sum.mean_ms(),
         "ms_route": t_route.mean_ms(),
-        "ms_attention": ms_attn,
+        "ms_attention": t_attn.mean_ms(),
         "alg_flops": alg,
-        "exec_flops": execd,
+        "pair_flops": pair,
         "dense_causal_flops": dense,
-        "active_chunk_frac_per_row": per_row,
+        "route_scores": scores,
+        "routed_chunks_per_row": per_row,
     }
     del Q, K, V, S, ws, O, bits
     torch.cuda.empty_cache()
@@ -359,20 +363,21 @@ def main():
     log(f"prefill done: {pre['wall_ms']:.3f} ms/step")
     ms_step = pre["ms_summarize"] + pre["ms_route"] + pre["ms_attention"]
     value = wp.N / (ms_step / 1e3)
-    ach = pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12
+    # Dominant kernel: the routing (dash_route: a 4 us summary split, then
+    # k_route_prefill), bound by VALU issue. Algorithmic work: 2 fp32 operations
+    # (running max, candidate test) per routing score.
+    route_ops = 2.0 * pre["route_scores"]
+    ach = route_ops / (pre["ms_route"] / 1e3) / 1e12
     roof = {
-        "kernel": "k_sparse_prefill",
-        "bound": "mfma",
+        "kernel": "k_route_prefill",
+        "bound": "alu",
         "achieved": ach,
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": PEAK_VALU_TOPS,
         "unit": "TFLOP/s",
-        "frac": ach / PEAK_BF16_TFLOPS,
-        "traffic": measured_traffic("k_sparse_prefill"),
-        "executed_tflops": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
-        "executed_frac": pre["exec_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-        "alg_flops_per_launch": pre["alg_flops"],
-        "exec_flops_per_launch": pre["exec_flops"],
-        "ms_per_launch": pre["ms_attention"],
+        "frac": ach / PEAK_VALU_TOPS,
+        "traffic": measured_traffic("k_route_prefill"),
+        "alg_ops_per_launch": route_ops,
+        "ms_per_launch": pre["ms_route"],
     }
     out = {
         "metric": "sparse prefill tokens/s at 32K + decode us/step at 128K; % of MFMA/HBM roofline",
@@ -396,10 +401,15 @@ def main():
         "prefill": {
             "ms_summarize": pre["ms_summarize"], "ms_route": pre["ms_route"], "ms_attention": pre["ms_attention"],
             "wall_ms_per_step": pre["wall_ms"],
-            "active_chunk_frac_per_row": pre["active_chunk_frac_per_row"],
-            "exec_over_alg": pre["exec_flops"] / pre["alg_flops"],
+            "routed_chunks_per_row": pre["routed_chunks_per_row"],
             "alg_over_dense": pre["alg_flops"] / pre["dense_causal_flops"],
             "dense_equiv_tflops": pre["dense_causal_flops"] / (ms_step / 1e3) / 1e12,
+            # sparse attention (dash_sparse_attn_prefill, all of its kernels): MFMA
+            # rate on the executed (row, chunk) pair blocks and on the algorithmic work
+            "attention_pair_tflops": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
+            "attention_pair_frac": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attention_alg_tflops": pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
+            "attention_traffic": measured_traffic("k_prefill_cm"),
         },
         "roofline": roof,
     }
