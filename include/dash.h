@@ -141,12 +141,17 @@ size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int 
  * works" 3) over rows 0 .. N-1:
  *   O_i = sum_j softmax_j(<q_i, k_j> / sqrt(d) + log w_{i, c(j)}) v_j
  * over the tokens j of the chunks routed to row i (j <= i when causal), w the
- * routing prior (1 for an always-attended own chunk). Reads the work lists
- * that dash_route (prefill mode, same sizes and params) left in `workspace`
- * and uses the rest of it for per-(row, chunk) partial results: a row's first
- * routed past chunks are attended chunk by chunk (all rows that routed a chunk
- * share one pass over it), the rest row by row, and the partials are merged
- * (the online-softmax merge is exact in any order).
+ * routing prior (1 for an always-attended own chunk). Reads the work that
+ * dash_route (prefill mode, same sizes and params) left in `workspace` and
+ * uses the rest of it for partial results. Every attended (row, chunk) pair is
+ * computed chunk by chunk -- all pairs of a chunk share one pass over its keys
+ * and values -- into a partial result (the log of its weight sum and its
+ * normalised output), and each row's partials are then merged (the
+ * online-softmax merge is exact in any order). Tiles of 128 rows whose pairs
+ * did not fit the partial-result pool (16 per row on average; only near-dense
+ * routing at long lengths exceeds it) are attended row by row instead; their
+ * results match up to rounding, so only then can two identical calls differ
+ * in the last bits.
  *   Q [B, Hq, N, d], K/V [B, Hkv, Lmax, d], O [B, Hq, N, d], all dtype dt.
  * --------------------------------------------------------------------------- */
 dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V,
