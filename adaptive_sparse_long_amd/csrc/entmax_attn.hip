@@ -38,6 +38,8 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
   return __builtin_amdgcn_perm(y, x, 0x07060302u);
 }
 
+__device__ __forceinline__ size_t bh_of(const EntmaxAttnArgs& a, int b, int h) { return (size_t)b * a.H + h; }
+
 template <typename T>
 struct Elem;
 template <>
@@ -76,6 +78,12 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
   const T* Vp = static_cast<const T*>(a.V) + bh * (size_t)N * D;
   const int nT = (N + 63) / 64;
 
+  if (a.only_marked) {
+    // redo this row block only if the single-pass kernel left it (tau = NaN)
+    const int row = blockIdx.x * 128 + (int)threadIdx.x;
+    const bool marked = threadIdx.x < 128 && row < N && isnan(a.tau[bh_of(a, b, h) * (size_t)N + row]);
+    if (!__syncthreads_or(marked)) return;
+  }
   for (int i = threadIdx.x; i < 4 * kMaxMaskWords; i += blockDim.x) (&s_cand[0][0])[i] = 0u;
   for (int i = threadIdx.x; i < 2 * kMaxMaskWords; i += blockDim.x) (&s_mask[0][0])[i] = 0u;
   __syncthreads();
@@ -326,9 +334,264 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Single-pass kernel (bf16). Four wavefronts x 32 rows per workgroup share each
+// 64-key K tile, staged once in a double-buffered LDS ring. A lane keeps, in its
+// own LDS list, the scores of its row that lie above the row's running max - 1
+// (the only ones that can carry weight, since tau >= max u - 1), pruning the
+// list whenever the max grows. After the pass, tau is solved over the row's
+// two lists (lanes l and l ^ 32) and the output gathers the V rows of the
+// support directly: O_i = sum_j P_ij v_j / sum_j P_ij. A wavefront with a list
+// past kEntmaxCap writes tau = NaN for its rows and leaves its row block to
+// the general kernel, launched after this one.
+// ---------------------------------------------------------------------------
+template <int D, int KIND>
+__global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
+  constexpr int NS = D / 16;
+  constexpr int KROW = D + 8;
+  constexpr int CAP = kEntmaxCap;
+  constexpr int NLD = D / 32;  // 16-byte K loads per thread and tile
+  constexpr int HD = D / 2;    // output dims per lane
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * KROW];
+  __shared__ float s_cu[4][CAP][kWave];     // candidate raw scores: [wavefront][entry][lane]
+  __shared__ uint16_t s_ck[4][CAP][kWave];  // their keys
+  __shared__ uint32_t s_mask[2][kMaxMaskWords];
+
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int hi32 = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int N = a.N;
+  const int L = a.varlen ? min(max(a.varlen[b], 0), N) : N;
+  const int r0 = blockIdx.x * 128 + w * 32;
+  const int qi = r0 + (lane & 31);
+  const bool row_ok = qi < L;
+  const bool causal = a.causal != 0;
+  const size_t bh = (size_t)b * a.H + h;
+  const uint16_t* Qp = static_cast<const uint16_t*>(a.Q) + bh * (size_t)N * D;
+  const uint16_t* Kp = static_cast<const uint16_t*>(a.K) + bh * (size_t)N * D;
+  const uint16_t* Vp = static_cast<const uint16_t*>(a.V) + bh * (size_t)N * D;
+  const int nT = (N + 63) / 64;
+
+  for (int i = tid; i < 2 * kMaxMaskWords; i += blockDim.x) (&s_mask[0][0])[i] = 0u;
+
+  // key tiles of the workgroup (uniform) and of this wavefront
+  const int wg_r0 = blockIdx.x * 128;
+  const int n_kt_wg = wg_r0 < L ? (causal ? min(L - 1, wg_r0 + 127) : L - 1) / 64 + 1 : 0;
+  const int n_kt = r0 < L ? (causal ? min(L - 1, r0 + 31) : L - 1) / 64 + 1 : 0;
+
+  // Q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
+  bf16x8 qb[NS];
+  {
+    const uint16_t* qp = Qp + (size_t)qi * D + 8 * hi32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(row_ok ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0});
+  }
+
+  // K tiles in flight: registers of NP tiles ahead of the one being computed
+  constexpr int NP = 2;
+  u32x4 kr[NP][NLD];
+  auto load_tile = [&](int J, u32x4 (&dst)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + 256 * i;
+      const int key = J * 64 + idx / (D / 8);
+      dst[i] = key < L ? ldg16(Kp + (size_t)key * D + (idx % (D / 8)) * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf, const u32x4 (&src)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int idx = tid + 256 * i;
+      *reinterpret_cast<u32x4*>(&sK[buf][(idx / (D / 8)) * KROW + (idx % (D / 8)) * 8]) = src[i];
+    }
+  };
+
+  // ---- the pass over the key tiles, in raw score units s (u = scale * s,
+  // scale > 0): a candidate has s > max s - 1 / scale
+  const float inv_scale = 1.f / a.scale;
+  const bool rows_full = r0 + 31 < L;  // every row of the wavefront is valid
+  float m_run = -INFINITY;
+  int cnt = 0;  // candidates of this lane (past CAP: overflow)
+  auto process = [&](int J, int buf) {
+    // S^T = K Q^T: lane's query qi, keys J*64 + 32 kb + 8 (r/4) + 4 hi32 + r%4
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+    const uint16_t* ka = &sK[buf][(lane & 31) * KROW + 8 * hi32];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      s0 = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ka + 16 * s), qb[s], s0);
+      s1 = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ka + 32 * KROW + 16 * s), qb[s], s1);
+    }
+    // masks only where the tile reaches the sequence end or the causal diagonal
+    if (!(rows_full && J * 64 + 63 < L && (!causal || J * 64 + 63 <= r0))) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = J * 64 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+        const bool v0 = row_ok && kk < L && (!causal || kk <= qi);
+        const bool v1 = row_ok && kk + 32 < L && (!causal || kk + 32 <= qi);
+        s0[r] = v0 ? s0[r] : -INFINITY;
+        s1[r] = v1 ? s1[r] : -INFINITY;
+      }
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
+    const float tmax = max_xor32(lmax);
+    if (tmax > m_run) {
+      // the row's max grows: keep only the entries above the new max - 1 / scale
+      m_run = tmax;
+      if (cnt <= CAP) {
+        int k2 = 0;
+        for (int e = 0; e < cnt; ++e) {
+          const float v = s_cu[w][e][lane];
+          if (v > m_run - inv_scale) {
+            s_cu[w][k2][lane] = v;
+            s_ck[w][k2][lane] = s_ck[w][e][lane];
+            ++k2;
+          }
+        }
+        cnt = k2;
+      }
+    }
+    const float thr = m_run - inv_scale;
+    if (lmax > thr) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = J * 64 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+        if (s0[r] > thr) {
+          if (cnt < CAP) {
+            s_cu[w][cnt][lane] = s0[r];
+            s_ck[w][cnt][lane] = (uint16_t)kk;
+          }
+          ++cnt;
+        }
+        if (s1[r] > thr) {
+          if (cnt < CAP) {
+            s_cu[w][cnt][lane] = s1[r];
+            s_ck[w][cnt][lane] = (uint16_t)(kk + 32);
+          }
+          ++cnt;
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    if (p < n_kt_wg) load_tile(p, kr[p]);
+  if (n_kt_wg > 0) store_tile(0, kr[0]);
+  __syncthreads();
+  for (int J0 = 0; J0 < n_kt_wg; J0 += NP) {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const int J = J0 + q;
+      if (J < n_kt_wg) {
+        if (J + NP < n_kt_wg) load_tile(J + NP, kr[q]);  // kr[q] (tile J) is already in LDS
+        if (J < n_kt) process(J, J & 1);
+        if (J + 1 < n_kt_wg) store_tile((J + 1) & 1, kr[(q + 1) % NP]);
+        __syncthreads();
+      }
+    }
+  }
+
+  if (wave_any(cnt > CAP)) {
+    // leave the row block to the general kernel
+    if (lane < 32 && qi < N) a.tau[bh * (size_t)N + qi] = __builtin_nanf("");
+  } else {
+    // ---- tau over the row's candidates: this lane's list and its partner's
+    const int pl = lane ^ 32;
+    const int cnt_p = __shfl_xor(cnt, 32);
+    float tau = 0.f;
+    const float mu = a.scale * m_run;  // max u of the row
+    if (wave_any(row_ok)) {
+      float lo = mu - 1.f;
+      float hi = row_ok ? tau_upper(mu, max(1, cnt + cnt_p), a.alpha) : lo;
+      tau = lo;
+      for (int it = 0; it < a.n_iter; ++it) {
+        float f0 = 0.f, f1 = 0.f, f2 = 0.f;
+        for (int e = 0; e < cnt; ++e) tau_terms<KIND>(a.scale * s_cu[w][e][lane], tau, a.beta, f0, f1, f2);
+        f0 = sum_xor32(f0);
+        f1 = sum_xor32(f1);
+        if (KIND != 1) f2 = sum_xor32(f2);
+        float nt = tau;
+        if (row_ok) nt = tau_step<KIND>(tau, f0, f1, f2, a.beta, lo, hi);
+        const bool conv = !row_ok || tau_converged(tau, nt);
+        tau = nt;
+        if (wave_all(conv)) break;
+      }
+    }
+    // ---- output: O_i = sum_j P_ij v_j / sum_j P_ij over both lists; this lane
+    // accumulates dims hi32 * D/2 .. +D/2
+    float acc[HD];
+#pragma unroll
+    for (int j = 0; j < HD; ++j) acc[j] = 0.f;
+    float psum = 0.f;
+    const int tile_row = (qi >> 6) - 2 * blockIdx.x;  // 0 or 1: this row's 64-row tile in the workgroup
+    for (int side = 0; side < 2; ++side) {
+      const int src = side == 0 ? lane : pl;
+      const int n = side == 0 ? cnt : cnt_p;
+      for (int e = 0; e < n; ++e) {
+        const float p = row_ok ? prior_of<KIND>(a.scale * s_cu[w][e][src] - tau, a.beta) : 0.f;
+        if (p > 0.f) {
+          const int key = s_ck[w][e][src];
+          psum += p;
+          if (side == 0) atomicOr(&s_mask[tile_row][(key >> 6) >> 5], 1u << ((key >> 6) & 31));
+          const uint16_t* vp = Vp + (size_t)key * D + hi32 * HD;
+#pragma unroll
+          for (int c = 0; c < HD / 8; ++c) {
+            const u32x4 v = ldg16(vp + 8 * c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[8 * c + 2 * q] = fmaf(p, bf16lo(v[q]), acc[8 * c + 2 * q]);
+              acc[8 * c + 2 * q + 1] = fmaf(p, bf16hi(v[q]), acc[8 * c + 2 * q + 1]);
+            }
+          }
+        }
+      }
+    }
+    if (qi < N) {
+      const float inv = psum > 0.f ? 1.f / psum : 0.f;
+      if (lane < 32) a.tau[bh * (size_t)N + qi] = row_ok ? tau : 0.f;
+      uint16_t* op = static_cast<uint16_t*>(a.O) + (bh * N + qi) * (size_t)D + hi32 * HD;
+#pragma unroll
+      for (int c = 0; c < HD / 8; ++c) {
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(acc[8 * c + 2 * q] * inv, acc[8 * c + 2 * q + 1] * inv);
+        *reinterpret_cast<u32x4*>(op + 8 * c) = v;
+      }
+    }
+  }
+  __syncthreads();
+  if (a.mask) {
+    for (int i = tid; i < 2 * a.mask_words; i += blockDim.x) {
+      const int ii = i / a.mask_words, wd = i % a.mask_words;
+      const int I = blockIdx.x * 2 + ii;
+      if (I < nT) a.mask[(bh * nT + I) * a.mask_words + wd] = s_mask[ii][wd];
+    }
+  }
+}
+
 template <typename T, int D>
-static hipError_t entmax_td(const EntmaxAttnArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H, a.B);
+static hipError_t entmax_td(const EntmaxAttnArgs& a0, hipStream_t stream) {
+  dim3 grid((a0.N + 127) / 128, a0.H, a0.B);
+  EntmaxAttnArgs a = a0;
+  a.only_marked = 0;
+  if constexpr (Elem<T>::bf16) {
+    // single pass, then the general kernel for the row blocks it left
+    if (a.alpha == 1.5f)
+      hipLaunchKernelGGL((k_entmax_buf<D, 2>), grid, dim3(256), 0, stream, a);
+    else if (a.alpha == 2.0f)
+      hipLaunchKernelGGL((k_entmax_buf<D, 1>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_entmax_buf<D, 0>), grid, dim3(256), 0, stream, a);
+    a.only_marked = 1;
+  }
   if (a.alpha == 1.5f)
     hipLaunchKernelGGL((k_entmax_attn<T, D, 2>), grid, dim3(256), 0, stream, a);
   else if (a.alpha == 2.0f)

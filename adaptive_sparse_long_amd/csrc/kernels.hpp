@@ -247,6 +247,7 @@ struct EntmaxAttnArgs {
   float* tau;
   uint32_t* mask;
   int mask_words;
+  int only_marked;  // general kernel: only row blocks a row of which has tau = NaN
 };
 
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
@@ -261,5 +262,6 @@ constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in regist
 constexpr int kRouteCap = 128;               // routing candidates per row held in LDS
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
+constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel
 
 }  // namespace dash

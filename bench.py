@@ -52,7 +52,7 @@ KERNEL_SOURCES = {
     "k_route_prefill": ["route.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_prefill_cm": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
-    "k_entmax_attn": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_buf": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
 
 
@@ -437,10 +437,10 @@ def main():
         log("entmax varlen")
         ent = bench_entmax(we, args.steps, args.warmup)
         out["entmax"] = {"workload": we.name, **ent,
-                         "roofline": {"kernel": "k_entmax_attn", "bound": "mfma", "achieved": ent["tflops_qk_pass"],
+                         "roofline": {"kernel": "k_entmax_buf", "bound": "mfma", "achieved": ent["tflops_qk_pass"],
                                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": ent["tflops_qk_pass"] / PEAK_BF16_TFLOPS,
-                                      "traffic": measured_traffic("k_entmax_attn")}}
+                                      "traffic": measured_traffic("k_entmax_buf")}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(wp)

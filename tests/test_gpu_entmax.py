@@ -82,6 +82,17 @@ def test_entmax_small(B, H, N, d, alpha, causal, lens, scale, dtype):
     check_entmax(q, k, v, alpha, causal, varlen, where=f"{dtype} N{N} a{alpha}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_entmax_candidate_overflow_falls_back(causal):
+    """Zero query rows score every key equally, so every key is a candidate and
+    the single-pass kernel's per-lane candidate lists overflow: it leaves those
+    row blocks to the general kernel. Rows 0..63 are zero (first row block),
+    the rest random (single pass)."""
+    q, k, v, _ = dense_entmax_inputs(1, 2, 300, 64, 77, dtype="bf16", scale=1.0, device="cuda")
+    q[:, :, :64] = 0
+    check_entmax(q, k, v, 1.5, causal, where=f"overflow causal={causal}")
+
+
 def test_entmax_deterministic():
     q, k, v, _ = dense_entmax_inputs(2, 2, 900, 64, 4, dtype="bf16", scale=2.0, device="cuda")
     a = api.entmax_attn(q, k, v, alpha=2.0, causal=False)
