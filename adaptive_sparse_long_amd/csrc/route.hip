@@ -92,6 +92,8 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
+  // after the single-pass kernel: only the tiles it left
+  if (a.only_marked && a.tdone[((size_t)b * a.Hq + h) * a.n_tiles + tile] != 0) return;
   const int hk = h / a.g;
   const int N = a.Nq;
   const int i0 = tile * kTileRows + w * 16;  // first row of this wavefront
@@ -646,6 +648,505 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
 }
 
+// ============================================================================
+// Prefill routing, list-based (the common case). Four wavefronts x 32 query
+// rows per 128-row tile and query head. The pre-scaled split summaries pass
+// through LDS 32 chunks at a time; S^T = summaries x Q^T with
+// v_mfma_f32_32x32x16_bf16 (hi and lo parts into one accumulator) gives each
+// lane 16 scores (u units) of its query row per block, lanes l and l ^ 32
+// sharing a row. Only scores above max u - 1 can carry weight (tau >= max u -
+// 1): a first pass finds each row's max, a second writes the scores above max
+// - 1 as (u, row, chunk) entries into the wavefront's part of an LDS list. A
+// tile with a wavefront whose entries do not fit is left to the general kernel
+// (tdone = 0) before anything else is written.
+//
+// Everything after that is spread evenly over the entries, whatever their
+// rows: each lane takes a contiguous run of its wavefront's entries. The tau
+// sums are added per row in 2^-32 fixed point, so their order (and with it the
+// result) does not depend on which lane adds what. The routed chunks go into
+// per-row bitmasks, from which the tile's chunk union, each pair's rank in its
+// row and its place among the pairs of its chunk follow without contended
+// atomics.
+// ============================================================================
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
+  constexpr int D = 128;
+  constexpr int NS = D / 16;  // k-steps of the 32x32x16 MFMA
+  constexpr int SROW = D + 8;
+  constexpr int WCAP = kRouteListCap / 4;  // entries per wavefront
+  constexpr int NWMAX = kRoutePrefillMaxSlots / 32;
+  constexpr int NE = kRoutePrefillMaxSlots;
+  // summary stage (hi and lo parts of 32 chunks); after the passes, the per-row
+  // bitmasks [kTileRows][NWMAX] and the per-entry row masks [NE][4]
+  __shared__ __attribute__((aligned(16))) uint16_t s_stage[2 * 32 * SROW];
+  static_assert(2 * 32 * SROW * 2 >= (kTileRows * NWMAX + NE * 4) * 4, "scratch fits the stage");
+  static_assert(NE <= 512 && kTileRows <= 128, "entries pack row and chunk into 16 bits");
+  uint16_t* const sSh = s_stage;
+  uint16_t* const sSl = s_stage + 32 * SROW;
+  uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_stage);
+  uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(reinterpret_cast<uint32_t*>(s_stage) + kTileRows * NWMAX);
+  __shared__ float s_lu[kRouteListCap];     // entry scores
+  __shared__ uint16_t s_lk[kRouteListCap];  // entry (tile row << 9) | chunk
+  __shared__ float s_lc[4][kChunk];         // own-chunk key logits <k, cls> / sqrt(d)
+  __shared__ unsigned long long s_sum[3][kTileRows];  // tau sums per row, 2^-32 fixed point
+  __shared__ float s_t[kTileRows];          // tau iterate per row
+  __shared__ uint32_t s_s0[kTileRows];      // first pool slot per row
+  __shared__ uint32_t s_wun[4][NWMAX], s_union[NWMAX];
+  __shared__ int s_pre[NWMAX + 1];
+  __shared__ int s_cl[NE], s_eoff[NE];
+  __shared__ int s_wtot[4], s_tmp[4];
+  __shared__ long long s_tbase;
+
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int hi32 = lane >> 5;
+  const int row = lane & 31;   // the wavefront's row of this lane
+  const int R = w * 32 + row;  // the tile's row of this lane
+  const bool owner = hi32 == 0;  // lanes 0..31 keep the per-row state
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = a.g;
+  const int hk = h / g;
+  const int hh = h % g;
+  const int N = a.Nq;
+  const size_t bh = (size_t)b * a.Hq + h;
+  const int i0 = tile * kTileRows + w * 32;  // first row of this wavefront
+  const int qi = i0 + row;
+  const int cw = i0 / kChunk;                // own chunk of the wavefront's rows
+  const bool wave_valid = i0 < N;
+  const bool row_ok = qi < N;
+  const bool causal = a.causal != 0;
+  const bool est = causal && a.est != 0;
+  const int n_slots = a.n_slots;
+  const int NW = (n_slots + 31) / 32;
+  const int ncomp = wave_valid ? (causal ? cw : n_slots) : 0;  // complete-chunk candidates of the rows
+  const int last_row = min(tile * kTileRows + kTileRows, N) - 1;
+  const int ncomp_wg = causal ? last_row / kChunk : n_slots;
+  const int nblk_wg = (ncomp_wg + 31) / 32;
+  const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
+  const int wreg = w * WCAP;  // this wavefront's part of the list
+
+  // ---- q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
+  bf16x8 qb[NS];
+  {
+    const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * hi32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
+  }
+
+  // ---- passes over the summary blocks of the tile: body(kb, u) with u the
+  // row's scores of block kb (-inf past the candidates), for the wavefront's blocks
+  u32x4 gl[4];
+  auto load_stage = [&](int kb) {  // 32 chunks x (hi, lo) x 16 segments of 16 bytes
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int c = min(kb * 32 + (idx >> 5), max(ncomp_wg - 1, 0));
+      const int part = idx & 31;
+      gl[k] = ldg16((part < 16 ? a.s_hi : a.s_lo) + sbase + (size_t)c * D + 8 * (part & 15));
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = tid + 256 * k;
+      const int part = idx & 31;
+      *reinterpret_cast<u32x4*>(&(part < 16 ? sSh : sSl)[(idx >> 5) * SROW + 8 * (part & 15)]) = gl[k];
+    }
+  };
+  auto scan_blocks = [&](auto&& body) {
+    if (nblk_wg > 0) load_stage(0);
+    for (int kb = 0; kb < nblk_wg; ++kb) {
+      const bool more = kb + 1 < nblk_wg;
+      store_stage();
+      __syncthreads();
+      if (more) load_stage(kb + 1);
+      if (kb * 32 < ncomp) {
+        // u of row qi for chunks kb*32 + 8 (r/4) + 4 hi32 + r%4
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const uint16_t* ah = &sSh[row * SROW + 8 * hi32];
+        const uint16_t* al = &sSl[row * SROW + 8 * hi32];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ah + 16 * s), qb[s], acc);
+          acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(al + 16 * s), qb[s], acc);
+        }
+        if (kb * 32 + 32 > ncomp) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[r] = kb * 32 + 8 * (r >> 2) + 4 * hi32 + (r & 3) < ncomp ? acc[r] : -INFINITY;
+        }
+        body(kb, acc);
+      }
+      __syncthreads();
+    }
+  };
+
+  // pass 1: the row's max u over its past chunks
+  float m_run = -INFINITY;
+  scan_blocks([&](int, const f32x16& u) {
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
+    m_run = fmaxf(m_run, max_xor32(lmax));
+  });
+  // pass 2: the scores above max - 1, block by block, lane by lane
+  int cnt = 0;   // this lane's entries
+  int wcnt = 0;  // the wavefront's entries (uniform)
+  {
+    const float thr = m_run - 1.f;
+    scan_blocks([&](int kb, const f32x16& u) {
+      uint32_t msk = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) msk |= (row_ok && u[r] > thr) ? (1u << r) : 0u;
+      // this lane's place among the wavefront's entries of the block: the
+      // prefix of n (<= 16) bit by bit with ballots and mbcnt
+      const int n = __popc(msk);
+      int pre = 0, tot = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t bm = __ballot((n >> bit) & 1);
+        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
+        tot += __popcll(bm) << bit;
+      }
+      if (wcnt + tot <= WCAP) {
+        int pos = wreg + wcnt + pre;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if ((msk >> r) & 1u) {
+            s_lu[pos] = u[r];
+            s_lk[pos] = (uint16_t)((R << 9) | (kb * 32 + 8 * (r >> 2) + 4 * hi32 + (r & 3)));
+            ++pos;
+          }
+      }
+      wcnt += tot;
+      cnt += n;
+    });
+  }
+  if (__syncthreads_or(wcnt > WCAP)) {  // uniform: the tile goes to the general kernel
+    if (tid == 0) a.tdone[bh * a.n_tiles + tile] = 0;
+    return;
+  }
+  if (tid == 0) a.tdone[bh * a.n_tiles + tile] = 1;
+
+  // ---- own-chunk estimate: score against the summary of tokens [cw*C, i]
+  float ud = -INFINITY;
+  const float uscale = (a.alpha - 1.f) * a.zscale;
+  if (est && wave_valid) {
+    const uint16_t* kbase = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)cw * kChunk) * D;
+    const int lim = N - 1 - cw * kChunk;  // last key of the chunk inside the sequence
+    {
+      const uint16_t* kp = kbase + (size_t)min(lane, lim) * D;
+      const uint16_t* cp = a.cls + (size_t)hk * D;
+      float l = 0.f;
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        const u32x4 kv = ldg16(kp + 8 * c8);
+        const u32x4 cv = ldg16(cp + 8 * c8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l = fmaf(bf16lo(kv[e]), bf16lo(cv[e]), l);
+          l = fmaf(bf16hi(kv[e]), bf16hi(cv[e]), l);
+        }
+      }
+      s_lc[w][lane] = l * a.inv_sqrt_d;
+    }
+    f32x16 e0, e1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e0[r] = 0.f;
+      e1[r] = 0.f;
+    }
+    const uint16_t* k0 = kbase + (size_t)min(row, lim) * D + 8 * hi32;
+    const uint16_t* k1 = kbase + (size_t)min(row + 32, lim) * D + 8 * hi32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      e0 = mfma32x32x16(as_bf16x8(ldg16(k0 + 16 * s)), qb[s], e0);
+      e1 = mfma32x32x16(as_bf16x8(ldg16(k1 + 16 * s)), qb[s], e1);
+    }
+    wave_lds_fence();
+    const int pi = qi - cw * kChunk;  // keys 0 .. pi of the chunk are the row's
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+      if (kk <= pi) M = fmaxf(M, s_lc[w][kk]);
+      if (kk + 32 <= pi) M = fmaxf(M, s_lc[w][kk + 32]);
+    }
+    M = max_xor32(M);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 8 * (r >> 2) + 4 * hi32 + (r & 3);
+      if (kk <= pi) {
+        const float e = fast_exp2((s_lc[w][kk] - M) * kLog2e);
+        num = fmaf(e, e0[r], num);
+        den += e;
+      }
+      if (kk + 32 <= pi) {
+        const float e = fast_exp2((s_lc[w][kk + 32] - M) * kLog2e);
+        num = fmaf(e, e1[r], num);
+        den += e;
+      }
+    }
+    num = sum_xor32(num);
+    den = sum_xor32(den);
+    ud = row_ok ? num / den * uscale : -INFINITY;
+    if (row_ok) m_run = fmaxf(m_run, ud);  // list entries at or below the new max - 1 stay inert
+  }
+
+  // ---- this lane's run of its wavefront's entries
+  const int run = (wcnt + kWave - 1) / kWave;
+  const int e_beg = wreg + min(wcnt, lane * run);
+  const int e_end = wreg + min(wcnt, lane * run + run);
+
+  // ---- tau: safeguarded Halley on the bracket [m - 1, m - n^-(alpha-1)], the
+  // rows of the wavefront together
+  const bool has = row_ok && m_run > -INFINITY;
+  float tau = INFINITY;
+  {
+    float lo = m_run - 1.f;
+    const int n = cnt + __shfl_xor(cnt, 32) + ((est && ud > lo) ? 1 : 0);
+    float hi = has ? tau_upper(m_run, max(1, n), a.alpha) : lo;
+    float t = lo;
+    // fixed point: terms and sums are >= 0; sums stay far below 2^32
+    auto to_fx = [](float x) -> unsigned long long {
+      x = fminf(x, 1.0e9f);
+      const float xi = floorf(x);
+      const uint32_t hw = (uint32_t)xi;
+      const uint32_t lw = (uint32_t)fminf((x - xi) * 4294967296.f, 4294967040.f);
+      return ((unsigned long long)hw << 32) | lw;
+    };
+    auto from_fx = [](unsigned long long v) {
+      return (float)(uint32_t)(v >> 32) + (float)(uint32_t)v * 2.3283064365386963e-10f;
+    };
+    if (owner) {
+      s_t[R] = has ? t : INFINITY;
+      s_sum[0][R] = 0ull;
+      s_sum[1][R] = 0ull;
+      s_sum[2][R] = 0ull;
+    }
+    wave_lds_fence();
+    if (wave_any(has)) {
+      for (int it = 0; it < a.n_iter; ++it) {
+        float f0 = 0.f, f1 = 0.f, f2 = 0.f;
+        int cur = -1;
+        float tc = 0.f;
+        auto flush = [&]() {
+          atomicAdd(&s_sum[0][cur], to_fx(f0));
+          atomicAdd(&s_sum[1][cur], to_fx(f1));
+          if (KIND != 1) atomicAdd(&s_sum[2][cur], to_fx(f2));
+          f0 = f1 = f2 = 0.f;
+        };
+        for (int e = e_beg; e < e_end; ++e) {
+          const int rr = s_lk[e] >> 9;
+          if (rr != cur) {
+            if (cur >= 0) flush();
+            cur = rr;
+            tc = s_t[rr];
+          }
+          tau_terms<KIND>(s_lu[e], tc, a.beta, f0, f1, f2);
+        }
+        if (cur >= 0) flush();
+        wave_lds_fence();
+        bool conv = true;
+        if (owner && has) {
+          float F0 = from_fx(s_sum[0][R]), F1 = from_fx(s_sum[1][R]), F2 = from_fx(s_sum[2][R]);
+          if (est) tau_terms<KIND>(ud, t, a.beta, F0, F1, F2);
+          const float nt = tau_step<KIND>(t, F0, F1, F2, a.beta, lo, hi);
+          conv = tau_converged(t, nt);
+          t = nt;
+          s_t[R] = t;
+          s_sum[0][R] = 0ull;
+          s_sum[1][R] = 0ull;
+          s_sum[2][R] = 0ull;
+        }
+        wave_lds_fence();
+        if (wave_all(conv)) break;
+      }
+    }
+    if (has) tau = t;
+  }
+  if (owner && row_ok) a.tau[bh * (size_t)N + qi] = tau;
+
+  // ---- own chunk: routed (estimate) or always attended with weight 1
+  const float td = ud - tau;
+  const bool dact = row_ok && (est ? (td > 0.f) : causal);
+  const float lwd = !row_ok ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
+  const bool own_pair = owner && causal && dact;  // the lane that emits the own-chunk pair
+
+  // ---- per-row bitmasks of the attended chunks (the stage is no longer read)
+  for (int x = tid; x < kTileRows * NWMAX; x += blockDim.x) (&s_bits[0][0])[x] = 0u;
+  __syncthreads();
+  for (int e = e_beg; e < e_end; ++e) {
+    const int pk = s_lk[e];
+    const int rr = pk >> 9, c = pk & 511;
+    if (s_lu[e] > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
+  }
+  if (own_pair) atomicOr(&s_bits[R][cw >> 5], 1u << (cw & 31));
+  __syncthreads();
+  if (a.bits != nullptr) {
+    for (int x = tid; x < kTileRows * a.bits_words; x += blockDim.x) {
+      const int r = x / a.bits_words, wd = x % a.bits_words;
+      const int q = tile * kTileRows + r;
+      if (q < N) a.bits[(bh * (size_t)N + q) * a.bits_words + wd] = wd < NW ? s_bits[r][wd] : 0u;
+    }
+  }
+  // attended chunks of the row (routed past chunks, then the own chunk)
+  int nsl = 0;
+  if (owner)
+    for (int wd = 0; wd < NW; ++wd) nsl += __popc(s_bits[R][wd]);
+  const int nrt = nsl - (own_pair ? 1 : 0);  // routed past chunks (owner lanes)
+  // the wavefront's union: lane l ORs word l % 16 of rows 8 (l / 16) .. +7
+  {
+    const int wd = lane & 15;
+    uint32_t x = 0u;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x |= s_bits[w * 32 + 8 * (lane >> 4) + r][wd];
+    x |= __shfl_xor(x, 16);
+    x |= __shfl_xor(x, 32);
+    if (lane < NWMAX) s_wun[w][lane] = x;
+  }
+
+  // ---- pool slots: one per attended chunk of every row of the tile, taken
+  // with one atomic; the slots of a row are consecutive, in chunk order
+  int row_pre;
+  {
+    int x = (owner && row_ok) ? nsl : 0;
+    const int x0 = x;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      x += lane >= off ? y : 0;
+    }
+    row_pre = x - x0;
+    if (lane == kWave - 1) s_wtot[w] = x;
+  }
+  __syncthreads();
+  if (tid < NWMAX) s_union[tid] = s_wun[0][tid] | s_wun[1][tid] | s_wun[2][tid] | s_wun[3][tid];
+  if (tid == kWave) {
+    const int tot = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
+    long long pbase = -1;
+    if (tot > 0) {
+      const int part = (int)((blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z)) % kPools);
+      const unsigned long long cap = (unsigned long long)a.pool_cap / kPools;
+      const unsigned long long got = atomicAdd(&a.pool[part], (unsigned long long)tot);
+      pbase = got + (unsigned long long)tot <= cap ? (long long)(part * cap + got) : -1;
+    }
+    s_tbase = pbase;
+    a.tbase[bh * a.n_tiles + tile] = pbase >= 0 ? (uint32_t)pbase : 0u;
+  }
+  __syncthreads();
+  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  const long long tb = s_tbase;
+  int wpre = 0;
+  for (int ww = 0; ww < w; ++ww) wpre += s_wtot[ww];
+  const long long s0 = tb + wpre + row_pre;  // the row's first slot (owner lanes)
+  if (owner && row_ok) {
+    a.cmcnt[bh * (size_t)N + qi] = pooled ? (uint16_t)nsl : (uint16_t)0;
+    a.rslot[bh * (size_t)N + qi] = pooled ? (uint32_t)s0 : 0u;
+  }
+  if (owner) s_s0[R] = (uint32_t)s0;
+
+  // ---- the tile's attended chunks: chunk-major list if pooled, else row-major
+  if (tid == 0) {
+    int acc = 0;
+    for (int wd = 0; wd < NW; ++wd) {
+      s_pre[wd] = acc;
+      acc += __popc(s_union[wd]);
+    }
+    s_pre[NW] = acc;
+    a.ccounts[bh * a.n_tiles + tile] = pooled ? acc : 0;
+    a.counts[bh * a.n_tiles + tile] = pooled ? 0 : acc;
+  }
+  __syncthreads();
+  const long long toff = bh * a.per_head + prefill_tile_offset(tile, n_slots, causal);
+  if (tid < NW) {
+    uint32_t bits = s_union[tid];
+    int pos = s_pre[tid];
+    int* lst = (pooled ? a.clists : a.lists) + toff;
+    while (bits) {
+      const int c = tid * 32 + __ffs(bits) - 1;
+      s_cl[pos] = c;
+      lst[pos++] = c;
+      bits &= bits - 1u;
+    }
+  }
+  auto epos = [&](int c) { return s_pre[c >> 5] + __popc(s_union[c >> 5] & ((1u << (c & 31)) - 1u)); };
+  // rank of chunk c among the attended chunks of tile row rr
+  auto rank_in_row = [&](int rr, int c) {
+    int k = __popc(s_bits[rr][c >> 5] & ((1u << (c & 31)) - 1u));
+    for (int wd = 0; wd < (c >> 5); ++wd) k += __popc(s_bits[rr][wd]);
+    return k;
+  };
+  const int ne = s_pre[NW];
+  __syncthreads();
+
+  if (pooled) {
+    // ---- row masks of every entry (a lane per entry in each wavefront), the
+    // pairs per entry and their place: the pairs of a chunk in row order
+    for (int e = lane; e < ne; e += kWave) {
+      const int c = s_cl[e];
+      uint32_t m = 0u;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) m |= ((s_bits[w * 32 + r][c >> 5] >> (c & 31)) & 1u) << r;
+      s_rm[e][w] = m;
+    }
+    __syncthreads();
+    // entries 2t and 2t+1 per thread (up to 512)
+    auto ecount = [&](int e) { return __popc(s_rm[e][0]) + __popc(s_rm[e][1]) + __popc(s_rm[e][2]) + __popc(s_rm[e][3]); };
+    const int c0 = 2 * tid < ne ? ecount(2 * tid) : 0;
+    const int c1 = 2 * tid + 1 < ne ? ecount(2 * tid + 1) : 0;
+    int first = 0;
+    block_excl_scan<4>(c0 + c1, s_tmp, first);
+    int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      if (e < ne) {
+        const int f = first + (q ? c0 : 0);
+        const int n = q ? c1 : c0;
+        s_eoff[e] = f;
+        a.ceo[toff + e] = make_int2(f, n);
+        a.cbase[toff + e] = atomicAdd(&cmp[s_cl[e]], n);  // the entry's pairs among all pairs of its chunk
+      }
+    }
+    __syncthreads();
+    auto place = [&](int e, int rr) {
+      const int wr = rr >> 5;
+      int j = s_eoff[e] + __popc(s_rm[e][wr] & ((1u << (rr & 31)) - 1u));
+      for (int ww = 0; ww < wr; ++ww) j += __popc(s_rm[e][ww]);
+      return j;
+    };
+    for (int e = e_beg; e < e_end; ++e) {
+      const int pk = s_lk[e];
+      const int rr = pk >> 9, c = pk & 511;
+      const float uu = s_lu[e], tr = s_t[rr];
+      if (uu > tr)
+        a.trec[tb + place(epos(c), rr)] = make_int4((tile * kTileRows + rr) * g + hh, (int)(s_s0[rr] + rank_in_row(rr, c)),
+                                                    __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
+    }
+    if (own_pair) a.trec[tb + place(epos(cw), R)] = make_int4(qi * g + hh, (int)(s0 + nrt), __float_as_int(lwd), 0);
+  } else {
+    // ---- row-major list: -inf for every (entry, row), then the log2 weights
+    // of the attended pairs
+    float* const bw = a.bias + (size_t)toff * kTileRows;
+    for (int x = tid; x < ne * kTileRows; x += blockDim.x) bw[x] = -INFINITY;
+    __syncthreads();  // the fills are done before any weight lands on them
+    for (int e = e_beg; e < e_end; ++e) {
+      const int pk = s_lk[e];
+      const int rr = pk >> 9, c = pk & 511;
+      const float uu = s_lu[e], tr = s_t[rr];
+      if (uu > tr) bw[(size_t)epos(c) * kTileRows + rr] = log2_prior<KIND>(uu - tr, a.beta);
+    }
+    if (own_pair) bw[(size_t)epos(cw) * kTileRows + R] = lwd;
+  }
+}
+
 // Scale the float32 summaries of the chunks the prefill routing reads into u
 // units ((alpha - 1) * scaling_factor / sqrt(d)) and split them into bf16 high
 // parts and bf16 low parts (x - high), once per call; also clears the
@@ -911,11 +1412,15 @@ static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_split_summaries, dim3(blocks), dim3(256), 0, stream, a, n_need);
   }
   dim3 grid(a.n_tiles, a.Hq, a.B);
+  // single pass, then the general kernel for the tiles it left
+  hipLaunchKernelGGL((k_route_fast<KIND>), grid, dim3(256), 0, stream, a);
+  RouteArgs am = a;
+  am.only_marked = 1;
   const int nb = (a.n_slots + 15) / 16;
-#define DASH_RP(NBV)                                                                   \
-  if (nb <= NBV) {                                                                     \
-    hipLaunchKernelGGL((k_route_prefill<NBV, KIND>), grid, dim3(512), 0, stream, a); \
-    return hipGetLastError();                                                          \
+#define DASH_RP(NBV)                                                                    \
+  if (nb <= NBV) {                                                                      \
+    hipLaunchKernelGGL((k_route_prefill<NBV, KIND>), grid, dim3(512), 0, stream, am); \
+    return hipGetLastError();                                                           \
   }
   DASH_RP(2) DASH_RP(4) DASH_RP(8) DASH_RP(16) DASH_RP(32)
 #undef DASH_RP
