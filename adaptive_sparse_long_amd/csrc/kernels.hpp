@@ -264,7 +264,7 @@ hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t st
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
 constexpr int kRouteCap = 128;               // routing candidates per row held in LDS
-constexpr int kRouteListCap = 4096;          // routing candidates per tile (a quarter per wavefront) in LDS
+constexpr int kRouteListCap = 3584;          // routing candidates per tile (a quarter per wavefront) in LDS
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel

@@ -669,7 +669,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 // atomics.
 // ============================================================================
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
+__global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 16;  // k-steps of the 32x32x16 MFMA
   constexpr int SROW = D + 8;
@@ -679,21 +679,28 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
   // summary stage (hi and lo parts of 32 chunks); after the passes, the per-row
   // bitmasks [kTileRows][NWMAX] and the per-entry row masks [NE][4]
   __shared__ __attribute__((aligned(16))) uint16_t s_stage[2 * 32 * SROW];
-  static_assert(2 * 32 * SROW * 2 >= (kTileRows * NWMAX + NE * 4) * 4, "scratch fits the stage");
+  static_assert(2 * 32 * SROW * 2 >= (kTileRows * NWMAX + NE * 4) * 4 && 2 * 32 * SROW * 2 >= 4 * kChunk * 4,
+                "scratch fits the stage");
   static_assert(NE <= 512 && kTileRows <= 128, "entries pack row and chunk into 16 bits");
   uint16_t* const sSh = s_stage;
   uint16_t* const sSl = s_stage + 32 * SROW;
   uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_stage);
   uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(reinterpret_cast<uint32_t*>(s_stage) + kTileRows * NWMAX);
-  __shared__ float s_lu[kRouteListCap];     // entry scores
-  __shared__ uint16_t s_lk[kRouteListCap];  // entry (tile row << 9) | chunk
-  __shared__ float s_lc[4][kChunk];         // own-chunk key logits <k, cls> / sqrt(d)
-  __shared__ unsigned long long s_sum[3][kTileRows];  // tau sums per row, 2^-32 fixed point
-  __shared__ float s_t[kTileRows];          // tau iterate per row
-  __shared__ uint32_t s_s0[kTileRows];      // first pool slot per row
+  // own-chunk key logits <k, cls> / sqrt(d), in the stage once the passes are done
+  float (*const s_lc)[kChunk] = reinterpret_cast<float (*)[kChunk]>(s_stage);
+  // the entry list: scores, then (tile row << 9) | chunk; once every lane holds
+  // its run in registers, the per-row tau state and the chunk entries
+  __shared__ __attribute__((aligned(16))) unsigned char s_list[kRouteListCap * 6];
+  float* const s_lu = reinterpret_cast<float*>(s_list);
+  uint16_t* const s_lk = reinterpret_cast<uint16_t*>(s_list + kRouteListCap * 4);
+  unsigned long long (*const s_sum)[kTileRows] = reinterpret_cast<unsigned long long (*)[kTileRows]>(s_list);
+  float* const s_t = reinterpret_cast<float*>(s_list + 3 * kTileRows * 8);            // tau iterate per row
+  uint32_t* const s_s0 = reinterpret_cast<uint32_t*>(s_list + 3 * kTileRows * 8 + kTileRows * 4);  // first pool slot per row
+  int* const s_cl = reinterpret_cast<int*>(s_list + 3 * kTileRows * 8 + kTileRows * 8);
+  int* const s_eoff = s_cl + NE;
+  static_assert(3 * kTileRows * 8 + kTileRows * 8 + NE * 8 <= kRouteListCap * 6, "row state fits the list");
   __shared__ uint32_t s_wun[4][NWMAX], s_union[NWMAX];
   __shared__ int s_pre[NWMAX + 1];
-  __shared__ int s_cl[NE], s_eoff[NE];
   __shared__ int s_wtot[4], s_tmp[4];
   __shared__ long long s_tbase;
 
@@ -902,7 +909,19 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
   // ---- this lane's run of its wavefront's entries
   const int run = (wcnt + kWave - 1) / kWave;
   const int e_beg = wreg + min(wcnt, lane * run);
-  const int e_end = wreg + min(wcnt, lane * run + run);
+  const int nl = min(wcnt, lane * run + run) - min(wcnt, lane * run);
+  constexpr int RUNMAX = WCAP / kWave;
+  // the run in registers (run <= RUNMAX; loops over it stop at the uniform run)
+  float eu[RUNMAX];
+  uint32_t ek[RUNMAX];
+#pragma unroll
+  for (int j = 0; j < RUNMAX; ++j) {
+    if (j >= run) break;
+    eu[j] = j < nl ? s_lu[e_beg + j] : -INFINITY;
+    ek[j] = j < nl ? s_lk[e_beg + j] : 0u;
+  }
+
+  __syncthreads();  // the list buffer is free from here on
 
   // ---- tau: safeguarded Halley on the bracket [m - 1, m - n^-(alpha-1)], the
   // rows of the wavefront together
@@ -942,14 +961,18 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
           if (KIND != 1) atomicAdd(&s_sum[2][cur], to_fx(f2));
           f0 = f1 = f2 = 0.f;
         };
-        for (int e = e_beg; e < e_end; ++e) {
-          const int rr = s_lk[e] >> 9;
-          if (rr != cur) {
-            if (cur >= 0) flush();
-            cur = rr;
-            tc = s_t[rr];
+#pragma unroll
+        for (int j = 0; j < RUNMAX; ++j) {
+          if (j >= run) break;
+          if (j < nl) {
+            const int rr = ek[j] >> 9;
+            if (rr != cur) {
+              if (cur >= 0) flush();
+              cur = rr;
+              tc = s_t[rr];
+            }
+            tau_terms<KIND>(eu[j], tc, a.beta, f0, f1, f2);
           }
-          tau_terms<KIND>(s_lu[e], tc, a.beta, f0, f1, f2);
         }
         if (cur >= 0) flush();
         wave_lds_fence();
@@ -982,10 +1005,11 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
   // ---- per-row bitmasks of the attended chunks (the stage is no longer read)
   for (int x = tid; x < kTileRows * NWMAX; x += blockDim.x) (&s_bits[0][0])[x] = 0u;
   __syncthreads();
-  for (int e = e_beg; e < e_end; ++e) {
-    const int pk = s_lk[e];
-    const int rr = pk >> 9, c = pk & 511;
-    if (s_lu[e] > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
+#pragma unroll
+  for (int j = 0; j < RUNMAX; ++j) {
+    if (j >= run) break;
+    const int rr = ek[j] >> 9, c = ek[j] & 511;
+    if (j < nl && eu[j] > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
   }
   if (own_pair) atomicOr(&s_bits[R][cw >> 5], 1u << (cw & 31));
   __syncthreads();
@@ -1122,11 +1146,12 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
       for (int ww = 0; ww < wr; ++ww) j += __popc(s_rm[e][ww]);
       return j;
     };
-    for (int e = e_beg; e < e_end; ++e) {
-      const int pk = s_lk[e];
-      const int rr = pk >> 9, c = pk & 511;
-      const float uu = s_lu[e], tr = s_t[rr];
-      if (uu > tr)
+#pragma unroll
+    for (int j = 0; j < RUNMAX; ++j) {
+      if (j >= run) break;
+      const int rr = ek[j] >> 9, c = ek[j] & 511;
+      const float uu = eu[j], tr = s_t[rr];
+      if (j < nl && uu > tr)
         a.trec[tb + place(epos(c), rr)] = make_int4((tile * kTileRows + rr) * g + hh, (int)(s_s0[rr] + rank_in_row(rr, c)),
                                                     __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
     }
@@ -1137,11 +1162,12 @@ __global__ __launch_bounds__(256, 2) void k_route_fast(RouteArgs a) {
     float* const bw = a.bias + (size_t)toff * kTileRows;
     for (int x = tid; x < ne * kTileRows; x += blockDim.x) bw[x] = -INFINITY;
     __syncthreads();  // the fills are done before any weight lands on them
-    for (int e = e_beg; e < e_end; ++e) {
-      const int pk = s_lk[e];
-      const int rr = pk >> 9, c = pk & 511;
-      const float uu = s_lu[e], tr = s_t[rr];
-      if (uu > tr) bw[(size_t)epos(c) * kTileRows + rr] = log2_prior<KIND>(uu - tr, a.beta);
+#pragma unroll
+    for (int j = 0; j < RUNMAX; ++j) {
+      if (j >= run) break;
+      const int rr = ek[j] >> 9, c = ek[j] & 511;
+      const float uu = eu[j], tr = s_t[rr];
+      if (j < nl && uu > tr) bw[(size_t)epos(c) * kTileRows + rr] = log2_prior<KIND>(uu - tr, a.beta);
     }
     if (own_pair) bw[(size_t)epos(cw) * kTileRows + R] = lwd;
   }
