@@ -159,7 +159,8 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.tbase = reinterpret_cast<uint32_t*>(ws + L.off_tbase);
   a.rslot = reinterpret_cast<uint32_t*>(ws + L.off_rslot);
   a.cmcnt = reinterpret_cast<uint16_t*>(ws + L.off_cmcnt);
-  a.tdone = reinterpret_cast<int*>(ws + L.off_tdone);
+  a.fb_tiles = reinterpret_cast<int2*>(ws + L.off_fb);
+  a.fb_count = reinterpret_cast<int*>(ws + L.off_fb_count);
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
   a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
   return from_hip(launch_route_prefill(a, stream));

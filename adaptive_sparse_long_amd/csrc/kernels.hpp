@@ -62,7 +62,7 @@ struct PrefillLayout {
   size_t off_ccounts = 0, off_clists = 0, off_ceo = 0, off_cbase = 0;  // chunk-major list
   size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0, off_trec = 0;  // chunk-major pairs
   size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_plse = 0, off_po = 0;  // partials
-  size_t off_tdone = 0;  // per tile: 1 once the single-pass routing kernel has done it
+  size_t off_fb = 0, off_fb_count = 0;  // tiles left to the general routing kernel
   long long pool_cap = 0;
   size_t off_split = 0, total = 0;
 };
@@ -104,7 +104,8 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_trec = o;    o += align256(pairs * 4 * sizeof(int));
   L.off_pool = o;    o += align256(kPools * sizeof(unsigned long long));
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
-  L.off_tdone = o;   o += align256(heads * L.n_tiles * sizeof(int));
+  L.off_fb = o;      o += align256(heads * L.n_tiles * 2 * sizeof(int));
+  L.off_fb_count = o; o += align256(sizeof(int));
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
   L.off_plse = o;    o += align256(pairs * sizeof(float));
@@ -182,8 +183,8 @@ struct RouteArgs {
   uint32_t* tbase;
   uint32_t* rslot;
   uint16_t* cmcnt;
-  int* tdone;       // per tile: done by the single-pass kernel (else left to the general one)
-  int only_marked;  // general kernel: only tiles with tdone == 0
+  int2* fb_tiles;   // tiles the list-based kernel left: (tile, b * Hq + h)
+  int* fb_count;     // their number, zeroed by the summary split
   // summaries split into bf16 high / low parts (prefill), [B, Hkv, n_slots, d] each
   uint16_t* s_hi;
   uint16_t* s_lo;
@@ -264,7 +265,7 @@ hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t st
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
 constexpr int kRouteCap = 128;               // routing candidates per row held in LDS
-constexpr int kRouteListCap = 3584;          // routing candidates per tile (a quarter per wavefront) in LDS
+constexpr int kRouteListCap = 5120;          // LDS list words per tile: candidates, then 1024 for the chunk entries
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel

@@ -61,6 +61,8 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& v, const float* w) {
 // ============================================================================
 // Prefill routing
 // ============================================================================
+// One workgroup per tile of the grid; the first ones take the tiles the
+// list-based kernel queued, the rest return at once.
 template <int NB, int KIND>
 __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   constexpr int D = 128;
@@ -89,11 +91,11 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
-  const int tile = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  // after the single-pass kernel: only the tiles it left
-  if (a.only_marked && a.tdone[((size_t)b * a.Hq + h) * a.n_tiles + tile] != 0) return;
+  const int q = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (q >= *a.fb_count) return;
+  const int tile = a.fb_tiles[q].x;
+  const int h = a.fb_tiles[q].y % a.Hq;
+  const int b = a.fb_tiles[q].y / a.Hq;
   const int hk = h / a.g;
   const int N = a.Nq;
   const int i0 = tile * kTileRows + w * 16;  // first row of this wavefront
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     long long base = -1;
     if (tot > 0) {
       // the workgroup's part of the pool
-      const int part = (int)((blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z)) % kPools);
+      const int part = (int)((tile + (size_t)a.n_tiles * (h + (size_t)a.Hq * b)) % kPools);
       const unsigned long long cap = (unsigned long long)a.pool_cap / kPools;
       const unsigned long long got = atomicAdd(&a.pool[part], (unsigned long long)tot);
       base = got + (unsigned long long)tot <= cap ? (long long)(part * cap + got) : -1;
@@ -656,9 +658,10 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 // lane 16 scores (u units) of its query row per block, lanes l and l ^ 32
 // sharing a row. Only scores above max u - 1 can carry weight (tau >= max u -
 // 1): a first pass finds each row's max, a second writes the scores above max
-// - 1 as (u, row, chunk) entries into the wavefront's part of an LDS list. A
-// tile with a wavefront whose entries do not fit is left to the general kernel
-// (tdone = 0) before anything else is written.
+// - 1 as (u, row, chunk) entries into the tile's LDS list, a segment per
+// wavefront and block. A tile whose entries do not fit (the list, or 16 per
+// lane of a wavefront) is queued for the general kernel before anything else
+// is written.
 //
 // Everything after that is spread evenly over the entries, whatever their
 // rows: each lane takes a contiguous run of its wavefront's entries. The tau
@@ -673,40 +676,44 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 16;  // k-steps of the 32x32x16 MFMA
   constexpr int SROW = D + 8;
-  constexpr int WCAP = kRouteListCap / 4;  // entries per wavefront
   constexpr int NWMAX = kRoutePrefillMaxSlots / 32;
   constexpr int NE = kRoutePrefillMaxSlots;
-  // summary stage (hi and lo parts of 32 chunks); after the passes, the per-row
-  // bitmasks [kTileRows][NWMAX] and the per-entry row masks [NE][4]
+  constexpr int LCAP = kRouteListCap - 2 * NE;  // entries per tile (the chunk entries take the tail)
+  // summary stage (hi and lo parts of 32 chunks). After the passes: the
+  // own-chunk key logits (estimate), then the tau sums (tau loop), then the
+  // per-row bitmasks [kTileRows][NWMAX] and the per-entry row masks [NE][4]
+  // (emission); the tau iterates and first pool slots per row at its end.
+  constexpr int kStageWords = 2 * 32 * SROW / 2;
   __shared__ __attribute__((aligned(16))) uint16_t s_stage[2 * 32 * SROW];
-  static_assert(2 * 32 * SROW * 2 >= (kTileRows * NWMAX + NE * 4) * 4 && 2 * 32 * SROW * 2 >= 4 * kChunk * 4,
-                "scratch fits the stage");
+  static_assert(kStageWords >= kTileRows * NWMAX + NE * 4 + 2 * kTileRows, "scratch fits the stage");
+  static_assert(kTileRows * NWMAX >= 6 * kTileRows && kTileRows * NWMAX >= 4 * kChunk, "early scratch fits");
   static_assert(NE <= 512 && kTileRows <= 128, "entries pack row and chunk into 16 bits");
   uint16_t* const sSh = s_stage;
   uint16_t* const sSl = s_stage + 32 * SROW;
-  uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_stage);
-  uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(reinterpret_cast<uint32_t*>(s_stage) + kTileRows * NWMAX);
-  // own-chunk key logits <k, cls> / sqrt(d), in the stage once the passes are done
-  float (*const s_lc)[kChunk] = reinterpret_cast<float (*)[kChunk]>(s_stage);
-  // the entry list: scores, then (tile row << 9) | chunk; once every lane holds
-  // its run in registers, the per-row tau state and the chunk entries
-  __shared__ __attribute__((aligned(16))) unsigned char s_list[kRouteListCap * 6];
-  float* const s_lu = reinterpret_cast<float*>(s_list);
-  uint16_t* const s_lk = reinterpret_cast<uint16_t*>(s_list + kRouteListCap * 4);
-  unsigned long long (*const s_sum)[kTileRows] = reinterpret_cast<unsigned long long (*)[kTileRows]>(s_list);
-  float* const s_t = reinterpret_cast<float*>(s_list + 3 * kTileRows * 8);            // tau iterate per row
-  uint32_t* const s_s0 = reinterpret_cast<uint32_t*>(s_list + 3 * kTileRows * 8 + kTileRows * 4);  // first pool slot per row
-  int* const s_cl = reinterpret_cast<int*>(s_list + 3 * kTileRows * 8 + kTileRows * 8);
+  uint32_t* const s_words = reinterpret_cast<uint32_t*>(s_stage);
+  float (*const s_lc)[kChunk] = reinterpret_cast<float (*)[kChunk]>(s_words);  // <k, cls> / sqrt(d)
+  unsigned long long (*const s_sum)[kTileRows] = reinterpret_cast<unsigned long long (*)[kTileRows]>(s_words);
+  uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_words);
+  uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(s_words + kTileRows * NWMAX);
+  float* const s_t = reinterpret_cast<float*>(s_words + kTileRows * NWMAX + NE * 4);  // tau iterate per row
+  uint32_t* const s_s0 = s_words + kTileRows * NWMAX + NE * 4 + kTileRows;           // first pool slot per row
+  // the entry list, an entry a 32-bit word: bits 10.. the distance below the
+  // row's max in units of 2^-22 (< 1), bits 5..9 the row in the wavefront, bits
+  // 0..4 the chunk in the block; the tile's chunk entries in its tail
+  __shared__ __attribute__((aligned(16))) uint32_t s_list[kRouteListCap];
+  int* const s_cl = reinterpret_cast<int*>(s_list + LCAP);
   int* const s_eoff = s_cl + NE;
-  static_assert(3 * kTileRows * 8 + kTileRows * 8 + NE * 8 <= kRouteListCap * 6, "row state fits the list");
   __shared__ uint32_t s_wun[4][NWMAX], s_union[NWMAX];
   __shared__ int s_pre[NWMAX + 1];
   __shared__ int s_wtot[4], s_tmp[4];
   __shared__ long long s_tbase;
+  __shared__ int s_cnt;                     // entries in the list
+  __shared__ int2 s_seg[4][kRoutePrefillMaxSlots / 32];  // per wavefront: (first, count | block << 16)
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
+  if (tid == 0) s_cnt = 0;  // ordered before any use by the barriers of the first pass
   const int hi32 = lane >> 5;
   const int row = lane & 31;   // the wavefront's row of this lane
   const int R = w * 32 + row;  // the tile's row of this lane
@@ -733,7 +740,6 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   const int ncomp_wg = causal ? last_row / kChunk : n_slots;
   const int nblk_wg = (ncomp_wg + 31) / 32;
   const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
-  const int wreg = w * WCAP;  // this wavefront's part of the list
 
   // ---- q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
   bf16x8 qb[NS];
@@ -801,9 +807,11 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
     m_run = fmaxf(m_run, max_xor32(lmax));
   });
-  // pass 2: the scores above max - 1, block by block, lane by lane
+  // pass 2: the scores above max - 1; per block, a segment of the list for the
+  // wavefront's entries, lane by lane
   int cnt = 0;   // this lane's entries
   int wcnt = 0;  // the wavefront's entries (uniform)
+  int nseg = 0;  // its segments (uniform)
   {
     const float thr = m_run - 1.f;
     scan_blocks([&](int kb, const f32x16& u) {
@@ -820,25 +828,33 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
         tot += __popcll(bm) << bit;
       }
-      if (wcnt + tot <= WCAP) {
-        int pos = wreg + wcnt + pre;
+      if (tot > 0) {
+        int first = 0;
+        if (lane == 0) {
+          first = atomicAdd(&s_cnt, tot);
+          s_seg[w][nseg] = make_int2(first, tot | (kb << 16));
+        }
+        first = __shfl(first, 0);
+        ++nseg;
+        if (first + tot <= LCAP) {
+          int pos = first + pre;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if ((msk >> r) & 1u) {
-            s_lu[pos] = u[r];
-            s_lk[pos] = (uint16_t)((R << 9) | (kb * 32 + 8 * (r >> 2) + 4 * hi32 + (r & 3)));
-            ++pos;
-          }
+          for (int r = 0; r < 16; ++r)
+            if ((msk >> r) & 1u) {
+              const uint32_t q = min((uint32_t)rintf((m_run - u[r]) * 4194304.f), (1u << 22) - 1u);
+              s_list[pos++] = (q << 10) | (uint32_t)(row << 5) | (uint32_t)(8 * (r >> 2) + 4 * hi32 + (r & 3));
+            }
+        }
       }
       wcnt += tot;
       cnt += n;
     });
   }
-  if (__syncthreads_or(wcnt > WCAP)) {  // uniform: the tile goes to the general kernel
-    if (tid == 0) a.tdone[bh * a.n_tiles + tile] = 0;
+  const float m_list = m_run;  // the row max the list entries are stored against
+  if (__syncthreads_or(s_cnt > LCAP)) {  // uniform: the tile goes to the general kernel
+    if (tid == 0) a.fb_tiles[atomicAdd(a.fb_count, 1)] = make_int2(tile, (int)bh);
     return;
   }
-  if (tid == 0) a.tdone[bh * a.n_tiles + tile] = 1;
 
   // ---- own-chunk estimate: score against the summary of tokens [cw*C, i]
   float ud = -INFINITY;
@@ -906,22 +922,53 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     if (row_ok) m_run = fmaxf(m_run, ud);  // list entries at or below the new max - 1 stay inert
   }
 
-  // ---- this lane's run of its wavefront's entries
+  // ---- this lane's run of its wavefront's entries (entry k of the wavefront
+  // lies in its segments, in order): the first RUNMAX in registers, the rest
+  // (heavy wavefronts only) read from the list when used. Loops over the run
+  // go to the uniform run length; fetch must be called by the whole wavefront.
   const int run = (wcnt + kWave - 1) / kWave;
-  const int e_beg = wreg + min(wcnt, lane * run);
-  const int nl = min(wcnt, lane * run + run) - min(wcnt, lane * run);
-  constexpr int RUNMAX = WCAP / kWave;
-  // the run in registers (run <= RUNMAX; loops over it stop at the uniform run)
+  const int k_beg = min(wcnt, lane * run);
+  const int nl = min(wcnt, lane * run + run) - k_beg;
+  constexpr int RUNMAX = 16;
+  auto fetch = [&](int j, float& uu, uint32_t& kk) {
+    uint32_t e = 0u;
+    int2 sgv = make_int2(0, 0);
+    if (j < nl) {
+      const int k = k_beg + j;
+      int sg = 0, sk = 0;
+      sgv = s_seg[w][0];
+      while (k >= sk + (sgv.y & 0xffff)) {
+        sk += sgv.y & 0xffff;
+        sgv = s_seg[w][++sg];
+      }
+      e = s_list[sgv.x + k - sk];
+    }
+    const int rw = (e >> 5) & 31;
+    const float mr = __shfl(m_list, rw);  // the max the distance is taken from
+    uu = j < nl ? mr - (float)(e >> 10) * 2.38418579e-7f : -INFINITY;
+    kk = (uint32_t)(((w * 32 + rw) << 9) | ((sgv.y >> 16) * 32 + (e & 31)));
+  };
   float eu[RUNMAX];
   uint32_t ek[RUNMAX];
 #pragma unroll
   for (int j = 0; j < RUNMAX; ++j) {
     if (j >= run) break;
-    eu[j] = j < nl ? s_lu[e_beg + j] : -INFINITY;
-    ek[j] = j < nl ? s_lk[e_beg + j] : 0u;
+    fetch(j, eu[j], ek[j]);
   }
-
-  __syncthreads();  // the list buffer is free from here on
+  // fn(j, u, key) for every j < run: registers, then the list
+  auto for_run = [&](auto&& fn) {
+#pragma unroll
+    for (int j = 0; j < RUNMAX; ++j) {
+      if (j >= run) break;
+      fn(j, eu[j], ek[j]);
+    }
+    for (int j = RUNMAX; j < run; ++j) {
+      float uu;
+      uint32_t kk;
+      fetch(j, uu, kk);
+      fn(j, uu, kk);
+    }
+  };
 
   // ---- tau: safeguarded Halley on the bracket [m - 1, m - n^-(alpha-1)], the
   // rows of the wavefront together
@@ -961,19 +1008,17 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
           if (KIND != 1) atomicAdd(&s_sum[2][cur], to_fx(f2));
           f0 = f1 = f2 = 0.f;
         };
-#pragma unroll
-        for (int j = 0; j < RUNMAX; ++j) {
-          if (j >= run) break;
+        for_run([&](int j, float uu, uint32_t kk) {
           if (j < nl) {
-            const int rr = ek[j] >> 9;
+            const int rr = kk >> 9;
             if (rr != cur) {
               if (cur >= 0) flush();
               cur = rr;
               tc = s_t[rr];
             }
-            tau_terms<KIND>(eu[j], tc, a.beta, f0, f1, f2);
+            tau_terms<KIND>(uu, tc, a.beta, f0, f1, f2);
           }
-        }
+        });
         if (cur >= 0) flush();
         wave_lds_fence();
         bool conv = true;
@@ -1002,15 +1047,14 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   const float lwd = !row_ok ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   const bool own_pair = owner && causal && dact;  // the lane that emits the own-chunk pair
 
-  // ---- per-row bitmasks of the attended chunks (the stage is no longer read)
+  // ---- per-row bitmasks of the attended chunks (over the tau sums)
+  __syncthreads();
   for (int x = tid; x < kTileRows * NWMAX; x += blockDim.x) (&s_bits[0][0])[x] = 0u;
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < RUNMAX; ++j) {
-    if (j >= run) break;
-    const int rr = ek[j] >> 9, c = ek[j] & 511;
-    if (j < nl && eu[j] > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
-  }
+  for_run([&](int j, float uu, uint32_t kk) {
+    const int rr = kk >> 9, c = kk & 511;
+    if (j < nl && uu > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
+  });
   if (own_pair) atomicOr(&s_bits[R][cw >> 5], 1u << (cw & 31));
   __syncthreads();
   if (a.bits != nullptr) {
@@ -1146,15 +1190,13 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
       for (int ww = 0; ww < wr; ++ww) j += __popc(s_rm[e][ww]);
       return j;
     };
-#pragma unroll
-    for (int j = 0; j < RUNMAX; ++j) {
-      if (j >= run) break;
-      const int rr = ek[j] >> 9, c = ek[j] & 511;
-      const float uu = eu[j], tr = s_t[rr];
+    for_run([&](int j, float uu, uint32_t kk) {
+      const int rr = kk >> 9, c = kk & 511;
+      const float tr = s_t[rr];
       if (j < nl && uu > tr)
         a.trec[tb + place(epos(c), rr)] = make_int4((tile * kTileRows + rr) * g + hh, (int)(s_s0[rr] + rank_in_row(rr, c)),
                                                     __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
-    }
+    });
     if (own_pair) a.trec[tb + place(epos(cw), R)] = make_int4(qi * g + hh, (int)(s0 + nrt), __float_as_int(lwd), 0);
   } else {
     // ---- row-major list: -inf for every (entry, row), then the log2 weights
@@ -1162,13 +1204,11 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     float* const bw = a.bias + (size_t)toff * kTileRows;
     for (int x = tid; x < ne * kTileRows; x += blockDim.x) bw[x] = -INFINITY;
     __syncthreads();  // the fills are done before any weight lands on them
-#pragma unroll
-    for (int j = 0; j < RUNMAX; ++j) {
-      if (j >= run) break;
-      const int rr = ek[j] >> 9, c = ek[j] & 511;
-      const float uu = eu[j], tr = s_t[rr];
+    for_run([&](int j, float uu, uint32_t kk) {
+      const int rr = kk >> 9, c = kk & 511;
+      const float tr = s_t[rr];
       if (j < nl && uu > tr) bw[(size_t)epos(c) * kTileRows + rr] = log2_prior<KIND>(uu - tr, a.beta);
-    }
+    });
     if (own_pair) bw[(size_t)epos(cw) * kTileRows + R] = lwd;
   }
 }
@@ -1182,6 +1222,7 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
   // the per-chunk pair counters the routing adds to start from zero
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_bhc; i += gridDim.x * blockDim.x) a.cmp[i] = 0;
   if (blockIdx.x == 0 && threadIdx.x < kPools) a.pool[threadIdx.x] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0;
   const float uscale = (a.alpha - 1.f) * a.zscale;
   const size_t per_bh = (size_t)n_need * (D / 8);
   const size_t total = (size_t)a.B * a.Hkv * per_bh;
@@ -1438,15 +1479,13 @@ static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_split_summaries, dim3(blocks), dim3(256), 0, stream, a, n_need);
   }
   dim3 grid(a.n_tiles, a.Hq, a.B);
-  // single pass, then the general kernel for the tiles it left
+  // the list-based kernel, then the general kernel for the tiles it queued
   hipLaunchKernelGGL((k_route_fast<KIND>), grid, dim3(256), 0, stream, a);
-  RouteArgs am = a;
-  am.only_marked = 1;
   const int nb = (a.n_slots + 15) / 16;
-#define DASH_RP(NBV)                                                                    \
-  if (nb <= NBV) {                                                                      \
-    hipLaunchKernelGGL((k_route_prefill<NBV, KIND>), grid, dim3(512), 0, stream, am); \
-    return hipGetLastError();                                                           \
+#define DASH_RP(NBV)                                                                 \
+  if (nb <= NBV) {                                                                   \
+    hipLaunchKernelGGL((k_route_prefill<NBV, KIND>), grid, dim3(512), 0, stream, a); \
+    return hipGetLastError();                                                        \
   }
   DASH_RP(2) DASH_RP(4) DASH_RP(8) DASH_RP(16) DASH_RP(32)
 #undef DASH_RP
