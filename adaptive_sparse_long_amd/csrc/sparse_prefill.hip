@@ -546,9 +546,12 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
 // ---------------------------------------------------------------------------
 // Merge: every row with partial results (the rows of tiles that got pool
 // slots) combines them, in the order of its slots (consecutive, so rows stream
-// through memory), weighting each by 2^(its log2 sum - the largest one), and
-// writes its output row. Eight lanes per row, lane p owning dims 16p .. 16p+15;
-// the loads of up to four partials are in flight together.
+// through memory). Eight lanes per row: first the row's largest log2 sum and
+// the sum of 2^(log2 sum - largest) over its partials (the lanes split the
+// partials, DPP reductions over the eight), then each partial's fp16 output
+// is added with its normalised weight (v_fma_mix: fp16 in, fp32 sums). Lane p
+// owns dims 8p .. 8p+7 and 64+8p .. 64+8p+7, so each load instruction of the
+// eight lanes reads 128 contiguous bytes; four partials are in flight together.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   constexpr int D = 128;
@@ -561,45 +564,63 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   if (n == 0) return;  // the row was attended row-major
   const size_t s0 = a.rslot[ri];
   if ((long long)(s0 + n) > a.pool_cap) return;
-  float m = kNegBig, l = 0.f;
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  for (int k0 = 0; k0 < n; k0 += NP) {
-    float lse[NP];
-    u32x4 v[NP][2];
+  auto max8 = [](float x) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    return fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  };
+  auto sum8 = [](float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    return x + dpp_f<kDppHalfMirror>(x);
+  };
+  // the first partials' loads go out before the weights are known
+  float lse[NP];
+  u32x4 v[NP][2];
+  auto load = [&](int k0) {
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
       const size_t sl = s0 + min(k0 + x, n - 1);
       lse[x] = a.plse[sl];
-      v[x][0] = ldg16(a.po + sl * D + 16 * p);
-      v[x][1] = ldg16(a.po + sl * D + 16 * p + 8);
+      v[x][0] = ldg16(a.po + sl * D + 8 * p);
+      v[x][1] = ldg16(a.po + sl * D + 64 + 8 * p);
     }
+  };
+  load(0);
+  float lp = p < n ? a.plse[s0 + p] : -INFINITY;
+  for (int k = p + 8; k < n; k += 8) lp = fmaxf(lp, a.plse[s0 + k]);
+  const float M = max8(lp);
+  float L = 0.f;
+  if (M > -INFINITY)
+    for (int k = p; k < n; k += 8) L += fast_exp2(a.plse[s0 + k] - M);
+  L = sum8(L);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float acc[16];
 #pragma unroll
-    for (int x = 0; x < NP; ++x) {
-      if (k0 + x < n && lse[x] > -INFINITY) {
-        const float M = fmaxf(m, lse[x]);
-        const float al = fast_exp2(m - M);
-        const float be = fast_exp2(lse[x] - M);
-        m = M;
-        l = fmaf(l, al, be);
+  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+  if (L > 0.f) {
+    for (int k0 = 0; k0 < n; k0 += NP) {
+      if (k0 > 0) load(k0);
+#pragma unroll
+      for (int x = 0; x < NP; ++x) {
+        const float wt = k0 + x < n ? fast_exp2(lse[x] - M) * inv : 0.f;
 #pragma unroll
         for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            acc[8 * hv + 2 * e] = fmaf(acc[8 * hv + 2 * e], al, be * f16lo(v[x][hv][e]));
-            acc[8 * hv + 2 * e + 1] = fmaf(acc[8 * hv + 2 * e + 1], al, be * f16hi(v[x][hv][e]));
+            const uint32_t u = v[x][hv][e];
+            acc[8 * hv + 2 * e] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)), wt, acc[8 * hv + 2 * e]);
+            acc[8 * hv + 2 * e + 1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)), wt, acc[8 * hv + 2 * e + 1]);
           }
       }
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int hv = 0; hv < 2; ++hv) {
     u32x4 out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e] * inv, acc[8 * hv + 2 * e + 1] * inv);
-    *reinterpret_cast<u32x4*>(a.O + ri * D + 16 * p + 8 * hv) = out;
+    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
+    *reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv) = out;
   }
 }
 
