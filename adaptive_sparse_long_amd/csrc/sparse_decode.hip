@@ -96,12 +96,6 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
       for (int s = 0; s < NS; ++s)
         kv[kb][s] = val ? ldg16(Kb + (size_t)key * D + 32 * s + 8 * rg) : u32x4{0, 0, 0, 0};
     }
-    u32x4 vv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = base + rg + 4 * r;
-      vv[r] = key < n_keys ? ldg16(Vb + (size_t)key * D + 8 * col) : u32x4{0, 0, 0, 0};
-    }
     float bias[HPG];
 #pragma unroll
     for (int q = 0; q < HPG; ++q) bias[q] = my_valid[q] ? a.bias[(gbase + pos) * G + my_head[q]] : -INFINITY;
@@ -115,6 +109,15 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
       for (int s = 0; s < NS; ++s) z = mfma16x16x32(qa[s], as_bf16x8(kv[kb][s]), z);
       sacc[kb] = z;
     }
+    // V after the scores: K's registers are free by then
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 vv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = base + rg + 4 * r;
+      vv[r] = key < n_keys ? ldg16(Vb + (size_t)key * D + 8 * col) : u32x4{0, 0, 0, 0};
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float alpha_h[HPG];
 #pragma unroll
     for (int q = 0; q < HPG; ++q) {
