@@ -112,6 +112,21 @@ def test_prefill_pool_exhausted_falls_back_to_row_major():
     assert_close(f64(O), ref.double().numpy(), TOL_BF16, "dense causal, pool exhausted")
 
 
+def test_prefill_routing_heavy_and_left_tiles():
+    """Rows with a zero query score every past chunk alike, so every chunk is a
+    routing candidate: some tiles then hold more candidates per lane than the
+    routing kernel keeps in registers (read back from LDS) and some more than
+    its LDS list (left to the general routing kernel), next to ordinary tiles
+    of the same call and of the other head."""
+    Q, K, V, cls = _inputs(1, 2, 1, 4096, 23)
+    Q[:, 0, 1536:3584] = 0
+    rng = np.random.default_rng(23)
+    fixed = np.array([0, 100, 1535, 1536, 1600, 2047, 2048, 2100, 2175, 2176, 3000, 3583, 3584, 4095])
+    check_prefill(Q, K, V, cls, api.Params(),
+                  rows_of=lambda b, h: np.unique(np.concatenate([fixed, rng.integers(1536, 3584, 10)])),
+                  where="heavy tiles")
+
+
 def test_prefill_deterministic():
     Q, K, V, cls = _inputs(1, 8, 2, 1536, 5)
     p = api.Params()
