@@ -163,6 +163,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.fb_count = reinterpret_cast<int*>(ws + L.off_fb_count);
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
   a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
+  a.s_err = reinterpret_cast<float*>(ws + L.off_serr);
   return from_hip(launch_route_prefill(a, stream));
 }
 

@@ -65,6 +65,7 @@ struct PrefillLayout {
   size_t off_fb = 0, off_fb_count = 0;  // tiles left to the general routing kernel
   long long pool_cap = 0;
   size_t off_split = 0, total = 0;
+  size_t off_serr = 0;  // per chunk: bound on |hi-only score - full score| / |q|
 };
 
 __host__ __device__ inline long long prefill_tile_offset(int tile, int n_slots, bool causal) {
@@ -111,6 +112,7 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_plse = o;    o += align256(pairs * sizeof(float));
   L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
   L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
+  L.off_serr = o;    o += align256((size_t)B * Hkv * L.n_slots * sizeof(float));
   L.total = o;
   return L;
 }
@@ -188,6 +190,9 @@ struct RouteArgs {
   // summaries split into bf16 high / low parts (prefill), [B, Hkv, n_slots, d] each
   uint16_t* s_hi;
   uint16_t* s_lo;
+  // per chunk: |s_lo| + 2^-14 |s| (u units), so that |q| times it bounds the
+  // difference between a score from the high parts alone and the full one
+  float* s_err;
   // decode scratch
   float* z;
 };

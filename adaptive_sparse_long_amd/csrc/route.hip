@@ -21,6 +21,7 @@
 // query heads (one wavefront each, 32+ candidates per lane), takes the union of
 // their routed chunks and writes the list with g log2 priors per chunk.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "tau_solve.hpp"
@@ -698,7 +699,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   float* const s_t = reinterpret_cast<float*>(s_words + kTileRows * NWMAX + NE * 4);  // tau iterate per row
   uint32_t* const s_s0 = s_words + kTileRows * NWMAX + NE * 4 + kTileRows;           // first pool slot per row
   // the entry list, an entry a 32-bit word: bits 10.. the distance below the
-  // row's max in units of 2^-22 (< 1), bits 5..9 the row in the wavefront, bits
+  // row's reference in units of 2^-21 (< 2), bits 5..9 the row in the wavefront, bits
   // 0..4 the chunk in the block; the tile's chunk entries in its tail
   __shared__ __attribute__((aligned(16))) uint32_t s_list[kRouteListCap];
   int* const s_cl = reinterpret_cast<int*>(s_list + LCAP);
@@ -708,6 +709,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   __shared__ int s_wtot[4], s_tmp[4];
   __shared__ long long s_tbase;
   __shared__ int s_cnt;                     // entries in the list
+  __shared__ float s_bmax[NWMAX];           // per block of 32 chunks: the largest error bound
   __shared__ int2 s_seg[4][kRoutePrefillMaxSlots / 32];  // per wavefront: (first, count | block << 16)
 
   const int lane = lane_id();
@@ -750,32 +752,38 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   }
 
   // ---- passes over the summary blocks of the tile: body(kb, u) with u the
-  // row's scores of block kb (-inf past the candidates), for the wavefront's blocks
+  // row's scores of block kb (-inf past the candidates), for the wavefront's
+  // blocks; HI: from the high parts of the summaries alone
   u32x4 gl[4];
-  auto load_stage = [&](int kb) {  // 32 chunks x (hi, lo) x 16 segments of 16 bytes
+  auto load_stage = [&](auto hi_tag, int kb) {  // 32 chunks x (hi[, lo]) x 16 segments of 16 bytes
+    constexpr bool HI = decltype(hi_tag)::value;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < (HI ? 2 : 4); ++k) {
       const int idx = tid + 256 * k;
-      const int c = min(kb * 32 + (idx >> 5), max(ncomp_wg - 1, 0));
-      const int part = idx & 31;
+      const int cc = HI ? (idx >> 4) : (idx >> 5);
+      const int part = HI ? (idx & 15) : (idx & 31);
+      const int c = min(kb * 32 + cc, max(ncomp_wg - 1, 0));
       gl[k] = ldg16((part < 16 ? a.s_hi : a.s_lo) + sbase + (size_t)c * D + 8 * (part & 15));
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](auto hi_tag) {
+    constexpr bool HI = decltype(hi_tag)::value;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < (HI ? 2 : 4); ++k) {
       const int idx = tid + 256 * k;
-      const int part = idx & 31;
-      *reinterpret_cast<u32x4*>(&(part < 16 ? sSh : sSl)[(idx >> 5) * SROW + 8 * (part & 15)]) = gl[k];
+      const int cc = HI ? (idx >> 4) : (idx >> 5);
+      const int part = HI ? (idx & 15) : (idx & 31);
+      *reinterpret_cast<u32x4*>(&(part < 16 ? sSh : sSl)[cc * SROW + 8 * (part & 15)]) = gl[k];
     }
   };
-  auto scan_blocks = [&](auto&& body) {
-    if (nblk_wg > 0) load_stage(0);
+  auto scan_blocks = [&](auto hi_tag, auto&& body) {
+    constexpr bool HI = decltype(hi_tag)::value;
+    if (nblk_wg > 0) load_stage(hi_tag, 0);
     for (int kb = 0; kb < nblk_wg; ++kb) {
       const bool more = kb + 1 < nblk_wg;
-      store_stage();
+      store_stage(hi_tag);
       __syncthreads();
-      if (more) load_stage(kb + 1);
+      if (more) load_stage(hi_tag, kb + 1);
       if (kb * 32 < ncomp) {
         // u of row qi for chunks kb*32 + 8 (r/4) + 4 hi32 + r%4
         f32x16 acc;
@@ -786,7 +794,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(ah + 16 * s), qb[s], acc);
-          acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(al + 16 * s), qb[s], acc);
+          if (!HI) acc = mfma32x32x16(*reinterpret_cast<const bf16x8*>(al + 16 * s), qb[s], acc);
         }
         if (kb * 32 + 32 > ncomp) {
 #pragma unroll
@@ -798,23 +806,67 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
       __syncthreads();
     }
   };
+  using HiOnly = std::integral_constant<bool, true>;
+  using Full = std::integral_constant<bool, false>;
 
-  // pass 1: the row's max u over its past chunks
-  float m_run = -INFINITY;
-  scan_blocks([&](int, const f32x16& u) {
+  // per block of 32 chunks, the largest error bound of its chunks (visible
+  // after the first barrier of pass 1)
+  {
+    const int clast = max(ncomp_wg - 1, 0);  // chunks past the tile's candidates repeat the last one
+    float e0 = a.s_err[(size_t)(b * a.Hkv + hk) * n_slots + min(tid, clast)];
+    float e1 = a.s_err[(size_t)(b * a.Hkv + hk) * n_slots + min(tid + 256, clast)];
+    e0 = max_xor16(max16(e0));  // over the 32 chunks of the half wavefront
+    e1 = max_xor16(max16(e1));
+    if ((lane & 31) == 0) {
+      s_bmax[tid >> 5] = e0;
+      s_bmax[8 + (tid >> 5)] = e1;
+    }
+  }
+  // |q| of the row (bf16 values as the MFMA sees them)
+  float qn;
+  {
+    float q2 = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 v = __builtin_bit_cast(u32x4, qb[s]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q2 = fmaf(bf16lo(v[e]), bf16lo(v[e]), q2);
+        q2 = fmaf(bf16hi(v[e]), bf16hi(v[e]), q2);
+      }
+    }
+    qn = sqrtf(sum_xor32(q2));
+  }
+
+  // pass 1, from the high parts: a lower bound of the row's max u, the largest
+  // hi-only score less |q| times its block's error bound
+  float lbound = -INFINITY;
+  float emax = 0.f;  // the largest block error bound the row saw
+  scan_blocks(HiOnly{}, [&](int kb, const f32x16& u) {
     float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
-    m_run = fmaxf(m_run, max_xor32(lmax));
+    const float e = s_bmax[kb];
+    lbound = fmaxf(lbound, max_xor32(lmax) - qn * e);
+    emax = fmaxf(emax, e);
   });
+  // every score above max u - 1 is above lbound - 1; the entries are stored
+  // below ref = lbound + 2 |q| emax, which no score exceeds
+  const float marg = qn * emax;
+  const float ref = lbound + 2.f * marg;
   // pass 2: the scores above max - 1; per block, a segment of the list for the
   // wavefront's entries, lane by lane
   int cnt = 0;   // this lane's entries
   int wcnt = 0;  // the wavefront's entries (uniform)
   int nseg = 0;  // its segments (uniform)
+  float m_run = -INFINITY;  // the row's max u (exact scores)
   {
-    const float thr = m_run - 1.f;
-    scan_blocks([&](int kb, const f32x16& u) {
+    const float thr = lbound - 1.f;
+    scan_blocks(Full{}, [&](int kb, const f32x16& u) {
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
+      m_run = fmaxf(m_run, lmax);
       uint32_t msk = 0u;
 #pragma unroll
       for (int r = 0; r < 16; ++r) msk |= (row_ok && u[r] > thr) ? (1u << r) : 0u;
@@ -841,7 +893,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if ((msk >> r) & 1u) {
-              const uint32_t q = min((uint32_t)rintf((m_run - u[r]) * 4194304.f), (1u << 22) - 1u);
+              const uint32_t q = min((uint32_t)rintf(fmaxf(ref - u[r], 0.f) * 2097152.f), (1u << 22) - 1u);
               s_list[pos++] = (q << 10) | (uint32_t)(row << 5) | (uint32_t)(8 * (r >> 2) + 4 * hi32 + (r & 3));
             }
         }
@@ -850,8 +902,11 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
       cnt += n;
     });
   }
-  const float m_list = m_run;  // the row max the list entries are stored against
-  if (__syncthreads_or(s_cnt > LCAP)) {  // uniform: the tile goes to the general kernel
+  m_run = max_xor32(m_run);
+  const float m_list = ref;  // what the list entries are stored against
+  // uniform: the tile goes to the general kernel if its list overflowed or a
+  // row's error bound leaves the entries' range
+  if (__syncthreads_or(s_cnt > LCAP || (row_ok && marg >= 0.5f))) {
     if (tid == 0) a.fb_tiles[atomicAdd(a.fb_count, 1)] = make_int2(tile, (int)bh);
     return;
   }
@@ -945,7 +1000,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     }
     const int rw = (e >> 5) & 31;
     const float mr = __shfl(m_list, rw);  // the max the distance is taken from
-    uu = j < nl ? mr - (float)(e >> 10) * 2.38418579e-7f : -INFINITY;
+    uu = j < nl ? mr - (float)(e >> 10) * 4.76837158e-7f : -INFINITY;
     kk = (uint32_t)(((w * 32 + rw) << 9) | ((sgv.y >> 16) * 32 + (e & 31)));
   };
   float eu[RUNMAX];
@@ -1244,6 +1299,21 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
     const size_t dst = (bh * a.n_slots + c) * D + e8;
     *reinterpret_cast<bf16x8*>(a.s_hi + dst) = hi;
     *reinterpret_cast<bf16x8*>(a.s_lo + dst) = lo;
+    // the chunk's error bound: |lo| (what a score from the high parts misses)
+    // plus 2^-14 |x| (fp32 rounding of the two dot products, with room to
+    // spare); the 16 lanes of a chunk are one DPP row
+    const u32x4 lw = __builtin_bit_cast(u32x4, lo);
+    float l2 = 0.f, x2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      l2 = fmaf(bf16lo(lw[e]), bf16lo(lw[e]), l2);
+      l2 = fmaf(bf16hi(lw[e]), bf16hi(lw[e]), l2);
+      x2 = fmaf(x0[e], x0[e], x2);
+      x2 = fmaf(x1[e], x1[e], x2);
+    }
+    l2 = sum16(l2);
+    x2 = sum16(x2);
+    if (e8 == 0) a.s_err[bh * a.n_slots + c] = sqrtf(l2) + 6.103515625e-05f * sqrtf(x2);
   }
 }
 
