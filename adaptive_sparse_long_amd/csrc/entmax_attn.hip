@@ -352,7 +352,9 @@ __global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
   constexpr int CAP = kEntmaxCap;
   constexpr int NLD = D / 32;  // 16-byte K loads per thread and tile
   constexpr int HD = D / 2;    // output dims per lane
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][64 * KROW];
+  // one K tile in LDS (D = 64: four workgroups per CU; two buffers would leave three)
+  constexpr int KBUF = D == 64 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[KBUF][64 * KROW];
   __shared__ float s_cu[4][CAP][kWave];     // candidate raw scores: [wavefront][entry][lane]
   __shared__ uint16_t s_ck[4][CAP][kWave];  // their keys
   __shared__ uint32_t s_mask[2][kMaxMaskWords];
@@ -443,14 +445,19 @@ __global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
     const float tmax = max_xor32(lmax);
-    if (tmax > m_run) {
-      // the row's max grows: keep only the entries above the new max - 1 / scale
-      m_run = tmax;
-      if (cnt <= CAP) {
+    // the row's max only grows; entries that fall below max - 1 / scale stay
+    // in the list (they carry no weight) until the list needs their room
+    m_run = fmaxf(m_run, tmax);
+    const float thr = m_run - inv_scale;
+    if (lmax > thr) {
+      int nn = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nn += (s0[r] > thr ? 1 : 0) + (s1[r] > thr ? 1 : 0);
+      if (cnt + nn > CAP && cnt <= CAP) {
         int k2 = 0;
         for (int e = 0; e < cnt; ++e) {
           const float v = s_cu[w][e][lane];
-          if (v > m_run - inv_scale) {
+          if (v > thr) {
             s_cu[w][k2][lane] = v;
             s_ck[w][k2][lane] = s_ck[w][e][lane];
             ++k2;
@@ -458,9 +465,6 @@ __global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
         }
         cnt = k2;
       }
-    }
-    const float thr = m_run - inv_scale;
-    if (lmax > thr) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = J * 64 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
@@ -492,8 +496,9 @@ __global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
       const int J = J0 + q;
       if (J < n_kt_wg) {
         if (J + NP < n_kt_wg) load_tile(J + NP, kr[q]);  // kr[q] (tile J) is already in LDS
-        if (J < n_kt) process(J, J & 1);
-        if (J + 1 < n_kt_wg) store_tile((J + 1) & 1, kr[(q + 1) % NP]);
+        if (J < n_kt) process(J, J % KBUF);
+        if (KBUF == 1) __syncthreads();  // the tile is read before the next one lands
+        if (J + 1 < n_kt_wg) store_tile((J + 1) % KBUF, kr[(q + 1) % NP]);
         __syncthreads();
       }
     }
@@ -512,9 +517,13 @@ __global__ __launch_bounds__(256, 2) void k_entmax_buf(EntmaxAttnArgs a) {
       float lo = mu - 1.f;
       float hi = row_ok ? tau_upper(mu, max(1, cnt + cnt_p), a.alpha) : lo;
       tau = lo;
+      float cu[CAP];  // this lane's list in u units
+#pragma unroll
+      for (int e = 0; e < CAP; ++e) cu[e] = e < cnt ? a.scale * s_cu[w][e][lane] : -INFINITY;
       for (int it = 0; it < a.n_iter; ++it) {
         float f0 = 0.f, f1 = 0.f, f2 = 0.f;
-        for (int e = 0; e < cnt; ++e) tau_terms<KIND>(a.scale * s_cu[w][e][lane], tau, a.beta, f0, f1, f2);
+#pragma unroll
+        for (int e = 0; e < CAP; ++e) tau_terms<KIND>(cu[e], tau, a.beta, f0, f1, f2);
         f0 = sum_xor32(f0);
         f1 = sum_xor32(f1);
         if (KIND != 1) f2 = sum_xor32(f2);
