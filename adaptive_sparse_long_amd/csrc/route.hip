@@ -867,12 +867,11 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
       m_run = fmaxf(m_run, lmax);
-      uint32_t msk = 0u;
+      int n = 0;  // this lane's entries in the block
 #pragma unroll
-      for (int r = 0; r < 16; ++r) msk |= (row_ok && u[r] > thr) ? (1u << r) : 0u;
+      for (int r = 0; r < 16; ++r) n += (row_ok && u[r] > thr) ? 1 : 0;
       // this lane's place among the wavefront's entries of the block: the
       // prefix of n (<= 16) bit by bit with ballots and mbcnt
-      const int n = __popc(msk);
       int pre = 0, tot = 0;
 #pragma unroll
       for (int bit = 0; bit < 5; ++bit) {
@@ -890,11 +889,13 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         ++nseg;
         if (first + tot <= LCAP) {
           int pos = first + pre;
+          const uint32_t kbase = (uint32_t)((row << 5) | (4 * hi32));
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if ((msk >> r) & 1u) {
-              const uint32_t q = min((uint32_t)rintf(fmaxf(ref - u[r], 0.f) * 2097152.f), (1u << 22) - 1u);
-              s_list[pos++] = (q << 10) | (uint32_t)(row << 5) | (uint32_t)(8 * (r >> 2) + 4 * hi32 + (r & 3));
+            if (row_ok && u[r] > thr) {
+              // the distance below ref in 2^-21 units, rounded (v_cvt_u32 truncates)
+              const uint32_t q = min((uint32_t)fmaxf(fmaf(ref - u[r], 2097152.f, 0.5f), 0.f), (1u << 22) - 1u);
+              s_list[pos++] = (q << 10) | kbase | (uint32_t)(8 * (r >> 2) + (r & 3));
             }
         }
       }
