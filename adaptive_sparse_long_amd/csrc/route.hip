@@ -666,7 +666,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 //
 // Everything after that is spread evenly over the entries, whatever their
 // rows: each lane takes a contiguous run of its wavefront's entries. The tau
-// sums are added per row in 2^-32 fixed point, so their order (and with it the
+// sums are added per row in fixed point, so their order (and with it the
 // result) does not depend on which lane adds what. The routed chunks go into
 // per-row bitmasks, from which the tile's chunk union, each pair's rank in its
 // row and its place among the pairs of its chunk follow without contended
@@ -687,13 +687,18 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   constexpr int kStageWords = 2 * 32 * SROW / 2;
   __shared__ __attribute__((aligned(16))) uint16_t s_stage[2 * 32 * SROW];
   static_assert(kStageWords >= kTileRows * NWMAX + NE * 4 + 2 * kTileRows, "scratch fits the stage");
-  static_assert(kTileRows * NWMAX >= 6 * kTileRows && kTileRows * NWMAX >= 4 * kChunk, "early scratch fits");
+  static_assert(kTileRows * NWMAX >= 4 * kChunk + 6 * kTileRows, "early scratch fits");
   static_assert(NE <= 512 && kTileRows <= 128, "entries pack row and chunk into 16 bits");
   uint16_t* const sSh = s_stage;
   uint16_t* const sSl = s_stage + 32 * SROW;
   uint32_t* const s_words = reinterpret_cast<uint32_t*>(s_stage);
   float (*const s_lc)[kChunk] = reinterpret_cast<float (*)[kChunk]>(s_words);  // <k, cls> / sqrt(d)
-  unsigned long long (*const s_sum)[kTileRows] = reinterpret_cast<unsigned long long (*)[kTileRows]>(s_words);
+  // tau sums per row in fixed point: 2^-22 units in 32 bits where every term
+  // is at most 1 (a row's sums then stay below 512), 2^-32 units in 64 bits for
+  // a general alpha
+  using Fx = std::conditional_t<KIND == 0, unsigned long long, uint32_t>;
+  // (after the own-chunk logits, which other wavefronts may still be reading)
+  Fx (*const s_sum)[kTileRows] = reinterpret_cast<Fx (*)[kTileRows]>(s_words + 4 * kChunk);
   uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_words);
   uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(s_words + kTileRows * NWMAX);
   float* const s_t = reinterpret_cast<float*>(s_words + kTileRows * NWMAX + NE * 4);  // tau iterate per row
@@ -1036,21 +1041,28 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     float hi = has ? tau_upper(m_run, max(1, n), a.alpha) : lo;
     float t = lo;
     // fixed point: terms and sums are >= 0; sums stay far below 2^32
-    auto to_fx = [](float x) -> unsigned long long {
-      x = fminf(x, 1.0e9f);
-      const float xi = floorf(x);
-      const uint32_t hw = (uint32_t)xi;
-      const uint32_t lw = (uint32_t)fminf((x - xi) * 4294967296.f, 4294967040.f);
-      return ((unsigned long long)hw << 32) | lw;
+    auto to_fx = [](float x) -> Fx {
+      if constexpr (KIND == 0) {
+        x = fminf(x, 1.0e9f);
+        const float xi = floorf(x);
+        const uint32_t hw = (uint32_t)xi;
+        const uint32_t lw = (uint32_t)fminf((x - xi) * 4294967296.f, 4294967040.f);
+        return ((unsigned long long)hw << 32) | lw;
+      } else {
+        return (uint32_t)fminf(fmaf(x, 4194304.f, 0.5f), 4294967040.f);
+      }
     };
-    auto from_fx = [](unsigned long long v) {
-      return (float)(uint32_t)(v >> 32) + (float)(uint32_t)v * 2.3283064365386963e-10f;
+    auto from_fx = [](Fx v) {
+      if constexpr (KIND == 0)
+        return (float)(uint32_t)(v >> 32) + (float)(uint32_t)v * 2.3283064365386963e-10f;
+      else
+        return (float)v * 2.384185791015625e-07f;
     };
     if (owner) {
       s_t[R] = has ? t : INFINITY;
-      s_sum[0][R] = 0ull;
-      s_sum[1][R] = 0ull;
-      s_sum[2][R] = 0ull;
+      s_sum[0][R] = 0;
+      s_sum[1][R] = 0;
+      s_sum[2][R] = 0;
     }
     wave_lds_fence();
     if (wave_any(has)) {
@@ -1085,9 +1097,9 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
           conv = tau_converged(t, nt);
           t = nt;
           s_t[R] = t;
-          s_sum[0][R] = 0ull;
-          s_sum[1][R] = 0ull;
-          s_sum[2][R] = 0ull;
+          s_sum[0][R] = 0;
+          s_sum[1][R] = 0;
+          s_sum[2][R] = 0;
         }
         wave_lds_fence();
         if (wave_all(conv)) break;
