@@ -1434,11 +1434,16 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
     }
     const int nval = t - ct * kChunk + 1;
     const uint16_t* kp = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ct * kChunk) * D;
-#pragma unroll 4
+    // all 16 loads in flight together (keys past the sequence read its last
+    // key and are masked below)
+    u32x4 kvs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) kvs[r] = ldg16(kp + (size_t)min(r * 4 + rg, nval - 1) * D + 8 * sub);
+#pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = r * 4 + rg;
       const bool val = key < nval;
-      u32x4 kv = val ? ldg16(kp + (size_t)key * D + 8 * sub) : zero4();
+      const u32x4 kv = kvs[r];
       const float pq = sum16(dot8_bf16(kv, wq));
       const float pc = sum16(dot8_bf16(kv, wc));
       if (sub == 0) {
@@ -1459,11 +1464,11 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   // ---- scores of complete chunks c = k*64 + lane
   float u[KPL];
   const float* zrow = a.z + bh * a.n_slots;
+  // (unconditional loads, so that they are all in flight together)
 #pragma unroll
-  for (int k = 0; k < KPL; ++k) {
-    const int c = k * 64 + lane;
-    u[k] = c < ncomp ? zrow[c] * am1 : -INFINITY;
-  }
+  for (int k = 0; k < KPL; ++k) u[k] = zrow[min(k * 64 + lane, max(ncomp - 1, 0))];
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) u[k] = k * 64 + lane < ncomp ? u[k] * am1 : -INFINITY;
   float tau = INFINITY;
   if (ncand > 0) {
     float m = -INFINITY;
