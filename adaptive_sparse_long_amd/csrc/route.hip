@@ -1248,10 +1248,17 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         const int n = q ? c1 : c0;
         s_eoff[e] = f;
         a.ceo[toff + e] = make_int2(f, n);
-        a.cbase[toff + e] = atomicAdd(&cmp[s_cl[e]], n);  // the entry's pairs among all pairs of its chunk
       }
     }
     __syncthreads();
+    // the entries' places among all pairs of their chunks (global atomics with
+    // return): requested now, their results stored after the records
+    int cb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * tid + q;
+      cb[q] = e < ne ? atomicAdd(&cmp[s_cl[e]], q ? c1 : c0) : 0;
+    }
     auto place = [&](int e, int rr) {
       const int wr = rr >> 5;
       int j = s_eoff[e] + __popc(s_rm[e][wr] & ((1u << (rr & 31)) - 1u));
@@ -1266,6 +1273,9 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
                                                     __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
     });
     if (own_pair) a.trec[tb + place(epos(cw), R)] = make_int4(qi * g + hh, (int)(s0 + nrt), __float_as_int(lwd), 0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (2 * tid + q < ne) a.cbase[toff + 2 * tid + q] = cb[q];
   } else {
     // ---- row-major list: -inf for every (entry, row), then the log2 weights
     // of the attended pairs
