@@ -658,11 +658,14 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 // v_mfma_f32_32x32x16_bf16 (hi and lo parts into one accumulator) gives each
 // lane 16 scores (u units) of its query row per block, lanes l and l ^ 32
 // sharing a row. Only scores above max u - 1 can carry weight (tau >= max u -
-// 1): a first pass finds each row's max, a second writes the scores above max
-// - 1 as (u, row, chunk) entries into the tile's LDS list, a segment per
-// wavefront and block. A tile whose entries do not fit (the list, or 16 per
-// lane of a wavefront) is queued for the general kernel before anything else
-// is written.
+// 1): a first pass, from the high parts alone, bounds each row's max from
+// below (the per-chunk error bound of the split covers the missing low
+// parts); a second, exact pass writes every score above that bound - 1 as a
+// (distance, row, chunk) entry into the tile's LDS list, a segment per
+// wavefront and block, and finds the exact row max. A tile whose entries do
+// not fit the list (or whose error bounds leave the entries' range) is queued
+// for the general kernel before anything else is written; entries past 16 per
+// lane are read back from the list when used.
 //
 // Everything after that is spread evenly over the entries, whatever their
 // rows: each lane takes a contiguous run of its wavefront's entries. The tau
