@@ -161,6 +161,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.cmcnt = reinterpret_cast<uint16_t*>(ws + L.off_cmcnt);
   a.fb_tiles = reinterpret_cast<int2*>(ws + L.off_fb);
   a.fb_count = reinterpret_cast<int*>(ws + L.off_fb_count);
+  a.n_rm = a.fb_count + 1;
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
   a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
   a.s_err = reinterpret_cast<float*>(ws + L.off_serr);
@@ -213,6 +214,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.tbase = reinterpret_cast<const uint32_t*>(ws + L.off_tbase);
   a.rslot = reinterpret_cast<const uint32_t*>(ws + L.off_rslot);
   a.cmcnt = reinterpret_cast<const uint16_t*>(ws + L.off_cmcnt);
+  a.n_rm = reinterpret_cast<const int*>(ws + L.off_fb_count) + 1;
   a.plse = reinterpret_cast<float*>(ws + L.off_plse);
   a.po = reinterpret_cast<uint16_t*>(ws + L.off_po);
   return from_hip(launch_sparse_prefill(a, stream));

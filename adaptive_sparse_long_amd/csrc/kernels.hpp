@@ -106,7 +106,7 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_pool = o;    o += align256(kPools * sizeof(unsigned long long));
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
   L.off_fb = o;      o += align256(heads * L.n_tiles * 2 * sizeof(int));
-  L.off_fb_count = o; o += align256(sizeof(int));
+  L.off_fb_count = o; o += align256(2 * sizeof(int));  // queued tiles, row-major tiles
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
   L.off_plse = o;    o += align256(pairs * sizeof(float));
@@ -187,6 +187,7 @@ struct RouteArgs {
   uint16_t* cmcnt;
   int2* fb_tiles;   // tiles the list-based kernel left: (tile, b * Hq + h)
   int* fb_count;     // their number, zeroed by the summary split
+  int* n_rm;         // tiles without pool slots (row-major), zeroed by the summary split
   // summaries split into bf16 high / low parts (prefill), [B, Hkv, n_slots, d] each
   uint16_t* s_hi;
   uint16_t* s_lo;
@@ -226,6 +227,7 @@ struct PrefillAttnArgs {
   const uint32_t* tbase;
   const uint32_t* rslot;
   const uint16_t* cmcnt;
+  const int* n_rm;  // tiles the routing left row-major
   float* plse;
   uint16_t* po;
 };

@@ -531,6 +531,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
   __syncthreads();
   const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  if (threadIdx.x == 0 && !pooled) atomicAdd(a.n_rm, 1);
   const long long tb = s_tbase;
   int wpre = 0;
 #pragma unroll
@@ -1181,6 +1182,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   }
   __syncthreads();
   const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  if (tid == 0 && !pooled) atomicAdd(a.n_rm, 1);
   const long long tb = s_tbase;
   int wpre = 0;
   for (int ww = 0; ww < w; ++ww) wpre += s_wtot[ww];
@@ -1303,7 +1305,10 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
   // the per-chunk pair counters the routing adds to start from zero
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_bhc; i += gridDim.x * blockDim.x) a.cmp[i] = 0;
   if (blockIdx.x == 0 && threadIdx.x < kPools) a.pool[threadIdx.x] = 0ull;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.fb_count = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *a.fb_count = 0;
+    *a.n_rm = 0;
+  }
   const float uscale = (a.alpha - 1.f) * a.zscale;
   const size_t per_bh = (size_t)n_need * (D / 8);
   const size_t total = (size_t)a.B * a.Hkv * per_bh;

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VROW];
 
+  if (*a.n_rm == 0) return;  // every tile went chunk-major
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;

@@ -82,6 +82,8 @@ def _inputs(B, Hq, Hkv, N, seed, planted="chunks"):
         (1, 4, 4, 300, api.Params(scaling_factor=3.0), None),
         (1, 1, 1, 64, api.Params(), None),
         (1, 1, 1, 37, api.Params(estimate_diagonal=False), None),
+        (1, 8, 1, 700, api.Params(), "needles"),
+        (2, 4, 2, 900, api.Params(estimate_diagonal=True), "chunks"),
     ],
 )
 def test_prefill_small(B, Hq, Hkv, N, p, planted):
