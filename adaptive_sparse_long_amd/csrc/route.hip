@@ -870,23 +870,23 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   int nseg = 0;  // its segments (uniform)
   float m_run = -INFINITY;  // the row's max u (exact scores)
   {
-    const float thr = lbound - 1.f;
+    // rows past the sequence end take no entries
+    const float thr = row_ok ? lbound - 1.f : INFINITY;
     scan_blocks(Full{}, [&](int kb, const f32x16& u) {
       float lmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
       m_run = fmaxf(m_run, lmax);
-      int n = 0;  // this lane's entries in the block
+      // this lane's place among the wavefront's entries of the block (lanes in
+      // order, a lane's entries in register order): per register a ballot,
+      // its lanes below this one counted with mbcnt
+      uint32_t pre = 0u;
+      int tot = 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) n += (row_ok && u[r] > thr) ? 1 : 0;
-      // this lane's place among the wavefront's entries of the block: the
-      // prefix of n (<= 16) bit by bit with ballots and mbcnt
-      int pre = 0, tot = 0;
-#pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
-        const uint64_t bm = __ballot((n >> bit) & 1);
-        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u)) << bit;
-        tot += __popcll(bm) << bit;
+      for (int r = 0; r < 16; ++r) {
+        const uint64_t bm = __ballot(u[r] > thr);
+        pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, pre));
+        tot += __popcll(bm);
       }
       if (tot > 0) {
         int first = 0;
@@ -897,19 +897,22 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         first = __shfl(first, 0);
         ++nseg;
         if (first + tot <= LCAP) {
-          int pos = first + pre;
+          uint32_t* lp = s_list + first + (int)pre;
+          uint32_t* const lp0 = lp;
           const uint32_t kbase = (uint32_t)((row << 5) | (4 * hi32));
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (row_ok && u[r] > thr) {
-              // the distance below ref in 2^-21 units, rounded (v_cvt_u32 truncates)
-              const uint32_t q = min((uint32_t)fmaxf(fmaf(ref - u[r], 2097152.f, 0.5f), 0.f), (1u << 22) - 1u);
-              s_list[pos++] = (q << 10) | kbase | (uint32_t)(8 * (r >> 2) + (r & 3));
+            if (u[r] > thr) {
+              // the distance below ref in 2^-21 units, rounded (v_cvt_u32
+              // truncates); below 2 (so 22 bits) while the error bound is
+              // under 0.5, which the tile needs to stay here
+              const uint32_t q = (uint32_t)fmaxf(fmaf(ref - u[r], 2097152.f, 0.5f), 0.f);
+              *lp++ = (q << 10) | kbase | (uint32_t)(8 * (r >> 2) + (r & 3));
             }
+          cnt += (int)(lp - lp0);
         }
       }
       wcnt += tot;
-      cnt += n;
     });
   }
   m_run = max_xor32(m_run);
