@@ -9,7 +9,8 @@ Method (DashAttention README page, "How it works"): ``summarize`` builds one
 key summary per chunk with head_cls, ``route`` runs alpha-entmax chunk routing,
 ``sparse_attn_prefill`` / ``sparse_attn_decode`` run the prior-induced sparse
 softmax over the routed chunks. ``entmax_attn`` is the dense alpha-entmax
-attention with block skipping of the AdaSplash README page.
+attention with block skipping of the AdaSplash README page, and ``entmax``
+its row-wise entmax activation ("Usage": Triton Entmax).
 """
 
 from __future__ import annotations
@@ -29,6 +30,7 @@ __all__ = [
     "sparse_attn_prefill",
     "sparse_attn_decode",
     "entmax_attn",
+    "entmax",
     "prefill",
     "decode_step",
 ]
@@ -176,6 +178,29 @@ def entmax_attn(Q, K, V, alpha=1.5, n_iter=10, causal=True, varlen=None, with_ma
                          int(bool(causal)), _p(out), _p(tau), _p(mask), _stream(Q.device))
     _lib.check(st, "entmax_attn")
     return out, tau, mask
+
+
+def entmax(x, alpha=1.5, n_iter=10, return_tau=False, out=None):
+    """Row-wise alpha-entmax over the last dimension (AdaSplash "Usage": Triton Entmax).
+
+    ``x`` is a contiguous float32 or bfloat16 GPU tensor; ``out`` (same shape
+    and dtype) may be ``x`` itself. Returns the probabilities, and tau per row
+    (float32, u units) when ``return_tau``."""
+    lib = _lib.load()
+    _need(x, "x")
+    if x.dim() < 1 or x.shape[-1] == 0:
+        raise ValueError("x needs a non-empty last dimension")
+    n = x.shape[-1]
+    rows = x.numel() // n
+    y = torch.empty_like(x) if out is None else out
+    if out is not None:
+        _need(out, "out", x.dtype)
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    tau = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if return_tau else None
+    st = lib.entmax_rows(_p(x), _p(y), _dt(x), rows, n, float(alpha), int(n_iter), _p(tau), _stream(x.device))
+    _lib.check(st, "entmax_rows")
+    return (y, tau) if return_tau else y
 
 
 def prefill(Q, K, V, head_cls, params: Params = Params(), with_bits=True, workspace=None, S=None):

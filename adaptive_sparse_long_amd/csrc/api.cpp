@@ -278,4 +278,22 @@ dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype 
   return from_hip(launch_entmax_attn(a, dt == DASH_BF16, stream));
 }
 
+dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, float alpha,
+                        int n_iter, float* tau, hipStream_t stream) {
+  if (!X || !Y) return DASH_ERR_INVALID_ARG;
+  if (rows <= 0 || n <= 0 || !finite_gt1(alpha) || n_iter < 1) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (n > kEntmaxRowsMax) return DASH_ERR_UNSUPPORTED;
+  EntmaxRowsArgs a{};
+  a.X = X;
+  a.Y = Y;
+  a.rows = rows;
+  a.n = n;
+  a.alpha = alpha;
+  a.beta = 1.f / (alpha - 1.f);
+  a.n_iter = n_iter;
+  a.tau = tau;
+  return from_hip(launch_entmax_rows(a, dt == DASH_BF16, stream));
+}
+
 }  // extern "C"

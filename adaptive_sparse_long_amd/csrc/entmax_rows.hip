@@ -1,0 +1,170 @@
+// entmax_rows.hip -- row-wise alpha-entmax, the activation the AdaSplash README
+// ("Usage", "Triton Entmax (Optimized Entmax Activation)") applies over the
+// last dimension of a 2-D tensor with its alpha and n_iter arguments, the
+// threshold found by Halley's method plus bisection. For every row x of n:
+//   u = (alpha - 1) x,  p_j = max(u_j - tau, 0)^(1/(alpha - 1)),  sum_j p_j = 1.
+//
+// The row stays in registers for the whole solve, so it is read from HBM once
+// and written once: one wavefront per row up to 2048 entries (four rows per
+// workgroup, no barrier), one 1024-thread workgroup per row up to 32768.
+// Entry j * STRIDE + t of the row belongs to thread t of the row, so every
+// load and store instruction of a wavefront covers 64 consecutive entries.
+// Each Halley step is one pass over the registers and one reduction of
+// (f, f', f''): DPP and permlane swaps within the wavefront, then, for the
+// workgroup variant, the 16 wavefront sums through LDS in a fixed order (so
+// every thread holds the same sums and takes the same step). The outputs are
+// divided by their sum, so they sum to one up to rounding also when n_iter
+// ends the solve before it converges.
+#include "kernels.hpp"
+#include "tau_solve.hpp"
+
+namespace dash {
+
+namespace {
+
+__device__ __forceinline__ float load_elem(const float* p) { return *p; }
+__device__ __forceinline__ float load_elem(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+}  // namespace
+
+// WAVES = 4: a row per wavefront; WAVES = 16: a row per workgroup. VPL entries
+// per thread (n <= VPL * 64, resp. VPL * 1024).
+template <typename T, int VPL, int KIND, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void k_entmax_rows(EntmaxRowsArgs a) {
+  constexpr bool WG = WAVES == 16;
+  constexpr int STRIDE = WG ? WAVES * kWave : kWave;
+  __shared__ float s_red[2][3][WAVES];  // wavefront sums, two parities
+  __shared__ float s_max[WAVES];
+
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const long long row = WG ? (long long)blockIdx.x : (long long)blockIdx.x * WAVES + w;
+  if (row >= a.rows) return;  // uniform over the row's threads
+  const int n = a.n;
+  const int t = WG ? (int)threadIdx.x : lane;
+  const T* x = static_cast<const T*>(a.X) + row * (long long)n;
+  T* y = static_cast<T*>(a.Y) + row * (long long)n;
+  const float am1 = a.alpha - 1.f;
+
+  float u[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = j * STRIDE + t;
+    u[j] = e < n ? am1 * load_elem(x + e) : -INFINITY;
+  }
+
+  int par = 0;
+  // (f0, f1, f2) summed over the row, the same in every thread of the row
+  auto row_sum3 = [&](float& f0, float& f1, float& f2) {
+    f0 = wave_sum(f0);
+    f1 = wave_sum(f1);
+    f2 = wave_sum(f2);
+    if constexpr (WG) {
+      if (lane == 0) {
+        s_red[par][0][w] = f0;
+        s_red[par][1][w] = f1;
+        s_red[par][2][w] = f2;
+      }
+      __syncthreads();  // also orders the reads of this parity two reductions back
+      f0 = f1 = f2 = 0.f;
+#pragma unroll
+      for (int k = 0; k < WAVES; ++k) {
+        f0 += s_red[par][0][k];
+        f1 += s_red[par][1][k];
+        f2 += s_red[par][2][k];
+      }
+      par ^= 1;
+    }
+  };
+
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) mx = fmaxf(mx, u[j]);
+  mx = wave_max(mx);
+  if constexpr (WG) {
+    if (lane == 0) s_max[w] = mx;
+    __syncthreads();
+    mx = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < WAVES; ++k) mx = fmaxf(mx, s_max[k]);
+  }
+
+  // ---- tau on the bracket [max u - 1, max u - n^-(alpha-1)]
+  float tau = INFINITY;  // a row without a finite entry
+  if (mx > -INFINITY) {
+    float lo = mx - 1.f;
+    float hi = tau_upper(mx, n, a.alpha);
+    float tt = lo;
+    for (int it = 0; it < a.n_iter; ++it) {
+      float f0 = 0.f, f1 = 0.f, f2 = 0.f;
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) tau_terms<KIND>(u[j], tt, a.beta, f0, f1, f2);
+      row_sum3(f0, f1, f2);
+      const float nt = tau_step<KIND>(tt, f0, f1, f2, a.beta, lo, hi);
+      const bool conv = tau_converged(tt, nt);
+      tt = nt;
+      if (conv) break;  // the same decision in every thread of the row
+    }
+    tau = tt;
+  }
+
+  // ---- p = max(u - tau, 0)^beta, divided by its sum
+  float ps = 0.f, dummy1 = 0.f, dummy2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    u[j] = prior_of<KIND>(u[j] - tau, a.beta);
+    ps += u[j];
+  }
+  row_sum3(ps, dummy1, dummy2);
+  const float inv = ps > 0.f ? 1.f / ps : 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int e = j * STRIDE + t;
+    if (e < n) store_elem(y + e, u[j] * inv);
+  }
+  if (a.tau != nullptr && t == 0) a.tau[row] = tau;
+}
+
+namespace {
+
+template <typename T, int KIND>
+hipError_t entmax_rows_t(const EntmaxRowsArgs& a, hipStream_t stream) {
+  if (a.n <= 64 * 32) {
+    const dim3 grid((unsigned)((a.rows + 3) / 4));
+    const int v = (a.n + 63) / 64;
+#define DASH_ER(V)                                                                           \
+  if (v <= V) {                                                                              \
+    hipLaunchKernelGGL((k_entmax_rows<T, V, KIND, 4>), grid, dim3(4 * kWave), 0, stream, a); \
+    return hipGetLastError();                                                                \
+  }
+    DASH_ER(1) DASH_ER(2) DASH_ER(4) DASH_ER(8) DASH_ER(16) DASH_ER(32)
+#undef DASH_ER
+  }
+  const dim3 grid((unsigned)a.rows);
+  const int v = (a.n + 1023) / 1024;
+#define DASH_ER(V)                                                                             \
+  if (v <= V) {                                                                                \
+    hipLaunchKernelGGL((k_entmax_rows<T, V, KIND, 16>), grid, dim3(16 * kWave), 0, stream, a); \
+    return hipGetLastError();                                                                  \
+  }
+  DASH_ER(4) DASH_ER(8) DASH_ER(16) DASH_ER(32)
+#undef DASH_ER
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t entmax_rows_kind(const EntmaxRowsArgs& a, hipStream_t stream) {
+  if (a.alpha == 1.5f) return entmax_rows_t<T, 2>(a, stream);
+  if (a.alpha == 2.0f) return entmax_rows_t<T, 1>(a, stream);
+  return entmax_rows_t<T, 0>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_entmax_rows(const EntmaxRowsArgs& a, bool bf16, hipStream_t stream) {
+  return bf16 ? entmax_rows_kind<uint16_t>(a, stream) : entmax_rows_kind<float>(a, stream);
+}
+
+}  // namespace dash

@@ -262,12 +262,23 @@ struct EntmaxAttnArgs {
   int only_marked;  // general kernel: only row blocks a row of which has tau = NaN
 };
 
+struct EntmaxRowsArgs {
+  const void* X;
+  void* Y;
+  long long rows;
+  int n;
+  float alpha, beta;  // beta = 1 / (alpha - 1)
+  int n_iter;
+  float* tau;  // or nullptr
+};
+
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_route_decode(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream);  // plan, scatter, chunk-major, row-major + merge
 hipError_t launch_sparse_decode(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_entmax_rows(const EntmaxRowsArgs& a, bool bf16, hipStream_t stream);
 
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
@@ -276,5 +287,6 @@ constexpr int kRouteListCap = 5120;          // LDS list words per tile: candida
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel
+constexpr int kEntmaxRowsMax = 32768;        // row-wise entmax: 32 entries per thread of 1024
 
 }  // namespace dash

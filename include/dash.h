@@ -196,6 +196,27 @@ dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype 
                         int causal, void* O, float* tau, uint32_t* block_mask,
                         hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * entmax_rows -- row-wise alpha-entmax (AdaSplash README, "Usage": "Triton
+ * Entmax (Optimized Entmax Activation)", the activation over the last
+ * dimension with alpha and n_iter). For each row r < rows of X:
+ *   u = (alpha - 1) x_r,
+ *   tau_r : sum_j max(u_j - tau_r, 0)^(1/(alpha-1)) = 1   (Halley + bisection,
+ *           at most n_iter steps),
+ *   Y_r  = max(u - tau_r, 0)^(1/(alpha-1)), divided by its sum.
+ * Entries equal to -inf get 0; a row with no finite entry gets Y = 0 and
+ * tau = +inf.
+ *   X, Y  [rows, n] row-major, dtype dt (DASH_F32 or DASH_BF16), device
+ *         memory owned by the caller; Y may be X (each entry is read before
+ *         it is written, by the same thread)
+ *   tau   [rows] float32 on the device, in u units, or NULL
+ * Errors: NULL X or Y, rows or n <= 0, alpha not a finite value > 1 or
+ * n_iter < 1 -> DASH_ERR_INVALID_ARG; n > 32768 -> DASH_ERR_UNSUPPORTED; a
+ * launch failure -> DASH_ERR_HIP. Nothing is allocated; no host sync.
+ * --------------------------------------------------------------------------- */
+dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, float alpha,
+                        int n_iter, float* tau, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* dash_status_string(dash_status s);
 

@@ -26,6 +26,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
+        "entmax_rows",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -121,3 +122,16 @@ def test_attention_validation(lib):
     assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.5, 10, 2, FAKE, FAKE, NULL, NULL) == INVALID
     assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 96, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == UNSUPPORTED
     assert e(FAKE, FAKE, FAKE, 1, 1, 1, 70000, 64, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == UNSUPPORTED
+
+
+def test_entmax_rows_validation(lib):
+    r = lib.entmax_rows
+    assert r(NULL, FAKE, 0, 4, 16, 1.5, 10, NULL, NULL) == INVALID
+    assert r(FAKE, NULL, 0, 4, 16, 1.5, 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 0, 16, 1.5, 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 4, 0, 1.5, 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 4, 16, 1.0, 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 4, 16, float("inf"), 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 4, 16, 1.5, 0, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 7, 4, 16, 1.5, 10, NULL, NULL) == INVALID
+    assert r(FAKE, FAKE, 0, 4, 32769, 1.5, 10, NULL, NULL) == UNSUPPORTED
