@@ -293,6 +293,7 @@ dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, 
   a.beta = 1.f / (alpha - 1.f);
   a.n_iter = n_iter;
   a.tau = tau;
+  a.n_cu = device_cus();
   return from_hip(launch_entmax_rows(a, dt == DASH_BF16, stream));
 }
 

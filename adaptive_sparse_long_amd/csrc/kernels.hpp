@@ -270,6 +270,7 @@ struct EntmaxRowsArgs {
   float alpha, beta;  // beta = 1 / (alpha - 1)
   int n_iter;
   float* tau;  // or nullptr
+  int n_cu;    // sizes the grid-stride grid
 };
 
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);

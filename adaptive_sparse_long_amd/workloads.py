@@ -70,6 +70,13 @@ WORKLOADS = {
         "varlen_entmax", 1005, "entmax", 8, 16, 16, 8192, 64, "bf16", 2.0,
         causal=False, scale=2.0, varlen_range=(512, 8192),
     ),
+    # row-wise entmax: B rows of N entries (Hq, Hkv, d unused)
+    "entmax_rows_64k_1024": Workload(
+        "entmax_rows_64k_1024", 1006, "entmax_rows", 65536, 1, 1, 1024, 1, "f32", 1.5, scale=2.0,
+    ),
+    "entmax_rows_128x256": Workload(
+        "entmax_rows_128x256", 1007, "entmax_rows", 128, 1, 1, 256, 1, "f32", 1.5,
+    ),
 }
 
 
@@ -97,6 +104,12 @@ def dense_entmax_inputs(B, H, N, d, seed, dtype="bf16", scale=1.0, varlen_range=
     k = torch.randn(B, H, N, d, generator=g, device=device) * scale
     v = torch.randn(B, H, N, d, generator=g, device=device) * scale
     return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype), lens
+
+
+def entmax_rows_inputs(rows, n, seed, dtype="f32", scale=1.0, device="cpu"):
+    """Scores ~ scale * N(0, 1) in [rows, n]."""
+    g = _gen(seed, device)
+    return _cast(torch.randn(rows, n, generator=g, device=device) * scale, dtype)
 
 
 def routed_prefill_inputs(B, Hq, Hkv, N, d, seed, planted=None, chunk_size=64, n_planted_chunks=20,

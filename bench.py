@@ -36,6 +36,7 @@ from adaptive_sparse_long_amd.workloads import (  # noqa: E402
     WORKLOADS,
     decode_inputs,
     dense_entmax_inputs,
+    entmax_rows_inputs,
     routed_prefill_inputs,
 )
 
@@ -50,6 +51,7 @@ KERNEL_SOURCES = {
     "k_prefill_cm": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_buf": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_rows": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
 
 
@@ -304,6 +306,24 @@ def bench_entmax(w, steps, warmup):
     }
 
 
+def bench_entmax_rows(w, steps, warmup):
+    """Row-wise entmax over w.B rows of w.N entries: HIP-event time per call and
+    the algorithmic HBM bytes (every entry read once and written once, tau out)."""
+    x = entmax_rows_inputs(w.B, w.N, w.seed, dtype=w.dtype, scale=w.scale, device="cuda")
+    y = torch.empty_like(x)
+    t = Timer()
+    for _ in range(warmup):
+        api.entmax(x, alpha=w.alpha, out=y)
+    for _ in range(steps):
+        e = t.start()
+        api.entmax(x, alpha=w.alpha, out=y)
+        t.stop(e)
+    ms = t.mean_ms()
+    nbytes = float(2 * x.numel() * x.element_size())
+    return {"rows": w.B, "n": w.N, "us": ms * 1e3, "bytes_per_launch": nbytes,
+            "GBps": nbytes / (ms / 1e3) / 1e9}
+
+
 # --------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(w, budget_s=20.0):
     """The float64 oracle on host cores, on a random sample of query rows of the
@@ -452,6 +472,15 @@ def main():
                                       "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                       "frac": ent["tflops_qk_pass"] / PEAK_BF16_TFLOPS,
                                       "traffic": measured_traffic("k_entmax_buf")}}
+    if not args.no_entmax:
+        log("entmax rows")
+        big = bench_entmax_rows(WORKLOADS["entmax_rows_64k_1024"], args.steps, args.warmup)
+        small = bench_entmax_rows(WORKLOADS["entmax_rows_128x256"], args.steps, args.warmup)
+        out["entmax_rows"] = {
+            "workload": "entmax_rows_64k_1024", **big, "us_128x256": small["us"],
+            "roofline": {"kernel": "k_entmax_rows", "bound": "hbm", "achieved": big["GBps"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": big["GBps"] / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("k_entmax_rows")}}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(wp)
