@@ -100,6 +100,29 @@ def test_entmax_deterministic():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
+@pytest.mark.parametrize("dtype,causal,alpha", [("bf16", False, 2.0), ("f32", True, 1.5)])
+def test_entmax_without_block_mask(dtype, causal, alpha):
+    """AdaSplash "without Block Masking": the same attention with no mask written
+    (block_mask NULL, no O(Tr x Tc) memory) gives bit-identical O and tau, and
+    both match the oracle; the single-pass and the general kernel both run
+    (zero query rows overflow the single pass for the first row block)."""
+    q, k, v, _ = dense_entmax_inputs(2, 2, 333, 64, 91, dtype=dtype, scale=1.0, device="cuda")
+    q[0, 1, :64] = 0
+    varlen = torch.tensor([333, 150], dtype=torch.int32, device="cuda")
+    O1, t1, m1 = api.entmax_attn(q, k, v, alpha=alpha, causal=causal, varlen=varlen, with_mask=True)
+    O0, t0, m0 = api.entmax_attn(q, k, v, alpha=alpha, causal=causal, varlen=varlen, with_mask=False)
+    torch.cuda.synchronize()
+    assert m0 is None
+    assert torch.equal(O0, O1) and torch.equal(t0, t1)
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    for b, L in ((0, 333), (1, 150)):
+        for h in range(2):
+            o_ref, t_ref, _ = oracle.entmax_attention_rows(f64(q[b, h, :L]), np.arange(L), f64(k[b, h]), f64(v[b, h]),
+                                                           L, alpha, causal)
+            assert_close(f64(O0[b, h, :L]), o_ref, tol, f"no mask b{b} h{h}")
+            tau_close(f64(t0[b, h, :L]), t_ref, f"no mask b{b} h{h}")
+
+
 def test_varlen_workload_sampled():
     w = WORKLOADS["varlen_entmax"]
     q, k, v, lens = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype=w.dtype, scale=w.scale,
