@@ -52,7 +52,13 @@ KERNEL_SOURCES = {
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_buf": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_rows": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_prefill_merge": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
 }
+# the kernels of one dash_sparse_attn_prefill call
+ATTN_KERNELS = ["k_cm_plan", "k_cm_scatter", "k_prefill_cm", "k_prefill_merge", "k_sparse_prefill"]
 
 
 def log(msg):
@@ -89,6 +95,13 @@ def measured_traffic(kernel: str):
     if rec.get("source_sha") != source_sha(kernel):
         return None
     return float(rec["hbm_bytes_per_launch"])
+
+
+def attention_traffic():
+    """Measured HBM bytes of one dash_sparse_attn_prefill call (its kernels summed),
+    or None if any of them changed since the counters were taken."""
+    parts = [measured_traffic(k) for k in ATTN_KERNELS]
+    return None if any(p is None for p in parts) else float(sum(parts))
 
 
 def calibrate_copy(nbytes=1 << 30, reps=3):
@@ -324,6 +337,39 @@ def bench_entmax_rows(w, steps, warmup):
             "GBps": nbytes / (ms / 1e3) / 1e9}
 
 
+def sparsity_report(w, alphas=(1.333, 1.5, 2.0), scalings=(0.5, 1.0, 2.0, 4.0), depth_bins=8):
+    """Measured routing sparsity on the needle workload: for each (alpha,
+    scaling_factor), the attended chunks per row and their fraction of the row's
+    candidates (its complete past chunks plus its own), overall, per query head
+    (min / median / max) and per depth bin (query position in N / depth_bins)."""
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cuda")
+    del V
+    n_c = -(-w.N // C)
+    S = torch.empty(w.B, w.Hkv, n_c, w.d, dtype=torch.float32, device="cuda")
+    ws = None
+    pos = torch.arange(w.N, device="cuda")
+    cand = (pos // C + 1).to(torch.float64)  # causal: complete past chunks + own
+    rows = []
+    for alpha in alphas:
+        for sf in scalings:
+            p = api.Params(alpha=alpha, scaling_factor=sf, causal=True, estimate_diagonal=w.estimate_diagonal)
+            api.summarize(K, cls, S, n_tokens=w.N, chunk_begin=0, chunk_end=w.N // C, params=p)
+            _, bits, ws = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
+            act = popcount32(bits).sum(dim=-1).to(torch.float64)[0]  # [Hq, N]
+            frac = act / cand[None, :]
+            head = frac.mean(dim=1).cpu().numpy()
+            depth = frac.view(w.Hq, depth_bins, -1).mean(dim=(0, 2)).cpu().numpy()
+            rows.append({
+                "alpha": alpha, "scaling_factor": sf,
+                "active_chunks_per_row": float(act.mean()),
+                "active_frac": float(frac.mean()),
+                "active_frac_by_head": [float(head.min()), float(np.median(head)), float(head.max())],
+                "active_frac_by_depth": [float(x) for x in depth],
+            })
+            log(f"sparsity alpha={alpha} sf={sf}: {rows[-1]['active_chunks_per_row']:.2f} chunks/row")
+    return {"workload": w.name, "depth_bins": depth_bins, "rows": rows}
+
+
 # --------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(w, budget_s=20.0):
     """The float64 oracle on host cores, on a random sample of query rows of the
@@ -374,6 +420,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-entmax", action="store_true")
+    ap.add_argument("--sparsity", action="store_true",
+                    help="only the measured-sparsity sweep (alpha x scaling_factor) on the 32K needle workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -382,6 +430,9 @@ def main():
               "in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.sparsity:
+        print(json.dumps(sparsity_report(WORKLOADS["routed_prefill_32k"])), flush=True)
+        return
 
     if args.calibrate_copy:
         calibrate_copy()
@@ -391,14 +442,35 @@ def main():
     log(f"prefill done: {pre['wall_ms']:.3f} ms/step")
     ms_step = pre["ms_summarize"] + pre["ms_route"] + pre["ms_attention"]
     value = wp.N / (ms_step / 1e3)
-    # Dominant kernel: the routing, k_route_fast (timed as the whole dash_route
-    # call: a 5 us summary split, k_route_fast, and the general kernel for the
-    # tiles it leaves, 6 us when it leaves none). Its lower bounds: HBM for the
-    # algorithmic bytes below (the largest), MFMA for the scores (2 d flops per
-    # score), VALU for the candidate tests.
+    # Dominant work: the sparse attention call (two thirds of the step; its
+    # k_prefill_cm is the longest kernel), timed with HIP events around the whole
+    # dash_sparse_attn_prefill call (k_cm_plan, k_cm_scatter, k_prefill_cm,
+    # k_prefill_merge, k_sparse_prefill). Bound: MFMA, on the algorithmic flops
+    # (4 d per row and visible key of a routed chunk); its measured HBM traffic
+    # (the gathered query rows and the partial results written and read back) is
+    # reported beside it.
+    attn_ach = pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12
+    attn_traffic = attention_traffic()
+    roof = {
+        "kernel": "dash_sparse_attn_prefill (k_prefill_cm + k_prefill_merge + k_cm_scatter + k_cm_plan + k_sparse_prefill)",
+        "bound": "mfma",
+        "achieved": attn_ach,
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": attn_ach / PEAK_BF16_TFLOPS,
+        "traffic": attn_traffic,
+        "alg_flops_per_launch": pre["alg_flops"],
+        "ms_per_launch": pre["ms_attention"],
+        "executed_pair_frac": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "hbm_GBps_measured": attn_traffic / (pre["ms_attention"] / 1e3) / 1e9 if attn_traffic else None,
+    }
+    # The routing (dash_route: a 5 us summary split, k_route_fast, and the general
+    # kernel for the tiles it leaves, 6 us when it leaves none). Its lower bounds:
+    # HBM for the algorithmic bytes below (the largest), MFMA for the scores (2 d
+    # flops per score), VALU for the candidate tests.
     route_bytes = route_alg_bytes(wp, pre["pairs"])
     ach = route_bytes / (pre["ms_route"] / 1e3) / 1e9
-    roof = {
+    route_roof = {
         "kernel": "k_route_fast",
         "bound": "hbm",
         "achieved": ach,
@@ -440,7 +512,8 @@ def main():
             "attention_pair_tflops": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
             "attention_pair_frac": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
             "attention_alg_tflops": pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
-            "attention_traffic": measured_traffic("k_prefill_cm"),
+            "attention_traffic": attn_traffic,
+            "route_roofline": route_roof,
         },
         "roofline": roof,
     }
