@@ -21,6 +21,7 @@ linked from its README builds on.
 from .entmax import (
     entmax_threshold,
     entmax,
+    entmax_backward,
     entmax_threshold_bruteforce,
 )
 from .dash import (
@@ -37,6 +38,7 @@ from .entmax_attention import entmax_attention, entmax_attention_rows
 __all__ = [
     "entmax_threshold",
     "entmax",
+    "entmax_backward",
     "entmax_threshold_bruteforce",
     "DashParams",
     "chunk_summary",

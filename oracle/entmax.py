@@ -38,6 +38,7 @@ __all__ = [
     "entmax_threshold",
     "entmax_threshold_rows",
     "entmax",
+    "entmax_backward",
     "entmax_threshold_bruteforce",
 ]
 
@@ -169,6 +170,30 @@ def entmax(z, alpha: float) -> np.ndarray:
         return np.zeros_like(z)
     u = np.where(np.isfinite(z), (alpha - 1.0) * z, -np.inf)
     return _power(u - tau, 1.0 / (alpha - 1.0))
+
+
+def entmax_backward(y, dy, alpha: float) -> np.ndarray:
+    """Vector-Jacobian product of alpha-entmax at its output ``y`` (1-D) for the
+    cotangent ``dy``: the gradient with respect to the scores z.
+
+    The AdaSplash README ("Usage", AdaSplash with Block Masking) runs its kernels
+    forward and backward; the Jacobian itself is the published one (Peters,
+    Niculae & Martins 2019): differentiating sum_i (u_i - tau)^beta = 1 with
+    u = (alpha - 1) z gives, with g_i = y_i^(2 - alpha) on the support and 0 off
+    it,
+        d y / d z = diag(g) - g g^T / sum(g),
+    a symmetric matrix, so dz = g * dy - g * (g . dy) / sum(g). A row without a
+    support (no finite score) gets dz = 0.
+    """
+    y = np.asarray(y, dtype=np.float64).ravel()
+    dy = np.asarray(dy, dtype=np.float64).ravel()
+    if y.shape != dy.shape:
+        raise ValueError("y and dy must have the same length")
+    g = np.where(y > 0.0, _power(y, 2.0 - alpha), 0.0)
+    sg = float(np.sum(g))
+    if sg <= 0.0:
+        return np.zeros_like(y)
+    return g * dy - g * (float(np.dot(g, dy)) / sg)
 
 
 def entmax_threshold_bruteforce(z, alpha: float) -> float:

@@ -18,6 +18,7 @@ from scipy.optimize import minimize
 
 from oracle.entmax import (
     entmax,
+    entmax_backward,
     entmax_threshold,
     entmax_threshold_bruteforce,
     entmax_threshold_rows,
@@ -155,3 +156,44 @@ def test_alpha_controls_sparsity():
     z = rng.normal(size=200)
     nnz = [np.count_nonzero(entmax(z, a)) for a in (1.333, 1.5, 2.0)]
     assert nnz[0] > nnz[1] > nnz[2]
+
+
+@pytest.mark.parametrize("alpha", ALPHAS)
+def test_backward_matches_finite_differences(alpha):
+    """The closed-form vector-Jacobian product against central differences of the
+    exact forward (a different computation: the sort-based threshold), at points
+    whose support does not change within the step."""
+    rng = np.random.default_rng(17)
+    checked = 0
+    for _ in range(40):
+        z = rng.normal(size=9) * 1.5
+        y = entmax(z, alpha)
+        tau = entmax_threshold(z, alpha)
+        if np.min(np.abs((alpha - 1.0) * z - tau)) < 1e-3:
+            continue  # too close to a support change for differences
+        dy = rng.normal(size=9)
+        h = 1e-6
+        fd = np.array([(entmax(z + h * e, alpha) - entmax(z - h * e, alpha)) @ dy / (2 * h) for e in np.eye(9)])
+        np.testing.assert_allclose(entmax_backward(y, dy, alpha), fd, atol=2e-6)
+        checked += 1
+    assert checked >= 20
+
+
+def test_backward_softmax_limit_and_invariants():
+    rng = np.random.default_rng(19)
+    z = rng.normal(size=24)
+    dy = rng.normal(size=24)
+    # alpha -> 1: the softmax Jacobian diag(p) - p p^T
+    sm = np.exp(z - z.max())
+    sm /= sm.sum()
+    vjp_sm = sm * dy - sm * float(sm @ dy)
+    errs = [np.abs(entmax_backward(entmax(z, a), dy, a) - vjp_sm).max() for a in (1.1, 1.01, 1.001)]
+    assert errs[0] > errs[1] > errs[2] and errs[2] < 5e-3
+    for alpha in ALPHAS:
+        y = entmax(z, alpha)
+        dz = entmax_backward(y, dy, alpha)
+        assert abs(dz.sum()) < 1e-12  # shifting z leaves y unchanged
+        assert np.all(dz[y == 0] == 0)  # off the support nothing moves
+        assert np.allclose(entmax_backward(y, np.full(24, 0.7), alpha), 0.0, atol=1e-12)
+    assert np.all(entmax_backward(np.zeros(5), rng.normal(size=5), 1.5) == 0)
+
