@@ -31,6 +31,8 @@ __all__ = [
     "sparse_attn_decode",
     "entmax_attn",
     "entmax",
+    "entmax_backward",
+    "entmax_fn",
     "prefill",
     "decode_step",
 ]
@@ -201,6 +203,45 @@ def entmax(x, alpha=1.5, n_iter=10, return_tau=False, out=None):
     st = lib.entmax_rows(_p(x), _p(y), _dt(x), rows, n, float(alpha), int(n_iter), _p(tau), _stream(x.device))
     _lib.check(st, "entmax_rows")
     return (y, tau) if return_tau else y
+
+
+def entmax_backward(y, dy, alpha=1.5, out=None):
+    """Gradient of :func:`entmax` with respect to its scores, from its output ``y``
+    and the cotangent ``dy`` (same shape and dtype); ``out`` may be ``dy``."""
+    lib = _lib.load()
+    _need(y, "y")
+    _need(dy, "dy", y.dtype)
+    if dy.shape != y.shape or y.dim() < 1 or y.shape[-1] == 0:
+        raise ValueError("y and dy must have one shape with a non-empty last dimension")
+    n = y.shape[-1]
+    dx = torch.empty_like(y) if out is None else out
+    if out is not None:
+        _need(out, "out", y.dtype)
+        if out.shape != y.shape:
+            raise ValueError("out must have the shape of y")
+    st = lib.entmax_rows_backward(_p(y), _p(dy), _p(dx), _dt(y), y.numel() // n, n, float(alpha), _stream(y.device))
+    _lib.check(st, "entmax_rows_backward")
+    return dx
+
+
+class _EntmaxFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, alpha, n_iter):
+        y = entmax(x, alpha=alpha, n_iter=n_iter)
+        ctx.save_for_backward(y)
+        ctx.alpha = alpha
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        (y,) = ctx.saved_tensors
+        return entmax_backward(y, dy.contiguous().to(y.dtype), alpha=ctx.alpha), None, None
+
+
+def entmax_fn(x, alpha=1.5, n_iter=10):
+    """:func:`entmax` with a backward (torch autograd): the gradient runs in
+    ``entmax_rows_backward``."""
+    return _EntmaxFn.apply(x, alpha, n_iter)
 
 
 def prefill(Q, K, V, head_cls, params: Params = Params(), with_bits=True, workspace=None, S=None):

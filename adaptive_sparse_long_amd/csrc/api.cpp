@@ -297,4 +297,22 @@ dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, 
   return from_hip(launch_entmax_rows(a, dt == DASH_BF16, stream));
 }
 
+dash_status entmax_rows_backward(const void* Y, const void* dY, void* dX, dash_dtype dt, int rows,
+                                 int n, float alpha, hipStream_t stream) {
+  if (!Y || !dY || !dX) return DASH_ERR_INVALID_ARG;
+  if (rows <= 0 || n <= 0 || !finite_gt1(alpha)) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (n > kEntmaxRowsMax) return DASH_ERR_UNSUPPORTED;
+  EntmaxRowsArgs a{};
+  a.X = Y;
+  a.dY = dY;
+  a.Y = dX;
+  a.rows = rows;
+  a.n = n;
+  a.alpha = alpha;
+  a.beta = 1.f / (alpha - 1.f);
+  a.n_cu = device_cus();
+  return from_hip(launch_entmax_rows(a, dt == DASH_BF16, stream));
+}
+
 }  // extern "C"

@@ -176,7 +176,101 @@ __global__ __launch_bounds__(WAVES * kWave) void k_entmax_rows(EntmaxRowsArgs a)
   }
 }
 
+// Backward: dX = g * dY - g * (g . dY) / sum(g), g = Y^(2 - alpha) on the
+// support (Y > 0) and 0 off it: the vector-Jacobian product of the row's
+// entmax, from its output alone. One pass: the row's Y and dY in registers,
+// two row sums, dX written; the next row is loaded meanwhile.
+template <typename T, int VPL, int KIND, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void k_entmax_rows_bwd(EntmaxRowsArgs a) {
+  constexpr bool WG = WAVES == 16;
+  constexpr int STRIDE = WG ? WAVES * kWave : kWave;
+  __shared__ float s_red[2][2][WAVES];
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+  const int n = a.n;
+  const int t = WG ? (int)threadIdx.x : lane;
+  const long long step = WG ? (long long)gridDim.x : (long long)gridDim.x * WAVES;
+  long long row = WG ? (long long)blockIdx.x : (long long)blockIdx.x * WAVES + w;
+  float yn[VPL], dn[VPL];
+  auto load_row = [&](long long r) {
+    const T* y = static_cast<const T*>(a.X) + r * (long long)n;
+    const T* dy = static_cast<const T*>(a.dY) + r * (long long)n;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int e = j * STRIDE + t;
+      yn[j] = e < n ? load_elem(y + e) : 0.f;
+      dn[j] = e < n ? load_elem(dy + e) : 0.f;
+    }
+  };
+  if (row < a.rows) load_row(row);
+  int par = 0;
+  const float gexp = 2.f - a.alpha;
+  for (; row < a.rows; row += step) {  // uniform over the row's threads
+    T* dx = static_cast<T*>(a.Y) + row * (long long)n;
+    float g[VPL], dy[VPL];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const float y = yn[j];
+      if constexpr (KIND == 2) g[j] = y > 0.f ? __builtin_sqrtf(y) : 0.f;
+      else if constexpr (KIND == 1) g[j] = y > 0.f ? 1.f : 0.f;
+      else g[j] = y > 0.f ? fast_exp2(gexp * fast_log2(y)) : 0.f;
+      dy[j] = dn[j];
+      s0 += g[j];
+      s1 = fmaf(g[j], dy[j], s1);
+    }
+    if (row + step < a.rows) load_row(row + step);
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
+    if constexpr (WG) {
+      if (lane == 0) {
+        s_red[par][0][w] = s0;
+        s_red[par][1][w] = s1;
+      }
+      __syncthreads();  // also orders the reads of this parity two rows back
+      s0 = s1 = 0.f;
+#pragma unroll
+      for (int k = 0; k < WAVES; ++k) {
+        s0 += s_red[par][0][k];
+        s1 += s_red[par][1][k];
+      }
+      par ^= 1;
+    }
+    const float c = s0 > 0.f ? s1 / s0 : 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int e = j * STRIDE + t;
+      if (e < n) store_elem(dx + e, g[j] * (dy[j] - c));
+    }
+  }
+}
+
 namespace {
+
+template <typename T, int KIND>
+hipError_t entmax_rows_bwd_t(const EntmaxRowsArgs& a, hipStream_t stream) {
+  if (a.n <= 64 * 32) {
+    const dim3 grid((unsigned)std::min<long long>((a.rows + 3) / 4, (long long)a.n_cu * 8));
+    const int v = (a.n + 63) / 64;
+#define DASH_ER(V)                                                                               \
+  if (v <= V) {                                                                                  \
+    hipLaunchKernelGGL((k_entmax_rows_bwd<T, V, KIND, 4>), grid, dim3(4 * kWave), 0, stream, a); \
+    return hipGetLastError();                                                                    \
+  }
+    DASH_ER(1) DASH_ER(2) DASH_ER(4) DASH_ER(8) DASH_ER(16) DASH_ER(32)
+#undef DASH_ER
+  }
+  const dim3 grid((unsigned)std::min<long long>(a.rows, (long long)a.n_cu * 2));
+  const int v = (a.n + 1023) / 1024;
+#define DASH_ER(V)                                                                                 \
+  if (v <= V) {                                                                                    \
+    hipLaunchKernelGGL((k_entmax_rows_bwd<T, V, KIND, 16>), grid, dim3(16 * kWave), 0, stream, a); \
+    return hipGetLastError();                                                                      \
+  }
+  DASH_ER(4) DASH_ER(8) DASH_ER(16) DASH_ER(32)
+#undef DASH_ER
+  return hipErrorInvalidValue;
+}
 
 template <typename T, int KIND>
 hipError_t entmax_rows_t(const EntmaxRowsArgs& a, hipStream_t stream) {
@@ -212,7 +306,15 @@ hipError_t entmax_rows_kind(const EntmaxRowsArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+template <typename T>
+hipError_t entmax_rows_bwd_kind(const EntmaxRowsArgs& a, hipStream_t stream) {
+  if (a.alpha == 1.5f) return entmax_rows_bwd_t<T, 2>(a, stream);
+  if (a.alpha == 2.0f) return entmax_rows_bwd_t<T, 1>(a, stream);
+  return entmax_rows_bwd_t<T, 0>(a, stream);
+}
+
 hipError_t launch_entmax_rows(const EntmaxRowsArgs& a, bool bf16, hipStream_t stream) {
+  if (a.dY != nullptr) return bf16 ? entmax_rows_bwd_kind<uint16_t>(a, stream) : entmax_rows_bwd_kind<float>(a, stream);
   return bf16 ? entmax_rows_kind<uint16_t>(a, stream) : entmax_rows_kind<float>(a, stream);
 }
 

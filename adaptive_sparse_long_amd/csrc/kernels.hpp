@@ -263,8 +263,9 @@ struct EntmaxAttnArgs {
 };
 
 struct EntmaxRowsArgs {
-  const void* X;
-  void* Y;
+  const void* X;      // forward: scores; backward: the forward's output Y
+  const void* dY;     // backward only: the cotangent (nullptr: forward)
+  void* Y;            // forward: probabilities; backward: dX
   long long rows;
   int n;
   float alpha, beta;  // beta = 1 / (alpha - 1)

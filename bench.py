@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_buf": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_rows": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_rows_bwd": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_prefill_merge": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
@@ -333,8 +334,20 @@ def bench_entmax_rows(w, steps, warmup):
         t.stop(e)
     ms = t.mean_ms()
     nbytes = float(2 * x.numel() * x.element_size())
+    # backward: Y and dY read, dX written
+    dy = entmax_rows_inputs(w.B, w.N, w.seed + 100, dtype=w.dtype, device="cuda")
+    dx = torch.empty_like(x)
+    tb = Timer()
+    for _ in range(warmup):
+        api.entmax_backward(y, dy, alpha=w.alpha, out=dx)
+    for _ in range(steps):
+        e = tb.start()
+        api.entmax_backward(y, dy, alpha=w.alpha, out=dx)
+        tb.stop(e)
+    ms_b = tb.mean_ms()
     return {"rows": w.B, "n": w.N, "us": ms * 1e3, "bytes_per_launch": nbytes,
-            "GBps": nbytes / (ms / 1e3) / 1e9}
+            "GBps": nbytes / (ms / 1e3) / 1e9, "us_backward": ms_b * 1e3,
+            "GBps_backward": 1.5 * nbytes / (ms_b / 1e3) / 1e9}
 
 
 def sparsity_report(w, alphas=(1.333, 1.5, 2.0), scalings=(0.5, 1.0, 2.0, 4.0), depth_bins=8):
@@ -551,6 +564,7 @@ def main():
         small = bench_entmax_rows(WORKLOADS["entmax_rows_128x256"], args.steps, args.warmup)
         out["entmax_rows"] = {
             "workload": "entmax_rows_64k_1024", **big, "us_128x256": small["us"],
+            "us_backward_128x256": small["us_backward"],
             "roofline": {"kernel": "k_entmax_rows", "bound": "hbm", "achieved": big["GBps"], "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": big["GBps"] / PEAK_HBM_GBS,
                          "traffic": measured_traffic("k_entmax_rows")}}

@@ -217,6 +217,23 @@ dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype 
 dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, float alpha,
                         int n_iter, float* tau, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * entmax_rows_backward -- the gradient of entmax_rows with respect to its
+ * scores (the AdaSplash README runs its entmax kernels forward and backward,
+ * "Usage"; the Jacobian is the published one of alpha-entmax): for each row,
+ *   g  = Y^(2 - alpha) where Y > 0, 0 elsewhere,
+ *   dX = g * dY - g * (sum g * dY) / (sum g)      (dX = 0 for a row with Y = 0).
+ *   Y   [rows, n] the forward's output, dtype dt (DASH_F32 or DASH_BF16)
+ *   dY  [rows, n] the cotangent, dtype dt
+ *   dX  [rows, n] dtype dt; may be dY or Y (each entry is read before it is
+ *       written, by the same thread)
+ * All device memory owned by the caller. Errors: NULL pointers, rows or n <= 0,
+ * alpha not a finite value > 1 -> DASH_ERR_INVALID_ARG; n > 32768 ->
+ * DASH_ERR_UNSUPPORTED; a launch failure -> DASH_ERR_HIP.
+ * --------------------------------------------------------------------------- */
+dash_status entmax_rows_backward(const void* Y, const void* dY, void* dX, dash_dtype dt, int rows,
+                                 int n, float alpha, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* dash_status_string(dash_status s);
 

@@ -26,7 +26,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
-        "entmax_rows",
+        "entmax_rows", "entmax_rows_backward",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -135,3 +135,11 @@ def test_entmax_rows_validation(lib):
     assert r(FAKE, FAKE, 0, 4, 16, 1.5, 0, NULL, NULL) == INVALID
     assert r(FAKE, FAKE, 7, 4, 16, 1.5, 10, NULL, NULL) == INVALID
     assert r(FAKE, FAKE, 0, 4, 32769, 1.5, 10, NULL, NULL) == UNSUPPORTED
+    b = lib.entmax_rows_backward
+    assert b(NULL, FAKE, FAKE, 0, 4, 16, 1.5, NULL) == INVALID
+    assert b(FAKE, NULL, FAKE, 0, 4, 16, 1.5, NULL) == INVALID
+    assert b(FAKE, FAKE, NULL, 0, 4, 16, 1.5, NULL) == INVALID
+    assert b(FAKE, FAKE, FAKE, 0, 0, 16, 1.5, NULL) == INVALID
+    assert b(FAKE, FAKE, FAKE, 0, 4, 16, 0.5, NULL) == INVALID
+    assert b(FAKE, FAKE, FAKE, 3, 4, 16, 1.5, NULL) == INVALID
+    assert b(FAKE, FAKE, FAKE, 0, 4, 40000, 1.5, NULL) == UNSUPPORTED

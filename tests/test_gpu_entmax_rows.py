@@ -3,7 +3,9 @@ against the float64 CPU oracle's exact threshold: float32 outputs within 1e-4,
 bfloat16 within 2e-2, tau within 1e-4, supports equal except for entries within
 1e-4 of tau; rows held by one wavefront and by one workgroup, ragged widths,
 the three tau solver specialisations, and the degenerate rows (-inf entries, a
-row with no finite entry, a single entry, a constant row, in place).
+row with no finite entry, a single entry, a constant row, in place). Its
+backward (entmax_rows_backward) against the oracle's vector-Jacobian product,
+directly and through torch autograd.
 """
 
 import numpy as np
@@ -11,7 +13,7 @@ import pytest
 import torch
 
 from adaptive_sparse_long_amd import api
-from oracle.entmax import entmax_threshold_rows
+from oracle.entmax import entmax, entmax_backward, entmax_threshold_rows
 
 from _helpers import TOL_BF16, TOL_F32, assert_close, assert_sets_match, f64, tau_close
 
@@ -84,3 +86,60 @@ def test_entmax_rows_in_place_and_batched_shape():
     torch.cuda.synchronize()
     assert y.data_ptr() == x.data_ptr()
     assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("n", [1, 37, 256, 2048, 2049, 5000])
+@pytest.mark.parametrize("alpha", [1.5, 2.0, 1.333])
+def test_entmax_rows_backward_f32(n, alpha):
+    x = _x(7, n, 200 + n, scale=2.0)
+    x[3, : n // 2] = -float("inf")  # a masked part (zeros of y)
+    y = api.entmax(x, alpha=alpha)
+    dy = _x(7, n, 300 + n)
+    dx = api.entmax_backward(y, dy, alpha=alpha)
+    torch.cuda.synchronize()
+    y_, dy_ = f64(y), f64(dy)
+    ref = np.stack([entmax_backward(y_[r], dy_[r], alpha) for r in range(7)])
+    assert_close(f64(dx), ref, TOL_F32, f"backward n={n} alpha={alpha}")
+    assert np.all(np.abs(f64(dx).sum(1)) < 1e-4)
+
+
+@pytest.mark.parametrize("n,alpha", [(300, 1.5), (3000, 2.0), (700, 3.0)])
+def test_entmax_rows_backward_bf16(n, alpha):
+    """bfloat16 gradients: 2e-2 absolute plus the bf16 rounding of the output
+    itself (2^-9 of its magnitude, taken twice): dX is not bounded (for alpha > 2
+    the factor y^(2-alpha) grows without limit at the edge of the support), so a
+    bound on the absolute error alone cannot hold for a bf16 result."""
+    x = _x(5, n, 400 + n, scale=1.5, dtype=torch.bfloat16)
+    y = api.entmax(x, alpha=alpha)
+    dy = _x(5, n, 500 + n, dtype=torch.bfloat16)
+    dx = api.entmax_backward(y, dy, alpha=alpha)
+    torch.cuda.synchronize()
+    y_, dy_ = f64(y), f64(dy)
+    ref = np.stack([entmax_backward(y_[r], dy_[r], alpha) for r in range(5)])
+    err = np.abs(f64(dx) - ref)
+    bound = TOL_BF16 + 2.0 ** -8 * np.abs(ref)
+    assert np.all(np.isfinite(f64(dx)))
+    assert np.all(err <= bound), f"bf16 backward n={n} alpha={alpha}: worst excess {float(np.max(err - bound)):.3e}"
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_entmax_autograd_matches_oracle(alpha):
+    """torch autograd through entmax_fn: the gradient of sum(w * entmax(x)) with
+    respect to x, against the oracle's exact forward and its Jacobian."""
+    x = _x(6, 500, 71, scale=2.0).requires_grad_(True)
+    w = _x(6, 500, 72)
+    (api.entmax_fn(x, alpha=alpha) * w).sum().backward()
+    x_, w_ = f64(x.detach()), f64(w)
+    ref = np.stack([entmax_backward(entmax(x_[r], alpha), w_[r], alpha) for r in range(6)])
+    assert_close(f64(x.grad), ref, TOL_F32, f"autograd alpha={alpha}")
+
+
+def test_entmax_rows_backward_in_place():
+    x = _x(4, 129, 81, scale=2.0)
+    y = api.entmax(x, alpha=1.5)
+    dy = _x(4, 129, 82)
+    ref = api.entmax_backward(y, dy, alpha=1.5)
+    out = api.entmax_backward(y, dy, alpha=1.5, out=dy)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == dy.data_ptr() and torch.equal(out, ref)
+
