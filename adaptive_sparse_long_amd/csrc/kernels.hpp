@@ -14,7 +14,7 @@ namespace dash {
 constexpr int kTileRows = 128;
 constexpr int kChunk = 64;
 // Routed chunks handled by one decode split (one workgroup, four wavefronts).
-constexpr int kDecodeSplit = 16;
+constexpr int kDecodeSplit = 24;
 // Partial-result pool of the chunk-major kernel: kCmSlots slots per query row
 // on average. Every routed past chunk of a row is attended by the chunk-major
 // kernel into a slot of its own; the row's own chunk by the row-major kernel,

@@ -5,7 +5,7 @@
 //
 // The g query heads of one KV head share one routed-chunk list (the union of
 // their routes), so each listed 16 KB K chunk and 16 KB V chunk is read from HBM
-// once for all g heads. Split-KV: a workgroup of four wavefronts takes 16 list
+// once for all g heads. Split-KV: a workgroup of four wavefronts takes 24 list
 // entries; each wavefront streams its chunks with no block barrier:
 //   * scores for the g heads: v_mfma_f32_16x16x32_bf16 with the query rows in A
 //     (head hh at row hh * 16/g, so each 16-lane row group of the output holds
