@@ -16,14 +16,14 @@ constexpr int kChunk = 64;
 // Routed chunks handled by one decode split (one workgroup, four wavefronts).
 constexpr int kDecodeSplit = 24;
 // Partial-result pool of the chunk-major kernel: kCmSlots slots per query row
-// on average. Every routed past chunk of a row is attended by the chunk-major
-// kernel into a slot of its own; the row's own chunk by the row-major kernel,
-// which merges the partials. A tile whose rows find the pool exhausted has all
-// its chunks attended row-major instead.
+// on average. Every attended chunk of a row (its routed past chunks and its
+// own chunk) is attended by the chunk-major kernel into a slot of its own, and
+// the merge kernel combines the row's partials. A tile whose rows find the pool
+// exhausted has all its chunks attended by the row-major kernel instead.
 constexpr int kCmSlots = 16;
 // Chunk-major work item: up to kCmBlocks blocks of 32 (row, chunk) pairs of one
 // (b, kv head, chunk).
-constexpr int kCmBlocks = 16;
+constexpr int kCmBlocks = 12;
 // The partial-result pool is split into kPools equal parts, each with its own
 // allocation counter (workgroup id modulo kPools picks the part).
 constexpr int kPools = 8;
