@@ -202,7 +202,7 @@ def check_decode(q, Kc, Vc, cls, seqlens, p: api.Params, pairs=None, where=""):
 
 
 @pytest.mark.parametrize("est", [True, False])
-@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
 def test_decode_small(est, g):
     Hkv = 2
     q, Kc, Vc, cls, _ = decode_inputs(3, Hkv * g, Hkv, 1100, 128, seed=31 + g, device="cuda", Lmax=1160)
