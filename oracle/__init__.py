@@ -33,7 +33,7 @@ from .dash import (
     dash_prefill,
     dash_decode,
 )
-from .entmax_attention import entmax_attention, entmax_attention_rows
+from .entmax_attention import entmax_attention, entmax_attention_rows, entmax_attention_backward
 
 __all__ = [
     "entmax_threshold",
@@ -49,4 +49,5 @@ __all__ = [
     "dash_decode",
     "entmax_attention",
     "entmax_attention_rows",
+    "entmax_attention_backward",
 ]

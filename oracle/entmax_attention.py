@@ -20,15 +20,21 @@ Readings (the page prints no formula):
 * block mask bit (I, J), 64 x 64 tiles: 1 iff some allowed (i, j) in the tile has
   P_ij > 0. Layout [B, H, nT, ceil(nT / 32)] uint32 with bit J % 32 of word
   J // 32, nT = ceil(N / 64).
+
+The backward (the page runs these kernels forward and backward, "Usage", and
+lists block-sparse forward and backward passes among its "Key Features") is the
+chain rule through those definitions, nothing more: dV = P^T dO, dP = dO V^T,
+dS_i = the alpha-entmax vector-Jacobian product of row i at (P_i, dP_i)
+(``oracle.entmax.entmax_backward``), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .entmax import entmax_threshold_rows
+from .entmax import entmax_backward, entmax_threshold_rows
 
-__all__ = ["entmax_attention", "entmax_attention_rows", "TILE"]
+__all__ = ["entmax_attention", "entmax_attention_rows", "entmax_attention_backward", "TILE"]
 
 TILE = 64
 
@@ -88,3 +94,27 @@ def entmax_attention(Q, K, V, alpha: float, causal: bool, varlen=None, row_block
                     for J in np.unique(np.nonzero(cols)[0] // TILE):
                         mask[b, h, I, J // 32] |= np.uint32(1) << np.uint32(J % 32)
     return O, tau, mask
+
+
+def entmax_attention_backward(Q, K, V, dO, alpha: float, causal: bool, varlen=None):
+    """Gradients of sum(O * dO) with respect to Q, K and V, float64.
+
+    Q/K/V/dO [B, H, N, d] -> (dQ, dK, dV), each [B, H, N, d]. Rows and keys at or
+    past varlen[b] get zero gradients (they take no part in the forward).
+    """
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, H, N, d = Q.shape
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for b in range(B):
+        L = N if varlen is None else int(varlen[b])
+        if L <= 0:
+            continue
+        pos = np.arange(L)
+        for h in range(H):
+            _, _, P = entmax_attention_rows(Q[b, h, :L], pos, K[b, h], V[b, h], L, alpha, causal)
+            dP = dO[b, h, :L] @ V[b, h, :L].T
+            dS = np.stack([entmax_backward(P[i], dP[i], alpha) for i in range(L)])
+            dV[b, h, :L] = P.T @ dO[b, h, :L]
+            dQ[b, h, :L] = dS @ K[b, h, :L] / np.sqrt(d)
+            dK[b, h, :L] = dS.T @ Q[b, h, :L] / np.sqrt(d)
+    return dQ, dK, dV

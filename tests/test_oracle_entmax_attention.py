@@ -105,3 +105,86 @@ def test_rows_sum_to_one_support():
         np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
         U = (alpha - 1) * (Q @ K.T) / np.sqrt(d)
         assert np.array_equal(P > 0, U > tau[:, None])
+
+
+# ---- backward (gradients of sum(O * dO)) ----
+
+from oracle.entmax_attention import entmax_attention_backward  # noqa: E402
+
+
+def _fd_grads(Q, K, V, dO, alpha, causal, varlen, eps=1e-6):
+    """Central differences of sum(O * dO) through the forward oracle."""
+    def loss(q, k, v):
+        return float(np.sum(entmax_attention(q, k, v, alpha, causal, varlen=varlen)[0] * dO))
+
+    out = []
+    for which in range(3):
+        args = [Q.copy(), K.copy(), V.copy()]
+        g = np.zeros_like(args[which])
+        for idx in np.ndindex(*g.shape):
+            a_p = [x.copy() for x in args]
+            a_m = [x.copy() for x in args]
+            a_p[which][idx] += eps
+            a_m[which][idx] -= eps
+            g[idx] = (loss(*a_p) - loss(*a_m)) / (2 * eps)
+        out.append(g)
+    return out
+
+
+@pytest.mark.parametrize(
+    "alpha,causal,varlen",
+    [(1.5, True, None), (2.0, False, None), (1.25, True, None), (1.5, False, [5, 9]), (2.0, True, [9, 3])],
+)
+def test_backward_matches_finite_differences(alpha, causal, varlen):
+    B = 1 if varlen is None else len(varlen)
+    N, d = 9, 4
+    Q, K, V = _rand((B, 1, N, d), 30, 1.5), _rand((B, 1, N, d), 31, 1.5), _rand((B, 1, N, d), 32)
+    dO = _rand((B, 1, N, d), 33)
+    lens = None if varlen is None else np.array(varlen)
+    dQ, dK, dV = entmax_attention_backward(Q, K, V, dO, alpha, causal, varlen=lens)
+    fQ, fK, fV = _fd_grads(Q, K, V, dO, alpha, causal, lens)
+    np.testing.assert_allclose(dQ, fQ, atol=1e-6)
+    np.testing.assert_allclose(dK, fK, atol=1e-6)
+    np.testing.assert_allclose(dV, fV, atol=1e-6)
+    # sparse weights leave some gradient entries exactly zero only off the support;
+    # the check above must not pass trivially
+    assert np.abs(dQ).max() > 1e-3 and np.abs(dK).max() > 1e-3
+
+
+@pytest.mark.parametrize("alpha,causal", [(1.5, True), (2.0, False), (1.333, True)])
+def test_backward_invariants(alpha, causal):
+    """Shift invariance of entmax makes every row of dS sum to 0, so the key
+    gradients of one (b, h) sum to 0; each row's weights sum to 1, so the value
+    gradients sum to the sum of dO over the valid rows. Causal row 0 has a single
+    key, hence a zero Jacobian and dQ_0 = 0."""
+    B, H, N, d = 2, 2, 70, 8
+    Q, K, V = _rand((B, H, N, d), 40, 2.0), _rand((B, H, N, d), 41, 2.0), _rand((B, H, N, d), 42)
+    dO = _rand((B, H, N, d), 43)
+    lens = np.array([70, 37])
+    dQ, dK, dV = entmax_attention_backward(Q, K, V, dO, alpha, causal, varlen=lens)
+    for b in range(B):
+        L = lens[b]
+        np.testing.assert_allclose(dK[b].sum(axis=1), 0.0, atol=1e-10)
+        np.testing.assert_allclose(dV[b].sum(axis=1), dO[b, :, :L].sum(axis=1), atol=1e-10)
+        assert np.all(dQ[b, :, L:] == 0) and np.all(dK[b, :, L:] == 0) and np.all(dV[b, :, L:] == 0)
+        if causal:
+            assert np.all(dQ[b, :, 0] == 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_softmax_limit(causal):
+    """alpha -> 1: the gradients approach those of softmax attention (torch autograd
+    through SDPA, float64 on the CPU), with the error shrinking with alpha - 1."""
+    N, d = 16, 8
+    Q, K, V = _rand((1, 1, N, d), 50), _rand((1, 1, N, d), 51), _rand((1, 1, N, d), 52)
+    dO = _rand((1, 1, N, d), 53)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (Q, K, V))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal)
+    out.backward(torch.from_numpy(dO))
+    ref = [t.grad.numpy() for t in (tq, tk, tv)]
+    errs = []
+    for a in (1.1, 1.01, 1.001):
+        g = entmax_attention_backward(Q, K, V, dO, a, causal)
+        errs.append(max(np.abs(x - r).max() for x, r in zip(g, ref)))
+    assert errs[0] > errs[1] > errs[2]
+    assert errs[2] < 1e-2 and errs[1] > 5 * errs[2]
