@@ -53,6 +53,7 @@ _SIGNATURES = {
     "dash_sparse_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, DashParams, _P, _P, _SZ, _P]),
     "dash_sparse_attn_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _I, DashParams, _P, _P, _SZ, _P]),
     "entmax_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P]),
+    "entmax_attn_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _P, _P, _P, _P, _P]),
     "entmax_rows": (_I, [_P, _P, _I, _I, _I, _F, _I, _P, _P]),
     "entmax_rows_backward": (_I, [_P, _P, _P, _I, _I, _I, _F, _P]),
 }

@@ -182,6 +182,56 @@ def entmax_attn(Q, K, V, alpha=1.5, n_iter=10, causal=True, varlen=None, with_ma
     return out, tau, mask
 
 
+def entmax_attn_backward(Q, K, V, dO, tau, mask=None, alpha=1.5, causal=True, varlen=None):
+    """Gradients (dQ, dK, dV) of :func:`entmax_attn` for the cotangent ``dO``, from
+    the forward's inputs, its ``tau`` and (optionally) its block ``mask``."""
+    lib = _lib.load()
+    _need(Q, "Q", dim=4)
+    for name, t in (("K", K), ("V", V), ("dO", dO)):
+        _need(t, name, Q.dtype, 4)
+        if t.shape != Q.shape:
+            raise ValueError(f"{name} must have the shape of Q")
+    B, H, N, d = Q.shape
+    _need(tau, "tau", torch.float32, 3)
+    if tuple(tau.shape) != (B, H, N):
+        raise ValueError("tau must be [B, H, N]")
+    if mask is not None:
+        nT = -(-N // 64)
+        _need(mask, "mask", torch.int32, 4)
+        if tuple(mask.shape) != (B, H, nT, -(-nT // 32)):
+            raise ValueError("mask must be [B, H, ceil(N/64), ceil(ceil(N/64)/32)]")
+    if varlen is not None:
+        _need(varlen, "varlen", torch.int32, 1)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    coef = torch.empty(B, H, N, dtype=torch.float32, device=Q.device)
+    st = lib.entmax_attn_backward(_p(Q), _p(K), _p(V), _p(dO), _p(tau), _p(mask), _dt(Q), B, H, N, d,
+                                  _p(varlen), float(alpha), int(bool(causal)), _p(dQ), _p(dK), _p(dV),
+                                  _p(coef), _stream(Q.device))
+    _lib.check(st, "entmax_attn_backward")
+    return dQ, dK, dV
+
+
+class _EntmaxAttnFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, alpha, n_iter, causal, varlen):
+        out, tau, mask = entmax_attn(Q, K, V, alpha=alpha, n_iter=n_iter, causal=causal, varlen=varlen)
+        ctx.save_for_backward(Q, K, V, tau, mask, varlen)
+        ctx.alpha, ctx.causal = alpha, causal
+        return out
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, tau, mask, varlen = ctx.saved_tensors
+        dQ, dK, dV = entmax_attn_backward(Q, K, V, dO.contiguous().to(Q.dtype), tau, mask, ctx.alpha, ctx.causal, varlen)
+        return dQ, dK, dV, None, None, None, None
+
+
+def entmax_attn_fn(Q, K, V, alpha=1.5, n_iter=10, causal=True, varlen=None):
+    """:func:`entmax_attn` with a backward (torch autograd): the gradients run in
+    ``entmax_attn_backward``, skipping the tiles the forward's block mask clears."""
+    return _EntmaxAttnFn.apply(Q, K, V, alpha, n_iter, causal, varlen)
+
+
 def entmax(x, alpha=1.5, n_iter=10, return_tau=False, out=None):
     """Row-wise alpha-entmax over the last dimension (AdaSplash "Usage": Triton Entmax).
 

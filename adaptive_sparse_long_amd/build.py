@@ -29,6 +29,7 @@ SOURCES = [
     "sparse_prefill.hip",
     "sparse_decode.hip",
     "entmax_attn.hip",
+    "entmax_attn_bwd.hip",
     "entmax_rows.hip",
 ]
 

@@ -278,6 +278,35 @@ dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype 
   return from_hip(launch_entmax_attn(a, dt == DASH_BF16, stream));
 }
 
+dash_status entmax_attn_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                 const float* tau, const uint32_t* block_mask, dash_dtype dt,
+                                 int B, int H, int Nmax, int d, const int* varlen, float alpha,
+                                 int causal, void* dQ, void* dK, void* dV, float* coef,
+                                 hipStream_t stream) {
+  if (!Q || !K || !V || !dO || !tau || !dQ || !dK || !dV || !coef) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || Nmax <= 0 || d <= 0) return DASH_ERR_INVALID_ARG;
+  if (!finite_gt1(alpha) || (causal != 0 && causal != 1)) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DASH_ERR_UNSUPPORTED;
+  const int nT = (Nmax + 63) / 64;
+  if (nT > kEntmaxMaxTiles) return DASH_ERR_UNSUPPORTED;
+  EntmaxBwdArgs a{};
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO;
+  a.tau = tau;
+  a.mask = block_mask;
+  a.mask_words = (nT + 31) / 32;
+  a.B = B; a.H = H; a.N = Nmax; a.d = d;
+  a.varlen = varlen;
+  a.alpha = alpha;
+  a.beta = 1.f / (alpha - 1.f);
+  a.scale = (alpha - 1.f) / sqrtf((float)d);
+  a.inv_sqrt_d = 1.f / sqrtf((float)d);
+  a.causal = causal;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.coef = coef;
+  return from_hip(launch_entmax_attn_bwd(a, dt == DASH_BF16, stream));
+}
+
 dash_status entmax_rows(const void* X, void* Y, dash_dtype dt, int rows, int n, float alpha,
                         int n_iter, float* tau, hipStream_t stream) {
   if (!X || !Y) return DASH_ERR_INVALID_ARG;

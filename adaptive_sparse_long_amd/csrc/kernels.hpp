@@ -262,6 +262,25 @@ struct EntmaxAttnArgs {
   int only_marked;  // general kernel: only row blocks a row of which has tau = NaN
 };
 
+struct EntmaxBwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* tau;
+  const uint32_t* mask;  // or nullptr
+  int mask_words;
+  int B, H, N, d;
+  const int* varlen;
+  float alpha, beta, scale;  // scale = (alpha - 1) / sqrt(d)
+  float inv_sqrt_d;
+  int causal;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* coef;  // [B, H, N] row terms sum(g dP) / sum(g)
+};
+
 struct EntmaxRowsArgs {
   const void* X;      // forward: scores; backward: the forward's output Y
   const void* dY;     // backward only: the cotangent (nullptr: forward)
@@ -281,6 +300,7 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream); 
 hipError_t launch_sparse_decode(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_entmax_rows(const EntmaxRowsArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_entmax_attn_bwd(const EntmaxBwdArgs& a, bool bf16, hipStream_t stream);
 
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers

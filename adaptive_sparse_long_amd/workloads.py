@@ -106,6 +106,12 @@ def dense_entmax_inputs(B, H, N, d, seed, dtype="bf16", scale=1.0, varlen_range=
     return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype), lens
 
 
+def cotangent(shape, seed, dtype="bf16", device="cpu"):
+    """A cotangent (upstream gradient) ~ N(0, 1) of the given shape."""
+    g = _gen(seed, device)
+    return _cast(torch.randn(*shape, generator=g, device=device), dtype)
+
+
 def entmax_rows_inputs(rows, n, seed, dtype="f32", scale=1.0, device="cpu"):
     """Scores ~ scale * N(0, 1) in [rows, n]."""
     g = _gen(seed, device)

@@ -197,6 +197,37 @@ dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype 
                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * entmax_attn_backward -- gradients of entmax_attn (the AdaSplash README runs
+ * its attention kernels forward and backward, "Usage", and lists block-sparse
+ * forward and backward passes under "Key Features"; the entmax Jacobian is the
+ * published one). For a cotangent dO of O, with t_ij = (alpha-1) s_ij - tau_i,
+ * P_ij = max(t_ij, 0)^(1/(alpha-1)) and g_ij = P_ij^(2 - alpha) on the support:
+ *   dP_ij = <dO_i, v_j>,   coef_i = sum_j g_ij dP_ij / sum_j g_ij,
+ *   dS_ij = g_ij (dP_ij - coef_i),
+ *   dQ_i = sum_j dS_ij k_j / sqrt(d),  dK_j = sum_i dS_ij q_i / sqrt(d),
+ *   dV_j = sum_i P_ij dO_i.
+ * Rows and keys at or past len_b get zero gradients.
+ *   Q/K/V/dO       [B, H, Nmax, d] dtype dt, the forward's inputs and the cotangent
+ *   tau            [B, H, Nmax] float32, the forward's tau output
+ *   block_mask     the forward's block mask (tiles with bit 0 are skipped), or
+ *                  NULL (every allowed tile is visited; same result)
+ *   varlen, alpha, causal: as given to the forward
+ *   dQ/dK/dV       [B, H, Nmax, d] dtype dt, written; must not overlap any input
+ *   coef           [B, H, Nmax] float32 scratch written with coef_i (row terms
+ *                  shared by the two kernels); caller-owned
+ * All device memory owned by the caller; work enqueued on stream, no host sync,
+ * nothing allocated. Errors: NULL pointers (other than varlen, block_mask), any
+ * size <= 0, alpha not a finite value > 1, causal not 0/1 ->
+ * DASH_ERR_INVALID_ARG; d not 64 or 128, Nmax > 65536 -> DASH_ERR_UNSUPPORTED;
+ * a launch failure -> DASH_ERR_HIP.
+ * --------------------------------------------------------------------------- */
+dash_status entmax_attn_backward(const void* Q, const void* K, const void* V, const void* dO,
+                                 const float* tau, const uint32_t* block_mask, dash_dtype dt,
+                                 int B, int H, int Nmax, int d, const int* varlen, float alpha,
+                                 int causal, void* dQ, void* dK, void* dV, float* coef,
+                                 hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * entmax_rows -- row-wise alpha-entmax (AdaSplash README, "Usage": "Triton
  * Entmax (Optimized Entmax Activation)", the activation over the last
  * dimension with alpha and n_iter). For each row r < rows of X:

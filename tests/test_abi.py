@@ -26,7 +26,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
-        "entmax_rows", "entmax_rows_backward",
+        "entmax_rows", "entmax_rows_backward", "entmax_attn_backward",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -143,3 +143,20 @@ def test_entmax_rows_validation(lib):
     assert b(FAKE, FAKE, FAKE, 0, 4, 16, 0.5, NULL) == INVALID
     assert b(FAKE, FAKE, FAKE, 3, 4, 16, 1.5, NULL) == INVALID
     assert b(FAKE, FAKE, FAKE, 0, 4, 40000, 1.5, NULL) == UNSUPPORTED
+
+
+def test_entmax_attn_backward_validation(lib):
+    e = lib.entmax_attn_backward
+    F5 = [FAKE] * 5
+    # Q K V dO tau mask dt B H N d varlen alpha causal dQ dK dV coef stream
+    assert e(NULL, *F5[1:], NULL, 1, 1, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5[:4], NULL, NULL, 1, 1, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, NULL, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 64, NULL, 1.5, 1, NULL, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 0, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 64, NULL, 1.0, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 64, NULL, float("nan"), 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 64, NULL, 1.5, 3, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 5, 1, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
+    assert e(*F5, NULL, 1, 1, 1, 128, 96, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == UNSUPPORTED
+    assert e(*F5, NULL, 1, 1, 1, 70000, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == UNSUPPORTED
