@@ -25,8 +25,8 @@
 //       blocks it builds S = Q K^T and dP = dO V^T (a lane owns one key), forms
 //       P and dS from tau and c, and accumulates dV^T += dO^T P and
 //       dK^T += Q^T dS with Q and dO staged transposed in LDS.
-// bfloat16 operands run on v_mfma_f32_32x32x16_bf16 with the weights split
-// into bf16 high and low parts (float32 accuracy); float32 operands on
+// bfloat16 operands run on v_mfma_f32_32x32x16_bf16 with the weights P and dS
+// split into bf16 high and low parts (float32 accuracy); float32 operands on
 // v_mfma_f32_32x32x2_f32, transposed operands read straight from memory
 // (32 consecutive floats per half-wavefront).
 #include "kernels.hpp"
@@ -37,13 +37,6 @@ namespace dash {
 namespace {
 constexpr int kRowPad = 4;
 constexpr int kTRow = 32 + kRowPad;  // LDS row of a transposed 32-line block (elements)
-
-__device__ __forceinline__ uint32_t perm_lo16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t perm_hi16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);
-}
 
 // g = max(t, 0)^((2 - alpha) beta), the entmax Jacobian's weight.
 template <int KIND>
@@ -91,37 +84,11 @@ __device__ __forceinline__ f32x16 dot32(const Frags<BF, D>& A, const Frags<BF, D
   return c;
 }
 
-// Stage rows [r0, r0 + 32) of a row-major [*, D] bf16 matrix transposed into
-// xt[D][kTRow] (rows >= n_ok as zeros). Lane combos: 4 rows x 8 dims each.
-template <int D>
-__device__ __forceinline__ void stage_t(uint16_t* xt, const uint16_t* X, int r0, int n_ok) {
-  const int lane = lane_id();
-  constexpr int NCOMBO = 8 * (D / 8);
-#pragma unroll
-  for (int pass = 0; pass < NCOMBO / 64; ++pass) {
-    const int combo = pass * 64 + lane;
-    const int kg = combo & 7, dg = combo >> 3;
-    u32x4 vr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 4 * kg + r;
-      vr[r] = row < n_ok ? ldg16(X + (size_t)row * D + 8 * dg) : u32x4{0, 0, 0, 0};
-    }
-    uint16_t* dst = xt + (8 * dg) * kTRow + 4 * kg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u32x2 lo2 = {perm_lo16(vr[0][e], vr[1][e]), perm_lo16(vr[2][e], vr[3][e])};
-      u32x2 hi2 = {perm_hi16(vr[0][e], vr[1][e]), perm_hi16(vr[2][e], vr[3][e])};
-      *reinterpret_cast<u32x2*>(dst + (2 * e) * kTRow) = lo2;
-      *reinterpret_cast<u32x2*>(dst + (2 * e + 1) * kTRow) = hi2;
-    }
-  }
-}
-
 // acc[db] (C[m = dim 32 db + .][n = lane's line]) += X^T W^T over the block's 32
 // lines, where W^T is this lane's column w (acc layout: line 8 (r/4) + 4 (l/32)
 // + r%4 of register r) and X the block's rows: bf16 from the transposed LDS
-// copy xt, float32 straight from memory (rows >= n_ok contribute zeros).
+// copy xt with W split into bf16 high and low parts (float32 accuracy),
+// float32 straight from memory (rows >= n_ok contribute zeros).
 template <bool BF, int D>
 __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w, const uint16_t* xt,
                                          const float* X, int r0, int n_ok) {
@@ -135,9 +102,8 @@ __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float a0 = w[8 * ks + 2 * e], a1 = w[8 * ks + 2 * e + 1];
-        const float r0f = round_bf16(a0), r1f = round_bf16(a1);
-        h[e] = pack_bf16x2(r0f, r1f);
-        l[e] = pack_bf16x2(a0 - r0f, a1 - r1f);
+        h[e] = pack_bf16x2(a0, a1);
+        l[e] = pack_bf16x2(a0 - bf16lo(h[e]), a1 - bf16hi(h[e]));
       }
       wh[ks] = as_bf16x8(h);
       wl[ks] = as_bf16x8(l);
@@ -194,11 +160,77 @@ __device__ __forceinline__ void store_line(void* out, size_t line, const f32x16 
   }
 }
 
-__device__ __forceinline__ bool tile_on(const EntmaxBwdArgs& a, size_t bh, int nT, int I, int J) {
-  if (!a.mask) return true;
-  return (a.mask[(bh * nT + I) * a.mask_words + (J >> 5)] >> (J & 31)) & 1u;
-}
 }  // namespace
+
+// Register-set index of a prefetching pass, as a type so that every access to
+// the two sets is static (a run-time index would put them in scratch memory).
+template <int S>
+struct Slot {
+  static constexpr int v = S;
+};
+
+// Visit the 32-line blocks b0 <= blk < n of a pass whose 64 x 64 tile is on
+// (bit (blk / 2) of the mask row `bits`, or every block when bits is null),
+// in order. bfloat16 passes load the next block's operands while the current
+// one is computed (load(blk, Slot) fills one of two register sets; a block at n
+// loads zeros without touching memory); float32 passes (twice the registers)
+// load each block when it is reached.
+template <bool PF, typename Load, typename Body>
+__device__ __forceinline__ void visit_blocks(int b0, int n, const uint32_t* bits, Load load, Body body) {
+  auto next = [&](int blk) {
+    if (!bits) return min(blk, n);
+    while (blk < n) {
+      const int t = blk >> 1;
+      const uint32_t w = bits[t >> 5] >> (t & 31);
+      if (w & 1u) return blk;
+      blk = w ? 2 * (t + (int)__builtin_ctz(w)) : 2 * ((t | 31) + 1);
+    }
+    return n;
+  };
+  int blk = next(b0);
+  if constexpr (PF) {
+    load(blk, Slot<0>{});
+    while (blk < n) {
+      int nb = next(blk + 1);
+      load(nb, Slot<1>{});
+      body(blk, Slot<0>{});
+      blk = nb;
+      if (blk >= n) break;
+      nb = next(blk + 1);
+      load(nb, Slot<0>{});
+      body(blk, Slot<1>{});
+      blk = nb;
+    }
+  } else {
+    while (blk < n) {
+      load(blk, Slot<0>{});
+      body(blk, Slot<0>{});
+      blk = next(blk + 1);
+    }
+  }
+}
+
+// Stage a 32-row bf16 block held as fragments (lane: row R = lane % 32, dims
+// 16 s + 8 (lane / 32) + e) transposed into xt[D][kTRow]. Neighbouring lanes
+// (rows R, R ^ 1) swap each 32-bit pair of dims through DPP, so every store
+// writes two rows of one dim: the even lane dim 2e' of rows (R, R + 1), the odd
+// lane dim 2e' + 1 of rows (R - 1, R).
+template <int D>
+__device__ __forceinline__ void stage_t_regs(uint16_t* xt, const Frags<true, D>& fr) {
+  const int lane = lane_id();
+  const int odd = lane & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  uint16_t* base = xt + (8 * (lane >> 5) + odd) * kTRow + (lane & 30);
+#pragma unroll
+  for (int s = 0; s < Frags<true, D>::NS; ++s) {
+    const u32x4 v = __builtin_bit_cast(u32x4, fr.b[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[e], kDppXor1, 0xF, 0xF, false);
+      *reinterpret_cast<uint32_t*>(base + (16 * s + 2 * e) * kTRow) = __builtin_amdgcn_perm(w, v[e], sel);
+    }
+  }
+}
 
 template <typename T, int D, int KIND>
 __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
@@ -227,41 +259,53 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
   int last_key = L - 1;
   if (causal) last_key = min(last_key, r0 + 31);
   const int n_kb = r0 < L ? last_key / 32 + 1 : 0;
-  const int I = r0 >> 6;
+  const uint32_t* bits = a.mask ? a.mask + (bh * nT + (r0 >> 6)) * a.mask_words : nullptr;
+  // blocks below kb_full have every (row, key) allowed: no per-entry tests there
+  const int kb_full = (r0 + 31 < L) ? (causal ? r0 / 32 : L / 32) : 0;
 
   Frags<BF, D> fq, fdo;
   load_frags<BF, D>(fq, Qp, qi, row_ok);
   load_frags<BF, D>(fdo, dOp, qi, row_ok);
 
-  // t = u - tau of the lane's row against keys key0 + 8 (r/4) + 4 hi32 + r%4
-  auto block_t = [&](int key0, f32x16& t, f32x16& dp) {
-    Frags<BF, D> fk, fv;
-    const int kr = key0 + (lane & 31);
-    load_frags<BF, D>(fk, Kp, kr, kr < L);
-    load_frags<BF, D>(fv, Vp, kr, kr < L);
-    const f32x16 s = dot32<BF, D>(fk, fq);
-    dp = dot32<BF, D>(fv, fdo);
+  Frags<BF, D> fk[BF ? 2 : 1], fv[BF ? 2 : 1];
+  auto load = [&](int kb, auto sl) {
+    constexpr int slot = decltype(sl)::v;
+    const int kr = kb * 32 + (lane & 31);
+    const bool ok = kb < n_kb && kr < L;
+    load_frags<BF, D>(fk[slot], Kp, kr, ok);
+    load_frags<BF, D>(fv[slot], Vp, kr, ok);
+  };
+  // t = u - tau of the lane's row against keys kb*32 + 8 (r/4) + 4 hi32 + r%4
+  // (-1 where the key is not allowed)
+  auto block_t = [&](int kb, auto sl, f32x16& t, f32x16& dp) {
+    constexpr int slot = decltype(sl)::v;
+    const f32x16 s = dot32<BF, D>(fk[slot], fq);
+    dp = dot32<BF, D>(fv[slot], fdo);
+    if (kb < kb_full) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = key0 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
-      const bool ok = row_ok && key < L && (!causal || key <= qi);
-      t[r] = ok ? fmaf(s[r], a.scale, -tau) : -1.f;
+      for (int r = 0; r < 16; ++r) t[r] = fmaf(s[r], a.scale, -tau);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+        const bool ok = row_ok && key < L && (!causal || key <= qi);
+        t[r] = ok ? fmaf(s[r], a.scale, -tau) : -1.f;
+      }
     }
   };
 
   // ---- pass 1: sum g and sum g dP per row
   float sg = 0.f, sgd = 0.f;
-  for (int kb = 0; kb < n_kb; ++kb) {
-    if (!tile_on(a, bh, nT, I, kb >> 1)) continue;
+  visit_blocks<BF>(0, n_kb, bits, load, [&](int kb, auto sl) {
     f32x16 t, dp;
-    block_t(kb * 32, t, dp);
+    block_t(kb, sl, t, dp);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float g = jac_weight<KIND>(t[r], a.alpha, a.beta);
       sg += g;
       sgd = fmaf(g, dp[r], sgd);
     }
-  }
+  });
   sg = sum_xor32(sg);
   sgd = sum_xor32(sgd);
   const float c = sg > 0.f ? sgd / sg : 0.f;
@@ -274,10 +318,10 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   uint16_t* kt = sKt[BF ? w : 0];
-  for (int kb = 0; kb < n_kb; ++kb) {
-    if (!tile_on(a, bh, nT, I, kb >> 1)) continue;
+  visit_blocks<BF>(0, n_kb, bits, load, [&](int kb, auto sl) {
+    constexpr int slot = decltype(sl)::v;
     f32x16 t, dp;
-    block_t(kb * 32, t, dp);
+    block_t(kb, sl, t, dp);
     bool nz = false;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -285,22 +329,27 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
       t[r] = g * (dp[r] - c);
       nz = nz || g > 0.f;
     }
-    if (!wave_any(nz)) continue;
-    if constexpr (BF) {
-      stage_t<D>(kt, reinterpret_cast<const uint16_t*>(Kp), kb * 32, L);
-      wave_lds_fence();
+    if (wave_any(nz)) {
+      if constexpr (BF) {
+        stage_t_regs<D>(kt, fk[slot]);
+        wave_lds_fence();
+      }
+      acc_xt_w<BF, D>(acc, t, kt, reinterpret_cast<const float*>(Kp), kb * 32, L);
+      if constexpr (BF) wave_lds_fence();
     }
-    acc_xt_w<BF, D>(acc, t, kt, reinterpret_cast<const float*>(Kp), kb * 32, L);
-    if constexpr (BF) wave_lds_fence();
-  }
+  });
   if (qi < N) store_line<BF, D>(a.dQ, bh * N + qi, acc, a.inv_sqrt_d);
 }
 
 template <typename T, int D, int KIND>
-__global__ __launch_bounds__(256) void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(T) == 2 ? 2 : 1)))
+void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
   constexpr bool BF = sizeof(T) == 2;
+  constexpr int kColWords = kEntmaxMaxTiles / 32;
   __shared__ __attribute__((aligned(16))) uint16_t sQt[BF ? 4 : 1][BF ? D * kTRow : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sOt[BF ? 4 : 1][BF ? D * kTRow : 8];
+  __shared__ uint32_t sCol[4][kColWords];
+  __shared__ __attribute__((aligned(16))) float sTC[4][2][32];
 
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
@@ -321,6 +370,24 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
   const T* dOp = static_cast<const T*>(a.dO) + bh * (size_t)N * D;
   const int J = k0 >> 6;
 
+  // the column of the block mask for this wavefront's key tile, as bits over
+  // the row tiles (read 64 row tiles per step)
+  const uint32_t* bits = nullptr;
+  if (a.mask) {
+    uint32_t* col = sCol[w];
+    for (int I0 = 0; I0 < nT; I0 += 64) {
+      const int I = I0 + lane;
+      const bool on = I < nT && ((a.mask[(bh * nT + I) * a.mask_words + (J >> 5)] >> (J & 31)) & 1u);
+      const uint64_t bal = __ballot(on);
+      if (lane == 0) {
+        col[I0 >> 5] = (uint32_t)bal;
+        if ((I0 >> 5) + 1 < kColWords) col[(I0 >> 5) + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+    wave_lds_fence();
+    bits = col;
+  }
+
   // the lane's K and V rows: held for the whole loop in bf16; float32 rows
   // (twice the registers) are re-read per block from the cache instead
   Frags<BF, D> fk, fv;
@@ -339,47 +406,78 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
     }
   uint16_t* qt = sQt[BF ? w : 0];
   uint16_t* ot = sOt[BF ? w : 0];
+  float* stau = sTC[w][0];
+  float* sc = sTC[w][1];
   const int qb0 = (causal ? k0 : 0) / 32;
   const int n_qb = k0 < L ? (L + 31) / 32 : 0;
-  for (int qb = qb0; qb < n_qb; ++qb) {
-    if (!tile_on(a, bh, nT, qb >> 1, J)) continue;
+  // blocks from qb_full on have every (row, key) allowed, up to the last full one
+  const bool keys_full = k0 + 31 < L;
+  const int qb_full = causal ? k0 / 32 + 1 : 0;
+  const int qb_last_full = L / 32;  // exclusive
+
+  Frags<BF, D> fq[BF ? 2 : 1], fdo[BF ? 2 : 1];
+  float tau_m[BF ? 2 : 1], c_m[BF ? 2 : 1];
+  // rows of query block qb; tau and c of row qb*32 + lane % 32
+  auto load = [&](int qb, auto sl) {
+    constexpr int slot = decltype(sl)::v;
+    const int qm = qb * 32 + (lane & 31);
+    const bool ok = qb < n_qb && qm < L;
+    load_frags<BF, D>(fq[slot], Qp, qm, ok);
+    load_frags<BF, D>(fdo[slot], dOp, qm, ok);
+    tau_m[slot] = ok ? a.tau[bh * N + qm] : 0.f;
+    c_m[slot] = ok ? a.coef[bh * N + qm] : 0.f;
+  };
+  visit_blocks<BF>(qb0, n_qb, bits, load, [&](int qb, auto sl) {
+    constexpr int slot = decltype(sl)::v;
     const int q0 = qb * 32;
-    // tau and c of the block's rows, one per lane < 32, read by the others through shuffles
-    const int qm = q0 + (lane & 31);
-    const float tau_m = qm < L ? a.tau[bh * N + qm] : 0.f;
-    const float c_m = qm < L ? a.coef[bh * N + qm] : 0.f;
-    Frags<BF, D> fq, fdo;
     if constexpr (!BF) load_frags<BF, D>(fk, Kp, kj, key_ok);
-    load_frags<BF, D>(fq, Qp, qm, qm < L);
-    const f32x16 s = dot32<BF, D>(fq, fk);  // S[query][key]
+    const f32x16 s = dot32<BF, D>(fq[slot], fk);  // S[query][key]
     if constexpr (!BF) load_frags<BF, D>(fv, Vp, kj, key_ok);
-    load_frags<BF, D>(fdo, dOp, qm, qm < L);
-    const f32x16 dp = dot32<BF, D>(fdo, fv);  // dP[query][key]
+    const f32x16 dp = dot32<BF, D>(fdo[slot], fv);  // dP[query][key]
+    // tau and c of the block's rows through the wavefront's LDS slot: register r
+    // of this lane holds row 8 (r/4) + 4 hi32 + r%4
+    if (lane < 32) {
+      stau[lane] = tau_m[slot];
+      sc[lane] = c_m[slot];
+    }
+    wave_lds_fence();
+    f32x4 tq[4], cq[4];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      tq[g4] = *reinterpret_cast<const f32x4*>(stau + 8 * g4 + 4 * hi32);
+      cq[g4] = *reinterpret_cast<const f32x4*>(sc + 8 * g4 + 4 * hi32);
+    }
     f32x16 p, ds;
     bool nz = false;
+    const bool full = keys_full && qb >= qb_full && qb < qb_last_full;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = 8 * (r >> 2) + 4 * hi32 + (r & 3);
-      const float tq = __shfl(tau_m, m);
-      const float cq = __shfl(c_m, m);
-      const int q = q0 + m;
-      const bool ok = key_ok && q < L && (!causal || kj <= q);
-      const float t = ok ? fmaf(s[r], a.scale, -tq) : -1.f;
+      const float tr = tq[r >> 2][r & 3];
+      float t;
+      if (full) {
+        t = fmaf(s[r], a.scale, -tr);
+      } else {
+        const int q = q0 + 8 * (r >> 2) + 4 * hi32 + (r & 3);
+        const bool ok = key_ok && q < L && (!causal || kj <= q);
+        t = ok ? fmaf(s[r], a.scale, -tr) : -1.f;
+      }
       p[r] = prior_of<KIND>(t, a.beta);
       const float g = jac_weight<KIND>(t, a.alpha, a.beta);
-      ds[r] = g * (dp[r] - cq);
+      ds[r] = g * (dp[r] - cq[r >> 2][r & 3]);
       nz = nz || g > 0.f;
     }
-    if (!wave_any(nz)) continue;
-    if constexpr (BF) {
-      stage_t<D>(qt, reinterpret_cast<const uint16_t*>(Qp), q0, L);
-      stage_t<D>(ot, reinterpret_cast<const uint16_t*>(dOp), q0, L);
-      wave_lds_fence();
+    if (wave_any(nz)) {
+      if constexpr (BF) {
+        stage_t_regs<D>(qt, fq[slot]);
+        stage_t_regs<D>(ot, fdo[slot]);
+        wave_lds_fence();
+      }
+      acc_xt_w<BF, D>(dv, p, ot, reinterpret_cast<const float*>(dOp), q0, L);
+      acc_xt_w<BF, D>(dk, ds, qt, reinterpret_cast<const float*>(Qp), q0, L);
     }
-    acc_xt_w<BF, D>(dv, p, ot, reinterpret_cast<const float*>(dOp), q0, L);
-    acc_xt_w<BF, D>(dk, ds, qt, reinterpret_cast<const float*>(Qp), q0, L);
-    if constexpr (BF) wave_lds_fence();
-  }
+    // the next block overwrites the LDS slots only after every lane has read them
+    wave_lds_fence();
+  });
   if (kj < N) {
     store_line<BF, D>(a.dK, bh * N + kj, dk, a.inv_sqrt_d);
     store_line<BF, D>(a.dV, bh * N + kj, dv, 1.f);

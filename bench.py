@@ -35,6 +35,7 @@ from adaptive_sparse_long_amd import api  # noqa: E402
 from adaptive_sparse_long_amd.workloads import (  # noqa: E402
     WORKLOADS,
     decode_inputs,
+    cotangent,
     dense_entmax_inputs,
     entmax_rows_inputs,
     routed_prefill_inputs,
@@ -311,12 +312,29 @@ def bench_entmax(w, steps, warmup):
     on = ((mask[..., c // 32] >> (c % 32)) & 1).bool()
     tiles_on = float(on.sum())
     tiles_all = float(np.sum(np.ceil(L / 64) ** 2) * w.Hq)
+    # backward (dQ, dK, dV for a random cotangent), skipping the mask's empty tiles
+    dO = cotangent(q.shape, w.seed + 500, dtype=w.dtype, device=dev)
+    tb = Timer()
+    for _ in range(warmup):
+        api.entmax_attn_backward(q, k, v, dO, tau, mask, alpha=w.alpha, causal=w.causal, varlen=lens)
+    for _ in range(steps):
+        e = tb.start()
+        api.entmax_attn_backward(q, k, v, dO, tau, mask, alpha=w.alpha, causal=w.causal, varlen=lens)
+        tb.stop(e)
+    ms_b = tb.mean_ms()
+    # algorithmic backward work: five products (S, dP, dV, dK, dQ) of 2 d flops per
+    # allowed (row, key) entry of the tiles the mask keeps
+    rows_in = torch.clamp(lens.to(dev).long()[:, None] - 64 * c[None, :], 0, 64).double()  # [B, nT]
+    ent = (on.double() * rows_in[:, None, :, None] * rows_in[:, None, None, :]).sum()
+    bwd_flops = float(ent) * 5 * 2 * w.d
     return {
         "ms": ms,
         "tokens_per_s": float(L.sum()) / (ms / 1e3),
         "qk_flops": qk_flops,
         "tflops_qk_pass": qk_flops / (ms / 1e3) / 1e12,
         "nonnull_tile_frac": tiles_on / tiles_all,
+        "backward": {"ms": ms_b, "alg_flops": bwd_flops, "tflops": bwd_flops / (ms_b / 1e3) / 1e12,
+                     "frac": bwd_flops / (ms_b / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
     }
 
 
