@@ -341,6 +341,8 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
   if (qi < N) store_line<BF, D>(a.dQ, bh * N + qi, acc, a.inv_sqrt_d);
 }
 
+// bf16 at head_dim 64: registers capped for two waves per SIMD (a few spill at
+// alpha != 2), which hides more of the MFMA and load latency than one wave does
 template <typename T, int D, int KIND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && sizeof(T) == 2 ? 2 : 1)))
 void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
