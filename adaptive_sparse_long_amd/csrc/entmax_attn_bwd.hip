@@ -16,11 +16,12 @@
 // is 0 contributes nothing and is skipped.
 //
 // Two kernels, both wavefront-per-32-lines, four wavefronts per workgroup:
-//   k_entmax_bwd_dq   (row pass): a wavefront owns 32 query rows. Pass 1 over
+//   k_entmax_bwd_dq   (row pass): a wavefront owns 32 query rows. One pass over
 //       the key blocks builds S^T = K Q^T and dP^T = V dO^T by MFMA (a lane owns
-//       one row) and sums g and g dP per row, giving c (stored for the second
-//       kernel). Pass 2 recomputes both products, forms dS and accumulates
-//       dQ^T += K^T dS^T, K staged transposed in the wavefront's LDS slot.
+//       one row), sums g and g dP per row and accumulates A^T += K^T (g dP)^T and
+//       G^T += K^T g^T (K staged transposed in the wavefront's LDS slot); then
+//       c = sum g dP / sum g (stored for the second kernel) and
+//       dQ = (A - c G) / sqrt(d).
 //   k_entmax_bwd_dkdv (column pass): a wavefront owns 32 keys. Over the query
 //       blocks it builds S = Q K^T and dP = dO V^T (a lane owns one key), forms
 //       P and dS from tau and c, and accumulates dV^T += dO^T P and
@@ -87,9 +88,10 @@ __device__ __forceinline__ f32x16 dot32(const Frags<BF, D>& A, const Frags<BF, D
 // acc[db] (C[m = dim 32 db + .][n = lane's line]) += X^T W^T over the block's 32
 // lines, where W^T is this lane's column w (acc layout: line 8 (r/4) + 4 (l/32)
 // + r%4 of register r) and X the block's rows: bf16 from the transposed LDS
-// copy xt with W split into bf16 high and low parts (float32 accuracy),
-// float32 straight from memory (rows >= n_ok contribute zeros).
-template <bool BF, int D>
+// copy xt with W split into bf16 high and low parts (float32 accuracy; SPLIT
+// false for weights that bf16 holds exactly), float32 straight from memory
+// (rows >= n_ok contribute zeros).
+template <bool BF, int D, bool SPLIT = true>
 __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w, const uint16_t* xt,
                                          const float* X, int r0, int n_ok) {
   const int lane = lane_id();
@@ -103,7 +105,7 @@ __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w,
       for (int e = 0; e < 4; ++e) {
         const float a0 = w[8 * ks + 2 * e], a1 = w[8 * ks + 2 * e + 1];
         h[e] = pack_bf16x2(a0, a1);
-        l[e] = pack_bf16x2(a0 - bf16lo(h[e]), a1 - bf16hi(h[e]));
+        if constexpr (SPLIT) l[e] = pack_bf16x2(a0 - bf16lo(h[e]), a1 - bf16hi(h[e]));
       }
       wh[ks] = as_bf16x8(h);
       wl[ks] = as_bf16x8(l);
@@ -117,7 +119,7 @@ __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w,
         u32x2 hi = *reinterpret_cast<const u32x2*>(xrow + 16 * ks + 8);
         const bf16x8 xa = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         acc[db] = mfma32x32x16(xa, wh[ks], acc[db]);
-        acc[db] = mfma32x32x16(xa, wl[ks], acc[db]);
+        if constexpr (SPLIT) acc[db] = mfma32x32x16(xa, wl[ks], acc[db]);
       }
     }
   } else {
@@ -294,29 +296,18 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
     }
   };
 
-  // ---- pass 1: sum g and sum g dP per row
-  float sg = 0.f, sgd = 0.f;
-  visit_blocks<BF>(0, n_kb, bits, load, [&](int kb, auto sl) {
-    f32x16 t, dp;
-    block_t(kb, sl, t, dp);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float g = jac_weight<KIND>(t[r], a.alpha, a.beta);
-      sg += g;
-      sgd = fmaf(g, dp[r], sgd);
-    }
-  });
-  sg = sum_xor32(sg);
-  sgd = sum_xor32(sgd);
-  const float c = sg > 0.f ? sgd / sg : 0.f;
-  if (lane < 32 && qi < N) a.coef[bh * N + qi] = row_ok ? c : 0.f;
-
-  // ---- pass 2: dS = g (dP - c); dQ^T += K^T dS^T
-  f32x16 acc[D / 32];
+  // ---- one pass: per row sum g and sum g dP, and with K^T as the common
+  // operand A^T += K^T (g dP)^T and G^T += K^T g^T; then c = sum g dP / sum g and
+  // dQ = (A - c G) / sqrt(d) = sum_j g (dP - c) k_j / sqrt(d)
+  f32x16 accA[D / 32], accG[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      accA[db][r] = 0.f;
+      accG[db][r] = 0.f;
+    }
+  float sg = 0.f, sgd = 0.f;
   uint16_t* kt = sKt[BF ? w : 0];
   visit_blocks<BF>(0, n_kb, bits, load, [&](int kb, auto sl) {
     constexpr int slot = decltype(sl)::v;
@@ -326,7 +317,11 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float g = jac_weight<KIND>(t[r], a.alpha, a.beta);
-      t[r] = g * (dp[r] - c);
+      const float gd = g * dp[r];
+      sg += g;
+      sgd += gd;
+      t[r] = g;
+      dp[r] = gd;
       nz = nz || g > 0.f;
     }
     if (wave_any(nz)) {
@@ -334,10 +329,20 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
         stage_t_regs<D>(kt, fk[slot]);
         wave_lds_fence();
       }
-      acc_xt_w<BF, D>(acc, t, kt, reinterpret_cast<const float*>(Kp), kb * 32, L);
+      acc_xt_w<BF, D>(accA, dp, kt, reinterpret_cast<const float*>(Kp), kb * 32, L);
+      acc_xt_w<BF, D, KIND != 1>(accG, t, kt, reinterpret_cast<const float*>(Kp), kb * 32, L);
       if constexpr (BF) wave_lds_fence();
     }
   });
+  sg = sum_xor32(sg);
+  sgd = sum_xor32(sgd);
+  const float c = sg > 0.f ? sgd / sg : 0.f;
+  if (lane < 32 && qi < N) a.coef[bh * N + qi] = row_ok ? c : 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) accA[db][r] = fmaf(-c, accG[db][r], accA[db][r]);
+  f32x16 (&acc)[D / 32] = accA;
   if (qi < N) store_line<BF, D>(a.dQ, bh * N + qi, acc, a.inv_sqrt_d);
 }
 
