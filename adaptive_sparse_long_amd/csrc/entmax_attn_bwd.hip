@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256) void k_entmax_bwd_dq(EntmaxBwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sKt[BF ? 4 : 1][BF ? D * kTRow : 8];
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  // wave-uniform (a scalar for the compiler, so block-level tests are scalar branches)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hi32 = lane >> 5;
   const int b = blockIdx.z, h = blockIdx.y;
   const int N = a.N;
@@ -359,7 +360,8 @@ void k_entmax_bwd_dkdv(EntmaxBwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sTC[4][2][32];
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  // wave-uniform (a scalar for the compiler, so block-level tests are scalar branches)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int hi32 = lane >> 5;
   const int b = blockIdx.z, h = blockIdx.y;
   const int N = a.N;
