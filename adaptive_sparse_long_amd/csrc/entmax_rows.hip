@@ -49,7 +49,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_entmax_rows(EntmaxRowsArgs a)
   __shared__ float s_cand[WG ? 1 : WAVES][WG ? 1 : NCAND];
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int n = a.n;
   const int t = WG ? (int)threadIdx.x : lane;
   const float am1 = a.alpha - 1.f;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_entmax_rows_bwd(EntmaxRowsArg
   constexpr int STRIDE = WG ? WAVES * kWave : kWave;
   __shared__ float s_red[2][2][WAVES];
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int n = a.n;
   const int t = WG ? (int)threadIdx.x : lane;
   const long long step = WG ? (long long)gridDim.x : (long long)gridDim.x * WAVES;

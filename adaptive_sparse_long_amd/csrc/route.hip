@@ -91,7 +91,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   __shared__ long long s_tbase;    // the tile's first pool slot, -1: none
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int q = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   if (q >= *a.fb_count) return;
   const int tile = a.fb_tiles[q].x;
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   __shared__ int2 s_seg[4][kRoutePrefillMaxSlots / 32];  // per wavefront: (first, count | block << 16)
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int tid = threadIdx.x;
   if (tid == 0) s_cnt = 0;  // ordered before any use by the barriers of the first pass
   const int hi32 = lane >> 5;
@@ -1360,7 +1360,7 @@ template <int G>
 __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
   constexpr int D = 128;
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int grp_id = blockIdx.y;
   const int b = grp_id / a.Hkv;
   const int hk = grp_id % a.Hkv;
@@ -1423,7 +1423,7 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   __shared__ float s_qk[G][64];
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int grp_id = blockIdx.x;
   const int b = grp_id / a.Hkv;
   const int hk = grp_id % a.Hkv;

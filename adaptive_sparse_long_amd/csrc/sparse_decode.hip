@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
   __shared__ float sO[4][G][D];
 
   const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int split = blockIdx.x;
   const int grp_id = blockIdx.y;
   const int b = grp_id / a.Hkv;

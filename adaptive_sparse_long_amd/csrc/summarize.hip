@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
   constexpr int RPI = kWave / LPR;    // rows per load instruction
   static_assert(LPR == 16, "summary kernel is laid out for head_dim 128");
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int c = chunk_begin + blockIdx.x * (blockDim.x / kWave) + wave;
   const int h = blockIdx.y;
   const int b = blockIdx.z;

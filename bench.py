@@ -58,6 +58,8 @@ KERNEL_SOURCES = {
     "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_entmax_bwd_dq": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_bwd_dkdv": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
 # the kernels of one dash_sparse_attn_prefill call
 ATTN_KERNELS = ["k_cm_plan", "k_cm_scatter", "k_prefill_cm", "k_prefill_merge", "k_sparse_prefill"]
@@ -97,6 +99,10 @@ def measured_traffic(kernel: str):
     if rec.get("source_sha") != source_sha(kernel):
         return None
     return float(rec["hbm_bytes_per_launch"])
+
+
+def _sum_or_none(parts):
+    return None if any(p is None for p in parts) else float(sum(parts))
 
 
 def attention_traffic():
@@ -334,7 +340,9 @@ def bench_entmax(w, steps, warmup):
         "tflops_qk_pass": qk_flops / (ms / 1e3) / 1e12,
         "nonnull_tile_frac": tiles_on / tiles_all,
         "backward": {"ms": ms_b, "alg_flops": bwd_flops, "tflops": bwd_flops / (ms_b / 1e3) / 1e12,
-                     "frac": bwd_flops / (ms_b / 1e3) / 1e12 / PEAK_BF16_TFLOPS},
+                     "frac": bwd_flops / (ms_b / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "traffic": _sum_or_none([measured_traffic("k_entmax_bwd_dq"),
+                                              measured_traffic("k_entmax_bwd_dkdv")])},
     }
 
 
