@@ -27,6 +27,7 @@ from .entmax import (
 from .dash import (
     DashParams,
     chunk_summary,
+    chunk_summary_backward,
     chunk_summaries,
     route_row,
     dash_rows,
@@ -42,6 +43,7 @@ __all__ = [
     "entmax_threshold_bruteforce",
     "DashParams",
     "chunk_summary",
+    "chunk_summary_backward",
     "chunk_summaries",
     "route_row",
     "dash_rows",

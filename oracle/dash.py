@@ -84,6 +84,28 @@ def chunk_summary(keys, cls) -> np.ndarray:
     return a @ keys
 
 
+def chunk_summary_backward(keys, cls, ds):
+    """Gradients of <chunk_summary(keys, cls), ds> with respect to the keys [n, d]
+    and head_cls [d]: the chain rule through s = sum_j a_j k_j and
+    a = softmax(e), e_j = <k_j, cls> / sqrt(d) (the pages differentiate the whole
+    hierarchy, "How it works"; the steps are the summary's own definition):
+        de_j = a_j (<k_j, ds> - <s, ds>),
+        dk_j = a_j ds + de_j cls / sqrt(d),   dcls = sum_j de_j k_j / sqrt(d).
+    """
+    keys = _f64(keys)
+    cls = _f64(cls)
+    ds = _f64(ds)
+    d = keys.shape[-1]
+    e = keys @ cls / np.sqrt(d)
+    a = np.exp(e - np.max(e))
+    a /= np.sum(a)
+    s = a @ keys
+    de = a * (keys @ ds - s @ ds)
+    dk = a[:, None] * ds[None, :] + de[:, None] * cls[None, :] / np.sqrt(d)
+    dcls = de @ keys / np.sqrt(d)
+    return dk, dcls
+
+
 def chunk_summaries(keys, cls, chunk_size: int, n_tokens: int) -> np.ndarray:
     """Summaries [ceil(n_tokens / C), d] of one KV head; the last may be partial."""
     keys = _f64(keys)

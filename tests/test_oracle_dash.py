@@ -197,3 +197,55 @@ def test_route_prior_is_entmax_of_scores():
     z.append(2.0 * q[0] @ chunk_summary(K[(N - 1) // C * C : N], cls) / np.sqrt(d))
     np.testing.assert_allclose(prior[0], entmax(np.array(z), 1.5), atol=1e-12)
     assert prior[0].sum() == pytest.approx(1.0, abs=1e-12)
+
+
+# ---- summary backward (gradients of <s, ds> with respect to the keys and head_cls)
+
+from oracle.dash import chunk_summary_backward  # noqa: E402
+
+
+@pytest.mark.parametrize("n,d,scale", [(7, 4, 1.0), (12, 6, 3.0), (1, 5, 1.0)])
+def test_summary_backward_matches_finite_differences(n, d, scale):
+    rng = np.random.default_rng(60 + n)
+    k, cls, ds = rng.normal(size=(n, d)), rng.normal(size=d) * scale, rng.normal(size=d)
+    dk, dcls = chunk_summary_backward(k, cls, ds)
+    eps = 1e-6
+    fk = np.zeros_like(k)
+    for idx in np.ndindex(*k.shape):
+        kp, km = k.copy(), k.copy()
+        kp[idx] += eps
+        km[idx] -= eps
+        fk[idx] = (chunk_summary(kp, cls) - chunk_summary(km, cls)) @ ds / (2 * eps)
+    fc = np.zeros_like(cls)
+    for i in range(d):
+        cp, cm = cls.copy(), cls.copy()
+        cp[i] += eps
+        cm[i] -= eps
+        fc[i] = (chunk_summary(k, cp) - chunk_summary(k, cm)) @ ds / (2 * eps)
+    np.testing.assert_allclose(dk, fk, atol=1e-7)
+    np.testing.assert_allclose(dcls, fc, atol=1e-7)
+
+
+def test_summary_backward_zero_cls_is_covariance():
+    """head_cls = 0 gives mean pooling: dk_j = ds / n, and dcls is the (biased)
+    covariance of the keys applied to ds, over sqrt(d)."""
+    rng = np.random.default_rng(70)
+    n, d = 9, 5
+    k, ds = rng.normal(size=(n, d)), rng.normal(size=d)
+    dk, dcls = chunk_summary_backward(k, np.zeros(d), ds)
+    np.testing.assert_allclose(dk, np.tile(ds / n, (n, 1)), atol=1e-14)
+    kc = k - k.mean(axis=0)
+    np.testing.assert_allclose(dcls, (kc.T @ kc / n) @ ds / np.sqrt(d), atol=1e-13)
+
+
+def test_summary_backward_identical_keys():
+    """Identical keys: the weights cannot move the summary, so dcls = 0 and each
+    key takes its weight's share of ds."""
+    rng = np.random.default_rng(71)
+    d = 6
+    v = rng.normal(size=d)
+    k = np.tile(v, (5, 1))
+    ds = rng.normal(size=d) + 1.0
+    dk, dcls = chunk_summary_backward(k, rng.normal(size=d), ds)
+    np.testing.assert_allclose(dcls, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dk, np.tile(ds / 5, (5, 1)), atol=1e-14)
