@@ -48,6 +48,7 @@ _SIGNATURES = {
     "dash_default_params": (None, [ctypes.POINTER(DashParams)]),
     "dash_status_string": (ctypes.c_char_p, [_I]),
     "dash_summarize": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, DashParams, _P]),
+    "dash_summarize_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, DashParams, _P, _P, _P, _P]),
     "dash_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, DashParams]),
     "dash_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, DashParams, _P, _P, _I, _P, _SZ, _P]),
     "dash_sparse_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, DashParams, _P, _P, _SZ, _P]),

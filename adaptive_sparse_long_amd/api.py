@@ -102,6 +102,28 @@ def summarize(K, head_cls, S, n_tokens=None, seqlens=None, chunk_begin=0, chunk_
     return S
 
 
+def summarize_backward(K, head_cls, dS, n_tokens=None, chunk_begin=0, chunk_end=None, params: Params = Params()):
+    """Gradients (dK float32 [B, Hkv, Lmax, d], dcls float32 [Hkv, d]) of the chunk
+    summaries over tokens [0, n_tokens) for their cotangent dS (float32
+    [B, Hkv, s_cap, d]); dK rows outside the chunks [chunk_begin, chunk_end) are 0."""
+    lib = _lib.load()
+    _need(K, "K", dim=4)
+    _need(head_cls, "head_cls", K.dtype, 2)
+    _need(dS, "dS", torch.float32, 4)
+    B, Hkv, Lmax, d = K.shape
+    n_tokens = Lmax if n_tokens is None else int(n_tokens)
+    if chunk_end is None:
+        chunk_end = -(-n_tokens // CHUNK)
+    dK = torch.zeros(B, Hkv, Lmax, d, dtype=torch.float32, device=K.device)
+    dcls = torch.empty(Hkv, d, dtype=torch.float32, device=K.device)
+    parts = torch.empty(B, Hkv, max(int(chunk_end) - int(chunk_begin), 1), d, dtype=torch.float32, device=K.device)
+    st = lib.dash_summarize_backward(_p(K), _p(head_cls), _p(dS), _dt(K), B, Hkv, Lmax, d, n_tokens,
+                                     int(chunk_begin), int(chunk_end), dS.shape[2], params.c(), _p(dK),
+                                     _p(dcls), _p(parts), _stream(K.device))
+    _lib.check(st, "dash_summarize_backward")
+    return dK, dcls
+
+
 def workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode: bool, params: Params = Params()) -> int:
     return int(_lib.load().dash_workspace_size(B, Hq, Hkv, Nq, Lmax, d, int(decode), params.c()))
 

@@ -81,6 +81,22 @@ dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_d
   return from_hip(launch_summarize(a, stream));
 }
 
+dash_status dash_summarize_backward(const void* K, const void* head_cls, const float* dS,
+                                    dash_dtype dt, int B, int Hkv, int Lmax, int d, int n_tokens,
+                                    int chunk_begin, int chunk_end, int s_cap, dash_params p,
+                                    float* dK, float* dcls, float* partials, hipStream_t stream) {
+  if (!K || !head_cls || !dS || !dK || !dcls || !partials) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || Lmax <= 0 || d <= 0 || s_cap <= 0) return DASH_ERR_INVALID_ARG;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > s_cap) return DASH_ERR_INVALID_ARG;
+  if (n_tokens <= 0 || n_tokens > Lmax || p.chunk_size <= 0) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (p.chunk_size != kChunk || dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if ((long long)chunk_end * kChunk > (long long)Lmax + kChunk - 1) return DASH_ERR_INVALID_ARG;
+  SummarizeBwdArgs a{K, head_cls, dS, dK, dcls, partials, B, Hkv, Lmax, d, n_tokens,
+                     chunk_begin, chunk_end, s_cap, kChunk, 1.f / sqrtf((float)d)};
+  return from_hip(launch_summarize_bwd(a, stream));
+}
+
 size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int decode,
                            dash_params p) {
   if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;

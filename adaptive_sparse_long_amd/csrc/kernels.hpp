@@ -155,6 +155,18 @@ struct SummarizeArgs {
   float inv_sqrt_d;
 };
 
+struct SummarizeBwdArgs {
+  const void* K;
+  const void* cls;
+  const float* dS;   // [B, Hkv, s_cap, d] cotangent of the summaries
+  float* dK;         // [B, Hkv, Lmax, d]
+  float* dcls;       // [Hkv, d]
+  float* partials;   // [B, Hkv, chunk_end - chunk_begin, d]
+  int B, Hkv, Lmax, d, n_tokens;
+  int chunk_begin, chunk_end, s_cap, C;
+  float inv_sqrt_d;
+};
+
 struct RouteArgs {
   const uint16_t* Q;
   const uint16_t* K;
@@ -294,6 +306,7 @@ struct EntmaxRowsArgs {
 };
 
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
+hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream);
 hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_route_decode(const RouteArgs& a, hipStream_t stream);
 hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream);  // plan, scatter, chunk-major, row-major + merge

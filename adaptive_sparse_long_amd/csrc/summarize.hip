@@ -110,3 +110,169 @@ hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace dash
+
+// ---------------------------------------------------------------------------
+// Backward of the summary: for a cotangent ds of s_c (the pages differentiate
+// the whole hierarchy; the steps are the summary's own chain rule),
+//     de_j = a_j (<k_j, ds> - <s_c, ds>),
+//     dk_j = a_j ds + de_j cls / sqrt(d),   dcls += sum_j de_j k_j / sqrt(d).
+// k_summarize_bwd keeps the forward's layout (one wavefront per chunk, the
+// chunk's keys read once into registers), recomputes a and s_c, writes dk of
+// every token of the chunk and the chunk's dcls term into a partial row;
+// k_summarize_bwd_reduce adds the partial rows of each kv head in a fixed order
+// (deterministic).
+namespace dash {
+
+template <int D>
+__global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPI = kWave / LPR;
+  static_assert(LPR == 16, "summary kernel is laid out for head_dim 128");
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int c = a.chunk_begin + blockIdx.x * (blockDim.x / kWave) + wave;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  if (c >= a.chunk_end) return;
+  const int col = (lane % LPR) * 8;
+  const int rsub = lane / LPR;
+  const int n_chunks = a.chunk_end - a.chunk_begin;
+  float* part = a.partials + (((size_t)b * a.Hkv + h) * n_chunks + (c - a.chunk_begin)) * D + col;
+  const int t0 = c * a.C;
+  const int t1 = min(t0 + a.C, a.n_tokens);
+  if (t1 <= t0) {  // no token in this chunk: a zero term
+    if (lane < LPR) {
+      *reinterpret_cast<f32x4*>(part) = f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(part + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
+  const int n_valid = t1 - t0;
+
+  float w_cls[8], g[8];
+  {
+    const u32x4 cv = ldg16(static_cast<const uint16_t*>(a.cls) + (size_t)h * D + col);
+    for (int e = 0; e < 4; ++e) {
+      w_cls[2 * e] = bf16lo(cv[e]);
+      w_cls[2 * e + 1] = bf16hi(cv[e]);
+    }
+    const float* gp = a.dS + (((size_t)b * a.Hkv + h) * a.s_cap + c) * D + col;
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gp + 4);
+    for (int e = 0; e < 4; ++e) {
+      g[e] = g0[e];
+      g[4 + e] = g1[e];
+    }
+  }
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.K) + (((size_t)b * a.Hkv + h) * a.Lmax + t0) * D;
+  constexpr int kMaxIt = 64 / RPI;
+  u32x4 kv[kMaxIt];
+  float logit[kMaxIt], dot[kMaxIt];
+  const int n_it = (a.C + RPI - 1) / RPI;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int row = it * RPI + rsub;
+    kv[it] = (it < n_it && row < n_valid) ? ldg16(kbase + (size_t)row * D + col) : u32x4{0, 0, 0, 0};
+  }
+  float mx = kNegBig;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    float pl = 0.f, pd = 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = bf16lo(kv[it][e]), k1 = bf16hi(kv[it][e]);
+      pl = fmaf(k0, w_cls[2 * e], pl);
+      pl = fmaf(k1, w_cls[2 * e + 1], pl);
+      pd = fmaf(k0, g[2 * e], pd);
+      pd = fmaf(k1, g[2 * e + 1], pd);
+    }
+    const int row = it * RPI + rsub;
+    const bool ok = it < n_it && row < n_valid;
+    logit[it] = ok ? sum16(pl) * a.inv_sqrt_d : -INFINITY;
+    dot[it] = sum16(pd);  // <k_j, ds>
+    mx = fmaxf(mx, logit[it]);
+  }
+  mx = max_xor32(max_xor16(mx));
+  float den = 0.f, sacc[8];
+  for (int e = 0; e < 8; ++e) sacc[e] = 0.f;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    logit[it] = fast_exp2((logit[it] - mx) * kLog2e);  // unnormalised weight, 0 for masked rows
+    den += logit[it];
+    for (int e = 0; e < 4; ++e) {
+      sacc[2 * e] = fmaf(logit[it], bf16lo(kv[it][e]), sacc[2 * e]);
+      sacc[2 * e + 1] = fmaf(logit[it], bf16hi(kv[it][e]), sacc[2 * e + 1]);
+    }
+  }
+  den = sum_xor32(sum_xor16(den));
+  const float inv = 1.f / den;
+  float sd = 0.f;  // <s_c, ds> over this lane's dims, then over the row
+  for (int e = 0; e < 8; ++e) sd = fmaf(sum_xor32(sum_xor16(sacc[e])) * inv, g[e], sd);
+  sd = sum16(sd);
+
+  float pc[8];
+  for (int e = 0; e < 8; ++e) pc[e] = 0.f;
+  float* dkbase = a.dK + (((size_t)b * a.Hkv + h) * a.Lmax + t0) * D + col;
+#pragma unroll
+  for (int it = 0; it < kMaxIt; ++it) {
+    const int row = it * RPI + rsub;
+    const float aj = logit[it] * inv;
+    const float de = aj * (dot[it] - sd);
+    const float dc = de * a.inv_sqrt_d;
+    float o[8];
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = bf16lo(kv[it][e]), k1 = bf16hi(kv[it][e]);
+      pc[2 * e] = fmaf(de, k0, pc[2 * e]);
+      pc[2 * e + 1] = fmaf(de, k1, pc[2 * e + 1]);
+      o[2 * e] = fmaf(aj, g[2 * e], dc * w_cls[2 * e]);
+      o[2 * e + 1] = fmaf(aj, g[2 * e + 1], dc * w_cls[2 * e + 1]);
+    }
+    if (it < n_it && row < n_valid) {
+      float* dst = dkbase + (size_t)row * D;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    }
+  }
+  for (int e = 0; e < 8; ++e) pc[e] = sum_xor32(sum_xor16(pc[e])) * a.inv_sqrt_d;
+  if (lane < LPR) {
+    *reinterpret_cast<f32x4*>(part) = f32x4{pc[0], pc[1], pc[2], pc[3]};
+    *reinterpret_cast<f32x4*>(part + 4) = f32x4{pc[4], pc[5], pc[6], pc[7]};
+  }
+}
+
+// dcls[h] = sum over b and chunks of the partial rows; thread t adds dim t % D
+// of the rows r = t / D, t / D + kStreams, ... then the streams are added in
+// order through LDS.
+template <int D>
+__global__ __launch_bounds__(1024) void k_summarize_bwd_reduce(SummarizeBwdArgs a) {
+  constexpr int kStreams = 1024 / D;
+  __shared__ float s_acc[kStreams][D];
+  const int h = blockIdx.x;
+  const int dim = threadIdx.x % D;
+  const int st = threadIdx.x / D;
+  const int n_chunks = a.chunk_end - a.chunk_begin;
+  const long long rows = (long long)a.B * n_chunks;
+  float acc = 0.f;
+  for (long long r = st; r < rows; r += kStreams) {
+    const int b = (int)(r / n_chunks), c = (int)(r % n_chunks);
+    acc += a.partials[(((size_t)b * a.Hkv + h) * n_chunks + c) * D + dim];
+  }
+  s_acc[st][dim] = acc;
+  __syncthreads();
+  if (st == 0) {
+    float t = 0.f;
+    for (int i = 0; i < kStreams; ++i) t += s_acc[i][dim];
+    a.dcls[(size_t)h * D + dim] = t;
+  }
+}
+
+hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream) {
+  const int n = a.chunk_end - a.chunk_begin;
+  if (n > 0) {
+    dim3 grid((n + 3) / 4, a.Hkv, a.B);
+    hipLaunchKernelGGL(k_summarize_bwd<128>, grid, dim3(256), 0, stream, a);
+  }
+  hipLaunchKernelGGL(k_summarize_bwd_reduce<128>, dim3(a.Hkv), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dash

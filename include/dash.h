@@ -95,6 +95,32 @@ dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_d
                            dash_params p, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dash_summarize_backward -- gradients through stage 1 (the DashAttention
+ * README calls the hierarchy differentiable, "How it works"; the steps are the
+ * summary's own chain rule). For a cotangent dS of the summaries S written by
+ * dash_summarize over tokens [0, n_tokens), for every (b, kv head h) and chunk
+ * c in [chunk_begin, chunk_end) holding tokens j (recomputing a and s_c):
+ *     de_j = a_j (<k_j, dS[b,h,c]> - <s_c, dS[b,h,c]>),
+ *     dK[b, h, j, :] = a_j dS[b,h,c] + de_j head_cls[h] / sqrt(d),
+ *     dcls[h, :]     = sum over b and the chunks of sum_j de_j k_j / sqrt(d).
+ *   K        [B, Hkv, Lmax, d]  dtype dt;   head_cls [Hkv, d] dtype dt
+ *   dS       [B, Hkv, s_cap, d] float32 (rows of the listed chunks are read)
+ *   dK       [B, Hkv, Lmax, d]  float32, written for the tokens of the listed
+ *            chunks only (other rows untouched)
+ *   dcls     [Hkv, d] float32, written (zeros for an empty chunk range)
+ *   partials [B, Hkv, chunk_end - chunk_begin, d] float32 scratch, caller-owned
+ * dcls is reduced in a fixed order (deterministic). Device memory is the
+ * caller's; nothing is allocated; no host sync. Errors: NULL pointers, sizes
+ * <= 0, a chunk range outside [0, s_cap] or past Lmax, n_tokens outside
+ * [1, Lmax] -> DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d != 128 or
+ * chunk_size != 64 -> DASH_ERR_UNSUPPORTED; a launch failure -> DASH_ERR_HIP.
+ * --------------------------------------------------------------------------- */
+dash_status dash_summarize_backward(const void* K, const void* head_cls, const float* dS,
+                                    dash_dtype dt, int B, int Hkv, int Lmax, int d, int n_tokens,
+                                    int chunk_begin, int chunk_end, int s_cap, dash_params p,
+                                    float* dK, float* dcls, float* partials, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * dash_route -- stage 2, "Entmax block routing" ("How it works" 2): routing
  * scores z = scaling_factor * <q_i, s_c> / sqrt(d) against every candidate
  * chunk summary, alpha-entmax over them with the threshold tau found by

@@ -26,7 +26,7 @@ def test_header_symbols_exported(lib):
     assert set(names) == {
         "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
-        "entmax_rows", "entmax_rows_backward", "entmax_attn_backward",
+        "entmax_rows", "entmax_rows_backward", "entmax_attn_backward", "dash_summarize_backward",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -160,3 +160,21 @@ def test_entmax_attn_backward_validation(lib):
     assert e(*F5, NULL, 5, 1, 1, 128, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == INVALID
     assert e(*F5, NULL, 1, 1, 1, 128, 96, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == UNSUPPORTED
     assert e(*F5, NULL, 1, 1, 1, 70000, 64, NULL, 1.5, 1, FAKE, FAKE, FAKE, FAKE, NULL) == UNSUPPORTED
+
+
+def test_summarize_backward_validation(lib):
+    f = lib.dash_summarize_backward
+    p = _lib.params()
+    F3 = [FAKE] * 3
+    # K cls dS dt B Hkv Lmax d n_tokens c0 c1 s_cap params dK dcls parts stream
+    assert f(NULL, FAKE, FAKE, 1, 1, 2, 256, 128, 256, 0, 4, 4, p, *F3, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 4, 4, p, FAKE, NULL, FAKE, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 4, 4, p, FAKE, FAKE, NULL, NULL) == INVALID
+    assert f(*F3, 1, 0, 2, 256, 128, 256, 0, 4, 4, p, *F3, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 300, 0, 4, 4, p, *F3, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 3, 2, 4, p, *F3, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 5, 4, p, *F3, NULL) == INVALID
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 6, 8, p, *F3, NULL) == INVALID
+    assert f(*F3, 0, 1, 2, 256, 128, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
+    assert f(*F3, 1, 1, 2, 256, 64, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
+    assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 4, 4, _lib.params(chunk_size=32), *F3, NULL) == UNSUPPORTED
