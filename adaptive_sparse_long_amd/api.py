@@ -102,10 +102,13 @@ def summarize(K, head_cls, S, n_tokens=None, seqlens=None, chunk_begin=0, chunk_
     return S
 
 
-def summarize_backward(K, head_cls, dS, n_tokens=None, chunk_begin=0, chunk_end=None, params: Params = Params()):
+def summarize_backward(K, head_cls, dS, n_tokens=None, chunk_begin=0, chunk_end=None, params: Params = Params(),
+                       out=None):
     """Gradients (dK float32 [B, Hkv, Lmax, d], dcls float32 [Hkv, d]) of the chunk
     summaries over tokens [0, n_tokens) for their cotangent dS (float32
-    [B, Hkv, s_cap, d]); dK rows outside the chunks [chunk_begin, chunk_end) are 0."""
+    [B, Hkv, s_cap, d]); dK rows outside the chunks [chunk_begin, chunk_end) are 0.
+    ``out`` = (dK, dcls, partials) reuses caller buffers (dK rows outside the
+    chunks are then left as they are)."""
     lib = _lib.load()
     _need(K, "K", dim=4)
     _need(head_cls, "head_cls", K.dtype, 2)
@@ -114,9 +117,20 @@ def summarize_backward(K, head_cls, dS, n_tokens=None, chunk_begin=0, chunk_end=
     n_tokens = Lmax if n_tokens is None else int(n_tokens)
     if chunk_end is None:
         chunk_end = -(-n_tokens // CHUNK)
-    dK = torch.zeros(B, Hkv, Lmax, d, dtype=torch.float32, device=K.device)
-    dcls = torch.empty(Hkv, d, dtype=torch.float32, device=K.device)
-    parts = torch.empty(B, Hkv, max(int(chunk_end) - int(chunk_begin), 1), d, dtype=torch.float32, device=K.device)
+    if out is None:
+        dK = torch.zeros(B, Hkv, Lmax, d, dtype=torch.float32, device=K.device)
+        dcls = torch.empty(Hkv, d, dtype=torch.float32, device=K.device)
+        parts = torch.empty(B, Hkv, max(int(chunk_end) - int(chunk_begin), 1), d, dtype=torch.float32,
+                            device=K.device)
+    else:
+        dK, dcls, parts = out
+        _need(dK, "dK", torch.float32, 4)
+        _need(dcls, "dcls", torch.float32, 2)
+        _need(parts, "partials", torch.float32)
+        if tuple(dK.shape) != (B, Hkv, Lmax, d) or tuple(dcls.shape) != (Hkv, d):
+            raise ValueError("dK must be [B, Hkv, Lmax, d] and dcls [Hkv, d]")
+        if parts.numel() < B * Hkv * max(int(chunk_end) - int(chunk_begin), 1) * d:
+            raise ValueError("partials must hold B * Hkv * (chunk_end - chunk_begin) * d floats")
     st = lib.dash_summarize_backward(_p(K), _p(head_cls), _p(dS), _dt(K), B, Hkv, Lmax, d, n_tokens,
                                      int(chunk_begin), int(chunk_end), dS.shape[2], params.c(), _p(dK),
                                      _p(dcls), _p(parts), _stream(K.device))

@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
     "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
     "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_summarize_bwd": ["summarize.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_bwd_dq": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_bwd_dkdv": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
@@ -214,9 +215,28 @@ def bench_prefill(w, steps, warmup):
     # work counts (outside the timed region)
     _, bits, _ = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
     alg, pair, dense, scores, per_row = prefill_work(bits, w.N, w.d)
+    # summary backward on the same keys (gradients of the summaries for a random
+    # cotangent into dK and head_cls), outside the step
+    dS = cotangent((w.B, w.Hkv, n_c, w.d), w.seed + 700, dtype="f32", device=dev)
+    bufs = (torch.zeros(w.B, w.Hkv, w.N, w.d, dtype=torch.float32, device=dev),
+            torch.empty(w.Hkv, w.d, dtype=torch.float32, device=dev),
+            torch.empty(w.B, w.Hkv, n_sum, w.d, dtype=torch.float32, device=dev))
+    t_sb = Timer()
+    for it in range(warmup + steps):
+        e = t_sb.start() if it >= warmup else None
+        api.summarize_backward(K, cls, dS, n_tokens=w.N, chunk_begin=0, chunk_end=n_sum, params=p, out=bufs)
+        if it >= warmup:
+            t_sb.stop(e)
+    ms_sb = t_sb.mean_ms()
+    # algorithmic bytes: K read (bf16), dK written (fp32), dS read, dcls partials written and read
+    sb_bytes = float(w.B * w.Hkv * n_sum * C * w.d * (2 + 4) + w.B * w.Hkv * n_sum * w.d * 4 * 3)
+    del dS, bufs
     res = {
         "wall_ms": wall * 1e3,
         "ms_summarize": t_sum.mean_ms(),
+        "summary_backward": {"us": ms_sb * 1e3, "bytes_per_launch": sb_bytes,
+                             "GBps": sb_bytes / (ms_sb / 1e3) / 1e9,
+                             "frac": sb_bytes / (ms_sb / 1e3) / 1e9 / PEAK_HBM_GBS},
         "ms_route": t_route.mean_ms(),
         "ms_attention": t_attn.mean_ms(),
         "alg_flops": alg,
@@ -553,6 +573,8 @@ def main():
             "attention_alg_tflops": pre["alg_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
             "attention_traffic": attn_traffic,
             "route_roofline": route_roof,
+            # the summaries' backward (dash_summarize_backward) on the same keys, against HBM
+            "summary_backward": pre["summary_backward"],
         },
         "roofline": roof,
     }
