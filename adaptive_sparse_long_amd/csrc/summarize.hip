@@ -239,29 +239,32 @@ __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
   }
 }
 
-// dcls[h] = sum over b and chunks of the partial rows; thread t adds dim t % D
-// of the rows r = t / D, t / D + kStreams, ... then the streams are added in
-// order through LDS.
+// dcls[h] = sum over b and chunks of the partial rows. Thread t reads dims
+// 4 (t % 32) .. +3 (one float4) of the rows r = t / 32, t / 32 + 32, ... (32
+// streams, loads unrolled so several are in flight); the streams are then added
+// in order through LDS (deterministic).
 template <int D>
 __global__ __launch_bounds__(1024) void k_summarize_bwd_reduce(SummarizeBwdArgs a) {
-  constexpr int kStreams = 1024 / D;
-  __shared__ float s_acc[kStreams][D];
+  constexpr int kCols = D / 4;            // float4 columns per row
+  constexpr int kStreams = 1024 / kCols;  // row streams
+  __shared__ f32x4 s_acc[kStreams][kCols];
   const int h = blockIdx.x;
-  const int dim = threadIdx.x % D;
-  const int st = threadIdx.x / D;
+  const int q = threadIdx.x % kCols;
+  const int st = threadIdx.x / kCols;
   const int n_chunks = a.chunk_end - a.chunk_begin;
-  const long long rows = (long long)a.B * n_chunks;
-  float acc = 0.f;
-  for (long long r = st; r < rows; r += kStreams) {
-    const int b = (int)(r / n_chunks), c = (int)(r % n_chunks);
-    acc += a.partials[(((size_t)b * a.Hkv + h) * n_chunks + c) * D + dim];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < a.B; ++b) {
+    const f32x4* rows = reinterpret_cast<const f32x4*>(a.partials + ((size_t)b * a.Hkv + h) * n_chunks * D) + q;
+#pragma unroll 4
+    for (int c = st; c < n_chunks; c += kStreams) acc += rows[(size_t)c * kCols];
   }
-  s_acc[st][dim] = acc;
+  s_acc[st][q] = acc;
   __syncthreads();
-  if (st == 0) {
+  if (threadIdx.x < D) {
+    const int dq = threadIdx.x / 4, e = threadIdx.x % 4;
     float t = 0.f;
-    for (int i = 0; i < kStreams; ++i) t += s_acc[i][dim];
-    a.dcls[(size_t)h * D + dim] = t;
+    for (int i = 0; i < kStreams; ++i) t += s_acc[i][dq][e];
+    a.dcls[(size_t)h * D + threadIdx.x] = t;
   }
 }
 
