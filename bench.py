@@ -485,8 +485,8 @@ def main():
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path (see the sharding notes "
-              "in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (prefill would shard by "
+              "(batch, KV head) with no exchange, decode by batch); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sparsity:
