@@ -163,3 +163,33 @@ def test_backward_varlen_workload():
             assert bool((sv <= 2.0 ** -8 * gv.abs().sum(0) + TOL_BF16).all()), f"sum dV b{b} h{h}: {float(sv.max()):.3e}"
             assert bool((dQ[b, h, L:] == 0).all() and (dK[b, h, L:] == 0).all() and (dV[b, h, L:] == 0).all())
     assert checked >= 100
+
+
+def test_backward_maximum_length():
+    """Nmax = 65536 (1024 tiles, the largest the library takes): the mask column of
+    a key tile spans all 32 words of its bitmap. One head, alpha = 2, non-causal,
+    length 65536 - 37 (a ragged last tile); sampled dQ rows against the oracle row
+    by row (rows with an entry within 1e-5 of tau skipped) and the two identities
+    per head."""
+    N, d, L = 65536, 64, 65536 - 37
+    q, k, v, _ = dense_entmax_inputs(1, 1, N, d, 4242, dtype="bf16", scale=2.0, device="cuda")
+    dO = cotangent(q.shape, 4243, dtype="bf16", device="cuda")
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    _, tau, mask = api.entmax_attn(q, k, v, alpha=2.0, causal=False, varlen=lens)
+    dQ, dK, dV = api.entmax_attn_backward(q, k, v, dO, tau, mask, alpha=2.0, causal=False, varlen=lens)
+    torch.cuda.synchronize()
+    qb, kb, vb, ob = f64(q[0, 0, :L]), f64(k[0, 0, :L]), f64(v[0, 0, :L]), f64(dO[0, 0, :L])
+    checked = 0
+    for i in [0, 1, 4095, 40000, L - 1] + list(np.random.default_rng(5).integers(0, L, 5)):
+        _, tr, P = oracle.entmax_attention_rows(qb[i : i + 1], np.array([i]), kb, vb, L, 2.0, False)
+        s = qb[i] @ kb.T / np.sqrt(d)
+        if np.any(np.abs(s - tr[0]) < NEAR):
+            continue
+        ref = oracle.entmax_backward(P[0], ob[i] @ vb.T, 2.0) @ kb / np.sqrt(d)
+        _close(f64(dQ[0, 0, i]), ref, q.dtype, f"N=65536 dQ row {i}")
+        checked += 1
+    assert checked >= 6
+    gk, gv = dK[0, 0, :L].double(), dV[0, 0, :L].double()
+    assert bool((gk.sum(0).abs() <= 2.0 ** -8 * gk.abs().sum(0) + TOL_BF16).all())
+    assert bool(((gv.sum(0) - dO[0, 0, :L].double().sum(0)).abs() <= 2.0 ** -8 * gv.abs().sum(0) + TOL_BF16).all())
+    assert bool((dQ[0, 0, L:] == 0).all() and (dK[0, 0, L:] == 0).all() and (dV[0, 0, L:] == 0).all())

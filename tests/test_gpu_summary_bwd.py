@@ -89,3 +89,30 @@ def test_summarize_backward_32k_workload():
     assert_close(f64(dcls), rc, TOL_F32 * 10, "dcls (sum of 512 chunk terms)")
     for c in sorted(sample):
         assert_close(f64(dK[:, :, c * C : (c + 1) * C]), rK[:, :, c * C : (c + 1) * C], TOL_F32, f"dK chunk {c}")
+
+
+def test_summarize_backward_decode_cache():
+    """The 128K decode cache at batch 16 (8 KV heads, 2048 chunks per sequence):
+    dcls of two heads in full (32768 chunk terms each), dK on sampled chunks."""
+    w = WORKLOADS["decode_128k"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    K = torch.randn(w.B, w.Hkv, w.N, w.d, generator=gen, device="cuda").to(torch.bfloat16)
+    cls = torch.randn(w.Hkv, w.d, generator=gen, device="cuda").to(torch.bfloat16)
+    n_c = w.N // C
+    dS = cotangent((w.B, w.Hkv, n_c, w.d), w.seed + 700, dtype="f32", device="cuda")
+    dK, dcls = api.summarize_backward(K, cls, dS)
+    torch.cuda.synchronize()
+    for h in (0, 7):
+        Kh, dSh, ch = f64(K[:, h]), f64(dS[:, h]), f64(cls[h])
+        ref = np.zeros(w.d)
+        for b in range(w.B):
+            for c in range(n_c):
+                ref += oracle.chunk_summary_backward(Kh[b, c * C : (c + 1) * C], ch, dSh[b, c])[1]
+        # 32768 chunk terms added in float32
+        assert_close(f64(dcls[h]), ref, TOL_F32 * 100, f"dcls head {h}")
+    rng = np.random.default_rng(w.seed)
+    for _ in range(8):
+        b, h, c = int(rng.integers(0, w.B)), int(rng.integers(0, w.Hkv)), int(rng.integers(0, n_c))
+        dk_ref, _ = oracle.chunk_summary_backward(f64(K[b, h, c * C : (c + 1) * C]), f64(cls[h]), f64(dS[b, h, c]))
+        assert_close(f64(dK[b, h, c * C : (c + 1) * C]), dk_ref, TOL_F32, f"dK b{b} h{h} c{c}")
