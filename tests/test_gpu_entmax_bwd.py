@@ -193,3 +193,18 @@ def test_backward_maximum_length():
     assert bool((gk.sum(0).abs() <= 2.0 ** -8 * gk.abs().sum(0) + TOL_BF16).all())
     assert bool(((gv.sum(0) - dO[0, 0, :L].double().sum(0)).abs() <= 2.0 ** -8 * gv.abs().sum(0) + TOL_BF16).all())
     assert bool((dQ[0, 0, L:] == 0).all() and (dK[0, 0, L:] == 0).all() and (dV[0, 0, L:] == 0).all())
+
+
+def test_backward_autograd_varlen_f32():
+    """torch autograd through api.entmax_attn_fn with varlen and causal masking,
+    float32, against the oracle's gradients."""
+    q, k, v, _ = dense_entmax_inputs(2, 1, 140, 64, 25, dtype="f32", device="cuda")
+    dO = cotangent(q.shape, 26, dtype="f32", device="cuda")
+    lens = torch.tensor([140, 77], dtype=torch.int32, device="cuda")
+    qs, ks, vs = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = api.entmax_attn_fn(qs, ks, vs, alpha=1.5, causal=True, varlen=lens)
+    out.backward(dO)
+    torch.cuda.synchronize()
+    refs = oracle.entmax_attention_backward(f64(q), f64(k), f64(v), f64(dO), 1.5, True, varlen=np.array([140, 77]))
+    for t, r, name in zip((qs, ks, vs), refs, ("dQ", "dK", "dV")):
+        _close(f64(t.grad), r, torch.float32, f"autograd varlen {name}")
