@@ -69,8 +69,19 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libdash.so; returns the library path."""
+def _stale(obj: str, src: str) -> bool:
+    """True if obj is missing or older than its source or any shared header."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    deps.append(os.path.join(INCLUDE, "dash.h"))
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(p) > t for p in deps)
+
+
+def build(verbose: bool = False, jobs: int | None = None, only_changed: bool = False) -> str:
+    """Compile every source (only_changed: only those newer than their object)
+    and link libdash.so; returns the library path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -78,9 +89,11 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
+        if only_changed and not _stale(obj, os.path.join(CSRC, src)):
+            continue
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         cmds.append([hipcc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
-    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
+    jobs = jobs or max(1, min(len(cmds), os.cpu_count() or 2))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
@@ -90,4 +103,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, only_changed="--changed" in sys.argv))

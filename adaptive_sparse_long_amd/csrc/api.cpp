@@ -175,6 +175,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.tbase = reinterpret_cast<uint32_t*>(ws + L.off_tbase);
   a.rslot = reinterpret_cast<uint32_t*>(ws + L.off_rslot);
   a.cmcnt = reinterpret_cast<uint16_t*>(ws + L.off_cmcnt);
+  a.own_lw = reinterpret_cast<float*>(ws + L.off_own);
   a.fb_tiles = reinterpret_cast<int2*>(ws + L.off_fb);
   a.fb_count = reinterpret_cast<int*>(ws + L.off_fb_count);
   a.n_rm = a.fb_count + 1;
@@ -230,6 +231,8 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.tbase = reinterpret_cast<const uint32_t*>(ws + L.off_tbase);
   a.rslot = reinterpret_cast<const uint32_t*>(ws + L.off_rslot);
   a.cmcnt = reinterpret_cast<const uint16_t*>(ws + L.off_cmcnt);
+  a.own_lw = reinterpret_cast<const float*>(ws + L.off_own);
+  a.qhead = reinterpret_cast<int*>(ws + L.off_qhead);
   a.n_rm = reinterpret_cast<const int*>(ws + L.off_fb_count) + 1;
   a.plse = reinterpret_cast<float*>(ws + L.off_plse);
   a.po = reinterpret_cast<uint16_t*>(ws + L.off_po);

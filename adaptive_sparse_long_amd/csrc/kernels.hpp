@@ -16,14 +16,14 @@ constexpr int kChunk = 64;
 // Routed chunks handled by one decode split (one workgroup, four wavefronts).
 constexpr int kDecodeSplit = 24;
 // Partial-result pool of the chunk-major kernel: kCmSlots slots per query row
-// on average. Every attended chunk of a row (its routed past chunks and its
-// own chunk) is attended by the chunk-major kernel into a slot of its own, and
-// the merge kernel combines the row's partials. A tile whose rows find the pool
-// exhausted has all its chunks attended by the row-major kernel instead.
+// on average. Every routed past chunk of a row is attended by the chunk-major
+// kernel into a slot of its own; the merge kernel attends the row's own chunk
+// (causal) and combines it with the row's partials. A tile whose rows find the
+// pool exhausted has all its chunks attended by the row-major kernel instead.
 constexpr int kCmSlots = 16;
 // Chunk-major work item: up to kCmBlocks blocks of 32 (row, chunk) pairs of one
 // (b, kv head, chunk).
-constexpr int kCmBlocks = 12;
+constexpr int kCmBlocks = 24;
 // The partial-result pool is split into kPools equal parts, each with its own
 // allocation counter (workgroup id modulo kPools picks the part).
 constexpr int kPools = 8;
@@ -46,11 +46,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // chunk (cbase, reserved by the routing). Per (b, kv head, chunk) "bhc": the
 // number of its pairs (cmp) and their start in the chunk-sorted pair records
 // (cs). Work items list (bhc, first block); recs hold one pair each.
-// Per tile: its first pool slot (tbase). Per row: its first slot (rslot) and
-// number of partials (cmcnt); a row's slots follow its attended chunks in
-// ascending order. pool: the slot allocation counter. Per slot: the log2 of
-// the partial's sum of exp2 weights (its max included) in float32 and its
-// output normalised by that sum in fp16, dims in natural order.
+// Per tile: its first pool slot (tbase). Per row: its first slot (rslot), its
+// number of partials (cmcnt) and the log2 weight of its own chunk (own_lw,
+// causal; -inf when not attended); a row's slots follow its routed past
+// chunks in ascending order. pool: the slot allocation counter. Per slot: the
+// log2 of the partial's sum of exp2 weights (its max included) in float32 and
+// its output normalised by that sum in fp16, dims in natural order. qhead: the
+// chunk-major kernel's work queue head.
 // ---------------------------------------------------------------------------
 struct PrefillLayout {
   int n_tiles = 0;
@@ -63,6 +65,7 @@ struct PrefillLayout {
   size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0, off_trec = 0;  // chunk-major pairs
   size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_plse = 0, off_po = 0;  // partials
   size_t off_fb = 0, off_fb_count = 0;  // tiles left to the general routing kernel
+  size_t off_own = 0, off_qhead = 0;
   long long pool_cap = 0;
   size_t off_split = 0, total = 0;
   size_t off_serr = 0;  // per chunk: bound on |hi-only score - full score| / |q|
@@ -109,6 +112,8 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_fb_count = o; o += align256(2 * sizeof(int));  // queued tiles, row-major tiles
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
+  L.off_own = o;     o += align256(rows * sizeof(float));
+  L.off_qhead = o;   o += align256(sizeof(int));
   L.off_plse = o;    o += align256(pairs * sizeof(float));
   L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
   L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
@@ -197,6 +202,7 @@ struct RouteArgs {
   uint32_t* tbase;
   uint32_t* rslot;
   uint16_t* cmcnt;
+  float* own_lw;     // per row: log2 weight of its own chunk (causal)
   int2* fb_tiles;   // tiles the list-based kernel left: (tile, b * Hq + h)
   int* fb_count;     // their number, zeroed by the summary split
   int* n_rm;         // tiles without pool slots (row-major), zeroed by the summary split
@@ -239,6 +245,8 @@ struct PrefillAttnArgs {
   const uint32_t* tbase;
   const uint32_t* rslot;
   const uint16_t* cmcnt;
+  const float* own_lw;
+  int* qhead;       // work queue head of the chunk-major kernel
   const int* n_rm;  // tiles the routing left row-major
   float* plse;
   uint16_t* po;

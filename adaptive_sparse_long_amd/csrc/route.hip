@@ -411,9 +411,6 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     dact[r] = row_ok[r] && (est ? (td > 0.f) : causal);
     lwd[r] = !row_ok[r] ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
   }
-  const float td_r = ud_r - tau_r;
-  const bool dact_r = row_ok_r && (est ? (td_r > 0.f) : causal);
-  const float lwd_r = !row_ok_r ? -INFINITY : (est ? (td_r > 0.f ? log2_prior<KIND>(td_r, a.beta) : -INFINITY) : 0.f);
 
   // ---- per-row bitmask output, only when asked for (lanes 0..15: row i0 + lane)
   if (a.bits != nullptr) {
@@ -491,7 +488,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   int nsl4[4] = {0, 0, 0, 0}, pre4[4] = {0, 0, 0, 0};  // block layout
   if (!ovf) {
     for_each_routed_row([](int, int, float) {});
-    nsl_r = run_r + (dact_r ? 1 : 0);
+    nsl_r = run_r;
     int x = sub == 0 ? nsl_r : 0;
     const int x0 = x;
 #pragma unroll
@@ -504,7 +501,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   } else {
     for_each_routed_blk([](int, int, int, float) {});
 #pragma unroll
-    for (int r = 0; r < 4; ++r) nsl4[r] = run4[r] + (dact[r] ? 1 : 0);
+    for (int r = 0; r < 4; ++r) nsl4[r] = run4[r];
     const int grp_tot = nsl4[0] + nsl4[1] + nsl4[2] + nsl4[3];
     const int g0 = __builtin_amdgcn_readlane(grp_tot, 0), g1 = __builtin_amdgcn_readlane(grp_tot, 16);
     const int g2 = __builtin_amdgcn_readlane(grp_tot, 32), g3 = __builtin_amdgcn_readlane(grp_tot, 48);
@@ -518,7 +515,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     int tot = 0;
 #pragma unroll
     for (int ww = 0; ww < 8; ++ww) tot += s_wtot[ww];
-    long long base = -1;
+    long long base = 0;  // a tile without routed past chunks needs no slots
     if (tot > 0) {
       // the workgroup's part of the pool
       const int part = (int)((tile + (size_t)a.n_tiles * (h + (size_t)a.Hq * b)) % kPools);
@@ -530,12 +527,18 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     a.tbase[bh * a.n_tiles + tile] = base >= 0 ? (uint32_t)base : 0u;
   }
   __syncthreads();
-  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every routed past chunk
   if (threadIdx.x == 0 && !pooled) atomicAdd(a.n_rm, 1);
   const long long tb = s_tbase;
   int wpre = 0;
 #pragma unroll
   for (int ww = 0; ww < 8; ++ww) wpre += ww < w ? s_wtot[ww] : 0;
+  // own-chunk log2 weight per row (the merge kernel attends it for pooled tiles)
+  if (causal && col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (row_ok[r]) a.own_lw[bh * (size_t)N + i0 + grp * 4 + r] = lwd[r];
+  }
   if (!ovf) {
     if (sub == 0 && row_ok_r) {
       const size_t ri = bh * (size_t)N + i0 + rr;
@@ -559,7 +562,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   } else {
     for_each_routed_blk([&](int, int c, int, float) { atomicOr(&un[c >> 5], 1u << (c & 31)); });
   }
-  if (causal && col == 0 && (dact[0] || dact[1] || dact[2] || dact[3])) atomicOr(&un[cw >> 5], 1u << (cw & 31));
+  if (!pooled && causal && col == 0 && (dact[0] || dact[1] || dact[2] || dact[3])) atomicOr(&un[cw >> 5], 1u << (cw & 31));
   __syncthreads();
   if (threadIdx.x == 0 || threadIdx.x == kWave) {
     const bool cm = threadIdx.x != 0;
@@ -598,12 +601,8 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     // rows of every entry, place the entries, then write the records
     if (!ovf) {
       for_each_routed_row([&](int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
-      if (causal && sub == 0 && dact_r) atomicAdd(&s_ecnt[epos(cw)], 1);
     } else {
       for_each_routed_blk([&](int, int c, int, float) { atomicAdd(&s_ecnt[epos(c)], 1); });
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (causal && col == 0 && dact[r]) atomicAdd(&s_ecnt[epos(cw)], 1);
     }
     __syncthreads();
     const int ne = s_cpre[NW];
@@ -627,14 +626,10 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       for_each_routed_row([&](int c, int rank, float uu) {
         put(epos(c), i0 + rr, s0 + rank, log2_prior<KIND>(uu - tau_r, a.beta));
       });
-      if (causal && sub == 0 && dact_r) put(epos(cw), i0 + rr, s0 + (nsl_r - 1), lwd_r);
     } else {
       for_each_routed_blk([&](int r, int c, int rank, float uu) {
         put(epos(c), i0 + grp * 4 + r, tb + wpre + pre4[r] + rank, log2_prior<KIND>(uu - tau[r], a.beta));
       });
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (causal && col == 0 && dact[r]) put(epos(cw), i0 + grp * 4 + r, tb + wpre + pre4[r] + (nsl4[r] - 1), lwd[r]);
     }
   } else {
     // ---- row-major list: -inf for every (entry, row) of this wavefront, then
@@ -718,6 +713,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   __shared__ int s_wtot[4], s_tmp[4];
   __shared__ long long s_tbase;
   __shared__ int s_cnt;                     // entries in the list
+  __shared__ int s_ownf[kTileRows];         // the row attends its own chunk
   __shared__ float s_bmax[NWMAX];           // per block of 32 chunks: the largest error bound
   __shared__ int2 s_seg[4][kRoutePrefillMaxSlots / 32];  // per wavefront: (first, count | block << 16)
 
@@ -1116,34 +1112,40 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   }
   if (owner && row_ok) a.tau[bh * (size_t)N + qi] = tau;
 
-  // ---- own chunk: routed (estimate) or always attended with weight 1
+  // ---- own chunk: routed (estimate) or always attended with weight 1. A
+  // pooled tile attends it in the merge kernel (one causal tile per 64 rows),
+  // from its log2 weight own_lw; a row-major tile lists it with the others.
   const float td = ud - tau;
   const bool dact = row_ok && (est ? (td > 0.f) : causal);
   const float lwd = !row_ok ? -INFINITY : (est ? (td > 0.f ? log2_prior<KIND>(td, a.beta) : -INFINITY) : 0.f);
-  const bool own_pair = owner && causal && dact;  // the lane that emits the own-chunk pair
+  const bool own_pair = owner && causal && dact;  // the lane that owns the row's own-chunk weight
+  if (owner && row_ok && causal) a.own_lw[bh * (size_t)N + qi] = lwd;
 
-  // ---- per-row bitmasks of the attended chunks (over the tau sums)
+  // ---- per-row bitmasks of the routed past chunks (over the tau sums)
   __syncthreads();
   for (int x = tid; x < kTileRows * NWMAX; x += blockDim.x) (&s_bits[0][0])[x] = 0u;
+  if (owner) s_ownf[R] = own_pair ? 1 : 0;
   __syncthreads();
   for_run([&](int j, float uu, uint32_t kk) {
     const int rr = kk >> 9, c = kk & 511;
     if (j < nl && uu > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
   });
-  if (own_pair) atomicOr(&s_bits[R][cw >> 5], 1u << (cw & 31));
   __syncthreads();
   if (a.bits != nullptr) {
+    // attended chunks: the routed past chunks and the own chunk
     for (int x = tid; x < kTileRows * a.bits_words; x += blockDim.x) {
       const int r = x / a.bits_words, wd = x % a.bits_words;
       const int q = tile * kTileRows + r;
-      if (q < N) a.bits[(bh * (size_t)N + q) * a.bits_words + wd] = wd < NW ? s_bits[r][wd] : 0u;
+      const int cq = q / kChunk;
+      uint32_t word = wd < NW ? s_bits[r][wd] : 0u;
+      if (s_ownf[r] && (cq >> 5) == wd) word |= 1u << (cq & 31);
+      if (q < N) a.bits[(bh * (size_t)N + q) * a.bits_words + wd] = word;
     }
   }
-  // attended chunks of the row (routed past chunks, then the own chunk)
+  // routed past chunks of the row (owner lanes)
   int nsl = 0;
   if (owner)
     for (int wd = 0; wd < NW; ++wd) nsl += __popc(s_bits[R][wd]);
-  const int nrt = nsl - (own_pair ? 1 : 0);  // routed past chunks (owner lanes)
   // the wavefront's union: lane l ORs word l % 16 of rows 8 (l / 16) .. +7
   {
     const int wd = lane & 15;
@@ -1173,7 +1175,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   if (tid < NWMAX) s_union[tid] = s_wun[0][tid] | s_wun[1][tid] | s_wun[2][tid] | s_wun[3][tid];
   if (tid == kWave) {
     const int tot = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
-    long long pbase = -1;
+    long long pbase = 0;  // a tile without routed past chunks needs no slots
     if (tot > 0) {
       const int part = (int)((blockIdx.x + (size_t)gridDim.x * (blockIdx.y + (size_t)gridDim.y * blockIdx.z)) % kPools);
       const unsigned long long cap = (unsigned long long)a.pool_cap / kPools;
@@ -1184,8 +1186,13 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     a.tbase[bh * a.n_tiles + tile] = pbase >= 0 ? (uint32_t)pbase : 0u;
   }
   __syncthreads();
-  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every attended chunk
+  const bool pooled = s_tbase >= 0;  // uniform: chunk-major for every routed past chunk
   if (tid == 0 && !pooled) atomicAdd(a.n_rm, 1);
+  if (!pooled) {
+    // the row-major list holds the own chunk too
+    if (own_pair) atomicOr(&s_union[cw >> 5], 1u << (cw & 31));
+    __syncthreads();
+  }
   const long long tb = s_tbase;
   int wpre = 0;
   for (int ww = 0; ww < w; ++ww) wpre += s_wtot[ww];
@@ -1280,7 +1287,6 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         a.trec[tb + place(epos(c), rr)] = make_int4((tile * kTileRows + rr) * g + hh, (int)(s_s0[rr] + rank_in_row(rr, c)),
                                                     __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
     });
-    if (own_pair) a.trec[tb + place(epos(cw), R)] = make_int4(qi * g + hh, (int)(s0 + nrt), __float_as_int(lwd), 0);
 #pragma unroll
     for (int q = 0; q < 2; ++q)
       if (2 * tid + q < ne) a.cbase[toff + 2 * tid + q] = cb[q];

@@ -284,27 +284,38 @@ namespace {
 constexpr int kCmWgPerCu = 3;  // resident chunk-major workgroups per CU
 }  // namespace
 
-__global__ __launch_bounds__(1024) void k_cm_plan(PrefillAttnArgs a) {
-  __shared__ int s_tmp[2][16];
-  int carry_p = 0, carry_i = 0;
-  for (int base = 0; base < a.n_bhc; base += 1024) {
-    const int idx = base + threadIdx.x;
-    const int P = idx < a.n_bhc ? a.cmp[idx] : 0;
-    const int ni = ((P + 31) / 32 + kCmBlocks - 1) / kCmBlocks;
-    int ep, ei;
-    const int tp = block_excl_scan<16>(P, s_tmp[0], ep);
-    const int ti = block_excl_scan<16>(ni, s_tmp[1], ei);
-    if (idx < a.n_bhc) {
-      a.cs[idx] = carry_p + ep;
-      for (int j = 0; j < ni; ++j) {
-        const long long it = (long long)carry_i + ei + j;
-        if (it < a.max_items) a.items[it] = make_int2(idx, j * kCmBlocks);
-      }
-    }
-    carry_p += tp;
-    carry_i += ti;
+// Workgroup j plans the (b, kv head, chunk) entries [256 j, 256 j + 256): the
+// pairs and work items of every entry before its range are summed first (each
+// workgroup reads the counts ahead of it, 16 KB at 32K), then its own entries
+// are scanned. Also resets the chunk-major kernel's queue head.
+__global__ __launch_bounds__(256) void k_cm_plan(PrefillAttnArgs a) {
+  __shared__ int s_tmp[4][4];
+  auto n_items = [](int P) { return ((P + 31) / 32 + kCmBlocks - 1) / kCmBlocks; };
+  const int base = blockIdx.x * 256;
+  int pp = 0, pi = 0;
+  for (int j = threadIdx.x; j < base; j += 256) {
+    const int P = a.cmp[j];
+    pp += P;
+    pi += n_items(P);
   }
-  if (threadIdx.x == 0) *a.nitems = carry_i;
+  int unused;
+  const int carry_p = block_excl_scan<4>(pp, s_tmp[0], unused);
+  const int carry_i = block_excl_scan<4>(pi, s_tmp[1], unused);
+  const int idx = base + threadIdx.x;
+  const int P = idx < a.n_bhc ? a.cmp[idx] : 0;
+  const int ni = n_items(P);
+  int ep, ei;
+  block_excl_scan<4>(P, s_tmp[2], ep);
+  const int ti = block_excl_scan<4>(ni, s_tmp[3], ei);
+  if (idx < a.n_bhc) {
+    a.cs[idx] = carry_p + ep;
+    for (int j = 0; j < ni; ++j) {
+      const long long it = (long long)carry_i + ei + j;
+      if (it < a.max_items) a.items[it] = make_int2(idx, j * kCmBlocks);
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) *a.nitems = carry_i + ti;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.qhead = 0;
 }
 
 // One workgroup per (tile, query head, b): copies the tile's pair records,
@@ -347,7 +358,6 @@ __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
 template <int D>
 __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs a) {
   constexpr int NS = D / 16;
-  constexpr int NDB = D / 32;
   constexpr int KROW = D + KPAD;
   constexpr int VROW = kChunk + VPAD;
   constexpr int NBW = kCmBlocks / 4;  // blocks of an item per wavefront
@@ -366,8 +376,16 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
   const int hi32 = lane >> 5;
   const bool causal = a.causal != 0;
   const int nitems = (int)min((long long)*a.nitems, a.max_items);
+  __shared__ int s_item;
 
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+  for (;;) {
+    // the next item from the queue; the barrier also orders the previous
+    // item's LDS reads before this item's staging
+    __syncthreads();
+    if (tid == 0) s_item = atomicAdd(a.qhead, 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= nitems) break;
     const int2 it = a.items[item];
     const int bhc = it.x;
     const int c = bhc % a.n_slots;
@@ -403,7 +421,6 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
     // ---- stage K (row-major) and V (transposed) of chunk c; keys past the
     // sequence end read its last row (masked below). The first block's query
     // rows are fetched meanwhile.
-    __syncthreads();  // the previous item's LDS reads are done
     bf16x8 qbuf[2][NS];
     {
       const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
@@ -545,26 +562,162 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
 }
 
 // ---------------------------------------------------------------------------
-// Merge: every row with partial results (the rows of tiles that got pool
-// slots) combines them, in the order of its slots (consecutive, so rows stream
-// through memory). Eight lanes per row: first the row's largest log2 sum and
-// the sum of 2^(log2 sum - largest) over its partials (the lanes split the
-// partials, DPP reductions over the eight), then each partial's fp16 output
-// is added with its normalised weight (v_fma_mix: fp16 in, fp32 sums). Lane p
-// owns dims 8p .. 8p+7 and 64+8p .. 64+8p+7, so each load instruction of the
-// eight lanes reads 128 contiguous bytes; four partials are in flight together.
+// Own chunk and merge. One workgroup per (b, query head, 64-row chunk c) of a
+// tile that got pool slots (row-major tiles are left to k_sparse_prefill):
+//   A (causal). The rows' own chunk c as one causal 64 x 64 tile: K and V^T
+//     of the chunk staged in LDS, four wavefronts of 16 rows each,
+//     S^T = K Q^T and O^T = V^T P^T by v_mfma_f32_16x16x32_bf16, the row's
+//     own-chunk log2 weight (own_lw) as bias; the normalised result and the
+//     log2 of its weight sum go to LDS.
+//   B. Every row combines its own-chunk result with its partials (routed past
+//     chunks, consecutive slots in chunk order), eight lanes per row: the
+//     largest log2 sum first, then each partial's fp16 output added with its
+//     normalised weight (fp32 sums); lane p owns dims 8p .. 8p+7 and
+//     64+8p .. 64+8p+7, so every load instruction of the eight lanes reads 128
+//     contiguous bytes; four partials are in flight together.
+// The order of the adds is fixed (own chunk, then the slots in order), so the
+// result is deterministic. The g heads of one (b, kv head, chunk) get work ids
+// that are equal modulo 8 (one XCD), so their K/V reads share that L2.
 // ---------------------------------------------------------------------------
+template <bool CAUSAL>
 __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   constexpr int D = 128;
-  constexpr int NP = 4;  // partials loaded together
-  const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t ri = (size_t)blockIdx.x * 32 + threadIdx.x / 8;
-  const int p = threadIdx.x & 7;
-  if (ri >= rows) return;
-  const int n = a.cmcnt[ri];
-  if (n == 0) return;  // the row was attended row-major
-  const size_t s0 = a.rslot[ri];
-  if ((long long)(s0 + n) > a.pool_cap) return;
+  constexpr int NP = 4;           // partials loaded together
+  constexpr int KROW = D + KPAD;  // staged K row (bf16)
+  constexpr int VROW = kChunk + VPAD;
+  constexpr int OROW = D + 4;     // own-chunk output row (fp32)
+  constexpr int kStageBytes = (kChunk * KROW + D * VROW) * 2;
+  constexpr int kOutBytes = kChunk * OROW * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[kStageBytes > kOutBytes ? kStageBytes : kOutBytes];
+  __shared__ float s_lse[kChunk];
+
+  const int g = a.g;
+  const int N = a.N;
+  const int nC = (N + kChunk - 1) / kChunk;
+  const int n_units = a.B * a.Hkv * nC;
+  const int idx = blockIdx.x;
+  const int grp8 = idx / (8 * g), rem = idx % (8 * g);
+  const int gh = rem / 8;
+  const int unit = grp8 * 8 + rem % 8;
+  if (unit >= n_units) return;
+  const int c = unit % nC;
+  const int bhk = unit / nC;
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const size_t bh = (size_t)b * a.Hq + hk * g + gh;
+  const int tile = c * kChunk / kTileRows;
+  if (a.counts[bh * a.n_tiles + tile] > 0) return;  // a row-major tile
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / kWave;
+  const int row0 = c * kChunk;
+  float* const sO = reinterpret_cast<float*>(s_raw);
+
+  if constexpr (CAUSAL) {
+    uint16_t* const sK = reinterpret_cast<uint16_t*>(s_raw);
+    uint16_t* const sV = sK + kChunk * KROW;
+    const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+    const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+    // wavefront w: rows row0 + 16 w + lane % 16; lanes l, l^16, l^32, l^48 share a row
+    const int rloc = 16 * w + (lane & 15);
+    const int qi = row0 + rloc;
+    const int q4 = lane >> 4;
+    const float lw = qi < N ? a.own_lw[bh * (size_t)N + qi] : -INFINITY;
+    bf16x8 qb[D / 32];  // Q^T as the B operand: column qi, dims 32 s + 8 q4 .. +7
+    {
+      const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(ldg16(qp + 32 * s));
+    }
+    {
+      // K rows (row-major) and V (transposed) of chunk c; keys past the sequence
+      // end read its last row (they lie in every row's future: masked)
+      const int k_row = tid >> 4, k_col = (tid & 15) * 8;
+      const int v_kg = tid & 15, v_dg = tid >> 4;
+      u32x4 kr[4], vr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        kr[r] = ldg16(Kb + (size_t)min(row0 + k_row + 16 * r, N - 1) * D + k_col);
+        vr[r] = ldg16(Vb + (size_t)min(row0 + 4 * v_kg + r, N - 1) * D + 8 * v_dg);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&sK[(k_row + 16 * r) * KROW + k_col]) = kr[r];
+      uint16_t* vt = &sV[(8 * v_dg) * VROW + 4 * v_kg];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x2 lo2 = {perm_lo(vr[0][e], vr[1][e]), perm_lo(vr[2][e], vr[3][e])};
+        u32x2 hi2 = {perm_hi(vr[0][e], vr[1][e]), perm_hi(vr[2][e], vr[3][e])};
+        *reinterpret_cast<u32x2*>(vt + (2 * e) * VROW) = lo2;
+        *reinterpret_cast<u32x2*>(vt + (2 * e + 1) * VROW) = hi2;
+      }
+    }
+    __syncthreads();
+    // ---- S^T = K Q^T: key block kb holds keys 16 kb + 4 q4 + r of row qi
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s)
+        sacc[kb] = mfma16x16x32(*reinterpret_cast<const bf16x8*>(&sK[(16 * kb + (lane & 15)) * KROW + 32 * s + 8 * q4]),
+                                qb[s], sacc[kb]);
+    }
+    // ---- causal mask inside the chunk, softmax in the exp2 domain with the bias
+    float smax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = 16 * kb + 4 * q4 + r <= rloc ? sacc[kb][r] : -INFINITY;
+        sacc[kb][r] = v;
+        smax = fmaxf(smax, v);
+      }
+    smax = max_xor32(max_xor16(smax));
+    const bool live = lw > -INFINITY;
+    const float sc = a.scale_log2;
+    const float m = live ? fmaf(smax, sc, lw) : 0.f;
+    const float off = live ? lw - m : -INFINITY;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], sc, off));
+        ls += sacc[kb][r];
+      }
+    const float l = sum_xor32(sum_xor16(ls));
+    // ---- O^T = V^T P^T. The k slots of step j are relabelled on both operands:
+    // slot e < 4 is key 32 j + 4 q4 + e, slot e >= 4 is key 32 j + 16 + 4 q4 + e - 4,
+    // which is how the S^T blocks 2j and 2j+1 already lie in this lane.
+    bf16x8 pb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pb[j] = as_bf16x8(u32x4{pack_bf16x2(sacc[2 * j][0], sacc[2 * j][1]), pack_bf16x2(sacc[2 * j][2], sacc[2 * j][3]),
+                              pack_bf16x2(sacc[2 * j + 1][0], sacc[2 * j + 1][1]),
+                              pack_bf16x2(sacc[2 * j + 1][2], sacc[2 * j + 1][3])});
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint16_t* vrow = &sV[(16 * db + (lane & 15)) * VROW + 32 * j + 4 * q4];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+        oacc[db] = mfma16x16x32(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb[j], oacc[db]);
+      }
+    }
+    __syncthreads();  // every wavefront is done with the staged K and V
+    // row rloc, dims 16 db + 4 q4 + r, normalised
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<f32x4*>(&sO[rloc * OROW + 16 * db + 4 * q4]) =
+          f32x4{oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    if (q4 == 0) s_lse[rloc] = l > 0.f ? m + fast_log2(l) : -INFINITY;
+    __syncthreads();
+  }
+
+  // ---- merge, 32 rows per pass
   auto max8 = [](float x) {
     x = fmaxf(x, dpp_f<kDppXor1>(x));
     x = fmaxf(x, dpp_f<kDppXor2>(x));
@@ -575,63 +728,90 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
     x += dpp_f<kDppXor2>(x);
     return x + dpp_f<kDppHalfMirror>(x);
   };
-  // the first partials' loads go out before the weights are known
-  float lse[NP];
-  u32x4 v[NP][2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int x = 0; x < NP; ++x) {
-      const size_t sl = s0 + min(k0 + x, n - 1);
-      lse[x] = a.plse[sl];
-      v[x][0] = ldg16(a.po + sl * D + 8 * p);
-      v[x][1] = ldg16(a.po + sl * D + 64 + 8 * p);
-    }
-  };
-  load(0);
-  float lp = p < n ? a.plse[s0 + p] : -INFINITY;
-  for (int k = p + 8; k < n; k += 8) lp = fmaxf(lp, a.plse[s0 + k]);
-  const float M = max8(lp);
-  float L = 0.f;
-  if (M > -INFINITY)
-    for (int k = p; k < n; k += 8) L += fast_exp2(a.plse[s0 + k] - M);
-  L = sum8(L);
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-  if (L > 0.f) {
-    for (int k0 = 0; k0 < n; k0 += NP) {
-      if (k0 > 0) load(k0);
+  const int p = tid & 7;
+#pragma unroll 1
+  for (int pass = 0; pass < kChunk / 32; ++pass) {
+    const int rloc = pass * 32 + tid / 8;
+    const int qi = row0 + rloc;
+    if (qi >= N) break;  // uniform over the row's eight lanes; later passes are further out
+    const size_t ri = bh * (size_t)N + qi;
+    int n = a.cmcnt[ri];
+    const size_t s0 = a.rslot[ri];
+    if ((long long)(s0 + n) > a.pool_cap) n = 0;
+    const float lse_o = CAUSAL ? s_lse[rloc] : -INFINITY;
+    float lse[NP];
+    u32x4 v[NP][2];
+    auto load = [&](int k0) {
 #pragma unroll
       for (int x = 0; x < NP; ++x) {
-        const float wt = k0 + x < n ? fast_exp2(lse[x] - M) * inv : 0.f;
+        const size_t sl = s0 + min(k0 + x, max(n - 1, 0));
+        lse[x] = a.plse[sl];
+        v[x][0] = ldg16(a.po + sl * D + 8 * p);
+        v[x][1] = ldg16(a.po + sl * D + 64 + 8 * p);
+      }
+    };
+    if (n > 0) load(0);
+    float lp = p < n ? a.plse[s0 + p] : -INFINITY;
+    for (int k = p + 8; k < n; k += 8) lp = fmaxf(lp, a.plse[s0 + k]);
+    const float M = fmaxf(max8(lp), lse_o);
+    float L = 0.f;
+    if (M > -INFINITY)
+      for (int k = p; k < n; k += 8) L += fast_exp2(a.plse[s0 + k] - M);
+    L = sum8(L);
+    const float wo = (M > -INFINITY && lse_o > -INFINITY) ? fast_exp2(lse_o - M) : 0.f;
+    L += wo;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float acc[16];
+    {
+      const float wt = wo * inv;
+      const f32x4* orow = reinterpret_cast<const f32x4*>(&sO[rloc * OROW]);
 #pragma unroll
-        for (int hv = 0; hv < 2; ++hv)
+      for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t u = v[x][hv][e];
-            acc[8 * hv + 2 * e] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu)), wt, acc[8 * hv + 2 * e]);
-            acc[8 * hv + 2 * e + 1] = fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)), wt, acc[8 * hv + 2 * e + 1]);
-          }
+        for (int e = 0; e < 2; ++e) {
+          const f32x4 x = CAUSAL ? orow[(64 * hv + 8 * p) / 4 + e] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[8 * hv + 4 * e + k] = x[k] * wt;
+        }
+    }
+    if (L > 0.f) {
+      for (int k0 = 0; k0 < n; k0 += NP) {
+        if (k0 > 0) load(k0);
+#pragma unroll
+        for (int x = 0; x < NP; ++x) {
+          const float wt = k0 + x < n ? fast_exp2(lse[x] - M) * inv : 0.f;
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t u = v[x][hv][e];
+              acc[8 * hv + 2 * e] = fmaf(f16lo(u), wt, acc[8 * hv + 2 * e]);
+              acc[8 * hv + 2 * e + 1] = fmaf(f16hi(u), wt, acc[8 * hv + 2 * e + 1]);
+            }
+        }
       }
     }
-  }
 #pragma unroll
-  for (int hv = 0; hv < 2; ++hv) {
-    u32x4 out;
+    for (int hv = 0; hv < 2; ++hv) {
+      u32x4 out;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
-    *reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv) = out;
+      for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
+      *reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv) = out;
+    }
   }
 }
 
 hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_cm_plan, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(k_cm_plan, dim3((a.n_bhc + 255) / 256), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_cm_scatter, dim3(a.n_tiles, a.Hq, a.B), dim3(256), 0, stream, a);
   const long long cm_grid = std::min<long long>(a.max_items, (long long)a.n_cu * kCmWgPerCu);
   hipLaunchKernelGGL(k_prefill_cm<128>, dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
-  const long long rows = (long long)a.B * a.Hq * a.N;
-  hipLaunchKernelGGL(k_prefill_merge, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, a);
+  const int m_units = a.B * a.Hkv * ((a.N + kChunk - 1) / kChunk);
+  const unsigned merge_grid = (unsigned)((m_units + 7) / 8) * 8 * a.g;
+  if (a.causal)
+    hipLaunchKernelGGL(k_prefill_merge<true>, dim3(merge_grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_prefill_merge<false>, dim3(merge_grid), dim3(256), 0, stream, a);
   // row-major fallback for tiles without pool slots (a persistent grid that
   // skips every other tile)
   const int n_units = a.n_tiles * a.B * a.Hkv;
