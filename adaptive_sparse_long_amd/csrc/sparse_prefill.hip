@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
         // order. Each 64-dim half passes through this wavefront's LDS rows, so
         // that every store instruction writes whole 128-byte lines.
         const uint32_t slot = valid ? (uint32_t)rec[i].y : 0u;
-        if (valid && hi32 == 0) a.plse[slot] = l > 0.f ? m + fast_log2(l) : -INFINITY;
+        if (valid && hi32 == 0) __builtin_nontemporal_store(l > 0.f ? m + fast_log2(l) : -INFINITY, a.plse + slot);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t* so = sO[w];
 #pragma unroll
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
             const u32x4 v = *reinterpret_cast<const u32x4*>(so + rr * OROW + 8 * c16);
             const int vr = __shfl((int)valid, rr);
             const size_t sr = (uint32_t)__shfl((int)slot, rr);
-            if (vr) *reinterpret_cast<u32x4*>(a.po + sr * D + 64 * half + 8 * c16) = v;
+            if (vr) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.po + sr * D + 64 * half + 8 * c16));
           }
           wave_lds_fence();
         }
@@ -576,7 +576,9 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
 //     64+8p .. 64+8p+7, so every load instruction of the eight lanes reads 128
 //     contiguous bytes; four partials are in flight together.
 // The order of the adds is fixed (own chunk, then the slots in order), so the
-// result is deterministic. The g heads of one (b, kv head, chunk) get work ids
+// result is deterministic. Partials are written and read once: their stores
+// and loads are non-temporal, so they do not displace the query rows and
+// chunks that the caches can still serve. The g heads of one (b, kv head, chunk) get work ids
 // that are equal modulo 8 (one XCD), so their K/V reads share that L2.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
@@ -745,9 +747,9 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
 #pragma unroll
       for (int x = 0; x < NP; ++x) {
         const size_t sl = s0 + min(k0 + x, max(n - 1, 0));
-        lse[x] = a.plse[sl];
-        v[x][0] = ldg16(a.po + sl * D + 8 * p);
-        v[x][1] = ldg16(a.po + sl * D + 64 + 8 * p);
+        lse[x] = __builtin_nontemporal_load(a.plse + sl);
+        v[x][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.po + sl * D + 8 * p));
+        v[x][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.po + sl * D + 64 + 8 * p));
       }
     };
     if (n > 0) load(0);
@@ -796,7 +798,7 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
       u32x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
-      *reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv) = out;
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv));
     }
   }
 }
