@@ -239,33 +239,48 @@ __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
   }
 }
 
-// dcls[h] = sum over b and chunks of the partial rows. Thread t reads dims
-// 4 (t % 32) .. +3 (one float4) of the rows r = t / 32, t / 32 + 32, ... (32
-// streams, loads unrolled so several are in flight); the streams are then added
-// in order through LDS (deterministic).
+// dcls[h] = sum over b and chunks of the partial rows, in two levels with a
+// fixed partition (so the result is deterministic):
+//   1. workgroup (j, h, b) adds the partial rows of chunks [j R, (j+1) R) of
+//      (b, h) -- 8 row streams x 32 float4 columns, the streams then added in
+//      order through LDS -- and writes the sum over the first row of its range
+//      (a row only it reads, read before it is written);
+//   2. workgroup h adds those range sums in (b, j) order.
+constexpr int kRedRows = 256;  // partial rows per first-level workgroup
+
 template <int D>
-__global__ __launch_bounds__(1024) void k_summarize_bwd_reduce(SummarizeBwdArgs a) {
-  constexpr int kCols = D / 4;            // float4 columns per row
-  constexpr int kStreams = 1024 / kCols;  // row streams
+__global__ __launch_bounds__(256) void k_summarize_bwd_reduce1(SummarizeBwdArgs a) {
+  constexpr int kCols = D / 4;           // float4 columns per row
+  constexpr int kStreams = 256 / kCols;  // row streams
   __shared__ f32x4 s_acc[kStreams][kCols];
-  const int h = blockIdx.x;
+  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int q = threadIdx.x % kCols;
   const int st = threadIdx.x / kCols;
   const int n_chunks = a.chunk_end - a.chunk_begin;
+  const int c0 = j * kRedRows, c1 = min(n_chunks, c0 + kRedRows);
+  f32x4* rows = reinterpret_cast<f32x4*>(a.partials + ((size_t)b * a.Hkv + h) * n_chunks * D);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < a.B; ++b) {
-    const f32x4* rows = reinterpret_cast<const f32x4*>(a.partials + ((size_t)b * a.Hkv + h) * n_chunks * D) + q;
 #pragma unroll 4
-    for (int c = st; c < n_chunks; c += kStreams) acc += rows[(size_t)c * kCols];
-  }
+  for (int c = c0 + st; c < c1; c += kStreams) acc += rows[(size_t)c * kCols + q];
   s_acc[st][q] = acc;
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int dq = threadIdx.x / 4, e = threadIdx.x % 4;
-    float t = 0.f;
-    for (int i = 0; i < kStreams; ++i) t += s_acc[i][dq][e];
-    a.dcls[(size_t)h * D + threadIdx.x] = t;
+  if (threadIdx.x < kCols) {
+    f32x4 t = s_acc[0][threadIdx.x];
+    for (int i = 1; i < kStreams; ++i) t += s_acc[i][threadIdx.x];
+    rows[(size_t)c0 * kCols + threadIdx.x] = t;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void k_summarize_bwd_reduce2(SummarizeBwdArgs a) {
+  const int h = blockIdx.x;
+  const int n_chunks = a.chunk_end - a.chunk_begin;
+  float t = 0.f;
+  for (int b = 0; b < a.B; ++b) {
+    const float* rows = a.partials + ((size_t)b * a.Hkv + h) * n_chunks * D + threadIdx.x;
+    for (int c0 = 0; c0 < n_chunks; c0 += kRedRows) t += rows[(size_t)c0 * D];
+  }
+  a.dcls[(size_t)h * D + threadIdx.x] = t;
 }
 
 hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream) {
@@ -273,8 +288,10 @@ hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream) {
   if (n > 0) {
     dim3 grid((n + 3) / 4, a.Hkv, a.B);
     hipLaunchKernelGGL(k_summarize_bwd<128>, grid, dim3(256), 0, stream, a);
+    dim3 g1((n + kRedRows - 1) / kRedRows, a.Hkv, a.B);
+    hipLaunchKernelGGL(k_summarize_bwd_reduce1<128>, g1, dim3(256), 0, stream, a);
   }
-  hipLaunchKernelGGL(k_summarize_bwd_reduce<128>, dim3(a.Hkv), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(k_summarize_bwd_reduce2<128>, dim3(a.Hkv), dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ from adaptive_sparse_long_amd.workloads import (  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 C = 64
+FLUSH_BYTES = 512 * 1024 * 1024  # twice the Infinity Cache
 CSRC = os.path.join(ROOT, "adaptive_sparse_long_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources each kernel's code depends on (a changed source voids its measured traffic).
@@ -179,7 +180,7 @@ def route_alg_bytes(w, pairs):
                  + w.B * w.Hq * w.N * 4 + pairs * 8)
 
 
-def bench_prefill(w, steps, warmup):
+def bench_prefill(w, steps, warmup, summary_backward=True):
     dev = torch.device("cuda")
     Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device=dev)
     p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
@@ -189,8 +190,11 @@ def bench_prefill(w, steps, warmup):
     O = torch.empty_like(Q)
     n_sum = w.N // C if w.causal else n_c
     t_sum, t_route, t_attn = Timer(), Timer(), Timer()
+    # the Infinity Cache (256 MB) is evicted before every step, outside the timed events
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
 
     def step(timed):
+        flush.zero_()
         e = t_sum.start() if timed else None
         api.summarize(K, cls, S, n_tokens=w.N, chunk_begin=0, chunk_end=n_sum, params=p)
         if timed:
@@ -206,15 +210,28 @@ def bench_prefill(w, steps, warmup):
 
     for _ in range(warmup):
         step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
+    del flush
     # work counts (outside the timed region)
     _, bits, _ = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
     alg, pair, dense, scores, per_row = prefill_work(bits, w.N, w.d)
+    res = {
+        "ms_summarize": t_sum.mean_ms(),
+        "ms_route": t_route.mean_ms(),
+        "ms_attention": t_attn.mean_ms(),
+        "alg_flops": alg,
+        "pair_flops": pair,
+        "dense_causal_flops": dense,
+        "route_scores": scores,
+        "routed_chunks_per_row": per_row,
+        "pairs": per_row * w.B * w.Hq * w.N,
+    }
+    if not summary_backward:
+        del Q, K, V, S, ws, O, bits
+        torch.cuda.empty_cache()
+        return res
     # summary backward on the same keys (gradients of the summaries for a random
     # cotangent into dK and head_cls), outside the step
     dS = cotangent((w.B, w.Hkv, n_c, w.d), w.seed + 700, dtype="f32", device=dev)
@@ -231,21 +248,9 @@ def bench_prefill(w, steps, warmup):
     # algorithmic bytes: K read (bf16), dK written (fp32), dS read, dcls partials written and read
     sb_bytes = float(w.B * w.Hkv * n_sum * C * w.d * (2 + 4) + w.B * w.Hkv * n_sum * w.d * 4 * 3)
     del dS, bufs
-    res = {
-        "wall_ms": wall * 1e3,
-        "ms_summarize": t_sum.mean_ms(),
-        "summary_backward": {"us": ms_sb * 1e3, "bytes_per_launch": sb_bytes,
-                             "GBps": sb_bytes / (ms_sb / 1e3) / 1e9,
-                             "frac": sb_bytes / (ms_sb / 1e3) / 1e9 / PEAK_HBM_GBS},
-        "ms_route": t_route.mean_ms(),
-        "ms_attention": t_attn.mean_ms(),
-        "alg_flops": alg,
-        "pair_flops": pair,
-        "dense_causal_flops": dense,
-        "route_scores": scores,
-        "routed_chunks_per_row": per_row,
-        "pairs": per_row * w.B * w.Hq * w.N,
-    }
+    res["summary_backward"] = {"us": ms_sb * 1e3, "bytes_per_launch": sb_bytes,
+                               "GBps": sb_bytes / (ms_sb / 1e3) / 1e9,
+                               "frac": sb_bytes / (ms_sb / 1e3) / 1e9 / PEAK_HBM_GBS}
     del Q, K, V, S, ws, O, bits
     torch.cuda.empty_cache()
     return res
@@ -263,7 +268,7 @@ def bench_decode(w, steps, warmup):
     O = torch.empty_like(q)
     lengths = [int(x) for x in seqlens.cpu()]
     # Infinity Cache (256 MB) holds the whole summary cache; evict it between steps
-    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     t_route, t_attn, t_step = Timer(), Timer(), Timer()
 
     def step(timed):
@@ -364,6 +369,26 @@ def bench_entmax(w, steps, warmup):
                      "traffic": _sum_or_none([measured_traffic("k_entmax_bwd_dq"),
                                               measured_traffic("k_entmax_bwd_dkdv")])},
     }
+
+
+def bench_entmax_small(w, steps, warmup):
+    """The 128-token float32 dense entmax attention: HIP-event time per call
+    (the whole entmax_attn call, launch included) over many back-to-back calls."""
+    q, k, v, _ = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype=w.dtype, device="cuda")
+    for _ in range(warmup):
+        api.entmax_attn(q, k, v, alpha=w.alpha, causal=w.causal)
+    reps = max(steps, 50)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        api.entmax_attn(q, k, v, alpha=w.alpha, causal=w.causal)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    flops = 2.0 * w.d * w.N * (w.N + 1) / 2.0 * 2 * w.B * w.Hq  # QK^T and PV over the causal triangle
+    return {"workload": w.name, "us_per_call": us, "calls": reps, "causal_flops": flops}
 
 
 def bench_entmax_rows(w, steps, warmup):
@@ -471,6 +496,77 @@ def cpu_baseline(w, budget_s=20.0):
     }
 
 
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = threadpool_info()
+        return [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")} for i in info]
+    except Exception:  # pragma: no cover
+        return []
+
+
+def oracle_timings():
+    """The float64 oracle on the other workloads (host cores; reported beside the
+    GPU figures, not targets): the 128-token entmax attention and the 4K routed
+    prefill in full, the varlen entmax workload and the batch-16 decode step on
+    bounded samples scaled to the whole workload (the sample is stated)."""
+    import oracle
+
+    out = {"numpy": np.__version__, "blas": _blas_info(), "host_cpus": os.cpu_count()}
+    # 1: dense entmax, 128 tokens, float32 inputs
+    w1 = WORKLOADS["dense_entmax_128"]
+    q, k, v, _ = dense_entmax_inputs(w1.B, w1.Hq, w1.N, w1.d, w1.seed, dtype=w1.dtype, device="cpu")
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        oracle.entmax_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(), w1.alpha, w1.causal)
+    out["dense_entmax_128"] = {"us_per_call": (time.perf_counter() - t0) / reps * 1e6, "sample": "full, 20 calls"}
+    # 2: routed prefill 4K, every head
+    w2 = WORKLOADS["routed_prefill_4k"]
+    Q, K, V, cls = routed_prefill_inputs(w2.B, w2.Hq, w2.Hkv, w2.N, w2.d, w2.seed, planted=w2.planted, device="cpu")
+    op = oracle.DashParams(chunk_size=C, alpha=w2.alpha, causal=w2.causal, estimate_diagonal=w2.estimate_diagonal)
+    t0 = time.perf_counter()
+    oracle.dash_prefill(Q.double().numpy(), K.double().numpy(), V.double().numpy(), cls.double().numpy(), op)
+    el = time.perf_counter() - t0
+    out["routed_prefill_4k"] = {"s": el, "tokens_per_s": w2.N / el, "sample": "full (32 heads, 4096 rows)"}
+    del Q, K, V, cls
+    # 5: varlen entmax, one sampled block of 64 rows in each of 8 (b, h) pairs, scaled by rows
+    w5 = WORKLOADS["varlen_entmax"]
+    q, k, v, lens = dense_entmax_inputs(w5.B, w5.Hq, w5.N, w5.d, w5.seed, dtype=w5.dtype, scale=w5.scale,
+                                        varlen_range=w5.varlen_range, device="cpu")
+    rng = np.random.default_rng(w5.seed)
+    L = lens.numpy()
+    rows_done, t0 = 0, time.perf_counter()
+    for _ in range(8):
+        b, h = int(rng.integers(0, w5.B)), int(rng.integers(0, w5.Hq))
+        r0 = int(rng.integers(0, max(1, L[b] - 64)))
+        pos = np.arange(r0, min(L[b], r0 + 64))
+        oracle.entmax_attention_rows(q[b, h, pos].double().numpy(), pos, k[b, h].double().numpy(),
+                                     v[b, h].double().numpy(), int(L[b]), w5.alpha, w5.causal)
+        rows_done += pos.size
+    el = time.perf_counter() - t0
+    total_rows = float(L.sum()) * w5.Hq
+    out["varlen_entmax"] = {"s_extrapolated": el / rows_done * total_rows,
+                            "tokens_per_s": float(L.sum()) / (el / rows_done * total_rows),
+                            "sample": f"{rows_done} rows (8 blocks of 64) of {int(total_rows)}, {el:.1f} s"}
+    del q, k, v
+    # 4: decode step, one (b, kv head) group of 4 query heads, scaled by the 128 groups
+    w4 = WORKLOADS["decode_128k"]
+    g = w4.Hq // w4.Hkv
+    qd, Kc, Vc, clsd, seqlens = decode_inputs(1, g, 1, w4.N, w4.d, w4.seed, device="cpu")
+    op4 = oracle.DashParams(chunk_size=C, alpha=w4.alpha, causal=True, estimate_diagonal=w4.estimate_diagonal)
+    t0 = time.perf_counter()
+    oracle.dash_decode(qd[:, :, 0].double().numpy(), Kc.float().numpy(), Vc.float().numpy(), clsd.double().numpy(),
+                       seqlens.numpy(), op4)
+    el = time.perf_counter() - t0
+    groups = w4.B * w4.Hkv
+    out["decode_128k"] = {"us_per_step_extrapolated": el * groups * 1e6,
+                          "sample": f"one (b, kv head) group of {g} query heads over {w4.N + 1} tokens, "
+                                    f"{el:.1f} s, x {groups} groups"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -479,6 +575,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-entmax", action="store_true")
+    ap.add_argument("--no-4k", action="store_true", help="skip the 4K routed prefill workload")
+    ap.add_argument("--no-oracle-timings", action="store_true",
+                    help="skip the oracle timings of the other workloads (the cpu_baseline leg stays)")
     ap.add_argument("--sparsity", action="store_true",
                     help="only the measured-sparsity sweep (alpha x scaling_factor) on the 32K needle workload")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -498,8 +597,8 @@ def main():
     wp = WORKLOADS["routed_prefill_32k"]
     log(f"prefill {wp.name}: steps={args.steps} warmup={args.warmup}")
     pre = bench_prefill(wp, args.steps, args.warmup)
-    log(f"prefill done: {pre['wall_ms']:.3f} ms/step")
     ms_step = pre["ms_summarize"] + pre["ms_route"] + pre["ms_attention"]
+    log(f"prefill done: {ms_step:.3f} ms/step")
     value = wp.N / (ms_step / 1e3)
     # Dominant work: the sparse attention call (two thirds of the step; its
     # k_prefill_cm is the longest kernel), timed with HIP events around the whole
@@ -562,10 +661,9 @@ def main():
         },
         "prefill": {
             "ms_summarize": pre["ms_summarize"], "ms_route": pre["ms_route"], "ms_attention": pre["ms_attention"],
-            "wall_ms_per_step": pre["wall_ms"],
             "routed_chunks_per_row": pre["routed_chunks_per_row"],
+            # algorithmic attention flops over those of dense causal attention
             "alg_over_dense": pre["alg_flops"] / pre["dense_causal_flops"],
-            "dense_equiv_tflops": pre["dense_causal_flops"] / (ms_step / 1e3) / 1e12,
             # sparse attention (dash_sparse_attn_prefill, all of its kernels): MFMA
             # rate on the executed (row, chunk) pair blocks and on the algorithmic work
             "attention_pair_tflops": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12,
@@ -578,6 +676,21 @@ def main():
         },
         "roofline": roof,
     }
+    if not args.no_4k:
+        w2 = WORKLOADS["routed_prefill_4k"]
+        log("prefill 4k")
+        p2 = bench_prefill(w2, args.steps, args.warmup, summary_backward=False)
+        ms2 = p2["ms_summarize"] + p2["ms_route"] + p2["ms_attention"]
+        out["prefill_4k"] = {
+            "workload": w2.name, "tokens_per_s": w2.N / (ms2 / 1e3), "ms_per_step": ms2,
+            "ms_summarize": p2["ms_summarize"], "ms_route": p2["ms_route"], "ms_attention": p2["ms_attention"],
+            "routed_chunks_per_row": p2["routed_chunks_per_row"],
+            "alg_flops": p2["alg_flops"], "pair_flops": p2["pair_flops"], "dense_causal_flops": p2["dense_causal_flops"],
+            "attention_alg_frac": p2["alg_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attention_pair_frac": p2["pair_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        }
+    if not args.no_entmax:
+        out["dense_entmax_128"] = bench_entmax_small(WORKLOADS["dense_entmax_128"], args.steps, args.warmup)
     if not args.no_decode:
         wd = WORKLOADS["decode_128k"]
         log("decode 128k")
@@ -595,6 +708,9 @@ def main():
                 "kernel": "k_sparse_decode", "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("k_sparse_decode"),
                 "bytes_per_launch": dec["kv_bytes"],
+                # the whole step (routing against the summary cache, attention, append)
+                "step_bytes": step_bytes,
+                "step_frac": step_bytes / (dec["us_per_step"] / 1e6) / 1e9 / PEAK_HBM_GBS,
             },
         }
     if not args.no_entmax:
@@ -619,6 +735,11 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(wp)
+        out["cpu_baseline"]["numpy"] = np.__version__
+        out["cpu_baseline"]["blas"] = _blas_info()
+        if not args.no_oracle_timings:
+            log("oracle timings of the other workloads")
+            out["oracle_timings"] = oracle_timings()
     print(json.dumps(out), flush=True)
 
 
