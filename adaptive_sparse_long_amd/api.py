@@ -35,6 +35,7 @@ __all__ = [
     "entmax_fn",
     "prefill",
     "decode_step",
+    "decode_step_noalloc",
 ]
 
 CHUNK = 64
@@ -197,6 +198,37 @@ def sparse_attn_decode(q, Kc, Vc, seqlens, workspace, params: Params = Params(),
                                      params.c(), _p(out), _p(workspace), workspace.numel(), _stream(q.device))
     _lib.check(st, "dash_sparse_attn_decode")
     return out
+
+
+def decode_step_noalloc(q, Kc, Vc, head_cls, S, seqlens, params: Params = Params(), with_bits=True, out=None):
+    """One decode step (routing against the summary cache, then attention over the
+    routed chunks) through ``dash_decode_step_noalloc``: the library's own static
+    scratch replaces the workspace, so the call allocates no device memory apart
+    from the outputs made here when ``out`` is None. ``out`` = (O, tau, bits or
+    None) reuses caller tensors. Calls that overlap on one GPU race for the
+    scratch. Returns (O, tau, bits). Appending completed chunks stays with the
+    caller (``summarize`` with ``seqlens``)."""
+    lib = _lib.load()
+    _need(q, "q", dim=4)
+    _need(Kc, "Kc", q.dtype, 4)
+    _need(Vc, "Vc", q.dtype, 4)
+    _need(head_cls, "head_cls", q.dtype, 2)
+    _need(S, "S", torch.float32, 4)
+    _need(seqlens, "seqlens", torch.int32, 1)
+    B, Hq, _, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    words = -(-(-(-Lmax // CHUNK)) // 32)
+    if out is None:
+        O = torch.empty_like(q)
+        tau = torch.empty(B, Hq, 1, dtype=torch.float32, device=q.device)
+        bits = torch.empty(B, Hq, 1, words, dtype=torch.int32, device=q.device) if with_bits else None
+    else:
+        O, tau, bits = out
+    st = lib.dash_decode_step_noalloc(_p(q), _p(Kc), _p(Vc), _p(head_cls), _p(S), _dt(q), B, Hq, Hkv, _p(seqlens),
+                                      Lmax, d, S.shape[2], params.c(), _p(O), _p(tau), _p(bits), words,
+                                      _stream(q.device))
+    _lib.check(st, "dash_decode_step_noalloc")
+    return O, tau, bits
 
 
 def entmax_attn(Q, K, V, alpha=1.5, n_iter=10, causal=True, varlen=None, with_mask=True):

@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 using namespace dash;
@@ -37,6 +39,30 @@ int device_cus() {
 
 // Pool slots are addressed with 32 bits.
 bool prefill_pool_fits(int B, int Hq, int N) { return (long long)B * Hq * N * kCmSlots < (1ll << 32); }
+
+// Scratch of the allocation-free decode step: a file-scope device array (each
+// GPU holds its own copy from the time the library is loaded until the process
+// ends). Host code never uses the array's name as an address: its device
+// address is looked up once per device (hipGetSymbolAddress, with the device
+// current) and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dash_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DASH_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DASH_OK;
+}
 
 }  // namespace
 
@@ -270,6 +296,37 @@ dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* V
   a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
   a.part = reinterpret_cast<float*>(ws + L.off_part);
   return from_hip(launch_sparse_decode(a, stream));
+}
+
+size_t dash_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+dash_status dash_decode_step_noalloc(const void* Q, const void* Kc, const void* Vc, const void* head_cls,
+                                     const float* S, dash_dtype dt, int B, int Hq, int Hkv,
+                                     const int* seqlens, int Lmax, int d, int s_cap, dash_params p,
+                                     void* O, float* tau, uint32_t* active_bits, int bits_words,
+                                     hipStream_t stream) {
+  if (!Q || !Kc || !Vc || !head_cls || !S || !seqlens || !O || !tau) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || Lmax <= 0 || d <= 0 || s_cap <= 0 || !gqa_ok(Hq, Hkv)) return DASH_ERR_INVALID_ARG;
+  const size_t need = dash_workspace_size(B, Hq, Hkv, 1, Lmax, d, 1, p);
+  if (need == 0) return DASH_ERR_INVALID_ARG;
+  if (need > kNoAllocScratchBytes) return DASH_ERR_WORKSPACE;  // beyond the static scratch
+  // the same host checks as the two calls below, before anything is launched
+  dash_status st = check_params(p);
+  if (st != DASH_OK) return st;
+  if (p.causal != 1) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 || d != 128 || !g_supported(Hq / Hkv)) return DASH_ERR_UNSUPPORTED;
+  if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete) return DASH_ERR_UNSUPPORTED;
+  if (s_cap < (Lmax - 1) / kChunk) return DASH_ERR_INVALID_ARG;
+  if (active_bits && bits_words < (decode_layout(B, Hq, Hkv, Lmax, d).n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != DASH_OK) return st;
+  st = dash_route(Q, Kc, head_cls, S, dt, B, Hq, Hkv, 1, Lmax, d, s_cap, seqlens, p, tau, active_bits,
+                  bits_words, ws, kNoAllocScratchBytes, stream);
+  if (st != DASH_OK) return st;
+  return dash_sparse_attn_decode(Q, Kc, Vc, dt, B, Hq, Hkv, seqlens, Lmax, d, p, O, ws, kNoAllocScratchBytes,
+                                 stream);
 }
 
 dash_status entmax_attn(const void* Q, const void* K, const void* V, dash_dtype dt, int B, int H,

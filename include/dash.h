@@ -13,9 +13,10 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a device pointer owned by the caller (for example
  *     a torch tensor's data_ptr()). The library never allocates device memory
- *     and keeps no state between calls except cached device properties, so
- *     calls are thread safe; calls that share a workspace must be ordered by
- *     the caller (same stream).
+ *     and keeps no state between calls except cached device properties and the
+ *     one static scratch array of dash_decode_step_noalloc, so calls are
+ *     thread safe; calls that share a workspace (or that scratch array) must be
+ *     ordered by the caller (same stream).
  *   - Tensors are contiguous row-major. q/k/v use [batch, heads, seq, head_dim]
  *     ("Usage" of both pages); head_cls is [kv_heads, head_dim].
  *   - Work is enqueued on `stream` (NULL = the null stream); nothing
@@ -199,6 +200,36 @@ dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* V
                                     const int* seqlens, int Lmax, int d, dash_params p,
                                     void* O, void* workspace, size_t ws_bytes,
                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * dash_decode_step_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): one decode step, exactly dash_route in decode mode followed by
+ * dash_sparse_attn_decode (same kernels, same results), with the workspace
+ * taken from a scratch array that the library holds in device memory instead
+ * of a caller buffer.
+ *   Q, Kc, Vc, head_cls, S, seqlens, Lmax, s_cap, p: as for dash_route
+ *   (decode mode, causal = 1) and dash_sparse_attn_decode.
+ *   O [B, Hq, 1, d], tau [B, Hq, 1], active_bits (NULL or [B, Hq, 1,
+ *   bits_words]): the outputs of those two calls.
+ * The scratch holds dash_decode_noalloc_max_bytes() bytes (64 MiB) on every
+ * GPU the library runs on, from the time it is loaded until the process ends;
+ * sizes whose dash_workspace_size(B, Hq, Hkv, 1, Lmax, d, 1, p) exceeds it
+ * return DASH_ERR_WORKSPACE before anything is launched. Nothing is allocated:
+ * no hipMalloc/hipFree, on any call. Every call on one GPU uses that GPU's one
+ * scratch array, so calls that overlap on one GPU (different streams or host
+ * threads without ordering) race; calls ordered on one stream are safe. The
+ * first call on a device looks up the scratch address (hipGetSymbolAddress)
+ * with that device current. Errors: as dash_route and dash_sparse_attn_decode.
+ * --------------------------------------------------------------------------- */
+dash_status dash_decode_step_noalloc(const void* Q, const void* Kc, const void* Vc,
+                                     const void* head_cls, const float* S, dash_dtype dt, int B,
+                                     int Hq, int Hkv, const int* seqlens, int Lmax, int d,
+                                     int s_cap, dash_params p, void* O, float* tau,
+                                     uint32_t* active_bits, int bits_words, hipStream_t stream);
+
+/* Size in bytes of the scratch array dash_decode_step_noalloc uses. */
+size_t dash_decode_noalloc_max_bytes(void);
 
 /* ---------------------------------------------------------------------------
  * entmax_attn -- dense alpha-entmax attention with block skipping (AdaSplash

@@ -27,6 +27,7 @@ def test_header_symbols_exported(lib):
         "dash_default_params", "dash_status_string", "dash_summarize", "dash_workspace_size",
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
         "entmax_rows", "entmax_rows_backward", "entmax_attn_backward", "dash_summarize_backward",
+        "dash_decode_step_noalloc", "dash_decode_noalloc_max_bytes",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -178,3 +179,25 @@ def test_summarize_backward_validation(lib):
     assert f(*F3, 0, 1, 2, 256, 128, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
     assert f(*F3, 1, 1, 2, 256, 64, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
     assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 4, 4, _lib.params(chunk_size=32), *F3, NULL) == UNSUPPORTED
+
+
+def test_decode_noalloc_validation(lib):
+    """The allocation-free decode step checks its arguments on the host: NULL
+    pointers, bad sizes and sizes beyond its static scratch are refused before
+    any HIP call (so this runs without a GPU)."""
+    cap = int(lib.dash_decode_noalloc_max_bytes())
+    assert cap == 64 << 20
+    p = _p()
+    P = ctypes.c_void_p(16)  # never dereferenced: every case fails on the host
+    # NULL q
+    assert lib.dash_decode_step_noalloc(None, P, P, P, P, 1, 16, 32, 8, P, 131073, 128, 2048, p, P, P, None, 0, None) == 1
+    # Hq not a multiple of Hkv
+    assert lib.dash_decode_step_noalloc(P, P, P, P, P, 1, 16, 30, 8, P, 131073, 128, 2048, p, P, P, None, 0, None) == 1
+    # the 128K batch-16 decode fits the scratch ...
+    assert lib.dash_workspace_size(16, 32, 8, 1, 131073, 128, 1, p) <= cap
+    # ... batch 64 at 256K does not
+    assert lib.dash_workspace_size(64, 32, 8, 1, 262145, 128, 1, p) > cap
+    assert lib.dash_decode_step_noalloc(P, P, P, P, P, 1, 64, 32, 8, P, 262145, 128, 4096, p, P, P, None, 0, None) == 3
+    # non-causal decode is refused
+    assert lib.dash_decode_step_noalloc(P, P, P, P, P, 1, 2, 8, 2, P, 1024, 128, 16, _p(causal=False), P, P, None, 0,
+                                        None) == 1
