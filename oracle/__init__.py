@@ -33,6 +33,7 @@ from .dash import (
     dash_rows,
     dash_prefill,
     dash_decode,
+    dash_backward,
 )
 from .entmax_attention import entmax_attention, entmax_attention_rows, entmax_attention_backward
 
@@ -49,6 +50,7 @@ __all__ = [
     "dash_rows",
     "dash_prefill",
     "dash_decode",
+    "dash_backward",
     "entmax_attention",
     "entmax_attention_rows",
     "entmax_attention_backward",

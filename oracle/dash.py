@@ -45,7 +45,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .entmax import entmax_threshold_rows
+from .entmax import entmax_backward, entmax_threshold_rows
 
 __all__ = [
     "DashParams",
@@ -55,6 +55,7 @@ __all__ = [
     "dash_rows",
     "dash_prefill",
     "dash_decode",
+    "dash_backward",
 ]
 
 
@@ -262,3 +263,110 @@ def dash_decode(q, Kc, Vc, head_cls, seqlens, p: DashParams):
                 tau[b, h] = tt[0]
                 bits[b][h] = bt[0]
     return O, tau, bits
+
+
+def dash_backward(Q, K, V, head_cls, dO, p: DashParams):
+    """Gradients of L = sum(O * dO) for the prefill O = dash_prefill(Q, K, V,
+    head_cls, p) with respect to Q, K, V and head_cls.
+
+    The DashAttention README calls the router "adaptive, differentiable" and has
+    stage 3 use the stage-1 prior "to preserve differentiability through the
+    hierarchy" ("Documentation", "How it works" item 3). The pages print no
+    formula; this is the chain rule through the forward defined above, step by
+    step, nothing more:
+
+    * attention (per row i, over its allowed tokens j): P = softmax(logits),
+      dP_ij = <dO_i, v_j>, dlogit_ij = P_ij (dP_ij - sum_j P_ij dP_ij),
+      dV_j += sum_i P_ij dO_i, dQ_i += sum_j dlogit_ij k_j / sqrt(d),
+      dK_j += sum_i dlogit_ij q_i / sqrt(d);
+    * prior (logit_ij contains log w_{i, c(j)}): g_ic = sum_{j in c} dlogit_ij
+      is the gradient of log w_ic; a routed chunk has w = pi, so
+      d pi_ic = g_ic / pi_ic; the own chunk attended with weight 1 (causal,
+      estimate_diagonal off) is not a routing candidate and passes nothing on;
+    * routing: pi_i = entmax_alpha(z_i) over the row's candidates, so
+      dz_i = the entmax vector-Jacobian product at (pi_i, d pi_i)
+      (``entmax_backward``; chunks off the support get 0);
+    * scores z_ic = scaling_factor <q_i, s_c> / sqrt(d):
+      dQ_i += scaling_factor / sqrt(d) sum_c dz_ic s_c, ds_c += scaling_factor /
+      sqrt(d) sum_i dz_ic q_i (over every row and query head of the KV head);
+      with estimate_diagonal the own chunk's candidate is scored against the
+      prefix summary s^_i of tokens [c_i C, i], whose gradient
+      scaling_factor / sqrt(d) dz_i,c_i q_i goes through ``chunk_summary_backward``
+      of those tokens;
+    * summaries: ``chunk_summary_backward`` of every summarised chunk for its ds.
+
+    Returns (dQ [B,Hq,N,d], dK [B,Hkv,N,d], dV [B,Hkv,N,d], dcls [Hkv,d]).
+    """
+    Q, K, V, head_cls, dO = _f64(Q), _f64(K), _f64(V), _f64(head_cls), _f64(dO)
+    B, Hq, N, d = Q.shape
+    Hkv = K.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    C = p.chunk_size
+    n_c = -(-N // C)
+    rt = p.scaling_factor / np.sqrt(d)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    dcls = np.zeros_like(head_cls)
+    pos = np.arange(N)
+    j = np.arange(N)
+    for b in range(B):
+        for hk in range(Hkv):
+            keys, vals, cls = K[b, hk], V[b, hk], head_cls[hk]
+            summ = chunk_summaries(keys, cls, C, N)
+            ds = np.zeros_like(summ)
+            for h in range(hk * g, (hk + 1) * g):
+                q, do = Q[b, h], dO[b, h]
+                Z, tau, prior, logw = route_row(q, pos, keys, cls, N, p, summ)
+                # ---- attention, dense then mask
+                bias = logw[:, j // C]
+                if p.causal:
+                    bias = np.where(j[None, :] <= pos[:, None], bias, -np.inf)
+                logits = (q @ keys.T) / np.sqrt(d) + bias
+                P = np.exp(logits - np.max(logits, axis=1, keepdims=True))
+                P /= np.sum(P, axis=1, keepdims=True)
+                dP = do @ vals.T
+                dlog = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+                dV[b, hk] += P.T @ do
+                dQ[b, h] += dlog @ keys / np.sqrt(d)
+                dK[b, hk] += dlog.T @ q / np.sqrt(d)
+                # ---- prior: gradient of log w per (row, chunk)
+                gw = np.zeros((N, n_c))
+                for c in range(n_c):
+                    gw[:, c] = np.sum(dlog[:, c * C : min((c + 1) * C, N)], axis=1)
+                # ---- routing: entmax over each row's candidates (finite Z)
+                dZ = np.zeros_like(Z)
+                for i in range(N):
+                    cand = np.isfinite(Z[i])
+                    if not cand.any():
+                        continue
+                    pi = prior[i, cand]
+                    dpi = np.where(pi > 0, gw[i, cand] / np.where(pi > 0, pi, 1.0), 0.0)
+                    dZ[i, cand] = entmax_backward(pi, dpi, p.alpha)
+                # ---- scores against the summaries (and the own-chunk estimate)
+                for i in range(N):
+                    ci = i // C
+                    for c in range(n_c):
+                        if dZ[i, c] == 0.0:
+                            continue
+                        if p.causal and c == ci:
+                            # the estimate of the own chunk from tokens [ci*C, i]
+                            s_hat = chunk_summary(keys[ci * C : i + 1], cls)
+                            dQ[b, h, i] += rt * dZ[i, c] * s_hat
+                            dk, dc = chunk_summary_backward(keys[ci * C : i + 1], cls, rt * dZ[i, c] * q[i])
+                            dK[b, hk, ci * C : i + 1] += dk
+                            dcls[hk] += dc
+                        else:
+                            dQ[b, h, i] += rt * dZ[i, c] * summ[c]
+                            ds[c] += rt * dZ[i, c] * q[i]
+            # ---- summaries of the chunks the routing read
+            for c in range(n_c):
+                if not np.any(ds[c]):
+                    continue
+                lo, hi = c * C, min((c + 1) * C, N)
+                dk, dc = chunk_summary_backward(keys[lo:hi], cls, ds[c])
+                dK[b, hk, lo:hi] += dk
+                dcls[hk] += dc
+    return dQ, dK, dV, dcls
