@@ -56,6 +56,9 @@ _SIGNATURES = {
     "dash_decode_step_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _I, _I, DashParams, _P, _P, _P,
                                       _I, _P]),
     "dash_decode_noalloc_max_bytes": (_SZ, []),
+    "dash_sparse_attn_prefill_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                               DashParams, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dash_backward_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, DashParams]),
     "entmax_attn": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P]),
     "entmax_attn_backward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _P, _P, _P, _P, _P]),
     "entmax_rows": (_I, [_P, _P, _I, _I, _I, _F, _I, _P, _P]),

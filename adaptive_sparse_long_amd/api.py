@@ -36,6 +36,8 @@ __all__ = [
     "prefill",
     "decode_step",
     "decode_step_noalloc",
+    "prefill_backward",
+    "dash_attn_fn",
 ]
 
 CHUNK = 64
@@ -198,6 +200,60 @@ def sparse_attn_decode(q, Kc, Vc, seqlens, workspace, params: Params = Params(),
                                      params.c(), _p(out), _p(workspace), workspace.numel(), _stream(q.device))
     _lib.check(st, "dash_sparse_attn_decode")
     return out
+
+
+def prefill_backward(Q, K, V, head_cls, S, dO, tau, bits, params: Params = Params(), workspace=None):
+    """Gradients (dQ, dK, dV, dcls) of :func:`prefill` for the cotangent ``dO`` of
+    its output, from the forward's inputs, its summaries ``S`` and its ``tau`` and
+    routed-chunk ``bits`` (``dash_sparse_attn_prefill_backward``). dcls is
+    float32; the rest have the inputs' dtype."""
+    lib = _lib.load()
+    _need(Q, "Q", dim=4)
+    for name, t in (("K", K), ("V", V), ("dO", dO)):
+        _need(t, name, Q.dtype, 4)
+    _need(head_cls, "head_cls", Q.dtype, 2)
+    _need(S, "S", torch.float32, 4)
+    _need(tau, "tau", torch.float32, 3)
+    _need(bits, "bits", torch.int32, 4)
+    B, Hq, N, d = Q.shape
+    Hkv, Lmax = K.shape[1], K.shape[2]
+    if dO.shape != Q.shape or V.shape != K.shape:
+        raise ValueError("dO must have Q's shape, V K's shape")
+    need = int(lib.dash_backward_workspace_size(B, Hq, Hkv, N, Lmax, d, params.c()))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    dQ = torch.empty_like(Q)
+    dK = torch.zeros_like(K)
+    dV = torch.zeros_like(V)
+    dcls = torch.empty(Hkv, d, dtype=torch.float32, device=Q.device)
+    st = lib.dash_sparse_attn_prefill_backward(
+        _p(Q), _p(K), _p(V), _p(head_cls), _p(S), _p(dO), _p(tau), _p(bits), bits.shape[-1], _dt(Q), B, Hq,
+        Hkv, N, Lmax, d, S.shape[2], params.c(), _p(dQ), _p(dK), _p(dV), _p(dcls), _p(workspace), workspace.numel(),
+        _stream(Q.device))
+    _lib.check(st, "dash_sparse_attn_prefill_backward")
+    return dQ, dK, dV, dcls
+
+
+class _DashPrefillFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, head_cls, params):
+        O, tau, bits, S, _ = prefill(Q, K, V, head_cls, params, with_bits=True)
+        ctx.save_for_backward(Q, K, V, head_cls, S, tau, bits)
+        ctx.params = params
+        return O
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, head_cls, S, tau, bits = ctx.saved_tensors
+        dQ, dK, dV, dcls = prefill_backward(Q, K, V, head_cls, S, dO.contiguous().to(Q.dtype), tau, bits, ctx.params)
+        return dQ, dK, dV, dcls.to(head_cls.dtype), None
+
+
+def dash_attn_fn(Q, K, V, head_cls, params: Params = Params()):
+    """The whole prefill (summaries, routing, sparse attention) with a backward
+    (torch autograd) through all three stages: gradients into Q, K, V and head_cls
+    run in ``dash_sparse_attn_prefill_backward``."""
+    return _DashPrefillFn.apply(Q, K, V, head_cls, params)
 
 
 def decode_step_noalloc(q, Kc, Vc, head_cls, S, seqlens, params: Params = Params(), with_bits=True, out=None):

@@ -30,6 +30,7 @@ SOURCES = [
     "sparse_decode.hip",
     "entmax_attn.hip",
     "entmax_attn_bwd.hip",
+    "dash_bwd.hip",
     "entmax_rows.hip",
 ]
 

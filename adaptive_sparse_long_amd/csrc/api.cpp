@@ -298,6 +298,72 @@ dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* V
   return from_hip(launch_sparse_decode(a, stream));
 }
 
+size_t dash_backward_workspace_size(int B, int Hq, int Hkv, int N, int Lmax, int d, dash_params p) {
+  if (B <= 0 || !gqa_ok(Hq, Hkv) || N <= 0 || Lmax < N || d <= 0 || p.chunk_size != kChunk) return 0;
+  return dash_bwd_layout(B, Hq, Hkv, N, Lmax, d, p.causal != 0).total;
+}
+
+dash_status dash_sparse_attn_prefill_backward(const void* Q, const void* K, const void* V,
+                                              const void* head_cls, const float* S,
+                                              const void* dO, const float* tau,
+                                              const uint32_t* active_bits, int bits_words,
+                                              dash_dtype dt, int B, int Hq, int Hkv, int N, int Lmax,
+                                              int d, int s_cap, dash_params p, void* dQ, void* dK,
+                                              void* dV, float* dcls, void* workspace,
+                                              size_t ws_bytes, hipStream_t stream) {
+  if (!Q || !K || !V || !head_cls || !S || !dO || !tau || !active_bits || !dQ || !dK || !dV || !dcls || !workspace)
+    return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || N <= 0 || Lmax < N || d <= 0 || s_cap <= 0 || !gqa_ok(Hq, Hkv)) return DASH_ERR_INVALID_ARG;
+  if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
+  dash_status st = check_params(p);
+  if (st != DASH_OK) return st;
+  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  const DashBwdLayout L = dash_bwd_layout(B, Hq, Hkv, N, Lmax, d, p.causal != 0);
+  if (L.n_slots > kDashBwdMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  if (s_cap < L.n_sum) return DASH_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  DashBwdArgs a{};
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.cls = static_cast<const uint16_t*>(head_cls);
+  a.S = S;
+  a.tau = tau;
+  a.bits = active_bits;
+  a.bits_words = bits_words;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = Hq / Hkv; a.N = N; a.Lmax = Lmax; a.s_cap = s_cap;
+  a.n_slots = L.n_slots;
+  a.n_sum = L.n_sum;
+  a.causal = p.causal;
+  a.est = p.causal ? p.estimate_diagonal : 0;
+  a.alpha = p.alpha;
+  a.beta = 1.f / (p.alpha - 1.f);
+  a.inv_sqrt_d = 1.f / sqrtf((float)d);
+  a.rt = p.scaling_factor * a.inv_sqrt_d;
+  a.sf = p.scaling_factor;
+  a.uscale = (p.alpha - 1.f) * a.rt;
+  a.scale_log2 = kLog2e * a.inv_sqrt_d;
+  a.WT = reinterpret_cast<float*>(ws + L.off_wt);
+  a.DZT = reinterpret_cast<float*>(ws + L.off_dzt);
+  a.lse = reinterpret_cast<float*>(ws + L.off_lse);
+  a.Dd = reinterpret_cast<float*>(ws + L.off_dd);
+  a.dQf = reinterpret_cast<float*>(ws + L.off_dqf);
+  a.dKf = reinterpret_cast<float*>(ws + L.off_dkf);
+  a.dSum = reinterpret_cast<float*>(ws + L.off_dsum);
+  a.dKs = reinterpret_cast<float*>(ws + L.off_dks);
+  a.sb_part = reinterpret_cast<float*>(ws + L.off_sbp);
+  a.dcls_s = reinterpret_cast<float*>(ws + L.off_dcs);
+  a.dcls_p = reinterpret_cast<float*>(ws + L.off_dcp);
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.dcls = dcls;
+  return from_hip(launch_dash_bwd(a, stream));
+}
+
 size_t dash_decode_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
 
 dash_status dash_decode_step_noalloc(const void* Q, const void* Kc, const void* Vc, const void* head_cls,

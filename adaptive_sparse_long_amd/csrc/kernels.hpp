@@ -267,6 +267,72 @@ struct DecodeAttnArgs {
   float* part;
 };
 
+// ---------------------------------------------------------------------------
+// DashAttention prefill backward. Column-layout per-(row, chunk) arrays are
+// [B, Hq, n_slots, N] (the rows of one chunk contiguous).
+// ---------------------------------------------------------------------------
+struct DashBwdLayout {
+  int n_slots = 0, n_sum = 0;  // chunk slots; chunks whose summaries the routing read
+  size_t off_wt = 0, off_dzt = 0, off_lse = 0, off_dd = 0, off_dqf = 0, off_dkf = 0, off_dsum = 0;
+  size_t off_dks = 0, off_sbp = 0, off_dcs = 0, off_dcp = 0, total = 0;
+};
+
+inline DashBwdLayout dash_bwd_layout(int B, int Hq, int Hkv, int N, int Lmax, int d, bool causal) {
+  DashBwdLayout L;
+  L.n_slots = (N + kChunk - 1) / kChunk;
+  L.n_sum = causal ? N / kChunk : L.n_slots;
+  const size_t rows = (size_t)B * Hq * N;
+  size_t o = 0;
+  L.off_wt = o;   o += align256(rows * L.n_slots * sizeof(float));
+  L.off_dzt = o;  o += align256(rows * L.n_slots * sizeof(float));
+  L.off_lse = o;  o += align256(rows * sizeof(float));
+  L.off_dd = o;   o += align256(rows * sizeof(float));
+  L.off_dqf = o;  o += align256(rows * d * sizeof(float));
+  L.off_dkf = o;  o += align256((size_t)B * Hkv * N * d * sizeof(float));
+  L.off_dsum = o; o += align256((size_t)B * Hkv * L.n_slots * d * sizeof(float));
+  L.off_dks = o;  o += align256((size_t)B * Hkv * Lmax * d * sizeof(float));
+  L.off_sbp = o;  o += align256((size_t)B * Hkv * (L.n_sum > 0 ? L.n_sum : 1) * d * sizeof(float));
+  L.off_dcs = o;  o += align256((size_t)Hkv * d * sizeof(float));
+  L.off_dcp = o;  o += align256((size_t)B * Hkv * L.n_slots * d * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+struct DashBwdArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* dO;
+  const uint16_t* cls;
+  const float* S;          // [B, Hkv, s_cap, d] summaries the forward routed against
+  const float* tau;        // [B, Hq, N]
+  const uint32_t* bits;    // [B, Hq, N, bits_words] attended chunks
+  int bits_words;
+  int B, Hq, Hkv, g, N, Lmax, s_cap, n_slots, n_sum;
+  int causal, est;
+  float alpha, beta;
+  float uscale;      // (alpha - 1) * scaling_factor / sqrt(d): u per <q, s>
+  float rt;          // scaling_factor / sqrt(d): z per <q, s>
+  float sf;          // scaling_factor
+  float scale_log2;  // log2(e) / sqrt(d)
+  float inv_sqrt_d;
+  float* WT;      // log2 weights, column layout (-inf: not attended)
+  float* DZT;     // gradients of the routing scores z, column layout
+  float* lse;     // [B, Hq, N] log2 of the row's softmax normaliser (exp2 domain)
+  float* Dd;      // [B, Hq, N] sum_j P_ij dP_ij
+  float* dQf;     // [B, Hq, N, d]
+  float* dKf;     // [B, Hkv, N, d] attention (and own-chunk estimate) part of dK
+  float* dSum;    // [B, Hkv, n_slots, d] gradients of the summaries
+  float* dKs;     // [B, Hkv, Lmax, d] summary part of dK
+  float* sb_part; // summary backward scratch
+  float* dcls_s;  // [Hkv, d] summary part of dcls
+  float* dcls_p;  // [B, Hkv, n_slots, d] own-chunk estimate part of dcls, per chunk
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* dcls;
+};
+
 struct EntmaxAttnArgs {
   const void* Q;
   const void* K;
@@ -322,6 +388,7 @@ hipError_t launch_sparse_decode(const DecodeAttnArgs& a, hipStream_t stream);
 hipError_t launch_entmax_attn(const EntmaxAttnArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_entmax_rows(const EntmaxRowsArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_entmax_attn_bwd(const EntmaxBwdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_dash_bwd(const DashBwdArgs& a, hipStream_t stream);
 
 // Limits of the current kernels (checked by the host API).
 constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
@@ -331,5 +398,6 @@ constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel
 constexpr int kEntmaxRowsMax = 32768;        // row-wise entmax: 32 entries per thread of 1024
+constexpr int kDashBwdMaxSlots = 1024;       // DashAttention backward: chunk slots per row (N <= 65536)
 
 }  // namespace dash

@@ -187,6 +187,57 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
                                      size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * dash_sparse_attn_prefill_backward -- gradients of the whole prefill
+ * (dash_summarize -> dash_route -> dash_sparse_attn_prefill) for a cotangent dO
+ * of O. The DashAttention README calls the router "adaptive, differentiable"
+ * and has stage 3 use the stage-1 prior "to preserve differentiability through
+ * the hierarchy" ("Documentation", "How it works" item 3); the steps are the
+ * chain rule through the forward:
+ *   attention: dP_ij = <dO_i, v_j>, dS_ij = P_ij (dP_ij - D_i) with
+ *     D_i = sum_j P_ij dP_ij (recomputed exactly, not from a rounded output),
+ *     dQ_i += sum_j dS_ij k_j / sqrt(d), dK_j += sum_i dS_ij q_i / sqrt(d),
+ *     dV_j += sum_i P_ij dO_i;
+ *   prior: g_ic = sum_{j in chunk c} dS_ij is the gradient of log pi_ic;
+ *   routing (the entmax Jacobian over the row's support, s = pi^(2-alpha)):
+ *     dz_ic = s_c g_ic / pi_ic - s_c (sum_c' s_c' g_ic' / pi_ic') / sum_c' s_c';
+ *   scores z = scaling_factor <q, s_c> / sqrt(d): dQ_i and the summaries'
+ *     gradients, and through dash_summarize's definition dK and head_cls (the
+ *     own-chunk estimate's prefix summary likewise).
+ * An own chunk attended with weight 1 (estimate_diagonal = 0) is not a routing
+ * candidate and takes no routing gradient.
+ *   Q, K, V, head_cls, S, tau, p, B, Hq, Hkv, N, Lmax, s_cap: exactly as given
+ *       to the forward's dash_summarize / dash_route (prefill mode, rows
+ *       0 .. N-1) / dash_sparse_attn_prefill;
+ *   active_bits [B, Hq, N, bits_words]: dash_route's attended-chunk bits (the
+ *       forward must be run with them);
+ *   dO [B, Hq, N, d]: the cotangent of the forward's output;
+ *   dQ [B, Hq, N, d], dK / dV [B, Hkv, Lmax, d]: written for rows < N (rows
+ *       N .. Lmax-1 untouched), dtype dt; dcls [Hkv, d] float32, written.
+ * The routing weights are recomputed from S, tau and the bits (a chunk the
+ * forward routed whose recomputed score does not exceed tau, a last-bit
+ * disagreement at the edge of the support, gets weight 0). Every sum has a
+ * fixed order (deterministic). Device memory is the caller's, the scratch is
+ * `workspace` (dash_backward_workspace_size bytes: about 2 * B * Hq * N *
+ * ceil(N/64) * 4 + 3 * B * Hq * N * d * 4 bytes), nothing is allocated, no
+ * host sync. Errors: NULL pointers, sizes <= 0, N > Lmax, Hq % Hkv != 0, bad
+ * params, bits_words too small, s_cap below the summarised chunks ->
+ * DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d != 128, chunk_size != 64,
+ * N > 65536 -> DASH_ERR_UNSUPPORTED; ws_bytes too small -> DASH_ERR_WORKSPACE;
+ * a launch failure -> DASH_ERR_HIP.
+ * --------------------------------------------------------------------------- */
+dash_status dash_sparse_attn_prefill_backward(const void* Q, const void* K, const void* V,
+                                              const void* head_cls, const float* S,
+                                              const void* dO, const float* tau,
+                                              const uint32_t* active_bits, int bits_words,
+                                              dash_dtype dt, int B, int Hq, int Hkv, int N, int Lmax,
+                                              int d, int s_cap, dash_params p, void* dQ, void* dK,
+                                              void* dV, float* dcls, void* workspace,
+                                              size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of workspace dash_sparse_attn_prefill_backward needs (0 for invalid sizes). */
+size_t dash_backward_workspace_size(int B, int Hq, int Hkv, int N, int Lmax, int d, dash_params p);
+
+/* ---------------------------------------------------------------------------
  * dash_sparse_attn_decode -- stage 3 for one new token per sequence, reading
  * only the routed chunks of the caches (prefill/decoding paragraph of "How it
  * works": decoding reuses the chunk-summary cache). Query row t_b =

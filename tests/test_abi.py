@@ -28,6 +28,7 @@ def test_header_symbols_exported(lib):
         "dash_route", "dash_sparse_attn_prefill", "dash_sparse_attn_decode", "entmax_attn",
         "entmax_rows", "entmax_rows_backward", "entmax_attn_backward", "dash_summarize_backward",
         "dash_decode_step_noalloc", "dash_decode_noalloc_max_bytes",
+        "dash_sparse_attn_prefill_backward", "dash_backward_workspace_size",
     }
     for n in names:
         assert hasattr(lib, n), n
