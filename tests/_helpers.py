@@ -33,10 +33,27 @@ def assert_sets_match(gpu_bits, ref_bits, u_minus_tau, where=""):
 
 
 def assert_close(gpu, ref, tol, where=""):
+    """|gpu - ref| <= tol elementwise; tol is a number or an array of ref's shape."""
     err = np.abs(np.asarray(gpu, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
-    worst = float(np.nanmax(err)) if err.size else 0.0
+    tol = np.broadcast_to(np.asarray(tol, dtype=np.float64), err.shape)
     assert np.all(np.isfinite(gpu)), f"{where}: non-finite values"
-    assert worst <= tol, f"{where}: max abs error {worst:.3e} > {tol:.1e} at {np.unravel_index(np.argmax(err), err.shape)}"
+    if err.size and not np.all(err <= tol):
+        at = np.unravel_index(np.argmax(err - tol), err.shape)
+        raise AssertionError(f"{where}: abs error {float(err[at]):.3e} > {float(tol[at]):.2e} at {at} "
+                             f"(max abs error {float(np.nanmax(err)):.3e})")
+
+
+def half_ulp_bf16(x):
+    """Half the spacing of bfloat16 numbers at |x| (8 significand bits)."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 8)
+
+
+def tol_bf16_out(ref):
+    """Bar for a bfloat16 output: 2e-2, or where bf16 cannot hold a value that
+    close (|ref| >= 8: neighbours 0.0625 apart) the correctly rounded neighbour,
+    half an ulp, plus 1e-3 of computation error."""
+    return np.maximum(TOL_BF16, half_ulp_bf16(ref) + 1e-3)
 
 
 def tau_close(gpu_tau, ref_tau, where=""):

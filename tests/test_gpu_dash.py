@@ -162,6 +162,29 @@ def test_prefill_32k_workload_sampled():
                   where="32k")
 
 
+def test_prefill_32k_workload_full_tiles():
+    """Complete 128-row tiles of the 32K needle workload at depths 4K, 8K, 16K
+    and 32K - 128, for all four query heads of KV head 0: every row of each
+    tile (its union list, pool slots and merge) against the oracle."""
+    w = WORKLOADS["routed_prefill_32k"]
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cuda")
+    p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    rows = np.concatenate([np.arange(t0, t0 + 128) for t0 in (4096, 8192, 16384, w.N - 128)])
+    check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: rows if h < 4 else [], where="32k tiles")
+
+
+def test_prefill_32k_workload_scaling4_sampled():
+    """The 32K needle workload at scaling_factor 4 (one of the measured-sparsity
+    sweep's points: sharper routing), sampled rows of four heads."""
+    w = WORKLOADS["routed_prefill_32k"]
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cuda")
+    p = api.Params(alpha=w.alpha, scaling_factor=4.0, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    rng = np.random.default_rng(w.seed + 4)
+    heads = {3, 12, 17, 30}
+    check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: _sample_rows(w.N, rng, 10) if h in heads else [],
+                  where="32k sf4")
+
+
 # ----------------------------------------------------------------------------- decode
 
 
@@ -250,5 +273,8 @@ def test_decode_128k_workload_sampled():
     rng = np.random.default_rng(w.seed)
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 6), rng.integers(0, w.Hq, 6))]
     pairs += [(0, 0), (w.B - 1, w.Hq - 1)]
+    # one complete (b, kv head) group: all g query heads that share its routed list
+    g = w.Hq // w.Hkv
+    pairs += [(5, 5 * g + j) for j in range(g)]
     check_decode(q, Kc, Vc, cls, seqlens, api.Params(alpha=w.alpha, estimate_diagonal=w.estimate_diagonal),
                  pairs=pairs, where="128k")

@@ -14,7 +14,7 @@ import oracle
 from adaptive_sparse_long_amd import api
 from adaptive_sparse_long_amd.workloads import WORKLOADS, dense_entmax_inputs
 
-from _helpers import MARGIN, TOL_BF16, TOL_F32, assert_close, f64, tau_close, unpack_bits
+from _helpers import MARGIN, TOL_BF16, TOL_F32, assert_close, f64, tau_close, tol_bf16_out, unpack_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -145,3 +145,39 @@ def test_varlen_workload_sampled():
             bits = unpack_bits(m[b, h], nT)
             assert not bits[t:].any() and not bits[:, t:].any()
             assert bits[:t, :t].any(axis=1).all()  # every row tile has support somewhere
+
+
+def test_varlen_workload_full_sequences():
+    """Two whole (b, h) sequences of the varlen workload -- the shortest and the
+    longest -- every row's O and tau, and the block mask tile by tile: a tile
+    holding an entry more than 1e-4 above its row's tau must be marked, a tile
+    whose entries all lie more than 1e-4 below must not (R13's margin rule)."""
+    w = WORKLOADS["varlen_entmax"]
+    q, k, v, lens = dense_entmax_inputs(w.B, w.Hq, w.N, w.d, w.seed, dtype=w.dtype, scale=w.scale,
+                                        varlen_range=w.varlen_range, device="cuda")
+    O, tau, mask = api.entmax_attn(q, k, v, alpha=w.alpha, causal=w.causal, varlen=lens)
+    torch.cuda.synchronize()
+    L_ = lens.cpu().numpy()
+    nT = -(-w.N // 64)
+    m = mask.cpu().numpy()
+    for b, h in ((int(np.argmin(L_)), 3), (int(np.argmax(L_)), 11)):
+        L = int(L_[b])
+        qb, kb, vb = f64(q[b, h, :L]), f64(k[b, h, :L]), f64(v[b, h, :L])
+        t = -(-L // 64)
+        hi = np.full((t, t), -np.inf)  # per tile: the largest u - tau of its entries
+        for r0 in range(0, L, 512):
+            pos = np.arange(r0, min(L, r0 + 512))
+            o_ref, t_ref, _ = oracle.entmax_attention_rows(qb[pos], pos, kb, vb, L, w.alpha, w.causal)
+            # V is scaled by 2: outputs reach past 8, where bf16 values lie 0.0625 apart
+            assert_close(f64(O[b, h, pos]), o_ref, tol_bf16_out(o_ref), f"full b{b} h{h} rows {r0}")
+            tau_close(f64(tau[b, h, pos]), t_ref, f"full b{b} h{h} rows {r0}")
+            umt = (w.alpha - 1.0) * (qb[pos] @ kb.T) / np.sqrt(w.d) - t_ref[:, None]
+            for I in np.unique(pos // 64):
+                rr = (pos // 64) == I
+                cols = umt[rr].max(axis=0)
+                for J in range(t):  # 512-row blocks hold whole 64-row tiles
+                    hi[I, J] = cols[J * 64:(J + 1) * 64].max()
+        bits = unpack_bits(m[b, h], nT)
+        assert bits[:t, :t][hi > 1e-4].all(), f"full b{b} h{h}: a tile with weight is not marked"
+        assert not bits[:t, :t][hi < -1e-4].any(), f"full b{b} h{h}: a tile without weight is marked"
+        assert not bits[t:].any() and not bits[:, t:].any()
