@@ -50,6 +50,8 @@ _SIGNATURES = {
     "dash_summarize": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, DashParams, _P]),
     "dash_summarize_backward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, DashParams, _P, _P, _P, _P]),
     "dash_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, _I, DashParams]),
+    "dash_prefill_workspace_size": (_SZ, [_I, _I, _I, _I, _I, _I, DashParams, ctypes.c_longlong]),
+    "dash_prefill_counters": (_I, [_P, _SZ, _I, _I, _I, _I, _I, DashParams, _P, _P]),
     "dash_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, DashParams, _P, _P, _I, _P, _SZ, _P]),
     "dash_sparse_attn_prefill": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, DashParams, _P, _P, _SZ, _P]),
     "dash_sparse_attn_decode": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _I, _I, DashParams, _P, _P, _SZ, _P]),

@@ -26,6 +26,8 @@ __all__ = [
     "Params",
     "summarize",
     "workspace_size",
+    "prefill_workspace_size",
+    "prefill_counters",
     "route",
     "sparse_attn_prefill",
     "sparse_attn_decode",
@@ -145,6 +147,24 @@ def workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode: bool, params: Params = Param
     return int(_lib.load().dash_workspace_size(B, Hq, Hkv, Nq, Lmax, d, int(decode), params.c()))
 
 
+def prefill_workspace_size(B, Hq, Hkv, Nq, Lmax, d, params: Params = Params(), pool_pairs: int = 0) -> int:
+    """Prefill workspace bytes with a partial-result pool of exactly pool_pairs
+    (row, routed past chunk) pairs; tiles that find the pool full are attended
+    row-major, so any pool size gives the same result up to rounding."""
+    return int(_lib.load().dash_prefill_workspace_size(B, Hq, Hkv, Nq, Lmax, d, params.c(), int(pool_pairs)))
+
+
+def prefill_counters(workspace, B, Hq, Hkv, N, d, params: Params = Params(), device=None) -> dict:
+    """Counters of the last prefill routing in `workspace` (synchronises the
+    stream): pool pairs used, pool capacity, tiles left to the general routing
+    kernel, tiles attended row-major."""
+    out = (ctypes.c_longlong * 4)()
+    st = _lib.load().dash_prefill_counters(_p(workspace), workspace.numel(), B, Hq, Hkv, N, d, params.c(),
+                                           ctypes.cast(out, ctypes.c_void_p), _stream(device or workspace.device))
+    _lib.check(st, "dash_prefill_counters")
+    return {"pool_pairs": out[0], "pool_capacity": out[1], "general_route_tiles": out[2], "row_major_tiles": out[3]}
+
+
 def route(Q, K, head_cls, S, params: Params = Params(), seqlens=None, with_bits=True, workspace=None):
     """Chunk routing ("How it works" 2). Returns (tau, active_bits or None, workspace)."""
     lib = _lib.load()
@@ -159,9 +179,15 @@ def route(Q, K, head_cls, S, params: Params = Params(), seqlens=None, with_bits=
         _need(seqlens, "seqlens", torch.int32, 1)
     n_slots = -(-(Lmax if decode else Nq) // CHUNK)
     words = -(-n_slots // 32)
-    ws_bytes = workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode, params)
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None:
+        ws_bytes = workspace_size(B, Hq, Hkv, Nq, Lmax, d, decode, params)
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=Q.device)
+    else:
+        # prefill: anything from the pool-free part up (the rest is the pool)
+        least = (workspace_size(B, Hq, Hkv, Nq, Lmax, d, True, params) if decode
+                 else prefill_workspace_size(B, Hq, Hkv, Nq, Lmax, d, params, 0))
+        if workspace.numel() < least:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, these sizes need at least {least}")
     tau = torch.empty(B, Hq, Nq, dtype=torch.float32, device=Q.device)
     bits = torch.empty(B, Hq, Nq, words, dtype=torch.int32, device=Q.device) if with_bits else None
     st = lib.dash_route(_p(Q), _p(K), _p(head_cls), _p(S), _dt(Q), B, Hq, Hkv, Nq, Lmax, d, S.shape[2],

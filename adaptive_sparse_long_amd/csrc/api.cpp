@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <vector>
 
 #include "kernels.hpp"
 
@@ -38,7 +39,6 @@ int device_cus() {
 }
 
 // Pool slots are addressed with 32 bits.
-bool prefill_pool_fits(int B, int Hq, int N) { return (long long)B * Hq * N * kCmSlots < (1ll << 32); }
 
 // Scratch of the allocation-free decode step: a file-scope device array (each
 // GPU holds its own copy from the time the library is loaded until the process
@@ -128,7 +128,14 @@ size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int 
   if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
   if (decode) return decode_layout(B, Hq, Hkv, Lmax, d).total;
   if (Nq <= 0 || Nq > Lmax) return 0;
-  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0).total;
+  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, prefill_default_pairs(B, Hq, Nq)).total;
+}
+
+size_t dash_prefill_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, dash_params p,
+                                   long long pool_pairs) {
+  if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
+  if (Nq <= 0 || Nq > Lmax || pool_pairs < 0 || pool_pairs > kPoolMaxPairs) return 0;
+  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, pool_pairs).total;
 }
 
 dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
@@ -177,18 +184,23 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
     return from_hip(launch_route_decode(a, stream));
   }
   if (Nq > Lmax) return DASH_ERR_INVALID_ARG;
-  const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0);
-  if (L.n_slots > kRoutePrefillMaxSlots || !prefill_pool_fits(B, Hq, Nq)) return DASH_ERR_UNSUPPORTED;
-  const int need_cap = p.causal ? Nq / kChunk : L.n_slots;
-  if (s_cap < need_cap) return DASH_ERR_INVALID_ARG;
-  if (active_bits && bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  const int n_slots = (Nq + kChunk - 1) / kChunk;
+  if (n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (s_cap < (p.causal ? Nq / kChunk : n_slots)) return DASH_ERR_INVALID_ARG;
+  if (active_bits && bits_words < (n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, Nq, d, p.causal != 0, ws_bytes);
+  if (pool < 0) return DASH_ERR_WORKSPACE;
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, pool);
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   a.n_tiles = L.n_tiles;
   a.n_slots = L.n_slots;
   a.per_head = L.per_head;
   a.counts = reinterpret_cast<int*>(ws + L.off_counts);
   a.lists = reinterpret_cast<int*>(ws + L.off_lists);
-  a.bias = reinterpret_cast<float*>(ws + L.off_bias);
+  a.bias = nullptr;
+  a.rm_tau = reinterpret_cast<float*>(ws + L.off_rmtau);
+  a.rm_bits = reinterpret_cast<uint32_t*>(ws + L.off_rmbits);
+  a.rm_words = L.words;
   a.ccounts = reinterpret_cast<int*>(ws + L.off_ccounts);
   a.clists = reinterpret_cast<int*>(ws + L.off_clists);
   a.ceo = reinterpret_cast<int2*>(ws + L.off_ceo);
@@ -222,8 +234,10 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
   if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
-  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0);
-  if (L.n_slots > kRoutePrefillMaxSlots || !prefill_pool_fits(B, Hq, N)) return DASH_ERR_UNSUPPORTED;
+  if ((N + kChunk - 1) / kChunk > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, d, p.causal != 0, ws_bytes);
+  if (pool < 0) return DASH_ERR_WORKSPACE;
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0, pool);
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   PrefillAttnArgs a{};
@@ -239,7 +253,12 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.per_head = L.per_head;
   a.counts = reinterpret_cast<const int*>(ws + L.off_counts);
   a.lists = reinterpret_cast<const int*>(ws + L.off_lists);
-  a.bias = reinterpret_cast<const float*>(ws + L.off_bias);
+  a.rm_tau = reinterpret_cast<const float*>(ws + L.off_rmtau);
+  a.rm_bits = reinterpret_cast<const uint32_t*>(ws + L.off_rmbits);
+  a.rm_words = L.words;
+  a.s_hi = reinterpret_cast<const uint16_t*>(ws + L.off_split);
+  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
+  a.beta = 1.f / (p.alpha - 1.f);
   a.ccounts = reinterpret_cast<const int*>(ws + L.off_ccounts);
   a.clists = reinterpret_cast<const int*>(ws + L.off_clists);
   a.ceo = reinterpret_cast<const int2*>(ws + L.off_ceo);
@@ -259,10 +278,35 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.cmcnt = reinterpret_cast<const uint16_t*>(ws + L.off_cmcnt);
   a.own_lw = reinterpret_cast<const float*>(ws + L.off_own);
   a.qhead = reinterpret_cast<int*>(ws + L.off_qhead);
+  a.bad = a.qhead + 1;
+  a.pool = reinterpret_cast<const unsigned long long*>(ws + L.off_pool);
   a.n_rm = reinterpret_cast<const int*>(ws + L.off_fb_count) + 1;
   a.plse = reinterpret_cast<float*>(ws + L.off_plse);
   a.po = reinterpret_cast<uint16_t*>(ws + L.off_po);
   return from_hip(launch_sparse_prefill(a, stream));
+}
+
+dash_status dash_prefill_counters(const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N,
+                                  int d, dash_params p, long long* out, hipStream_t stream) {
+  if (!workspace || !out) return DASH_ERR_INVALID_ARG;
+  if (B <= 0 || N <= 0 || d <= 0 || !gqa_ok(Hq, Hkv)) return DASH_ERR_INVALID_ARG;
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, d, p.causal != 0, ws_bytes);
+  if (pool < 0) return DASH_ERR_WORKSPACE;
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0, pool);
+  const char* ws = static_cast<const char*>(workspace);
+  std::vector<int> cmp((size_t)L.n_bhc);
+  int fb[2] = {0, 0};
+  hipError_t e = hipMemcpyAsync(cmp.data(), ws + L.off_cmp, cmp.size() * sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(fb, ws + L.off_fb_count, sizeof(fb), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return DASH_ERR_HIP;
+  long long pairs = 0;
+  for (int c : cmp) pairs += c;
+  out[0] = pairs;
+  out[1] = L.pool_cap;
+  out[2] = fb[0];
+  out[3] = fb[1];
+  return DASH_OK;
 }
 
 dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* Vc, dash_dtype dt,

@@ -15,12 +15,16 @@ constexpr int kTileRows = 128;
 constexpr int kChunk = 64;
 // Routed chunks handled by one decode split (one workgroup, four wavefronts).
 constexpr int kDecodeSplit = 24;
-// Partial-result pool of the chunk-major kernel: kCmSlots slots per query row
-// on average. Every routed past chunk of a row is attended by the chunk-major
-// kernel into a slot of its own; the merge kernel attends the row's own chunk
-// (causal) and combines it with the row's partials. A tile whose rows find the
-// pool exhausted has all its chunks attended by the row-major kernel instead.
-constexpr int kCmSlots = 16;
+// Partial-result pool of the chunk-major kernel: one slot per (row, routed
+// past chunk) pair. Every routed past chunk of a row is attended by the
+// chunk-major kernel into a slot of its own; the merge kernel attends the row's
+// own chunk (causal) and combines it with the row's partials. A tile whose rows
+// find the pool exhausted has all its chunks attended by the row-major kernel
+// instead. The pool takes whatever the caller's workspace holds beyond the
+// fixed part; the workspace query sizes it to kCmSlotsMax pairs per row at
+// short lengths, shrinking to kCmSlotsMin at long ones.
+constexpr int kCmSlotsMax = 16;
+constexpr int kCmSlotsMin = 5;
 // Chunk-major work item: up to kCmBlocks blocks of 32 (row, chunk) pairs of one
 // (b, kv head, chunk).
 constexpr int kCmBlocks = 24;
@@ -33,8 +37,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // ---------------------------------------------------------------------------
 // Prefill work lists, per (b, query head) and 128-row tile, each an ascending
 // list of chunk ids:
-//   row-major list ("rm", tiles without pool slots): every attended chunk, with
-//     one log2 weight per row of the tile (-inf: not attended by that row);
+//   row-major list ("rm", tiles without pool slots): every attended chunk; the
+//     row-major kernel recomputes each row's prior weight for a listed chunk
+//     from the row's tau and routed-chunk bits (rm_tau, rm_bits, written by the
+//     routing for these tiles only) and the split summaries;
 //   chunk-major list ("cm", tiles with pool slots): every attended chunk, with
 //     the (row, chunk) pair records of the rows attending it -- (row * g + head
 //     in group, pool slot, log2 weight) -- grouped by chunk in the tile's own
@@ -49,26 +55,34 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // Per tile: its first pool slot (tbase). Per row: its first slot (rslot), its
 // number of partials (cmcnt) and the log2 weight of its own chunk (own_lw,
 // causal; -inf when not attended); a row's slots follow its routed past
-// chunks in ascending order. pool: the slot allocation counter. Per slot: the
+// chunks in ascending order. pool: kPools slot allocation counters, then the
+// pool capacity the routing laid the workspace out for (checked by the
+// attention call, which must be given the same workspace size). Per slot: the
 // log2 of the partial's sum of exp2 weights (its max included) in float32 and
 // its output normalised by that sum in fp16, dims in natural order. qhead: the
-// chunk-major kernel's work queue head.
+// chunk-major kernel's work queue head; bad: set when the attention call finds
+// a pool capacity other than the routing's.
+// The per-slot arrays (and the work items, whose number follows the pool) come
+// last, so that everything before them depends on the shapes alone.
 // ---------------------------------------------------------------------------
 struct PrefillLayout {
   int n_tiles = 0;
   int n_slots = 0;        // chunk slots = ceil(N / 64)
+  int words = 0;          // bitmask words per row = ceil(n_slots / 32)
   long long per_head = 0; // list slots per (b, head)
   int n_bhc = 0;          // B * Hkv * n_slots
   long long max_items = 0;
-  size_t off_counts = 0, off_lists = 0, off_bias = 0;          // row-major list
+  size_t off_counts = 0, off_lists = 0;                                // row-major list
   size_t off_ccounts = 0, off_clists = 0, off_ceo = 0, off_cbase = 0;  // chunk-major list
-  size_t off_cmp = 0, off_cs = 0, off_nitems = 0, off_items = 0, off_recs = 0, off_trec = 0;  // chunk-major pairs
-  size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0, off_plse = 0, off_po = 0;  // partials
+  size_t off_cmp = 0, off_cs = 0, off_nitems = 0;                      // chunk-major pairs
+  size_t off_pool = 0, off_tbase = 0, off_rslot = 0, off_cmcnt = 0;    // slots
   size_t off_fb = 0, off_fb_count = 0;  // tiles left to the general routing kernel
-  size_t off_own = 0, off_qhead = 0;
-  long long pool_cap = 0;
-  size_t off_split = 0, total = 0;
+  size_t off_own = 0, off_qhead = 0, off_rmtau = 0, off_rmbits = 0;
+  size_t off_split = 0;
   size_t off_serr = 0;  // per chunk: bound on |hi-only score - full score| / |q|
+  size_t off_items = 0, off_recs = 0, off_trec = 0, off_plse = 0, off_po = 0;  // per pool slot
+  long long pool_cap = 0;
+  size_t fixed = 0, total = 0;
 };
 
 __host__ __device__ inline long long prefill_tile_offset(int tile, int n_slots, bool causal) {
@@ -78,24 +92,26 @@ __host__ __device__ inline int prefill_tile_cap(int tile, int n_slots, bool caus
   return causal ? min(n_slots, 2 * tile + 2) : n_slots;
 }
 
+// Pool slots are 32-bit indices.
+constexpr long long kPoolMaxPairs = 0xffffff00ll;
+
 // off_split: the summaries split into bf16 high and low parts, [B, Hkv, n_slots, d] each.
-inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool causal) {
+inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool causal, long long pool_pairs) {
   PrefillLayout L;
   L.n_tiles = (N + kTileRows - 1) / kTileRows;
   L.n_slots = (N + kChunk - 1) / kChunk;
+  L.words = (L.n_slots + 31) / 32;
   const int t = L.n_tiles - 1;
   L.per_head = prefill_tile_offset(t, L.n_slots, causal) + prefill_tile_cap(t, L.n_slots, causal);
   const size_t heads = (size_t)B * Hq;
-  const size_t entries = heads * (size_t)L.per_head * kTileRows;
   const size_t rows = heads * (size_t)N;
-  const size_t pairs = rows * kCmSlots;
+  const size_t pairs = (size_t)(pool_pairs < 0 ? 0 : pool_pairs);
   L.pool_cap = (long long)pairs;
   L.n_bhc = B * Hkv * L.n_slots;
   L.max_items = (long long)((pairs + 32 * kCmBlocks - 1) / (32 * kCmBlocks)) + L.n_bhc;
   size_t o = 0;
   L.off_counts = o;  o += align256(heads * L.n_tiles * sizeof(int));
   L.off_lists = o;   o += align256(heads * (size_t)L.per_head * sizeof(int));
-  L.off_bias = o;    o += align256(entries * sizeof(float));
   L.off_ccounts = o; o += align256(heads * L.n_tiles * sizeof(int));
   L.off_clists = o;  o += align256(heads * (size_t)L.per_head * sizeof(int));
   L.off_ceo = o;     o += align256(heads * (size_t)L.per_head * 2 * sizeof(int));
@@ -103,23 +119,50 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_cmp = o;     o += align256((size_t)L.n_bhc * sizeof(int));
   L.off_cs = o;      o += align256((size_t)L.n_bhc * sizeof(int));
   L.off_nitems = o;  o += align256(sizeof(int));
-  L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
-  L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
-  L.off_trec = o;    o += align256(pairs * 4 * sizeof(int));
-  L.off_pool = o;    o += align256(kPools * sizeof(unsigned long long));
+  L.off_pool = o;    o += align256((kPools + 1) * sizeof(unsigned long long));
   L.off_tbase = o;   o += align256(heads * L.n_tiles * sizeof(uint32_t));
   L.off_fb = o;      o += align256(heads * L.n_tiles * 2 * sizeof(int));
   L.off_fb_count = o; o += align256(2 * sizeof(int));  // queued tiles, row-major tiles
   L.off_rslot = o;   o += align256(rows * sizeof(uint32_t));
   L.off_cmcnt = o;   o += align256(rows * sizeof(uint16_t));
   L.off_own = o;     o += align256(rows * sizeof(float));
-  L.off_qhead = o;   o += align256(sizeof(int));
-  L.off_plse = o;    o += align256(pairs * sizeof(float));
-  L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
+  L.off_qhead = o;   o += align256(2 * sizeof(int));  // queue head, bad
+  L.off_rmtau = o;   o += align256(rows * sizeof(float));
+  L.off_rmbits = o;  o += align256(rows * L.words * sizeof(uint32_t));
   L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
   L.off_serr = o;    o += align256((size_t)B * Hkv * L.n_slots * sizeof(float));
+  L.fixed = o;
+  L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
+  L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
+  L.off_trec = o;    o += align256(pairs * 4 * sizeof(int));
+  L.off_plse = o;    o += align256(pairs * sizeof(float));
+  L.off_po = o;      o += align256(pairs * (size_t)d * sizeof(uint16_t));
   L.total = o;
   return L;
+}
+
+// Pool pairs the workspace query provides: 2048 / n_slots per row, within
+// [kCmSlotsMin, kCmSlotsMax] (16 up to N = 8192, 5 from N = 32768 on).
+inline long long prefill_default_pairs(int B, int Hq, int N) {
+  const int n_slots = (N + kChunk - 1) / kChunk;
+  int per_row = 2048 / n_slots;
+  if (per_row > kCmSlotsMax) per_row = kCmSlotsMax;
+  if (per_row < kCmSlotsMin) per_row = kCmSlotsMin;
+  const long long p = (long long)B * Hq * N * per_row;
+  return p < kPoolMaxPairs ? p : kPoolMaxPairs;
+}
+
+// The largest pool a workspace of ws_bytes holds (-1: not even the fixed part
+// fits). Deterministic in its arguments, so the routing and the attention call
+// agree when given the same workspace size.
+inline long long prefill_pool_from_bytes(int B, int Hq, int Hkv, int N, int d, bool causal, size_t ws_bytes) {
+  const PrefillLayout L0 = prefill_layout(B, Hq, Hkv, N, d, causal, 0);
+  if (ws_bytes < L0.total) return -1;
+  const size_t per_pair = 36 + 2 * (size_t)d + 1;
+  long long p = (long long)((ws_bytes - L0.total) / per_pair);
+  if (p > kPoolMaxPairs) p = kPoolMaxPairs;
+  while (p > 0 && prefill_layout(B, Hq, Hkv, N, d, causal, p).total > ws_bytes) p -= p / 4096 + 1;
+  return p;
 }
 
 // ---------------------------------------------------------------------------
@@ -189,7 +232,7 @@ struct RouteArgs {
   long long per_head;
   int* counts;
   int* lists;
-  float* bias;
+  float* bias;       // decode: g log2 weights per listed chunk
   int* ccounts;
   int* clists;
   int2* ceo;
@@ -197,12 +240,15 @@ struct RouteArgs {
   int* cbase;
   int* cmp;  // zeroed by the summary split, counted by the routing
   int n_bhc;
-  unsigned long long* pool;  // kPools counters, zeroed by the summary split
+  unsigned long long* pool;  // kPools counters, zeroed by the summary split, then the capacity
   long long pool_cap;
   uint32_t* tbase;
   uint32_t* rslot;
   uint16_t* cmcnt;
   float* own_lw;     // per row: log2 weight of its own chunk (causal)
+  float* rm_tau;     // per row of a row-major tile: tau
+  uint32_t* rm_bits; // per row of a row-major tile: routed past chunks, rm_words words
+  int rm_words;
   int2* fb_tiles;   // tiles the list-based kernel left: (tile, b * Hq + h)
   int* fb_count;     // their number, zeroed by the summary split
   int* n_rm;         // tiles without pool slots (row-major), zeroed by the summary split
@@ -227,7 +273,14 @@ struct PrefillAttnArgs {
   long long per_head;
   const int* counts;
   const int* lists;
-  const float* bias;
+  // row-major part: per row tau and routed-chunk bits, the split summaries
+  // (u units), alpha as beta = 1 / (alpha - 1)
+  const float* rm_tau;
+  const uint32_t* rm_bits;
+  int rm_words;
+  const uint16_t* s_hi;
+  const uint16_t* s_lo;
+  float beta;
   // chunk-major part
   const int* ccounts;
   const int* clists;
@@ -247,6 +300,8 @@ struct PrefillAttnArgs {
   const uint16_t* cmcnt;
   const float* own_lw;
   int* qhead;       // work queue head of the chunk-major kernel
+  int* bad;         // set: the workspace was laid out for another pool capacity
+  const unsigned long long* pool;  // the routing's counters and capacity
   const int* n_rm;  // tiles the routing left row-major
   float* plse;
   uint16_t* po;

@@ -632,18 +632,34 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       });
     }
   } else {
-    // ---- row-major list: -inf for every (entry, row) of this wavefront, then
-    // the log2 weights of the attended pairs
-    const int ne = s_pre[NW];
-    float* const bw = a.bias + (size_t)toff * kTileRows + w * 16;
-    for (int x = lane; x < ne * 16; x += kWave) bw[(size_t)(x >> 4) * kTileRows + (x & 15)] = -INFINITY;
-    __syncthreads();  // the fills are done before any weight lands on them
-    for_each_routed_blk([&](int r, int c, int, float uu) {
-      bw[(size_t)epos(c) * kTileRows + grp * 4 + r] = log2_prior<KIND>(uu - tau[r], a.beta);
-    });
+    // ---- row-major tile: the rows' tau and routed past chunks, from which the
+    // row-major kernel recomputes their weights
+    if (col == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (causal && col == 0 && dact[r]) bw[(size_t)epos(cw) * kTileRows + grp * 4 + r] = lwd[r];
+      for (int r = 0; r < 4; ++r)
+        if (row_ok[r]) a.rm_tau[bh * (size_t)N + i0 + grp * 4 + r] = tau[r];
+    }
+    const int rg = lane >> 2, r4 = lane & 3;  // D-layout owner of row `lane` (lanes 0..15)
+    uint32_t* bdst = a.rm_bits + ((bh * (size_t)N) + min(i0 + lane, N - 1)) * (size_t)a.rm_words;
+    const bool write_rm = wave_valid && lane < 16 && i0 + lane < N;
+#pragma unroll
+    for (int wd = 0; wd < NW; ++wd) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int blk = 2 * wd + half;
+        if (blk < NB) {
+          unsigned long long mb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
+          const unsigned long long mr = r4 == 0 ? mb[0] : r4 == 1 ? mb[1] : r4 == 2 ? mb[2] : mb[3];
+          word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
+        }
+      }
+      if (write_rm && wd < a.rm_words) bdst[wd] = word;
+    }
+    if (write_rm)
+      for (int wd = NW; wd < a.rm_words; ++wd) bdst[wd] = 0u;
   }
 }
 
@@ -1291,17 +1307,14 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     for (int q = 0; q < 2; ++q)
       if (2 * tid + q < ne) a.cbase[toff + 2 * tid + q] = cb[q];
   } else {
-    // ---- row-major list: -inf for every (entry, row), then the log2 weights
-    // of the attended pairs
-    float* const bw = a.bias + (size_t)toff * kTileRows;
-    for (int x = tid; x < ne * kTileRows; x += blockDim.x) bw[x] = -INFINITY;
-    __syncthreads();  // the fills are done before any weight lands on them
-    for_run([&](int j, float uu, uint32_t kk) {
-      const int rr = kk >> 9, c = kk & 511;
-      const float tr = s_t[rr];
-      if (j < nl && uu > tr) bw[(size_t)epos(c) * kTileRows + rr] = log2_prior<KIND>(uu - tr, a.beta);
-    });
-    if (own_pair) bw[(size_t)epos(cw) * kTileRows + R] = lwd;
+    // ---- row-major tile: the rows' tau and routed past chunks, from which the
+    // row-major kernel recomputes their weights
+    if (owner && row_ok) a.rm_tau[bh * (size_t)N + qi] = tau;
+    for (int x = tid; x < kTileRows * a.rm_words; x += blockDim.x) {
+      const int r = x / a.rm_words, wd = x % a.rm_words;
+      const int q = tile * kTileRows + r;
+      if (q < N) a.rm_bits[(bh * (size_t)N + q) * a.rm_words + wd] = wd < NW ? s_bits[r][wd] : 0u;
+    }
   }
 }
 
@@ -1313,7 +1326,8 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
   constexpr int D = 128;
   // the per-chunk pair counters the routing adds to start from zero
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < a.n_bhc; i += gridDim.x * blockDim.x) a.cmp[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < kPools) a.pool[threadIdx.x] = 0ull;
+  if (blockIdx.x == 0 && threadIdx.x <= kPools)
+    a.pool[threadIdx.x] = threadIdx.x < kPools ? 0ull : (unsigned long long)a.pool_cap;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *a.fb_count = 0;
     *a.n_rm = 0;

@@ -25,6 +25,7 @@
 #include <algorithm>
 
 #include "kernels.hpp"
+#include "tau_solve.hpp"
 
 namespace dash {
 
@@ -40,7 +41,7 @@ __device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
 }
 }  // namespace
 
-template <int D>
+template <int D, int KIND>
 __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   constexpr int NS = D / 16;  // k-steps of S^T = K Q^T
   constexpr int NDB = D / 32; // 32-dim blocks of O^T
@@ -49,8 +50,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   static_assert(D == 128, "staging is laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t sU[2][2 * D];  // the chunk's summary: high parts, low parts
 
-  if (*a.n_rm == 0) return;  // every tile went chunk-major
+  if (*a.n_rm == 0 || *a.bad != 0) return;  // every tile went chunk-major / inconsistent workspace
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int tid = threadIdx.x;
@@ -80,12 +82,18 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     if (count == 0) continue;  // every chunk of the tile went chunk-major
     const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, causal);
     const int* list = a.lists + toff;
-    const float* biasp = a.bias + toff * kTileRows + w * 32 + (lane & 31);
 
     const int row0 = tile * kTileRows + w * 32;
     const int cw = row0 / kChunk;
     const int qi = row0 + (lane & 31);
     const int hi32 = lane >> 5;
+    // the row's tau, routed past chunks and own-chunk weight
+    const size_t rix = bh * N + min(qi, N - 1);
+    const float tau_r = a.rm_tau[rix];
+    const uint32_t* rbits = a.rm_bits + rix * a.rm_words;
+    const float own_lw = causal ? a.own_lw[rix] : -INFINITY;
+    const uint16_t* Ub = a.s_hi + ((size_t)b * a.Hkv + hk) * (size_t)a.n_slots * D;
+    const size_t lo_off = (size_t)(a.s_lo - a.s_hi);
 
     // Q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
     bf16x8 qb[NS];
@@ -103,9 +111,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     const int v_kg = tid & 15, v_dg = tid >> 4;
     const int n_keys = N;
 
-    u32x4 kr[4], vr[4];
+    u32x4 kr[4], vr[4], ur;
     // Keys past the sequence end are read from its last row instead (a valid
     // address); their scores are masked, so their weights are exactly zero.
+    // Threads 0..31 also stage the chunk's split summary (16 bytes each).
     auto load_chunk = [&](int c) {
       const int base = c * kChunk;
 #pragma unroll
@@ -115,11 +124,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
         const int vkey = min(base + 4 * v_kg + r, n_keys - 1);
         vr[r] = ldg16(Vb + (size_t)vkey * D + 8 * v_dg);
       }
+      if (tid < 2 * D / 8) ur = ldg16(Ub + (tid >= D / 8 ? lo_off : 0) + (size_t)c * D + 8 * (tid % (D / 8)));
     };
     auto store_chunk = [&](int buf) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         *reinterpret_cast<u32x4*>(&sK[buf][(k_row + 16 * r) * KROW + k_col]) = kr[r];
+      if (tid < 2 * D / 8) *reinterpret_cast<u32x4*>(&sU[buf][8 * tid]) = ur;
       uint16_t* vt = &sV[buf][(8 * v_dg) * VROW + 4 * v_kg];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -139,10 +150,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     float m_run = kNegBig, l_run = 0.f;
     const float sc = a.scale_log2;
 
-    float bias_next = 0.f;
+    // the row's routed bit for chunk c, from its bitmask word
+    auto routed = [&](int c, uint32_t word) { return qi < N && ((word >> (c & 31)) & 1u) != 0u; };
+    uint32_t word_next = 0u;
     if (count > 0) {
       load_chunk(list[0]);
-      bias_next = biasp[0];
+      word_next = rbits[list[0] >> 5];
       store_chunk(0);
     }
     __syncthreads();
@@ -150,12 +163,40 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     for (int it = 0; it < count; ++it) {
       const int buf = it & 1;
       const int c = list[it];
-      const float bias = bias_next;
+      const uint32_t word = word_next;
       const bool more = it + 1 < count;
-      if (more) {
-        load_chunk(list[it + 1]);
-        bias_next = biasp[(size_t)(it + 1) * kTileRows];
+      if (more) word_next = rbits[list[it + 1] >> 5];
+      // ---- the row's log2 weight for chunk c: the own chunk's from the
+      // routing; a routed past chunk's recomputed, log2 of (u - tau)^beta with u
+      // = <q, summary> in u units (high parts + low parts, as the routing
+      // scored it); -inf otherwise
+      float bias = -INFINITY;
+      if (causal && c == cw) {
+        bias = qi < N ? own_lw : -INFINITY;
+      } else if (!(causal && c > cw)) {
+        const bool rt = routed(c, word);
+        if (wave_any(rt)) {
+          const uint16_t* up = &sU[buf][8 * hi32];
+          float dot = 0.f;
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const u32x4 q4 = __builtin_bit_cast(u32x4, qb[s]);
+            const u32x4 h4 = *reinterpret_cast<const u32x4*>(up + 16 * s);
+            const u32x4 l4 = *reinterpret_cast<const u32x4*>(up + D + 16 * s);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dot = fmaf(bf16lo(q4[e]), bf16lo(h4[e]), dot);
+              dot = fmaf(bf16hi(q4[e]), bf16hi(h4[e]), dot);
+              dot = fmaf(bf16lo(q4[e]), bf16lo(l4[e]), dot);
+              dot = fmaf(bf16hi(q4[e]), bf16hi(l4[e]), dot);
+            }
+          }
+          const float t = sum_xor32(dot) - tau_r;
+          bias = rt && t > 0.f ? log2_prior<KIND>(t, a.beta) : -INFINITY;
+        }
       }
+      // the next chunk's loads go out once the weight's registers are free
+      if (more) load_chunk(list[it + 1]);
       const bool skip = (causal && c > cw) || wave_all(bias == -INFINITY);
       if (!skip) {
         // ---- S^T = K Q^T
@@ -290,6 +331,17 @@ constexpr int kCmWgPerCu = 3;  // resident chunk-major workgroups per CU
 // are scanned. Also resets the chunk-major kernel's queue head.
 __global__ __launch_bounds__(256) void k_cm_plan(PrefillAttnArgs a) {
   __shared__ int s_tmp[4][4];
+  if (a.pool[kPools] != (unsigned long long)a.pool_cap) {
+    // the routing laid the pool out for another workspace size: no chunk-major
+    // work; the merge kernel writes NaN rows
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *a.nitems = 0;
+      *a.qhead = 0;
+      *a.bad = 1;
+    }
+    return;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.bad = 0;
   auto n_items = [](int P) { return ((P + 31) / 32 + kCmBlocks - 1) / kCmBlocks; };
   const int base = blockIdx.x * 256;
   int pp = 0, pi = 0;
@@ -330,6 +382,7 @@ __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const size_t bh = (size_t)b * a.Hq + h;
+  if (*a.bad != 0) return;
   const int cnt = min(a.ccounts[bh * a.n_tiles + tile], kRoutePrefillMaxSlots);
   if (cnt == 0) return;
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, a.causal != 0);
@@ -607,8 +660,16 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const size_t bh = (size_t)b * a.Hq + hk * g + gh;
   const int tile = c * kChunk / kTileRows;
-  if (a.counts[bh * a.n_tiles + tile] > 0) return;  // a row-major tile
   const int tid = threadIdx.x;
+  if (*a.bad != 0) {
+    // inconsistent workspace: every row of the unit reads NaN
+    for (int x = tid; x < kChunk * D / 2; x += blockDim.x) {
+      const int r = c * kChunk + x / (D / 2);
+      if (r < N) reinterpret_cast<uint32_t*>(a.O + (bh * N + r) * (size_t)D)[x % (D / 2)] = 0x7fc07fc0u;
+    }
+    return;
+  }
+  if (a.counts[bh * a.n_tiles + tile] > 0) return;  // a row-major tile
   const int lane = lane_id();
   const int w = tid / kWave;
   const int row0 = c * kChunk;
@@ -819,7 +880,12 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
   const int n_units = a.n_tiles * a.B * a.Hkv;
   const int n_work = ((n_units + 7) / 8) * 8 * a.g;
   const int rm_grid = std::min(n_work, ((a.n_cu * 2 + 7) / 8) * 8);
-  hipLaunchKernelGGL(k_sparse_prefill<128>, dim3(rm_grid), dim3(256), 0, stream, a);
+  if (a.beta == 2.f)
+    hipLaunchKernelGGL((k_sparse_prefill<128, 2>), dim3(rm_grid), dim3(256), 0, stream, a);
+  else if (a.beta == 1.f)
+    hipLaunchKernelGGL((k_sparse_prefill<128, 1>), dim3(rm_grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_sparse_prefill<128, 0>), dim3(rm_grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

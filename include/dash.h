@@ -151,6 +151,11 @@ dash_status dash_summarize_backward(const void* K, const void* head_cls, const f
  *               bits_words >= ceil(ceil(Lmax / C) / 32).
  *   workspace   the routed work lists and log2 priors read by the matching
  *               dash_sparse_attn_* call; size from dash_workspace_size().
+ *               Prefill: the part beyond the fixed lists is the partial-result
+ *               pool of dash_sparse_attn_prefill, one slot per (row, routed
+ *               past chunk) pair (2 * d + 36 bytes each), so a larger workspace
+ *               buys a larger pool (dash_prefill_workspace_size); the same
+ *               ws_bytes must then be passed to dash_sparse_attn_prefill.
  * --------------------------------------------------------------------------- */
 dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
                        dash_dtype dt, int B, int Hq, int Hkv, int Nq, int Lmax, int d,
@@ -159,9 +164,30 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
                        size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of workspace that dash_route and dash_sparse_attn_* need for these
- * sizes (decode = 1 for the seqlens mode). 0 for invalid sizes. */
+ * sizes (decode = 1 for the seqlens mode). 0 for invalid sizes. Prefill: the
+ * fixed part plus a pool of max(5, min(16, 2048 / ceil(Nq / 64))) pairs per
+ * query row (16 up to Nq = 8192, 5 from Nq = 32768 on; the routed past chunks
+ * per row at the 32K workload average about 3.4). */
 size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int decode,
                            dash_params p);
+
+/* Bytes of prefill workspace with a partial-result pool of exactly pool_pairs
+ * (row, chunk) pairs; 0 for invalid sizes or pool_pairs outside
+ * [0, 0xffffff00]. Tiles whose pairs do not fit the pool are attended by the
+ * row-major kernel (correct, slower), so any pool size is valid: 0 sends every
+ * tile there. A workspace smaller than the pool-free part is rejected with
+ * DASH_ERR_WORKSPACE. */
+size_t dash_prefill_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, dash_params p,
+                                   long long pool_pairs);
+
+/* Counters of the last prefill routing in `workspace` (same sizes, params and
+ * ws_bytes as that dash_route call), written to out[0..3]: the (row, past
+ * chunk) pairs placed in the partial-result pool, the pool's capacity, the
+ * 128-row tiles the list-based routing kernel left to the general one, and
+ * the tiles attended row-major (their pairs did not fit the pool). Copies
+ * them to the host: the call synchronises `stream`. */
+dash_status dash_prefill_counters(const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N,
+                                  int d, dash_params p, long long* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * dash_sparse_attn_prefill -- stage 3, "Prior-induced sparse softmax" ("How it
@@ -175,10 +201,13 @@ size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int 
  * and values -- into a partial result (the log of its weight sum and its
  * normalised output), and each row's partials are then merged (the
  * online-softmax merge is exact in any order). Tiles of 128 rows whose pairs
- * did not fit the partial-result pool (16 per row on average; only near-dense
- * routing at long lengths exceeds it) are attended row by row instead; their
+ * did not fit the partial-result pool (its size set by ws_bytes, see
+ * dash_route) are attended row by row instead, with each row's prior weights
+ * recomputed from its tau, its routed-chunk bits and the summaries; their
  * results match up to rounding, so only then can two identical calls differ
- * in the last bits.
+ * in the last bits. ws_bytes must equal dash_route's: a workspace laid out for
+ * another pool size is detected on the device and every row of O is set to
+ * NaN.
  *   Q [B, Hq, N, d], K/V [B, Hkv, Lmax, d], O [B, Hq, N, d], all dtype dt.
  * --------------------------------------------------------------------------- */
 dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V,

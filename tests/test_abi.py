@@ -29,6 +29,7 @@ def test_header_symbols_exported(lib):
         "entmax_rows", "entmax_rows_backward", "entmax_attn_backward", "dash_summarize_backward",
         "dash_decode_step_noalloc", "dash_decode_noalloc_max_bytes",
         "dash_sparse_attn_prefill_backward", "dash_backward_workspace_size",
+        "dash_prefill_workspace_size", "dash_prefill_counters",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -57,6 +58,30 @@ def test_workspace_size(lib):
     # causal tiles are packed in a triangle: smaller than the rectangle
     assert lib.dash_workspace_size(1, 4, 4, 4096, 4096, 128, 0, p) < lib.dash_workspace_size(
         1, 4, 4, 4096, 4096, 128, 0, _p(causal=False))
+
+
+def test_prefill_workspace_pool(lib):
+    """The prefill workspace is a fixed part plus the partial-result pool
+    (2 d + 36 bytes per pair, rounded to 256-byte arrays); the default pool is
+    16 pairs per row up to 8K tokens and 5 from 32K on, which keeps the 32K
+    workload (B 1, 32 query heads, 8 KV heads, d 128) under 2 GB."""
+    p = _p()
+    base = lib.dash_prefill_workspace_size(1, 32, 8, 32768, 32768, 128, p, 0)
+    assert base > 0
+    assert lib.dash_prefill_workspace_size(1, 32, 8, 32768, 32768, 128, p, -1) == 0
+    assert lib.dash_prefill_workspace_size(1, 32, 8, 32768, 32768, 128, p, 1 << 33) == 0
+    assert lib.dash_prefill_workspace_size(1, 6, 4, 128, 128, 128, p, 0) == 0  # Hq % Hkv
+    for pairs in (1000, 10 ** 6):
+        grown = lib.dash_prefill_workspace_size(1, 32, 8, 32768, 32768, 128, p, pairs) - base
+        assert pairs * 292 <= grown <= pairs * 292 + 5 * 256 + 8 * (pairs // 768 + 1) + 256
+    rows32 = 32 * 32768
+    assert lib.dash_workspace_size(1, 32, 8, 32768, 32768, 128, 0, p) == lib.dash_prefill_workspace_size(
+        1, 32, 8, 32768, 32768, 128, p, 5 * rows32)
+    assert lib.dash_workspace_size(1, 32, 8, 32768, 32768, 128, 0, p) < 2 * 2 ** 30
+    assert lib.dash_workspace_size(1, 32, 8, 4096, 4096, 128, 0, p) == lib.dash_prefill_workspace_size(
+        1, 32, 8, 4096, 4096, 128, p, 16 * 32 * 4096)
+    assert lib.dash_workspace_size(1, 32, 8, 16384, 16384, 128, 0, p) == lib.dash_prefill_workspace_size(
+        1, 32, 8, 16384, 16384, 128, p, 8 * 32 * 16384)
 
 
 def _summ(lib, K=FAKE, cls=FAKE, S=FAKE, dt=1, B=1, Hkv=1, Lmax=128, d=128, n=128, seqlens=NULL, c0=0, c1=2, cap=2, p=None):

@@ -27,11 +27,20 @@ def _oracle_params(p: api.Params) -> oracle.DashParams:
                              causal=p.causal, estimate_diagonal=p.estimate_diagonal)
 
 
-def check_prefill(Q, K, V, cls, p: api.Params, rows_of=None, where=""):
+def _pool_workspace(Q, K, p: api.Params, pool_pairs: int):
+    B, Hq, N, d = Q.shape
+    n = api.prefill_workspace_size(B, Hq, K.shape[1], N, K.shape[2], d, p, pool_pairs)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device=Q.device)
+
+
+def check_prefill(Q, K, V, cls, p: api.Params, rows_of=None, where="", pool_pairs=None):
     """Run the GPU prefill and compare rows with the oracle.
 
-    rows_of(b, h) -> array of rows to check (default: all)."""
-    O, tau, bits, S, _ = api.prefill(Q, K, V, cls, p)
+    rows_of(b, h) -> array of rows to check (default: all). pool_pairs: the
+    partial-result pool's size (default: the workspace query's)."""
+    ws = None if pool_pairs is None else _pool_workspace(Q, K, p, pool_pairs)
+    O, tau, bits, S, ws = api.prefill(Q, K, V, cls, p, workspace=ws)
     torch.cuda.synchronize()
     B, Hq, N, d = Q.shape
     Hkv = K.shape[1]
@@ -63,7 +72,7 @@ def check_prefill(Q, K, V, cls, p: api.Params, rows_of=None, where=""):
                 assert_close(O_[b, h, rows], o_ref, TOL_BF16, f"{where} O b{b} h{h}")
                 checked += rows.size
     assert checked > 0
-    return O, tau, bits
+    return api.prefill_counters(ws, B, Hq, Hkv, N, d, p)
 
 
 def _inputs(B, Hq, Hkv, N, seed, planted="chunks"):
@@ -91,6 +100,56 @@ def test_prefill_small(B, Hq, Hkv, N, p, planted):
     check_prefill(Q, K, V, cls, p, where=f"N={N} {p}")
 
 
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,N,p,planted",
+    [
+        (1, 4, 1, 1000, api.Params(causal=True, estimate_diagonal=True), "chunks"),
+        (1, 4, 1, 1000, api.Params(causal=True, estimate_diagonal=False), "needles"),
+        (2, 4, 2, 700, api.Params(causal=False), "chunks"),
+        (1, 8, 2, 2048, api.Params(alpha=2.0), "chunks"),
+        (1, 2, 2, 520, api.Params(alpha=1.333, estimate_diagonal=True), "chunks"),
+    ],
+)
+def test_prefill_row_major_recomputed_weights(B, Hq, Hkv, N, p, planted):
+    """With no partial-result pool every tile is attended row-major, each row's
+    prior weight for a listed chunk recomputed from its tau, its routed-chunk
+    bits and the split summaries: the same rows as the chunk-major path."""
+    Q, K, V, cls = _inputs(B, Hq, Hkv, N, 7 + N, planted)
+    cnt = check_prefill(Q, K, V, cls, p, where=f"N={N} {p} pool 0", pool_pairs=0)
+    assert cnt["pool_capacity"] == 0 and cnt["pool_pairs"] == 0 and cnt["row_major_tiles"] > 0, cnt
+
+
+def test_prefill_partial_pool_mixes_paths():
+    """A pool of 40% of the routed past pairs: the tiles that reserve first go
+    chunk-major, the rest row-major, in one call; every row matches the oracle."""
+    Q, K, V, cls = _inputs(1, 8, 2, 2048, 31, "chunks")
+    p = api.Params()
+    _, _, bits, _, _ = api.prefill(Q, K, V, cls, p)
+    n_slots = -(-2048 // C)
+    att = unpack_bits(bits.cpu().numpy(), n_slots).sum()  # attended chunks, own ones included
+    past = int(att) - 8 * 2048
+    assert past > 0
+    cnt = check_prefill(Q, K, V, cls, p, where="partial pool", pool_pairs=int(0.4 * past))
+    assert 0 < cnt["pool_pairs"] <= cnt["pool_capacity"] and cnt["row_major_tiles"] > 0, cnt
+
+
+def test_prefill_workspace_size_mismatch_gives_nan():
+    """The pool's size follows ws_bytes, so routing and attention must be given
+    the same size: a smaller one in the attention call is caught on the device
+    and every output row is NaN (instead of reading a misplaced pool)."""
+    Q, K, V, cls = _inputs(1, 4, 1, 1000, 5, "chunks")
+    p = api.Params()
+    ws = _pool_workspace(Q, K, p, 100000)
+    api.prefill(Q, K, V, cls, p, workspace=ws)  # routes with the full size
+    small = api.prefill_workspace_size(1, 4, 1, 1000, 1000, 128, p, 50000)
+    O = api.sparse_attn_prefill(Q, K, V, ws[:small], p)
+    torch.cuda.synchronize()
+    assert torch.isnan(O.float()).all()
+    O = api.sparse_attn_prefill(Q, K, V, ws, p)  # the matching size works
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all()
+
+
 def test_prefill_zero_scaling_is_dense_causal():
     """scaling_factor 0: uniform prior over all candidates, i.e. dense causal softmax."""
     Q, K, V, cls = _inputs(1, 4, 2, 640, 99, None)
@@ -102,10 +161,10 @@ def test_prefill_zero_scaling_is_dense_causal():
 
 
 def test_prefill_pool_exhausted_falls_back_to_row_major():
-    """Uniform routing over 4096 causal keys needs about twice the partial-result
-    pool (16 slots per row): tiles that find it exhausted attend all their
-    chunks row-major, the others chunk-major; both must give dense causal
-    attention."""
+    """Uniform routing over 4096 causal keys needs about twice the default
+    partial-result pool (16 pairs per row at this length): tiles that find it
+    exhausted attend all their chunks row-major, the others chunk-major; both
+    must give dense causal attention."""
     Q, K, V, cls = _inputs(1, 2, 1, 4096, 17, None)
     O, tau, bits, _, _ = api.prefill(Q, K, V, cls, api.Params(scaling_factor=0.0))
     ref = torch.nn.functional.scaled_dot_product_attention(
@@ -124,9 +183,10 @@ def test_prefill_routing_heavy_and_left_tiles():
     Q[:, 0, 1536:3584] = 0
     rng = np.random.default_rng(23)
     fixed = np.array([0, 100, 1535, 1536, 1600, 2047, 2048, 2100, 2175, 2176, 3000, 3583, 3584, 4095])
-    check_prefill(Q, K, V, cls, api.Params(),
-                  rows_of=lambda b, h: np.unique(np.concatenate([fixed, rng.integers(1536, 3584, 10)])),
-                  where="heavy tiles")
+    cnt = check_prefill(Q, K, V, cls, api.Params(),
+                        rows_of=lambda b, h: np.unique(np.concatenate([fixed, rng.integers(1536, 3584, 10)])),
+                        where="heavy tiles")
+    assert cnt["general_route_tiles"] > 0, cnt
 
 
 def test_prefill_deterministic():
@@ -158,8 +218,10 @@ def test_prefill_32k_workload_sampled():
     p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
     rng = np.random.default_rng(w.seed)
     heads = {0, 9, 22, 31}
-    check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: _sample_rows(w.N, rng, 10) if h in heads else [],
-                  where="32k")
+    cnt = check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: _sample_rows(w.N, rng, 10) if h in heads else [],
+                        where="32k")
+    # the default workspace's pool (5 pairs per row) holds every routed pair here
+    assert cnt["row_major_tiles"] == 0 and cnt["pool_pairs"] < 0.8 * cnt["pool_capacity"], cnt
 
 
 def test_prefill_32k_workload_full_tiles():
