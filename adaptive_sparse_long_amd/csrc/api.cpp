@@ -185,7 +185,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   }
   if (Nq > Lmax) return DASH_ERR_INVALID_ARG;
   const int n_slots = (Nq + kChunk - 1) / kChunk;
-  if (n_slots > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if (n_slots > kPrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
   if (s_cap < (p.causal ? Nq / kChunk : n_slots)) return DASH_ERR_INVALID_ARG;
   if (active_bits && bits_words < (n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
   const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, Nq, d, p.causal != 0, ws_bytes);
@@ -220,6 +220,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
   a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
   a.s_err = reinterpret_cast<float*>(ws + L.off_serr);
+  a.gscr = reinterpret_cast<float*>(ws + L.off_gscr);
   return from_hip(launch_route_prefill(a, stream));
 }
 
@@ -234,7 +235,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
   if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
-  if ((N + kChunk - 1) / kChunk > kRoutePrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
+  if ((N + kChunk - 1) / kChunk > kPrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
   const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, d, p.causal != 0, ws_bytes);
   if (pool < 0) return DASH_ERR_WORKSPACE;
   const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0, pool);

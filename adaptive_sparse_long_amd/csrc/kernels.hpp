@@ -31,6 +31,15 @@ constexpr int kCmBlocks = 24;
 // The partial-result pool is split into kPools equal parts, each with its own
 // allocation counter (workgroup id modulo kPools picks the part).
 constexpr int kPools = 8;
+// Beyond 512 chunk slots the general routing kernel keeps its scores in a
+// global scratch: kRouteGlbGrid workgroups walk the queued tiles, each with
+// its own part (eight wavefronts x up to 128 blocks x 4 x 64 floats).
+constexpr int kRouteGlbGrid = 256;
+inline size_t route_glb_scratch_bytes(int n_slots) {
+  if (n_slots <= 512) return 0;
+  const size_t nb = n_slots <= 1024 ? 64 : 128;
+  return (size_t)kRouteGlbGrid * 8 * nb * 4 * 64 * sizeof(float);
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -80,6 +89,7 @@ struct PrefillLayout {
   size_t off_own = 0, off_qhead = 0, off_rmtau = 0, off_rmbits = 0;
   size_t off_split = 0;
   size_t off_serr = 0;  // per chunk: bound on |hi-only score - full score| / |q|
+  size_t off_gscr = 0;  // scores of the general routing kernel beyond 512 chunk slots
   size_t off_items = 0, off_recs = 0, off_trec = 0, off_plse = 0, off_po = 0;  // per pool slot
   long long pool_cap = 0;
   size_t fixed = 0, total = 0;
@@ -131,6 +141,7 @@ inline PrefillLayout prefill_layout(int B, int Hq, int Hkv, int N, int d, bool c
   L.off_rmbits = o;  o += align256(rows * L.words * sizeof(uint32_t));
   L.off_split = o;   o += align256((size_t)2 * B * Hkv * L.n_slots * d * sizeof(uint16_t));
   L.off_serr = o;    o += align256((size_t)B * Hkv * L.n_slots * sizeof(float));
+  L.off_gscr = o;    o += align256(route_glb_scratch_bytes(L.n_slots));
   L.fixed = o;
   L.off_items = o;   o += align256((size_t)L.max_items * 2 * sizeof(int));
   L.off_recs = o;    o += align256(pairs * 4 * sizeof(int));
@@ -258,6 +269,7 @@ struct RouteArgs {
   // per chunk: |s_lo| + 2^-14 |s| (u units), so that |q| times it bounds the
   // difference between a score from the high parts alone and the full one
   float* s_err;
+  float* gscr;  // general kernel's score scratch beyond 512 chunk slots
   // decode scratch
   float* z;
 };
@@ -446,9 +458,9 @@ hipError_t launch_entmax_attn_bwd(const EntmaxBwdArgs& a, bool bf16, hipStream_t
 hipError_t launch_dash_bwd(const DashBwdArgs& a, hipStream_t stream);
 
 // Limits of the current kernels (checked by the host API).
-constexpr int kRoutePrefillMaxSlots = 512;   // 32 blocks of 16 chunks in registers
+constexpr int kPrefillMaxSlots = 2048;       // prefill: N <= 131072
+constexpr int kRouteRegSlots = 512;          // general routing kernel: scores in registers (32 blocks of 16 chunks)
 constexpr int kRouteCap = 128;               // routing candidates per row held in LDS
-constexpr int kRouteListCap = 5120;          // LDS list words per tile: candidates, then 1024 for the chunk entries
 constexpr int kRouteDecodeMaxComplete = 4096; // 64 per lane
 constexpr int kEntmaxMaxTiles = 1024;        // candidate-tile bitmask per wavefront
 constexpr int kEntmaxCap = 16;               // candidate scores per lane in the single-pass kernel

@@ -64,11 +64,15 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& v, const float* w) {
 // ============================================================================
 // One workgroup per tile of the grid; the first ones take the tiles the
 // list-based kernel queued, the rest return at once.
-template <int NB, int KIND>
-__global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
+// One queued tile q. GLB: the scores live in this workgroup's part of a global
+// scratch (eight wavefronts x NB blocks x 4 x 64 floats) instead of registers,
+// for more chunks than registers hold.
+template <int NB, int KIND, bool GLB>
+__device__ __forceinline__ void route_general_tile(const RouteArgs& a, int q) {
   constexpr int D = 128;
   constexpr int NS = D / 32;                // k-steps of the 16x16x32 MFMA
   constexpr int NW = (NB * 16 + 31) / 32;   // union words
+  constexpr int NBR = GLB ? 1 : NB;         // score blocks in registers
   // Split summaries of 64 chunks per stage, shared by the eight wavefronts:
   // per chunk 128 high parts, 128 low parts and 8 bf16 of padding (a chunk
   // stride of 132 dwords keeps eight consecutive lanes on distinct LDS banks).
@@ -92,8 +96,6 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-  const int q = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  if (q >= *a.fb_count) return;
   const int tile = a.fb_tiles[q].x;
   const int h = a.fb_tiles[q].y % a.Hq;
   const int b = a.fb_tiles[q].y / a.Hq;
@@ -136,7 +138,18 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   // group once (the next group's loads in flight while the current one is
   // multiplied), then every wavefront reads its B operands from LDS.
   const float uscale = (a.alpha - 1.f) * a.zscale;
-  float u[NB][4];
+  float u[NBR][4];
+  float* const gu = GLB ? a.gscr + ((size_t)blockIdx.x * 8 + w) * (size_t)(NB * 4 * kWave) : nullptr;
+  // score of row grp*4 + r for chunk blk*16 + col
+  auto UV = [&](int blk, int r) -> float {
+    if constexpr (GLB) return gu[(blk * 4 + r) * kWave + lane];
+    else return u[blk][r];
+  };
+  auto USET = [&](int blk, int r, float v) {
+    if constexpr (GLB) gu[(blk * 4 + r) * kWave + lane] = v;
+    else u[blk][r] = v;
+  };
+  const int nbl = GLB ? nblk : NB;  // blocks the loops below visit
   const int last_row = min(tile * kTileRows + kTileRows, N) - 1;
   const int ncomp_wg = causal ? last_row / kChunk : n_slots;  // most chunks any wavefront scores
   const int ngrp = (ncomp_wg + 63) / 64;
@@ -168,7 +181,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int gi = 0; gi < (NB + 3) / 4; ++gi) {
+  for (int gi = 0; gi < (GLB ? ngrp : (NB + 3) / 4); ++gi) {
     if (gi < ngrp) {  // uniform over the workgroup
       const bool more = gi + 1 < ngrp;
       if (more) load_grp(gi + 1);
@@ -187,16 +200,12 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
             }
             // the summaries are pre-scaled: acc is u. Only the last block can
             // hold columns past the candidates.
+            const bool cval = blk < nblk - 1 || blk * 16 + col < ncomp;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u[blk][r] = acc[r];
-            if (blk == nblk - 1) {
-              const bool cval = blk * 16 + col < ncomp;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) u[blk][r] = cval ? u[blk][r] : -INFINITY;
-            }
+            for (int r = 0; r < 4; ++r) USET(blk, r, cval ? acc[r] : -INFINITY);
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
+            for (int r = 0; r < 4; ++r) USET(blk, r, -INFINITY);
           }
         }
       }
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int blk = gi * 4 + j;
-        if (blk < NB) {
+        if (blk < NBR) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) u[blk][r] = -INFINITY;
         }
@@ -280,22 +289,23 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
   for (int r = 0; r < 4; ++r) {
     float m = -INFINITY;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) m = fmaxf(m, u[blk][r]);
+    for (int blk = 0; blk < nbl; ++blk) m = fmaxf(m, UV(blk, r));
     mx[r] = fmaxf(max16(m), ud[r]);  // -inf: no candidate at all
     lo[r] = mx[r] - 1.f;
   }
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
+  for (int blk = 0; blk < nbl; ++blk) {
     if (blk < nblk) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool cnd = u[blk][r] > lo[r];
+        const float ub = UV(blk, r);
+        const bool cnd = ub > lo[r];
         const unsigned long long m = __ballot(cnd);
         if (m != 0ull) {
           const uint32_t seg = seg_of(m);
           const int pos = nc[r] + __popc(seg & below);
           if (cnd && pos < kRouteCap) {
-            s_cu[(grp * 4 + r) * LROW + pos] = u[blk][r];
+            s_cu[(grp * 4 + r) * LROW + pos] = ub;
             s_cc[(grp * 4 + r) * LROW + pos] = (uint16_t)(blk * 16 + col);
           }
           nc[r] += __popc(seg);
@@ -375,18 +385,21 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
       tau[r] = lo[r];
     }
     // blocks holding none of the candidates are left out of the iterations
-    uint32_t live = 0u;
+    uint32_t live = ~0u;
+    if constexpr (!GLB) {
+      live = 0u;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
-      live |= wave_any(any) ? (1u << blk) : 0u;
+      for (int blk = 0; blk < NB; ++blk) {
+        const bool any = (u[blk][0] > lo[0]) || (u[blk][1] > lo[1]) || (u[blk][2] > lo[2]) || (u[blk][3] > lo[3]);
+        live |= wave_any(any) ? (1u << blk) : 0u;
+      }
     }
     solve([&](float (&f0)[4], float (&f1)[4], float (&f2)[4]) {
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-              if ((live >> blk) & 1u) {
+            for (int blk = 0; blk < nbl; ++blk) {
+              if (GLB || ((live >> blk) & 1u)) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) tau_terms<KIND>(u[blk][r], tau[r], a.beta, f0[r], f1[r], f2[r]);
+                for (int r = 0; r < 4; ++r) tau_terms<KIND>(UV(blk, r), tau[r], a.beta, f0[r], f1[r], f2[r]);
               }
             }
           },
@@ -427,10 +440,10 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int blk = 2 * wd + half;
-        if (blk < NB) {
+        if (blk < nbl) {
           unsigned long long mb[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
+          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && UV(blk, r) > tau[r]);
           const unsigned long long mr = r4 == 0 ? mb[0] : r4 == 1 ? mb[1] : r4 == 2 ? mb[2] : mb[3];
           word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
         }
@@ -466,15 +479,16 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) run4[r] = 0;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
+    for (int blk = 0; blk < nbl; ++blk) {
       if (blk < nblk) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool act = row_ok[r] && u[blk][r] > tau[r];
+          const float ub = UV(blk, r);
+          const bool act = row_ok[r] && ub > tau[r];
           const uint32_t seg = seg_of(__ballot(act));
           const int rank = run4[r] + __popc(seg & below);
           run4[r] += __popc(seg);
-          if (act) fn(r, blk * 16 + col, rank, u[blk][r]);
+          if (act) fn(r, blk * 16 + col, rank, ub);
         }
       }
     }
@@ -608,13 +622,26 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     const int ne = s_cpre[NW];
     int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
     int first = 0;
-    const int cnt_e = (int)threadIdx.x < ne ? s_ecnt[threadIdx.x] : 0;
-    block_excl_scan<8>(cnt_e, s_tmp, first);
-    if ((int)threadIdx.x < ne) {
-      s_eoff[threadIdx.x] = first;
-      a.ceo[toff + threadIdx.x] = make_int2(first, cnt_e);
-      // the entry's pairs among all pairs of its chunk
-      a.cbase[toff + threadIdx.x] = atomicAdd(&cmp[s_cl[threadIdx.x]], cnt_e);
+    // entries EPT t .. EPT t + EPT - 1 per thread
+    constexpr int EPT = (NW * 32 + 511) / 512;
+    int esum = 0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = EPT * (int)threadIdx.x + k;
+      esum += e < ne ? s_ecnt[e] : 0;
+    }
+    block_excl_scan<8>(esum, s_tmp, first);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const int e = EPT * (int)threadIdx.x + k;
+      if (e < ne) {
+        const int cnt_e = s_ecnt[e];
+        s_eoff[e] = first;
+        a.ceo[toff + e] = make_int2(first, cnt_e);
+        // the entry's pairs among all pairs of its chunk
+        a.cbase[toff + e] = atomicAdd(&cmp[s_cl[e]], cnt_e);
+        first += cnt_e;
+      }
     }
     __syncthreads();
     auto put = [&](int e, int row, long long slot, float lw) {
@@ -648,10 +675,10 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int blk = 2 * wd + half;
-        if (blk < NB) {
+        if (blk < nbl) {
           unsigned long long mb[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && u[blk][r] > tau[r]);
+          for (int r = 0; r < 4; ++r) mb[r] = __ballot(row_ok[r] && UV(blk, r) > tau[r]);
           const unsigned long long mr = r4 == 0 ? mb[0] : r4 == 1 ? mb[1] : r4 == 2 ? mb[2] : mb[3];
           word |= (uint32_t)((mr >> (16 * rg)) & 0xffffull) << (16 * half);
         }
@@ -660,6 +687,22 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
     }
     if (write_rm)
       for (int wd = NW; wd < a.rm_words; ++wd) bdst[wd] = 0u;
+  }
+}
+
+// The general prefill routing for the tiles the list-based kernel queued: a
+// grid of workgroups walks the queue.
+template <int NB, int KIND, bool GLB>
+__global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
+  const int nq = *a.fb_count;
+  if constexpr (GLB) {
+    for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+      route_general_tile<NB, KIND, GLB>(a, q);
+      __syncthreads();  // the next tile reuses the LDS
+    }
+  } else {
+    // one workgroup per tile of the grid, the first nq of them take one each
+    if ((int)blockIdx.x < nq) route_general_tile<NB, KIND, GLB>(a, blockIdx.x);
   }
 }
 
@@ -687,23 +730,31 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 // row and its place among the pairs of its chunk follow without contended
 // atomics.
 // ============================================================================
-template <int KIND>
-__global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
+template <int KIND, int MS>
+__global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 16;  // k-steps of the 32x32x16 MFMA
   constexpr int SROW = D + 8;
-  constexpr int NWMAX = kRoutePrefillMaxSlots / 32;
-  constexpr int NE = kRoutePrefillMaxSlots;
-  constexpr int LCAP = kRouteListCap - 2 * NE;  // entries per tile (the chunk entries take the tail)
+  constexpr int NWMAX = MS / 32;  // chunk slots of the tile, in words
+  // tile list entries: every slot up to 512; beyond, 1024 (a tile whose
+  // chunk union is larger goes to the general kernel), so that two
+  // workgroups fit a CU's LDS
+  constexpr int NE = MS <= 512 ? MS : 1024;
+  constexpr int SH = MS <= 512 ? 9 : 11;  // a run key: tile row << SH | chunk
+  constexpr uint32_t CMASK = (1u << SH) - 1u;
+  constexpr int EPT = (NE + 255) / 256;   // tile list entries per thread
+  constexpr int kListWords = 4096 + 2 * NE;
+  constexpr int LCAP = kListWords - 2 * NE;  // entries per tile (the chunk entries take the tail)
+  static_assert(MS <= 2048 && (MS & (MS - 1)) == 0, "chunk slots: a power of two up to 2048");
   // summary stage (hi and lo parts of 32 chunks). After the passes: the
   // own-chunk key logits (estimate), then the tau sums (tau loop), then the
   // per-row bitmasks [kTileRows][NWMAX] and the per-entry row masks [NE][4]
   // (emission); the tau iterates and first pool slots per row at its end.
   constexpr int kStageWords = 2 * 32 * SROW / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t s_stage[2 * 32 * SROW];
-  static_assert(kStageWords >= kTileRows * NWMAX + NE * 4 + 2 * kTileRows, "scratch fits the stage");
+  constexpr int kLateWords = kTileRows * NWMAX + NE * 4 + 2 * kTileRows;
+  __shared__ __attribute__((aligned(16))) uint32_t s_scr[kStageWords > kLateWords ? kStageWords : kLateWords];
+  uint16_t* const s_stage = reinterpret_cast<uint16_t*>(s_scr);
   static_assert(kTileRows * NWMAX >= 4 * kChunk + 6 * kTileRows, "early scratch fits");
-  static_assert(NE <= 512 && kTileRows <= 128, "entries pack row and chunk into 16 bits");
   uint16_t* const sSh = s_stage;
   uint16_t* const sSl = s_stage + 32 * SROW;
   uint32_t* const s_words = reinterpret_cast<uint32_t*>(s_stage);
@@ -721,7 +772,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   // the entry list, an entry a 32-bit word: bits 10.. the distance below the
   // row's reference in units of 2^-21 (< 2), bits 5..9 the row in the wavefront, bits
   // 0..4 the chunk in the block; the tile's chunk entries in its tail
-  __shared__ __attribute__((aligned(16))) uint32_t s_list[kRouteListCap];
+  __shared__ __attribute__((aligned(16))) uint32_t s_list[kListWords];
   int* const s_cl = reinterpret_cast<int*>(s_list + LCAP);
   int* const s_eoff = s_cl + NE;
   __shared__ uint32_t s_wun[4][NWMAX], s_union[NWMAX];
@@ -731,7 +782,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   __shared__ int s_cnt;                     // entries in the list
   __shared__ int s_ownf[kTileRows];         // the row attends its own chunk
   __shared__ float s_bmax[NWMAX];           // per block of 32 chunks: the largest error bound
-  __shared__ int2 s_seg[4][kRoutePrefillMaxSlots / 32];  // per wavefront: (first, count | block << 16)
+  __shared__ int2 s_seg[4][MS / 32];  // per wavefront: (first, count | block << 16)
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -834,13 +885,11 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   // after the first barrier of pass 1)
   {
     const int clast = max(ncomp_wg - 1, 0);  // chunks past the tile's candidates repeat the last one
-    float e0 = a.s_err[(size_t)(b * a.Hkv + hk) * n_slots + min(tid, clast)];
-    float e1 = a.s_err[(size_t)(b * a.Hkv + hk) * n_slots + min(tid + 256, clast)];
-    e0 = max_xor16(max16(e0));  // over the 32 chunks of the half wavefront
-    e1 = max_xor16(max16(e1));
-    if ((lane & 31) == 0) {
-      s_bmax[tid >> 5] = e0;
-      s_bmax[8 + (tid >> 5)] = e1;
+#pragma unroll
+    for (int c0 = 0; c0 < MS; c0 += 256) {
+      float e = a.s_err[(size_t)(b * a.Hkv + hk) * n_slots + min(c0 + tid, clast)];
+      e = max_xor16(max16(e));  // over the 32 chunks of the half wavefront
+      if ((lane & 31) == 0) s_bmax[(c0 + tid) >> 5] = e;
     }
   }
   // |q| of the row (bf16 values as the MFMA sees them)
@@ -1026,7 +1075,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     const int rw = (e >> 5) & 31;
     const float mr = __shfl(m_list, rw);  // the max the distance is taken from
     uu = j < nl ? mr - (float)(e >> 10) * 4.76837158e-7f : -INFINITY;
-    kk = (uint32_t)(((w * 32 + rw) << 9) | ((sgv.y >> 16) * 32 + (e & 31)));
+    kk = (uint32_t)(((w * 32 + rw) << SH) | ((sgv.y >> 16) * 32 + (e & 31)));
   };
   float eu[RUNMAX];
   uint32_t ek[RUNMAX];
@@ -1097,7 +1146,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
         };
         for_run([&](int j, float uu, uint32_t kk) {
           if (j < nl) {
-            const int rr = kk >> 9;
+            const int rr = kk >> SH;
             if (rr != cur) {
               if (cur >= 0) flush();
               cur = rr;
@@ -1143,7 +1192,7 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   if (owner) s_ownf[R] = own_pair ? 1 : 0;
   __syncthreads();
   for_run([&](int j, float uu, uint32_t kk) {
-    const int rr = kk >> 9, c = kk & 511;
+    const int rr = kk >> SH, c = kk & CMASK;
     if (j < nl && uu > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
   });
   __syncthreads();
@@ -1162,8 +1211,9 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
   int nsl = 0;
   if (owner)
     for (int wd = 0; wd < NW; ++wd) nsl += __popc(s_bits[R][wd]);
-  // the wavefront's union: lane l ORs word l % 16 of rows 8 (l / 16) .. +7
-  {
+  // the wavefront's union
+  if constexpr (NWMAX == 16) {
+    // lane l ORs word l % 16 of rows 8 (l / 16) .. +7
     const int wd = lane & 15;
     uint32_t x = 0u;
 #pragma unroll
@@ -1171,6 +1221,12 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     x |= __shfl_xor(x, 16);
     x |= __shfl_xor(x, 32);
     if (lane < NWMAX) s_wun[w][lane] = x;
+  } else {
+    for (int wd = lane; wd < NWMAX; wd += kWave) {
+      uint32_t x = 0u;
+      for (int r = 0; r < 32; ++r) x |= s_bits[w * 32 + r][wd];
+      s_wun[w][wd] = x;
+    }
   }
 
   // ---- pool slots: one per attended chunk of every row of the tile, taken
@@ -1188,7 +1244,19 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
     if (lane == kWave - 1) s_wtot[w] = x;
   }
   __syncthreads();
-  if (tid < NWMAX) s_union[tid] = s_wun[0][tid] | s_wun[1][tid] | s_wun[2][tid] | s_wun[3][tid];
+  for (int x = tid; x < NWMAX; x += blockDim.x) s_union[x] = s_wun[0][x] | s_wun[1][x] | s_wun[2][x] | s_wun[3][x];
+  if constexpr (NE < MS) {
+    // a union (plus a row-major tile's own chunk) past NE entries: the tile
+    // goes to the general kernel before the pool is touched (what it wrote so
+    // far, tau, own-chunk weights and bits, the general kernel rewrites)
+    __syncthreads();
+    int ne_tile = 1;
+    for (int x = 0; x < NW; ++x) ne_tile += __popc(s_union[x]);
+    if (ne_tile > NE) {
+      if (tid == 0) a.fb_tiles[atomicAdd(a.fb_count, 1)] = make_int2(tile, (int)bh);
+      return;
+    }
+  }
   if (tid == kWave) {
     const int tot = s_wtot[0] + s_wtot[1] + s_wtot[2] + s_wtot[3];
     long long pbase = 0;  // a tile without routed past chunks needs no slots
@@ -1264,31 +1332,35 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
       s_rm[e][w] = m;
     }
     __syncthreads();
-    // entries 2t and 2t+1 per thread (up to 512)
+    // entries EPT t .. EPT t + EPT - 1 per thread
     auto ecount = [&](int e) { return __popc(s_rm[e][0]) + __popc(s_rm[e][1]) + __popc(s_rm[e][2]) + __popc(s_rm[e][3]); };
-    const int c0 = 2 * tid < ne ? ecount(2 * tid) : 0;
-    const int c1 = 2 * tid + 1 < ne ? ecount(2 * tid + 1) : 0;
+    int ec[EPT];
+    int esum = 0;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      ec[q] = EPT * tid + q < ne ? ecount(EPT * tid + q) : 0;
+      esum += ec[q];
+    }
     int first = 0;
-    block_excl_scan<4>(c0 + c1, s_tmp, first);
+    block_excl_scan<4>(esum, s_tmp, first);
     int* cmp = a.cmp + ((size_t)b * a.Hkv + hk) * n_slots;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = 2 * tid + q;
+    for (int q = 0; q < EPT; ++q) {
+      const int e = EPT * tid + q;
       if (e < ne) {
-        const int f = first + (q ? c0 : 0);
-        const int n = q ? c1 : c0;
-        s_eoff[e] = f;
-        a.ceo[toff + e] = make_int2(f, n);
+        s_eoff[e] = first;
+        a.ceo[toff + e] = make_int2(first, ec[q]);
       }
+      first += ec[q];
     }
     __syncthreads();
     // the entries' places among all pairs of their chunks (global atomics with
     // return): requested now, their results stored after the records
-    int cb[2];
+    int cb[EPT];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = 2 * tid + q;
-      cb[q] = e < ne ? atomicAdd(&cmp[s_cl[e]], q ? c1 : c0) : 0;
+    for (int q = 0; q < EPT; ++q) {
+      const int e = EPT * tid + q;
+      cb[q] = e < ne ? atomicAdd(&cmp[s_cl[e]], ec[q]) : 0;
     }
     auto place = [&](int e, int rr) {
       const int wr = rr >> 5;
@@ -1297,15 +1369,15 @@ __global__ __launch_bounds__(256, 4) void k_route_fast(RouteArgs a) {
       return j;
     };
     for_run([&](int j, float uu, uint32_t kk) {
-      const int rr = kk >> 9, c = kk & 511;
+      const int rr = kk >> SH, c = kk & CMASK;
       const float tr = s_t[rr];
       if (j < nl && uu > tr)
         a.trec[tb + place(epos(c), rr)] = make_int4((tile * kTileRows + rr) * g + hh, (int)(s_s0[rr] + rank_in_row(rr, c)),
                                                     __float_as_int(log2_prior<KIND>(uu - tr, a.beta)), 0);
     });
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (2 * tid + q < ne) a.cbase[toff + 2 * tid + q] = cb[q];
+    for (int q = 0; q < EPT; ++q)
+      if (EPT * tid + q < ne) a.cbase[toff + EPT * tid + q] = cb[q];
   } else {
     // ---- row-major tile: the rows' tau and routed past chunks, from which the
     // row-major kernel recomputes their weights
@@ -1608,15 +1680,22 @@ static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_split_summaries, dim3(blocks), dim3(256), 0, stream, a, n_need);
   }
   dim3 grid(a.n_tiles, a.Hq, a.B);
+  const unsigned n_grid_tiles = (unsigned)a.n_tiles * a.Hq * a.B;
   // the list-based kernel, then the general kernel for the tiles it queued
-  hipLaunchKernelGGL((k_route_fast<KIND>), grid, dim3(256), 0, stream, a);
-  const int nb = (a.n_slots + 15) / 16;
-#define DASH_RP(NBV)                                                                 \
-  if (nb <= NBV) {                                                                   \
-    hipLaunchKernelGGL((k_route_prefill<NBV, KIND>), grid, dim3(512), 0, stream, a); \
-    return hipGetLastError();                                                        \
+  if (a.n_slots <= kRouteRegSlots) {
+    hipLaunchKernelGGL((k_route_fast<KIND, kRouteRegSlots>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_route_fast<KIND, kPrefillMaxSlots>), grid, dim3(256), 0, stream, a);
   }
-  DASH_RP(2) DASH_RP(4) DASH_RP(8) DASH_RP(16) DASH_RP(32)
+  const int nb = (a.n_slots + 15) / 16;
+#define DASH_RP(NBV, GLB, GRID)                                                                  \
+  if (nb <= NBV) {                                                                               \
+    hipLaunchKernelGGL((k_route_prefill<NBV, KIND, GLB>), dim3(GRID), dim3(512), 0, stream, a); \
+    return hipGetLastError();                                                                    \
+  }
+  DASH_RP(2, false, n_grid_tiles) DASH_RP(4, false, n_grid_tiles) DASH_RP(8, false, n_grid_tiles)
+  DASH_RP(16, false, n_grid_tiles) DASH_RP(32, false, n_grid_tiles)
+  DASH_RP(64, true, kRouteGlbGrid) DASH_RP(128, true, kRouteGlbGrid)
 #undef DASH_RP
   return hipErrorInvalidValue;
 }

@@ -376,14 +376,14 @@ __global__ __launch_bounds__(256) void k_cm_plan(PrefillAttnArgs a) {
 // the same chunk). Thread q copies record q; its group is found by binary
 // search over the groups' first records.
 __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
-  __shared__ int s_first[kRoutePrefillMaxSlots];
-  __shared__ long long s_dst[kRoutePrefillMaxSlots];  // destination of record q: s_dst[group] + q
+  __shared__ int s_first[kPrefillMaxSlots];
+  __shared__ long long s_dst[kPrefillMaxSlots];  // destination of record q: s_dst[group] + q
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
   const size_t bh = (size_t)b * a.Hq + h;
   if (*a.bad != 0) return;
-  const int cnt = min(a.ccounts[bh * a.n_tiles + tile], kRoutePrefillMaxSlots);
+  const int cnt = min(a.ccounts[bh * a.n_tiles + tile], kPrefillMaxSlots);
   if (cnt == 0) return;
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, a.n_slots, a.causal != 0);
   const int* cs = a.cs + ((size_t)b * a.Hkv + h / a.g) * a.n_slots;

@@ -62,6 +62,15 @@ WORKLOADS = {
         "routed_prefill_32k", 1003, "prefill", 1, 32, 8, 32768, 128, "bf16", 1.5,
         causal=True, estimate_diagonal=False, planted="needles",
     ),
+    # the 32K recipe at longer contexts (beyond the 32K headline, for the length ceiling)
+    "routed_prefill_64k": Workload(
+        "routed_prefill_64k", 1008, "prefill", 1, 32, 8, 65536, 128, "bf16", 1.5,
+        causal=True, estimate_diagonal=False, planted="needles",
+    ),
+    "routed_prefill_128k": Workload(
+        "routed_prefill_128k", 1009, "prefill", 1, 32, 8, 131072, 128, "bf16", 1.5,
+        causal=True, estimate_diagonal=False, planted="needles",
+    ),
     "decode_128k": Workload(
         "decode_128k", 1004, "decode", 16, 32, 8, 131072, 128, "bf16", 1.5,
         causal=True, estimate_diagonal=True,

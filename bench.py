@@ -229,8 +229,11 @@ def bench_prefill(w, steps, warmup, summary_backward=True):
     del flush
     # work counts (outside the timed region)
     _, bits, _ = api.route(Q, K, cls, S, p, with_bits=True, workspace=ws)
+    counters = api.prefill_counters(ws, w.B, w.Hq, w.Hkv, w.N, w.d, p)
     alg, pair, dense, scores, per_row = prefill_work(bits, w.N, w.d)
     res = {
+        "workspace_GB": ws.numel() / 1e9,
+        "counters": counters,
         "ms_summarize": t_sum.mean_ms(),
         "ms_route": t_route.mean_ms(),
         "ms_attention": t_attn.mean_ms(),
@@ -589,6 +592,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-entmax", action="store_true")
     ap.add_argument("--no-4k", action="store_true", help="skip the 4K routed prefill workload")
+    ap.add_argument("--no-long", action="store_true", help="skip the 64K and 128K routed prefill workloads")
     ap.add_argument("--no-oracle-timings", action="store_true",
                     help="skip the oracle timings of the other workloads (the cpu_baseline leg stays)")
     ap.add_argument("--sparsity", action="store_true",
@@ -675,6 +679,9 @@ def main():
         "prefill": {
             "ms_summarize": pre["ms_summarize"], "ms_route": pre["ms_route"], "ms_attention": pre["ms_attention"],
             "routed_chunks_per_row": pre["routed_chunks_per_row"],
+            "workspace_GB": pre["workspace_GB"],
+            # pool pairs used / capacity, tiles left to the general routing kernel, row-major tiles
+            "counters": pre["counters"],
             # algorithmic attention flops over those of dense causal attention
             "alg_over_dense": pre["alg_flops"] / pre["dense_causal_flops"],
             # sparse attention (dash_sparse_attn_prefill, all of its kernels): MFMA
@@ -702,6 +709,23 @@ def main():
             "attention_alg_frac": p2["alg_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
             "attention_pair_frac": p2["pair_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         }
+    if not args.no_long:
+        # the 32K recipe at 64K and 128K tokens: the length ceiling of the path
+        out["prefill_long"] = {}
+        for name in ("routed_prefill_64k", "routed_prefill_128k"):
+            wl = WORKLOADS[name]
+            log(f"prefill {name}")
+            pl = bench_prefill(wl, min(args.steps, 10), min(args.warmup, 3), summary_backward=False)
+            msl = pl["ms_summarize"] + pl["ms_route"] + pl["ms_attention"]
+            out["prefill_long"][name] = {
+                "tokens_per_s": wl.N / (msl / 1e3), "ms_per_step": msl,
+                "ms_summarize": pl["ms_summarize"], "ms_route": pl["ms_route"], "ms_attention": pl["ms_attention"],
+                "routed_chunks_per_row": pl["routed_chunks_per_row"],
+                "alg_over_dense": pl["alg_flops"] / pl["dense_causal_flops"],
+                "attention_alg_frac": pl["alg_flops"] / (pl["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                "attention_pair_frac": pl["pair_flops"] / (pl["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                "workspace_GB": pl["workspace_GB"], "counters": pl["counters"],
+            }
     if not args.no_entmax:
         out["dense_entmax_128"] = bench_entmax_small(WORKLOADS["dense_entmax_128"], args.steps, args.warmup)
     if not args.no_decode:

@@ -118,7 +118,7 @@ def test_route_validation(lib):
     assert _route(lib, dt=0) == UNSUPPORTED
     assert _route(lib, p=_p(chunk_size=128)) == UNSUPPORTED
     assert _route(lib, Nq=300, Lmax=256) == INVALID
-    assert _route(lib, Nq=40000, Lmax=40000, cap=700) == UNSUPPORTED   # > 512 chunk slots in prefill
+    assert _route(lib, Nq=140000, Lmax=140000, cap=2200) == UNSUPPORTED  # > 2048 chunk slots in prefill
     assert _route(lib, cap=2) == INVALID                             # summary cache too small
     assert _route(lib, bits=FAKE, words=0) == INVALID
     assert _route(lib, ws_bytes=16) == WORKSPACE

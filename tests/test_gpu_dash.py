@@ -47,7 +47,7 @@ def check_prefill(Q, K, V, cls, p: api.Params, rows_of=None, where="", pool_pair
     g = Hq // Hkv
     op = _oracle_params(p)
     n_slots = -(-N // C)
-    O_, tau_, bits_, S_ = f64(O), f64(tau), bits.cpu().numpy(), f64(S)
+    S_ = f64(S)
     checked = 0
     for b in range(B):
         for hk in range(Hkv):
@@ -61,15 +61,16 @@ def check_prefill(Q, K, V, cls, p: api.Params, rows_of=None, where="", pool_pair
                 rows = np.arange(N) if rows_of is None else np.asarray(rows_of(b, h))
                 if rows.size == 0:
                     continue
-                qr = f64(Q[b, h, rows])
+                ri = torch.as_tensor(rows, device=O.device)
+                qr = f64(Q[b, h, ri])
+                o_got, t_got, b_got = f64(O[b, h, ri]), f64(tau[b, h, ri]), bits[b, h, ri].cpu().numpy()
                 Z, t_ref, _, logw = oracle.route_row(qr, rows, keys, clsv, N, op, summ)
                 o_ref, t2, b_ref = oracle.dash_rows(qr, rows, keys, vals, clsv, N, op, summ)
-                tau_close(tau_[b, h, rows], t_ref, f"{where} b{b} h{h}")
+                tau_close(t_got, t_ref, f"{where} b{b} h{h}")
                 with np.errstate(invalid="ignore"):
                     umt = (p.alpha - 1.0) * Z - t_ref[:, None]
-                assert_sets_match(unpack_bits(bits_[b, h, rows], n_slots), np.isfinite(logw), umt,
-                                  f"{where} b{b} h{h}")
-                assert_close(O_[b, h, rows], o_ref, TOL_BF16, f"{where} O b{b} h{h}")
+                assert_sets_match(unpack_bits(b_got, n_slots), np.isfinite(logw), umt, f"{where} b{b} h{h}")
+                assert_close(o_got, o_ref, TOL_BF16, f"{where} O b{b} h{h}")
                 checked += rows.size
     assert checked > 0
     return api.prefill_counters(ws, B, Hq, Hkv, N, d, p)
@@ -245,6 +246,37 @@ def test_prefill_32k_workload_scaling4_sampled():
     heads = {3, 12, 17, 30}
     check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: _sample_rows(w.N, rng, 10) if h in heads else [],
                   where="32k sf4")
+
+
+def test_prefill_long_general_routing_in_global_scratch():
+    """Past 512 chunk slots (here 40000 tokens: 625) the list-based routing uses
+    its 2048-slot form, and tiles it cannot keep (zero queries make every chunk
+    a candidate) go to the general kernel's global-scratch form; sampled rows of
+    both kinds of tile against the oracle."""
+    Q, K, V, cls = _inputs(1, 2, 1, 40000, 41)
+    Q[:, 0, 20000:24000] = 0
+    rng = np.random.default_rng(41)
+    fixed = np.array([0, 63, 64, 4095, 19999, 20000, 20100, 22000, 23999, 24000, 32767, 32768, 39935, 39999])
+    cnt = check_prefill(Q, K, V, cls, api.Params(),
+                        rows_of=lambda b, h: np.unique(np.concatenate([fixed, rng.integers(0, 40000, 8)])),
+                        where="40k general")
+    assert cnt["general_route_tiles"] > 0, cnt
+
+
+@pytest.mark.parametrize("name", ["routed_prefill_64k", "routed_prefill_128k"])
+def test_prefill_long_workload_sampled(name):
+    """The 32K needle recipe at 64K and 128K tokens (1024 and 2048 chunk
+    slots): sampled rows of two heads, plus a complete tile at the end."""
+    w = WORKLOADS[name]
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cuda")
+    p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    rng = np.random.default_rng(w.seed)
+    last = np.arange(w.N - 128, w.N)
+    cnt = check_prefill(Q, K, V, cls, p,
+                        rows_of=lambda b, h: (np.unique(np.concatenate([_sample_rows(w.N, rng, 8), last]))
+                                              if h in (5, 26) else []),
+                        where=name)
+    assert cnt["row_major_tiles"] == 0, cnt
 
 
 # ----------------------------------------------------------------------------- decode
