@@ -11,7 +11,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdash.so")
+# DASH_LIB names another build of the same library (the CPU ABI tests use it for
+# the host-sanitized build); the default is the in-tree libdash.so.
+LIB_PATH = os.environ.get("DASH_LIB") or os.path.join(PKG, "libdash.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "dash.h")
 
 DASH_F32 = 0

@@ -466,12 +466,15 @@ def decode_step(q, Kc, Vc, head_cls, S, seqlens, params: Params = Params(), leng
     Routes against the summary cache, attends over the routed chunks, then
     appends the summary of every chunk this token completed. ``lengths`` holds
     the same lengths on the host (ints); it only selects which chunk indices to
-    append, so no device-to-host copy is needed. Returns (O, tau, bits, workspace).
+    append. Without it the lengths are copied from ``seqlens`` to the host (one
+    stream synchronisation), so no completed chunk is ever left out of the cache.
+    Returns (O, tau, bits, workspace).
     """
     tau, bits, workspace = route(q, Kc, head_cls, S, params, seqlens=seqlens, with_bits=with_bits, workspace=workspace)
     O = sparse_attn_decode(q, Kc, Vc, seqlens, workspace, params)
-    if lengths is not None:
-        done = sorted({int(n) // CHUNK - 1 for n in lengths if int(n) % CHUNK == 0})
-        for c in done:
-            summarize(Kc, head_cls, S, seqlens=seqlens, chunk_begin=c, chunk_end=c + 1, params=params)
+    if lengths is None:
+        lengths = seqlens.tolist()
+    done = sorted({int(n) // CHUNK - 1 for n in lengths if int(n) % CHUNK == 0})
+    for c in done:
+        summarize(Kc, head_cls, S, seqlens=seqlens, chunk_begin=c, chunk_end=c + 1, params=params)
     return O, tau, bits, workspace

@@ -103,5 +103,34 @@ def build(verbose: bool = False, jobs: int | None = None, only_changed: bool = F
     return LIB
 
 
+# Host-code checking build: the C ABI layer (api.cpp: argument validation,
+# workspace layouts, launch set-up) compiled with AddressSanitizer and
+# UndefinedBehaviorSanitizer on its host side only (GPU code is never
+# instrumented), linked with the regular kernel objects. Loaded by the CPU ABI
+# tests with the ASan runtime preloaded; never by the product path.
+SAN_LIB = os.path.join(BUILD_DIR, "libdash_hostsan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Build _build/libdash_hostsan.so (needs the regular objects: run build() first)."""
+    hipcc = _hipcc()
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj):
+            raise RuntimeError(f"{obj} is missing: build the library first")
+        objs.append(obj)
+    api_obj = os.path.join(BUILD_DIR, "api_hostsan.o")
+    _run([hipcc, *_flags(), *SAN_FLAGS, "-O1", "-x", "hip", "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj], verbose)
+    objs = [api_obj if o.endswith(os.sep + "api.o") else o for o in objs]
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *SAN_FLAGS, "-o", SAN_LIB, *objs],
+         verbose)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv, only_changed="--changed" in sys.argv))
+    if "--host-sanitize" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))

@@ -78,8 +78,9 @@ void dash_default_params(dash_params* p) {
   p->estimate_diagonal = 1;
 }
 
-const char* dash_status_string(dash_status s) {
-  switch (s) {
+const char* dash_status_string(int status) {
+  // an int, not dash_status: any value a caller passes is valid to read
+  switch (status) {
     case DASH_OK: return "ok";
     case DASH_ERR_INVALID_ARG: return "invalid argument";
     case DASH_ERR_UNSUPPORTED: return "unsupported configuration";

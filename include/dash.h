@@ -53,7 +53,14 @@ typedef enum {
   DASH_ERR_HIP = 4
 } dash_status;
 
-typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+/* The two sentinels give the type the range of int, so that validation can
+ * read (and reject) any value a caller passes. */
+typedef enum {
+  DASH_F32 = 0,
+  DASH_BF16 = 1,
+  DASH_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  DASH_DTYPE_RANGE_MAX_ = 2147483647
+} dash_dtype;
 
 /* Arguments of the DashAttention wrapper ("Core API": chunk_size,
  * estimate_diagonal, scaling_factor) plus the entmax alpha and iteration
@@ -403,7 +410,7 @@ dash_status entmax_rows_backward(const void* Y, const void* dY, void* dX, dash_d
                                  int n, float alpha, hipStream_t stream);
 
 /* Human-readable name of a status code (static storage). */
-const char* dash_status_string(dash_status s);
+const char* dash_status_string(int status);
 
 #ifdef __cplusplus
 }
