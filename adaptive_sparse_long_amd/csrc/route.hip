@@ -4,16 +4,20 @@
 // Entmax"), the routed set (the entmax support) and the routing prior, packed as
 // work lists for the stage-3 attention kernels.
 //
-// Prefill: one workgroup of eight wavefronts per (b, query head, 128-row tile).
-// Each wavefront owns 16 query rows and keeps all their routing scores in
-// registers (16 rows x up to 512 chunks, the 16x16 MFMA output layout: every
-// lane holds 4 rows of one chunk per 16-chunk block), so the tau iterations
-// re-read registers, not memory. Scores come from v_mfma_f32_16x16x32_bf16 with
-// each float32 summary split into bf16 high and low parts (q is exact in bf16),
-// which keeps about 16 mantissa bits at bf16 MFMA rate. Row reductions are DPP
-// sums over the 16 lanes of a row group. The routed chunks of the 128 rows are
-// OR-ed into an LDS bitmask, compacted into an ascending list, and each row's
-// log2 prior for every listed chunk is written next to it.
+// Prefill: k_split_summaries scales the float32 summaries into u units and
+// splits them into bf16 high and low parts once per call. k_route_fast, one
+// workgroup of four wavefronts (32 rows each) per (b, query head, 128-row
+// tile), computes the scores with v_mfma_f32_32x32x16_bf16 on both parts (q is
+// exact in bf16, so about 16 mantissa bits reach the fp32 accumulator) in two
+// passes over the summaries staged through LDS: the high parts alone bound
+// each row's max from below, then the exact scores above that bound - 1 (the
+// only ones that can carry weight) go into an LDS list; tau, the routed set and
+// the work for stage 3 follow from the list. A 2048-slot form of the same
+// kernel serves N up to 131072. Tiles whose list or chunk union does not fit
+// are queued for k_route_prefill, the general kernel: eight wavefronts of 16
+// rows keep every score (registers up to 512 chunk slots, a per-workgroup
+// global scratch beyond), per-row LDS candidate lists, tau in a four-lanes-per-
+// row layout.
 //
 // Decode: a bandwidth-bound score kernel streams the float32 summary cache once
 // (eight lanes per summary row, four float4 loads each, all g query heads of a

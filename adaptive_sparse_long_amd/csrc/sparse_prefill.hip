@@ -4,24 +4,31 @@
 // over the tokens of the chunks routed to row i, with w the routing prior.
 // Visiting the routed chunks in any order gives the same result (the
 // order-invariance of the online softmax, "Axiom ledger" Property 2 on the CoSA
-// review page), so each tile walks its ascending chunk list.
+// review page), which is what lets the work be cut by chunk instead of by row.
 //
-// One workgroup (four wavefronts, 32 query rows each) per (b, query head, 128-row
-// tile), walking the union list of chunks routed to any of its rows. Per chunk:
-//   * the 64 x 128 K chunk (row-major) and V chunk (transposed) are staged in a
-//     double-buffered LDS ring, the next chunk's global loads in flight while
-//     the current one is computed;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (K from LDS as A, Q^T held in
-//     registers as B) -- in this orientation every lane owns one query row, so
-//     its bias, running max and sum are per-lane scalars and the score
-//     registers are directly the B operand P^T of the next product;
-//   * scores get the row's log2 weight, the causal mask on the own chunk, an
-//     online softmax in the exp2 domain, and O^T += V^T P^T accumulates in
-//     registers (V^T from LDS as A).
-// A wavefront skips a chunk that lies in its rows' future or that none of its
-// rows routed, so executed work follows 32-row unions, not 128-row ones.
-// Workgroups are issued longest-tile first, and the g query heads sharing a KV
-// head are placed on the same XCD so their chunk reads share that XCD's L2.
+// Rows close together rarely route the same chunks, so a row block's chunk
+// union is mostly empty pairs. The main path is chunk-major instead:
+//   * k_cm_plan / k_cm_scatter: the (row, routed past chunk) pairs the routing
+//     recorded per tile are sorted by (b, kv head, chunk) and cut into work
+//     items of up to kCmBlocks blocks of 32 pairs;
+//   * k_prefill_cm: a persistent grid walks the items; per item the chunk's K
+//     (row-major) and V (transposed) are staged once in LDS and each wavefront
+//     attends whole blocks of 32 pairs with v_mfma_f32_32x32x16_bf16 (S^T = K
+//     Q^T, a lane owns a pair; O^T = V^T P^T), gathering the pairs' query rows,
+//     and leaves one partial result per pair in the pool (log2 of its weight
+//     sum, float32; its normalised output, fp16);
+//   * k_prefill_merge: per (b, kv head, chunk, query head), the 64 rows' own
+//     (diagonal) chunk is attended as one causal 64 x 64 tile
+//     (v_mfma_f32_16x16x32_bf16) and merged with each row's partials (an exact
+//     online-softmax merge in a fixed order), so the always-attended own chunk
+//     never goes through the pool.
+// Tiles of 128 rows whose pairs did not fit the pool are attended by the
+// row-major fallback k_sparse_prefill: one workgroup (four wavefronts of 32
+// rows) per (b, query head, tile) walks the tile's chunk union with K/V chunks
+// in a double-buffered LDS ring, recomputing each row's prior weight for a
+// listed chunk from its tau and routed-chunk bits (a dot product with the
+// chunk's split summary). Work is spread so that the g query heads sharing a
+// KV head land on the same XCD and share its L2.
 #include <algorithm>
 
 #include "kernels.hpp"
@@ -674,6 +681,17 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   const int w = tid / kWave;
   const int row0 = c * kChunk;
   float* const sO = reinterpret_cast<float*>(s_raw);
+  // the merge's rows (32 per pass, eight lanes each): partial counts and first
+  // slots requested now, so that they arrive while the own chunk is attended
+  int n_ps[2];
+  uint32_t s0_ps[2];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qi = row0 + pass * 32 + tid / 8;
+    const size_t ri = bh * (size_t)N + min(qi, N - 1);
+    n_ps[pass] = qi < N ? (int)a.cmcnt[ri] : 0;
+    s0_ps[pass] = a.rslot[ri];
+  }
 
   if constexpr (CAUSAL) {
     uint16_t* const sK = reinterpret_cast<uint16_t*>(s_raw);
@@ -798,8 +816,8 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
     const int qi = row0 + rloc;
     if (qi >= N) break;  // uniform over the row's eight lanes; later passes are further out
     const size_t ri = bh * (size_t)N + qi;
-    int n = a.cmcnt[ri];
-    const size_t s0 = a.rslot[ri];
+    int n = pass == 0 ? n_ps[0] : n_ps[1];
+    const size_t s0 = pass == 0 ? s0_ps[0] : s0_ps[1];
     if ((long long)(s0 + n) > a.pool_cap) n = 0;
     const float lse_o = CAUSAL ? s_lse[rloc] : -INFINITY;
     float lse[NP];
