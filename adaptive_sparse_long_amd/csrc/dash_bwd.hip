@@ -170,14 +170,34 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   load_frags<BF, D>(fdo, a.dO + bh * (size_t)N * D, qi, row_ok);
   auto wrow = [&](int c) { return row_ok ? wt[(size_t)c * N + qi] : -INFINITY; };
 
-  // ---- the chunks some row of the wavefront attends
+  // ---- the chunks some row of the wavefront attends: the OR of the rows'
+  // routed-chunk bits (a listed chunk whose recomputed weight is -inf for every
+  // row only costs its visit), words loaded together
   const int c_end = causal ? min(r0 + 31, N - 1) / kChunk + 1 : a.n_slots;
   int* list = s_list[w];
   int nl = 0;
-  for (int c = 0; c < c_end; ++c) {
-    if (wave_any(wrow(c) > -INFINITY)) {
-      if (lane == 0) list[nl] = c;
-      ++nl;
+  {
+    const uint32_t* brow = a.bits + (bh * N + min(qi, N - 1)) * (size_t)a.bits_words;
+    const int nw = (c_end + 31) / 32;
+    for (int w0 = 0; w0 < nw; w0 += 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (row_ok && w0 + k < nw) ? brow[w0 + k] : 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t u = x[k];
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) u |= __shfl_xor(u, off);
+        const int wd = w0 + k;
+        if (wd * 32 + 32 > c_end) u &= wd * 32 >= c_end ? 0u : ((1u << (c_end - wd * 32)) - 1u);
+        u = __builtin_amdgcn_readfirstlane(u);
+        while (u) {
+          const int c = wd * 32 + __ffs(u) - 1;
+          if (lane == 0) list[nl] = c;
+          ++nl;
+          u &= u - 1u;
+        }
+      }
     }
   }
   wave_lds_fence();
@@ -192,42 +212,58 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
     }
   };
 
+  // The listed chunks' 32-key halves are visited in order, the next half's K
+  // and V fragments loaded while the current one is used (two fragment sets).
+  // The row's weight for the chunk comes with them.
+  Frags<BF, D> fk2, fv2;
+  float wc1 = -INFINITY, wc2 = -INFINITY;
+  auto load_half = [&](Frags<BF, D>& k_, Frags<BF, D>& v_, float& wc_, int j) {  // half j % 2 of entry j / 2
+    const int c = list[j >> 1];
+    const int kr = (2 * c + (j & 1)) * 32 + (lane & 31);
+    load_frags<BF, D>(k_, Kp, kr, kr < N);
+    load_frags<BF, D>(v_, Vp, kr, kr < N);
+    wc_ = wrow(c);
+  };
+  // fn(k fragments, v fragments, weight, half index j) over every half, prefetching
+  auto sweep = [&](auto&& fn) {
+    if (nl > 0) load_half(fk, fv, wc1, 0);
+    for (int e = 0; e < nl; ++e) {
+      load_half(fk2, fv2, wc2, 2 * e + 1);
+      fn(fk, fv, wc1, 2 * e);
+      if (e + 1 < nl) load_half(fk, fv, wc1, 2 * e + 2);
+      fn(fk2, fv2, wc2, 2 * e + 1);
+    }
+  };
+
   // ---- sweep 1: the softmax normaliser of every row and D_i = sum_j P_ij dP_ij
   // (= <dO_i, O_i> of the exact output), both online: l and t are rescaled
   // together whenever the running max grows
   float m = -INFINITY, l = 0.f, t = 0.f;
-  for (int e = 0; e < nl; ++e) {
-    const int c = list[e];
-    const float wc = wrow(c);
-#pragma unroll 1
-    for (int hb = 0; hb < 2; ++hb) {
-      const int kb = 2 * c + hb;
-      const int kr = kb * 32 + (lane & 31);
-      load_frags<BF, D>(fk, Kp, kr, kr < N);
-      load_frags<BF, D>(fv, Vp, kr, kr < N);
-      const f32x16 s = dot32<BF, D>(fk, fq);
-      const f32x16 dp = dot32<BF, D>(fv, fdo);
-      f32x16 x;
-      logits(kb, wc, s, x);
-      float bm = -INFINITY;
+  sweep([&](const Frags<BF, D>& k_, const Frags<BF, D>& v_, float wc, int j) {
+    const int c = list[j >> 1];
+    const int kb = 2 * c + (j & 1);
+    const f32x16 s = dot32<BF, D>(k_, fq);
+    const f32x16 dp = dot32<BF, D>(v_, fdo);
+    f32x16 x;
+    logits(kb, wc, s, x);
+    float bm = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[r]);
-      const float mn = fmaxf(m, bm);
-      if (mn > -INFINITY) {
-        float bl = 0.f, bt = 0.f;
+    for (int r = 0; r < 16; ++r) bm = fmaxf(bm, x[r]);
+    const float mn = fmaxf(m, bm);
+    if (mn > -INFINITY) {
+      float bl = 0.f, bt = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float ex = fast_exp2(x[r] - mn);
-          bl += ex;
-          bt = fmaf(ex, dp[r], bt);
-        }
-        const float sc_old = fast_exp2(m - mn);
-        l = fmaf(l, sc_old, bl);
-        t = fmaf(t, sc_old, bt);
-        m = mn;
+      for (int r = 0; r < 16; ++r) {
+        const float ex = fast_exp2(x[r] - mn);
+        bl += ex;
+        bt = fmaf(ex, dp[r], bt);
       }
+      const float sc_old = fast_exp2(m - mn);
+      l = fmaf(l, sc_old, bl);
+      t = fmaf(t, sc_old, bt);
+      m = mn;
     }
-  }
+  });
   {
     const float mo = max_xor32(m);
     const float f = (mo > -INFINITY && m > -INFINITY) ? fast_exp2(m - mo) : 0.f;
@@ -249,60 +285,67 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   uint16_t* kt = sKt[w];
-  for (int e = 0; e < nl; ++e) {
-    const int c = list[e];
-    const float wc = wrow(c);
-    float gs = 0.f;
-#pragma unroll 1
-    for (int hb = 0; hb < 2; ++hb) {
-      const int kb = 2 * c + hb;
-      const int kr = kb * 32 + (lane & 31);
-      load_frags<BF, D>(fk, Kp, kr, kr < N);
-      load_frags<BF, D>(fv, Vp, kr, kr < N);
-      const f32x16 s = dot32<BF, D>(fk, fq);
-      f32x16 dp = dot32<BF, D>(fv, fdo);
-      f32x16 x;
-      logits(kb, wc, s, x);
+  float gs = 0.f;
+  sweep([&](const Frags<BF, D>& k_, const Frags<BF, D>& v_, float wc, int j) {
+    const int c = list[j >> 1];
+    const int kb = 2 * c + (j & 1);
+    const f32x16 s = dot32<BF, D>(k_, fq);
+    f32x16 dp = dot32<BF, D>(v_, fdo);
+    f32x16 x;
+    logits(kb, wc, s, x);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(x[r] - lse);  // 0 where masked (x = -inf)
-        const float ds = p * (dp[r] - Di);
-        gs += ds;
-        dp[r] = ds;
-      }
-      stage_t_regs<D>(kt, fk);
-      wave_lds_fence();
-      acc_xt_w<BF, D>(acc, dp, kt, nullptr, 0, 0);
-      wave_lds_fence();
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(x[r] - lse);  // 0 where masked (x = -inf)
+      const float ds = p * (dp[r] - Di);
+      gs += ds;
+      dp[r] = ds;
     }
-    const float g = sum_xor32(gs);
-    if (row_ok) dzt[(size_t)c * N + qi] = g;  // both lanes of the row write the same value
-  }
+    stage_t_regs<D>(kt, k_);
+    wave_lds_fence();
+    acc_xt_w<BF, D>(acc, dp, kt, nullptr, 0, 0);
+    wave_lds_fence();
+    if (j & 1) {
+      const float g = sum_xor32(gs);
+      if (row_ok) dzt[(size_t)c * N + qi] = g;  // both lanes of the row write the same value
+      gs = 0.f;
+    }
+  });
 
   // ---- routing: the entmax Jacobian over the row's candidates
   // candidate: a past chunk; the own chunk only with the estimate (causal); every chunk (non-causal)
   auto candidate = [&](int c) { return !causal || c < ci || (a.est && c == ci); };
-  float A1 = 0.f, A2 = 0.f;
-  for (int e = 0; e < nl; ++e) {
+  // (weight, g) of entry e, the next entry's requested before this one is used
+  auto wg = [&](int e, float& wc_, float& g_) {
     const int c = list[e];
-    const float wc = wrow(c);
-    if (candidate(c) && wc > -INFINITY) {
-      const float g = dzt[(size_t)c * N + qi];
-      A1 = fmaf(fast_exp2((1.f - a.alpha) * wc), g, A1);
-      A2 += fast_exp2((2.f - a.alpha) * wc);
+    wc_ = wrow(c);
+    g_ = row_ok ? dzt[(size_t)c * N + qi] : 0.f;
+  };
+  float A1 = 0.f, A2 = 0.f;
+  {
+    float wn = -INFINITY, gn = 0.f;
+    if (nl > 0) wg(0, wn, gn);
+    for (int e = 0; e < nl; ++e) {
+      const int c = list[e];
+      const float wc = wn, g = gn;
+      if (e + 1 < nl) wg(e + 1, wn, gn);
+      if (candidate(c) && wc > -INFINITY) {
+        A1 = fmaf(fast_exp2((1.f - a.alpha) * wc), g, A1);
+        A2 += fast_exp2((2.f - a.alpha) * wc);
+      }
     }
   }
   const float ratio = A2 > 0.f ? A1 / A2 : 0.f;
   // dQ = acc / sqrt(d) + rt * sum_c dz_c s_c: the routing term enters acc times sqrt(d) = sf / rt
   const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * a.s_cap * D;
+  float wn = -INFINITY, gn = 0.f;
+  if (nl > 0) wg(0, wn, gn);
   for (int e = 0; e < nl; ++e) {
     const int c = list[e];
-    const float wc = wrow(c);
+    const float wc = wn, g = gn;
+    if (e + 1 < nl) wg(e + 1, wn, gn);
     float dz = 0.f;
-    if (candidate(c) && wc > -INFINITY) {
-      const float g = dzt[(size_t)c * N + qi];
+    if (candidate(c) && wc > -INFINITY)
       dz = fmaf(fast_exp2((1.f - a.alpha) * wc), g, -fast_exp2((2.f - a.alpha) * wc) * ratio);
-    }
     if (row_ok) dzt[(size_t)c * N + qi] = dz;
     // the own chunk's estimate passes its gradient on in k_dbwd_est
     if (dz != 0.f && !(causal && c == ci)) {
@@ -326,9 +369,12 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
   constexpr bool BF = true;
+  constexpr int LC = 512;  // pair list entries per wavefront
   __shared__ __attribute__((aligned(16))) uint16_t sQt[4][D * kTRow];
   __shared__ __attribute__((aligned(16))) uint16_t sOt[4][D * kTRow];
   __shared__ __attribute__((aligned(16))) float sRow[4][4][32];
+  __shared__ int sRowIdx[4][32];
+  __shared__ int s_pairs[4][LC];  // (head in group << 20) | row
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -363,63 +409,108 @@ __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
   float* srl = sRow[w][1];
   float* srd = sRow[w][2];
   float* srz = sRow[w][3];
-  const int qb0 = causal ? k0 / 32 : 0;
-  const int n_qb = (N + 31) / 32;
-  for (int hh = 0; hh < a.g; ++hh) {
-    const size_t bh = (size_t)b * a.Hq + hk * a.g + hh;
-    const float* wtc = a.WT + (bh * a.n_slots + c) * (size_t)N;
-    const float* dztc = a.DZT + (bh * a.n_slots + c) * (size_t)N;
-    const uint16_t* Qp = a.Q + bh * (size_t)N * D;
-    const uint16_t* dOp = a.dO + bh * (size_t)N * D;
-    for (int qb = qb0; qb < n_qb; ++qb) {
-      const int q0 = qb * 32;
-      const int qm = q0 + (lane & 31);
-      const bool ok = qm < N;
-      const float wq = ok ? wtc[qm] : -INFINITY;
-      if (wave_all(wq == -INFINITY)) continue;  // no row of the block attends chunk c
-      load_frags<BF, D>(fq, Qp, qm, ok);
-      load_frags<BF, D>(fdo, dOp, qm, ok);
-      const f32x16 s = dot32<BF, D>(fq, fk);    // S[row][key]
-      const f32x16 dp = dot32<BF, D>(fdo, fv);  // dP[row][key]
-      if (lane < 32) {
-        srw[lane] = wq;
-        srl[lane] = ok ? a.lse[bh * N + qm] : 0.f;
-        srd[lane] = ok ? a.Dd[bh * N + qm] : 0.f;
-        // the summary gradient takes dz of rows that route c as a past (or, non-causal, any)
-        // chunk; dz is stored only where the row's wavefront listed c, which it did if the row attends c
-        srz[lane] = (ok && wq > -INFINITY && (!causal || qm / kChunk > c)) ? dztc[qm] : 0.f;
-      }
-      wave_lds_fence();
-      f32x16 p, ds, z;
-      bool any_z = false;
+  int* sri = sRowIdx[w];
+  int* pairs = s_pairs[w];
+  const size_t bh0 = (size_t)b * a.Hq + hk * a.g;
+
+  // ---- 32 listed (head, row) pairs attending chunk c at a time: their query and
+  // dO rows gathered (a lane per pair), S^T and dP^T against the wavefront's 32
+  // keys, then dV^T += dO^T P, dK^T += Q^T dS and the chunk's summary gradient
+  auto process = [&](int e0, int ne) {
+    const int m = lane & 31;
+    const bool ok = m < ne;
+    const int ent = ok ? pairs[e0 + m] : 0;
+    const int hh = ent >> 20, row = ent & 0xfffff;
+    const size_t bh = bh0 + hh;
+    load_frags<BF, D>(fq, a.Q + bh * (size_t)N * D, row, ok);
+    load_frags<BF, D>(fdo, a.dO + bh * (size_t)N * D, row, ok);
+    const f32x16 s = dot32<BF, D>(fq, fk);    // S[pair][key]
+    const f32x16 dp = dot32<BF, D>(fdo, fv);  // dP[pair][key]
+    if (lane < 32) {
+      const float wq = ok ? a.WT[(bh * a.n_slots + c) * (size_t)N + row] : -INFINITY;
+      srw[m] = wq;
+      srl[m] = ok ? a.lse[bh * N + row] : 0.f;
+      srd[m] = ok ? a.Dd[bh * N + row] : 0.f;
+      // the summary gradient takes dz of rows that route c as a past (or,
+      // non-causal, any) chunk
+      srz[m] = (ok && wq > -INFINITY && (!causal || row / kChunk > c))
+                   ? a.DZT[(bh * a.n_slots + c) * (size_t)N + row] : 0.f;
+      sri[m] = ok ? row : -1;
+    }
+    wave_lds_fence();
+    f32x16 p, ds, z;
+    bool any_z = false;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(srw + 8 * g4 + 4 * hi32);
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(srl + 8 * g4 + 4 * hi32);
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(srd + 8 * g4 + 4 * hi32);
-        const f32x4 zv = *reinterpret_cast<const f32x4*>(srz + 8 * g4 + 4 * hi32);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(srw + 8 * g4 + 4 * hi32);
+      const f32x4 lv = *reinterpret_cast<const f32x4*>(srl + 8 * g4 + 4 * hi32);
+      const f32x4 dv4 = *reinterpret_cast<const f32x4*>(srd + 8 * g4 + 4 * hi32);
+      const f32x4 zv = *reinterpret_cast<const f32x4*>(srz + 8 * g4 + 4 * hi32);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 4 * g4 + k;
+        const int q = sri[8 * g4 + 4 * hi32 + k];
+        const bool on = key_ok && q >= 0 && (!causal || kj <= q) && wv[k] > -INFINITY;
+        const float pr = on ? fast_exp2(fmaf(s[r], sc, wv[k]) - lv[k]) : 0.f;
+        p[r] = pr;
+        ds[r] = pr * (dp[r] - dv4[k]);
+        z[r] = zv[k];
+        any_z = any_z || zv[k] != 0.f;
+      }
+    }
+    stage_t_regs<D>(qt, fq);
+    stage_t_regs<D>(ot, fdo);
+    wave_lds_fence();
+    acc_xt_w<BF, D>(dv, p, ot, nullptr, 0, 0);
+    acc_xt_w<BF, D>(dk, ds, qt, nullptr, 0, 0);
+    if (first_half && wave_any(any_z)) acc_xt_w<BF, D>(dsum, z, qt, nullptr, 0, 0);
+    // the next block overwrites the LDS slots only after every lane has read them
+    wave_lds_fence();
+  };
+
+  // ---- the pairs: rows (that can see a key of this wavefront) whose weight for
+  // chunk c is finite, in (head, row) order, 256 rows of a head per step (four
+  // per lane), two steps' loads in flight; full blocks of 32 are processed
+  // whenever the list nears its capacity, the rest at the end
+  const int r_begin = causal ? k0 : 0;
+  int np = 0;
+  for (int hh = 0; hh < a.g; ++hh) {
+    const float* wtc = a.WT + ((bh0 + hh) * a.n_slots + c) * (size_t)N;
+    for (int r = r_begin; r < N; r += 512) {
+      float wv[2][4];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int rr = r + 256 * st + 4 * lane;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wv[st][k] = rr + k < N ? wtc[rr + k] : -INFINITY;
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int rr = r + 256 * st + 4 * lane;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int r = 4 * g4 + k;
-          const int q = q0 + 8 * g4 + 4 * hi32 + k;
-          const bool on = key_ok && q < N && (!causal || kj <= q) && wv[k] > -INFINITY;
-          const float pr = on ? fast_exp2(fmaf(s[r], sc, wv[k]) - lv[k]) : 0.f;
-          p[r] = pr;
-          ds[r] = pr * (dp[r] - dv4[k]);
-          z[r] = zv[k];
-          any_z = any_z || zv[k] != 0.f;
+          const bool on = wv[st][k] > -INFINITY;
+          const uint64_t bm = __ballot(on);
+          const int pos = np + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
+          if (on) pairs[pos] = (hh << 20) | (rr + k);
+          np += __popcll(bm);
+        }
+        if (np > LC - 256) {
+          wave_lds_fence();
+          const int full = np & ~31;
+          for (int e0 = 0; e0 < full; e0 += 32) process(e0, 32);
+          const int rest = np - full;
+          const int moved = lane < rest ? pairs[full + lane] : 0;
+          wave_lds_fence();
+          if (lane < rest) pairs[lane] = moved;
+          np = rest;
         }
       }
-      stage_t_regs<D>(qt, fq);
-      stage_t_regs<D>(ot, fdo);
-      wave_lds_fence();
-      acc_xt_w<BF, D>(dv, p, ot, nullptr, 0, 0);
-      acc_xt_w<BF, D>(dk, ds, qt, nullptr, 0, 0);
-      if (first_half && wave_any(any_z)) acc_xt_w<BF, D>(dsum, z, qt, nullptr, 0, 0);
-      // the next block overwrites the LDS slots only after every lane has read them
-      wave_lds_fence();
     }
   }
+  wave_lds_fence();
+  for (int e0 = 0; e0 < np; e0 += 32) process(e0, min(32, np - e0));
+
   if (key_ok) {
     store_line<false, D>(a.dKf, ((size_t)b * a.Hkv + hk) * N + kj, dk, a.inv_sqrt_d);
     store_line<true, D>(a.dV, ((size_t)b * a.Hkv + hk) * a.Lmax + kj, dv, 1.f);

@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from adaptive_sparse_long_amd import api  # noqa: E402
+from adaptive_sparse_long_amd import _lib, api  # noqa: E402
 from adaptive_sparse_long_amd.workloads import (  # noqa: E402
     WORKLOADS,
     decode_inputs,
@@ -270,6 +270,37 @@ def bench_prefill(w, steps, warmup, summary_backward=True):
     del Q, K, V, S, ws, O, bits
     torch.cuda.empty_cache()
     return res
+
+
+def bench_dash_backward(w, steps, warmup):
+    """dash_sparse_attn_prefill_backward on a prefill workload: gradients into Q,
+    K, V and head_cls for a random cotangent, timed with HIP events per call."""
+    dev = torch.device("cuda")
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device=dev)
+    p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    _, tau, bits, S, ws = api.prefill(Q, K, V, cls, p)
+    alg_fwd = prefill_work(bits, w.N, w.d)[0]
+    del ws
+    torch.cuda.empty_cache()
+    dO = cotangent(tuple(Q.shape), w.seed + 800, dtype="bf16", device=dev)
+    need = int(_lib.load().dash_backward_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.N, w.d, p.c()))
+    wsb = torch.empty(need, dtype=torch.uint8, device=dev)
+    flush = CacheEvictor(dev)
+    t = Timer()
+    for it in range(warmup + steps):
+        flush()
+        e = t.start() if it >= warmup else None
+        api.prefill_backward(Q, K, V, cls, S, dO, tau, bits, p, workspace=wsb)
+        if it >= warmup:
+            t.stop(e)
+    torch.cuda.synchronize()
+    ms = t.mean_ms()
+    # five products per visible routed (row, key) entry: S and dP recomputed, dV, dQ, dK
+    alg = alg_fwd * 2.5
+    del Q, K, V, cls, tau, bits, S, dO, wsb, flush
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "ms": ms, "alg_flops": alg, "alg_tflops": alg / (ms / 1e3) / 1e12,
+            "alg_frac": alg / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_GB": need / 1e9}
 
 
 # --------------------------------------------------------------------------- decode
@@ -593,6 +624,7 @@ def main():
     ap.add_argument("--no-entmax", action="store_true")
     ap.add_argument("--no-4k", action="store_true", help="skip the 4K routed prefill workload")
     ap.add_argument("--no-long", action="store_true", help="skip the 64K and 128K routed prefill workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the 32K prefill backward")
     ap.add_argument("--no-oracle-timings", action="store_true",
                     help="skip the oracle timings of the other workloads (the cpu_baseline leg stays)")
     ap.add_argument("--sparsity", action="store_true",
@@ -726,6 +758,9 @@ def main():
                 "attention_pair_frac": pl["pair_flops"] / (pl["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                 "workspace_GB": pl["workspace_GB"], "counters": pl["counters"],
             }
+    if not args.no_backward:
+        log("prefill backward 32k")
+        out["prefill_backward"] = bench_dash_backward(wp, min(args.steps, 10), min(args.warmup, 3))
     if not args.no_entmax:
         out["dense_entmax_128"] = bench_entmax_small(WORKLOADS["dense_entmax_128"], args.steps, args.warmup)
     if not args.no_decode:

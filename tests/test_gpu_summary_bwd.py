@@ -24,6 +24,7 @@ def _reference(K, cls, dS, n_tokens, c0, c1, chunks=None):
     B, Hkv, Lmax, d = K.shape
     dK = np.zeros((B, Hkv, Lmax, d))
     dcls = np.zeros((Hkv, d))
+    n_terms, term_max = 0, 0.0
     for b in range(B):
         for h in range(Hkv):
             for c in range(c0, c1):
@@ -32,9 +33,19 @@ def _reference(K, cls, dS, n_tokens, c0, c1, chunks=None):
                     continue
                 dk, dc = oracle.chunk_summary_backward(K[b, h, t0:t1], cls[h], dS[b, h, c])
                 dcls[h] += dc
+                n_terms += 1 if h == 0 else 0
+                term_max = max(term_max, float(np.abs(dc).max()))
                 if chunks is None or c in chunks:
                     dK[b, h, t0:t1] = dk
+    _reference.last_terms = (n_terms, term_max)
     return dK, dcls
+
+
+def dcls_tol(n_terms, term_max):
+    """dcls is a float32 sum of n per-chunk terms (each within float32 rounding of
+    its exact value): its error grows with n times the largest term. The bar is
+    1e-4 plus n * 2^-22 (four float32 ulps) times that largest term."""
+    return TOL_F32 + n_terms * 2.0 ** -22 * term_max
 
 
 @pytest.mark.parametrize("B,Hkv,Lmax,n_tokens,c0,c1,cls_scale", [
@@ -85,8 +96,9 @@ def test_summarize_backward_32k_workload():
     rng = np.random.default_rng(w.seed)
     sample = set(int(c) for c in np.concatenate([[0, n_c - 1], rng.integers(0, n_c, 6)]))
     rK, rc = _reference(f64(K), f64(cls), f64(dS), w.N, 0, n_c, chunks=sample)
-    # dcls adds 512 chunk terms (up to ~10 each with the x4 needle keys) in float32
-    assert_close(f64(dcls), rc, TOL_F32 * 10, "dcls (sum of 512 chunk terms)")
+    # dcls adds 512 chunk terms per head (up to ~10 each with the x4 needle keys)
+    n_terms, term_max = _reference.last_terms
+    assert_close(f64(dcls), rc, dcls_tol(n_terms, term_max), f"dcls (sum of {n_terms} chunk terms)")
     for c in sorted(sample):
         assert_close(f64(dK[:, :, c * C : (c + 1) * C]), rK[:, :, c * C : (c + 1) * C], TOL_F32, f"dK chunk {c}")
 
@@ -106,11 +118,14 @@ def test_summarize_backward_decode_cache():
     for h in (0, 7):
         Kh, dSh, ch = f64(K[:, h]), f64(dS[:, h]), f64(cls[h])
         ref = np.zeros(w.d)
+        term_max = 0.0
         for b in range(w.B):
             for c in range(n_c):
-                ref += oracle.chunk_summary_backward(Kh[b, c * C : (c + 1) * C], ch, dSh[b, c])[1]
+                dc = oracle.chunk_summary_backward(Kh[b, c * C : (c + 1) * C], ch, dSh[b, c])[1]
+                ref += dc
+                term_max = max(term_max, float(np.abs(dc).max()))
         # 32768 chunk terms added in float32
-        assert_close(f64(dcls[h]), ref, TOL_F32 * 100, f"dcls head {h}")
+        assert_close(f64(dcls[h]), ref, dcls_tol(w.B * n_c, term_max), f"dcls head {h}")
     rng = np.random.default_rng(w.seed)
     for _ in range(8):
         b, h, c = int(rng.integers(0, w.B)), int(rng.integers(0, w.Hkv)), int(rng.integers(0, n_c))
