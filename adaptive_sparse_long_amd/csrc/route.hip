@@ -770,7 +770,10 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   // (after the own-chunk logits, which other wavefronts may still be reading)
   Fx (*const s_sum)[kTileRows] = reinterpret_cast<Fx (*)[kTileRows]>(s_words + 4 * kChunk);
   uint32_t (*const s_bits)[NWMAX] = reinterpret_cast<uint32_t (*)[NWMAX]>(s_words);
+  // per list entry (per chunk in the 512-slot form, where that is the same
+  // size): the rows of each wavefront that take it
   uint32_t (*const s_rm)[4] = reinterpret_cast<uint32_t (*)[4]>(s_words + kTileRows * NWMAX);
+  constexpr bool kRmByChunk = NE == MS;
   float* const s_t = reinterpret_cast<float*>(s_words + kTileRows * NWMAX + NE * 4);  // tau iterate per row
   uint32_t* const s_s0 = s_words + kTileRows * NWMAX + NE * 4 + kTileRows;           // first pool slot per row
   // the entry list, an entry a 32-bit word: bits 10.. the distance below the
@@ -819,17 +822,10 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   const int nblk_wg = (ncomp_wg + 31) / 32;
   const size_t sbase = ((size_t)b * a.Hkv + hk) * (size_t)n_slots * D;
 
-  // ---- q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
-  bf16x8 qb[NS];
-  {
-    const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * hi32;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
-  }
-
   // ---- passes over the summary blocks of the tile: body(kb, u) with u the
   // row's scores of block kb (-inf past the candidates), for the wavefront's
   // blocks; HI: from the high parts of the summaries alone
+  bf16x8 qb[NS];  // q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7 (loaded below)
   u32x4 gl[4];
   auto load_stage = [&](auto hi_tag, int kb) {  // 32 chunks x (hi[, lo]) x 16 segments of 16 bytes
     constexpr bool HI = decltype(hi_tag)::value;
@@ -852,9 +848,10 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
       *reinterpret_cast<u32x4*>(&(part < 16 ? sSh : sSl)[cc * SROW + 8 * (part & 15)]) = gl[k];
     }
   };
-  auto scan_blocks = [&](auto hi_tag, auto&& body) {
+  // first_loaded: the first block's loads were issued by the caller
+  auto scan_blocks = [&](auto hi_tag, bool first_loaded, auto&& body) {
     constexpr bool HI = decltype(hi_tag)::value;
-    if (nblk_wg > 0) load_stage(hi_tag, 0);
+    if (nblk_wg > 0 && !first_loaded) load_stage(hi_tag, 0);
     for (int kb = 0; kb < nblk_wg; ++kb) {
       const bool more = kb + 1 < nblk_wg;
       store_stage(hi_tag);
@@ -884,6 +881,18 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   };
   using HiOnly = std::integral_constant<bool, true>;
   using Full = std::integral_constant<bool, false>;
+
+  // pass 1's first summary loads go out before anything else, so that their
+  // latency overlaps the query loads and the set-up below
+  if (nblk_wg > 0) load_stage(HiOnly{}, 0);
+
+  // ---- q^T as the B operand
+  {
+    const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * hi32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
+  }
+
 
   // per block of 32 chunks, the largest error bound of its chunks (visible
   // after the first barrier of pass 1)
@@ -916,7 +925,7 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   // hi-only score less |q| times its block's error bound
   float lbound = -INFINITY;
   float emax = 0.f;  // the largest block error bound the row saw
-  scan_blocks(HiOnly{}, [&](int kb, const f32x16& u) {
+  scan_blocks(HiOnly{}, true, [&](int kb, const f32x16& u) {
     float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
@@ -937,7 +946,7 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   {
     // rows past the sequence end take no entries
     const float thr = row_ok ? lbound - 1.f : INFINITY;
-    scan_blocks(Full{}, [&](int kb, const f32x16& u) {
+    scan_blocks(Full{}, false, [&](int kb, const f32x16& u) {
       float lmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, u[r]);
@@ -1193,11 +1202,16 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   // ---- per-row bitmasks of the routed past chunks (over the tau sums)
   __syncthreads();
   for (int x = tid; x < kTileRows * NWMAX; x += blockDim.x) (&s_bits[0][0])[x] = 0u;
+  if constexpr (kRmByChunk)
+    for (int x = tid; x < NE * 4; x += blockDim.x) (&s_rm[0][0])[x] = 0u;
   if (owner) s_ownf[R] = own_pair ? 1 : 0;
   __syncthreads();
   for_run([&](int j, float uu, uint32_t kk) {
     const int rr = kk >> SH, c = kk & CMASK;
-    if (j < nl && uu > s_t[rr]) atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
+    if (j < nl && uu > s_t[rr]) {
+      atomicOr(&s_bits[rr][c >> 5], 1u << (c & 31));
+      if constexpr (kRmByChunk) atomicOr(&s_rm[c][rr >> 5], 1u << (rr & 31));
+    }
   });
   __syncthreads();
   if (a.bits != nullptr) {
@@ -1328,16 +1342,22 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   if (pooled) {
     // ---- row masks of every entry (a lane per entry in each wavefront), the
     // pairs per entry and their place: the pairs of a chunk in row order
-    for (int e = lane; e < ne; e += kWave) {
-      const int c = s_cl[e];
-      uint32_t m = 0u;
+    if constexpr (!kRmByChunk) {
+      for (int e = lane; e < ne; e += kWave) {
+        const int c = s_cl[e];
+        uint32_t m = 0u;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) m |= ((s_bits[w * 32 + r][c >> 5] >> (c & 31)) & 1u) << r;
-      s_rm[e][w] = m;
+        for (int r = 0; r < 32; ++r) m |= ((s_bits[w * 32 + r][c >> 5] >> (c & 31)) & 1u) << r;
+        s_rm[e][w] = m;
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    auto rmask = [&](int e) -> const uint32_t* { return s_rm[kRmByChunk ? s_cl[e] : e]; };
     // entries EPT t .. EPT t + EPT - 1 per thread
-    auto ecount = [&](int e) { return __popc(s_rm[e][0]) + __popc(s_rm[e][1]) + __popc(s_rm[e][2]) + __popc(s_rm[e][3]); };
+    auto ecount = [&](int e) {
+      const uint32_t* m = rmask(e);
+      return __popc(m[0]) + __popc(m[1]) + __popc(m[2]) + __popc(m[3]);
+    };
     int ec[EPT];
     int esum = 0;
 #pragma unroll
@@ -1368,8 +1388,9 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
     }
     auto place = [&](int e, int rr) {
       const int wr = rr >> 5;
-      int j = s_eoff[e] + __popc(s_rm[e][wr] & ((1u << (rr & 31)) - 1u));
-      for (int ww = 0; ww < wr; ++ww) j += __popc(s_rm[e][ww]);
+      const uint32_t* m = rmask(e);
+      int j = s_eoff[e] + __popc(m[wr] & ((1u << (rr & 31)) - 1u));
+      for (int ww = 0; ww < wr; ++ww) j += __popc(m[ww]);
       return j;
     };
     for_run([&](int j, float uu, uint32_t kk) {
