@@ -63,15 +63,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources each kernel's code depends on (a changed source voids its measured traffic).
 KERNEL_SOURCES = {
     "k_route_fast": ["route.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
-    "k_prefill_cm": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_prefill_cm": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_sparse_decode": ["sparse_decode.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_buf": ["entmax_attn.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_rows": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_rows_bwd": ["entmax_rows.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
-    "k_prefill_merge": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
-    "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
-    "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
-    "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp"],
+    "k_prefill_merge": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_cm_scatter": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_summarize_bwd": ["summarize.hip", "kernels.hpp", "cdna4.hpp"],
     "k_entmax_bwd_dq": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_entmax_bwd_dkdv": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
@@ -102,28 +102,29 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, key: str = "hbm_bytes_per_launch"):
     """HBM bytes per launch from the committed PMC profile (FETCH_SIZE + WRITE_SIZE,
-    each scaled by the plain-copy calibration), or None if the kernel source has
-    changed since the counters were taken."""
+    each scaled by the plain-copy calibration; key "hbm_bytes_gather_scaled": the
+    reads scaled by the random-row gather calibration instead), or None if the
+    kernel source has changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)["kernels"][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("source_sha") != source_sha(kernel):
+    if rec.get("source_sha") != source_sha(kernel) or key not in rec:
         return None
-    return float(rec["hbm_bytes_per_launch"])
+    return float(rec[key])
 
 
 def _sum_or_none(parts):
     return None if any(p is None for p in parts) else float(sum(parts))
 
 
-def attention_traffic():
+def attention_traffic(key: str = "hbm_bytes_per_launch"):
     """Measured HBM bytes of one dash_sparse_attn_prefill call (its kernels summed),
     or None if any of them changed since the counters were taken."""
-    parts = [measured_traffic(k) for k in ATTN_KERNELS]
+    parts = [measured_traffic(k, key) for k in ATTN_KERNELS]
     return None if any(p is None for p in parts) else float(sum(parts))
 
 
@@ -137,6 +138,24 @@ def calibrate_copy(nbytes=1 << 30, reps=3):
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"calibration copy: {reps} x {nbytes} bytes")
+    del src, dst
+    calibrate_gather()
+
+
+def calibrate_gather(rows=1 << 22, table_rows=1 << 23, reps=3):
+    """A gather of known size with the query gathers' access pattern: `rows`
+    distinct 256-byte rows (128 bf16) in random order out of a 2 GiB table (far
+    larger than the 256 MB Infinity Cache, so nothing is re-read), for checking
+    that the copy's scaling of the PMC byte counters holds for gathers."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    table = torch.ones(table_rows, 128, dtype=torch.bfloat16, device="cuda")
+    idx = torch.randperm(table_rows, generator=g, device="cuda")[:rows].contiguous()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.index_select(table, 0, idx)
+    torch.cuda.synchronize()
+    log(f"calibration gather: {reps} x {rows} rows of 256 bytes (+ {rows * 8} bytes of indices)")
 
 
 class Timer:
@@ -666,6 +685,9 @@ def main():
         "unit": "TFLOP/s",
         "frac": attn_ach / PEAK_BF16_TFLOPS,
         "traffic": attn_traffic,
+        # the same counters with the reads scaled as a 256-byte-row gather reads
+        # (the copy's scaling overstates gathered rows): the traffic lies between
+        "traffic_gather_scaled": attention_traffic("hbm_bytes_gather_scaled"),
         "alg_flops_per_launch": pre["alg_flops"],
         "ms_per_launch": pre["ms_attention"],
         "executed_pair_frac": pre["pair_flops"] / (pre["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
