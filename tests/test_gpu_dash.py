@@ -263,6 +263,17 @@ def test_prefill_long_general_routing_in_global_scratch():
     assert cnt["general_route_tiles"] > 0, cnt
 
 
+def test_prefill_long_noncausal_sampled():
+    """Non-causal past 512 chunk slots (36000 tokens: 563 slots, a partial last
+    chunk): every row routes over every chunk, sampled rows against the oracle."""
+    Q, K, V, cls = _inputs(1, 4, 2, 36000, 43, "chunks")
+    rng = np.random.default_rng(43)
+    fixed = np.array([0, 1, 127, 128, 17999, 35935, 35936, 35999])
+    check_prefill(Q, K, V, cls, api.Params(causal=False),
+                  rows_of=lambda b, h: np.unique(np.concatenate([fixed, rng.integers(0, 36000, 6)])),
+                  where="36k non-causal")
+
+
 @pytest.mark.parametrize("name", ["routed_prefill_64k", "routed_prefill_128k"])
 def test_prefill_long_workload_sampled(name):
     """The 32K needle recipe at 64K and 128K tokens (1024 and 2048 chunk
@@ -359,6 +370,42 @@ def test_decode_append_matches_prefill_summary():
         for hk in range(2):
             ref = oracle.chunk_summary(f64(Kc[b, hk, 192:256]), f64(cls[hk]))
             assert_close(f64(S[b, hk, 3]), ref, 1e-5, "appended summary")
+
+
+def test_decode_multi_step_with_appends_matches_prefill():
+    """Resume from a prefix: the summary cache is built for the complete chunks of
+    T tokens, then 20 decode steps each attend the next token and append the
+    chunk it completes (batch entries at different lengths, each crossing a chunk
+    boundary mid-way). Every step must equal the prefill's row at that position
+    (which the prefill tests hold to the oracle), and the cache must end equal
+    to the prefill's summaries."""
+    T, steps = [250, 186], 20
+    N = max(T) + steps
+    Q, K, V, cls = _inputs(2, 4, 2, N, 61, "chunks")
+    p = api.Params()
+    O_pre, tau_pre, _, S_pre, _ = api.prefill(Q, K, V, cls, p)
+    Lmax = 320
+    Kc = torch.zeros(2, 2, Lmax, 128, dtype=K.dtype, device="cuda")
+    Vc = torch.zeros_like(Kc)
+    Kc[:, :, :N], Vc[:, :, :N] = K, V
+    S = torch.zeros(2, 2, Lmax // C, 128, dtype=torch.float32, device="cuda")
+    lens0 = torch.tensor(T, dtype=torch.int32, device="cuda")
+    api.summarize(Kc, cls, S, seqlens=lens0, chunk_begin=0, chunk_end=Lmax // C, params=p)
+    ws = None
+    for k in range(steps):
+        t = [T[0] + k, T[1] + k]
+        seqlens = torch.tensor([t[0] + 1, t[1] + 1], dtype=torch.int32, device="cuda")
+        q = torch.stack([Q[0, :, t[0]], Q[1, :, t[1]]])[:, :, None].contiguous()
+        Od, td, _, ws = api.decode_step(q, Kc, Vc, cls, S, seqlens, p, lengths=[t[0] + 1, t[1] + 1], workspace=ws)
+        torch.cuda.synchronize()
+        for b in range(2):
+            assert_close(f64(Od[b, :, 0]), f64(O_pre[b, :, t[b]]), 2e-2, f"step {k} b{b} row {t[b]}")
+            assert_close(f64(td[b, :, 0]), f64(tau_pre[b, :, t[b]]), 2e-5, f"tau step {k} b{b} row {t[b]}")
+    # chunks completed by the end: 0 .. (T + steps) // 64 - 1 per entry
+    for b in range(2):
+        n_done = (T[b] + steps) // C
+        assert_close(f64(S[b, :, :n_done]), f64(S_pre[b, :, :n_done]), 1e-5, f"summary cache b{b}")
+    assert T[0] // C < (T[0] + steps) // C and T[1] // C < (T[1] + steps) // C  # both crossed a boundary
 
 
 def test_decode_128k_workload_sampled():
