@@ -52,7 +52,10 @@ struct Elem<float> {
 };
 }  // namespace
 
-template <typename T, int D, int KIND>
+// KEEP > 0 (N <= 64 KEEP): the scores of a wavefront's KEEP key tiles stay in
+// registers from pass 1 on, instead of being recomputed in every tau step and
+// in the output pass (short rows, where the recomputation is most of the time).
+template <typename T, int D, int KIND, int KEEP>
 __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
   constexpr bool BF = Elem<T>::bf16;
   constexpr int NS = BF ? D / 16 : D / 2;  // k-steps of S^T = K Q^T
@@ -155,16 +158,39 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
     return max_xor32(m);
   };
   uint32_t* cand = s_cand[w];
+  // fn(J) for the wavefront's key tiles in order (unrolled when the scores are kept)
+  auto for_tiles = [&](auto&& fn) {
+    if constexpr (KEEP > 0) {
+#pragma unroll
+      for (int J = 0; J < KEEP; ++J)
+        if (J < n_kt) fn(J);
+    } else {
+      for (int J = 0; J < n_kt; ++J) fn(J);
+    }
+  };
+  f32x16 uk0[KEEP > 0 ? KEEP : 1], uk1[KEEP > 0 ? KEEP : 1];
+  auto get_u = [&](int J, f32x16& u0, f32x16& u1) {
+    if constexpr (KEEP > 0) {
+      u0 = uk0[J];
+      u1 = uk1[J];
+    } else {
+      tile_u(J, u0, u1);
+    }
+  };
 
   // ---- pass 1: row maxima and candidate tiles
   float m_run = -INFINITY;
-  for (int J = 0; J < n_kt; ++J) {
+  for_tiles([&](int J) {
     f32x16 u0, u1;
     tile_u(J, u0, u1);
+    if constexpr (KEEP > 0) {
+      uk0[J] = u0;
+      uk1[J] = u1;
+    }
     const float mt = tile_max(u0, u1);
     m_run = fmaxf(m_run, mt);
     if (wave_any(row_ok && mt > m_run - 1.f) && lane == 0) cand[J >> 5] |= 1u << (J & 31);
-  }
+  });
   wave_lds_fence();
 
   // ---- pass 2: tau
@@ -175,10 +201,10 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
     tau = lo;
     for (int it = 0; it < a.n_iter; ++it) {
       float f0 = 0.f, f1 = 0.f, f2 = 0.f;
-      for (int J = 0; J < n_kt; ++J) {
-        if (!((cand[J >> 5] >> (J & 31)) & 1u)) continue;
+      for_tiles([&](int J) {
+        if (!((cand[J >> 5] >> (J & 31)) & 1u)) return;
         f32x16 u0, u1;
-        tile_u(J, u0, u1);
+        get_u(J, u0, u1);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           tau_terms<KIND>(u0[r], tau, a.beta, f0, f1, f2);
@@ -186,7 +212,7 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
         }
         const float mt = tile_max(u0, u1);
         if (!wave_any(row_ok && mt > lo) && lane == 0) cand[J >> 5] &= ~(1u << (J & 31));
-      }
+      });
       wave_lds_fence();
       f0 = sum_xor32(f0);
       f1 = sum_xor32(f1);
@@ -207,10 +233,10 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float psum = 0.f;
   uint32_t* mrow = s_mask[w >> 1];
-  for (int J = 0; J < n_kt; ++J) {
-    if (!((cand[J >> 5] >> (J & 31)) & 1u)) continue;
+  for_tiles([&](int J) {
+    if (!((cand[J >> 5] >> (J & 31)) & 1u)) return;
     f32x16 u0, u1;
-    tile_u(J, u0, u1);
+    get_u(J, u0, u1);
     bool nz = false;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -219,7 +245,7 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
       nz = nz || u0[r] > 0.f || u1[r] > 0.f;
       psum += u0[r] + u1[r];
     }
-    if (!wave_any(nz)) continue;
+    if (!wave_any(nz)) return;
     if (lane == 0) atomicOr(&mrow[J >> 5], 1u << (J & 31));
     if constexpr (BF) {
       // stage V tile transposed: combos (kg, dg) = keys 4 kg .. +3, dims 8 dg .. +7
@@ -295,7 +321,7 @@ __global__ __launch_bounds__(256) void k_entmax_attn(EntmaxAttnArgs a) {
         }
       }
     }
-  }
+  });
 
   // ---- outputs
   psum = sum_xor32(psum);
@@ -601,12 +627,22 @@ static hipError_t entmax_td(const EntmaxAttnArgs& a0, hipStream_t stream) {
       hipLaunchKernelGGL((k_entmax_buf<D, 0>), grid, dim3(256), 0, stream, a);
     a.only_marked = 1;
   }
+  // rows of at most 128 keys keep their scores in registers
+  if (a.N <= 128) {
+    if (a.alpha == 1.5f)
+      hipLaunchKernelGGL((k_entmax_attn<T, D, 2, 2>), grid, dim3(256), 0, stream, a);
+    else if (a.alpha == 2.0f)
+      hipLaunchKernelGGL((k_entmax_attn<T, D, 1, 2>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_entmax_attn<T, D, 0, 2>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.alpha == 1.5f)
-    hipLaunchKernelGGL((k_entmax_attn<T, D, 2>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_entmax_attn<T, D, 2, 0>), grid, dim3(256), 0, stream, a);
   else if (a.alpha == 2.0f)
-    hipLaunchKernelGGL((k_entmax_attn<T, D, 1>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_entmax_attn<T, D, 1, 0>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_entmax_attn<T, D, 0>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_entmax_attn<T, D, 0, 0>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
