@@ -1072,30 +1072,37 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   const int k_beg = min(wcnt, lane * run);
   const int nl = min(wcnt, lane * run + run) - k_beg;
   constexpr int RUNMAX = 16;
-  auto fetch = [&](int j, float& uu, uint32_t& kk) {
+  // the segment cursor of a walk over increasing j: (segment, its first entry
+  // index in the wavefront's order, its record)
+  struct SegCursor {
+    int sg, sk;
+    int2 v;
+  };
+  auto cursor = [&]() { return SegCursor{0, 0, s_seg[w][0]}; };
+  auto fetch = [&](SegCursor& cur, int j, float& uu, uint32_t& kk) {
     uint32_t e = 0u;
-    int2 sgv = make_int2(0, 0);
     if (j < nl) {
       const int k = k_beg + j;
-      int sg = 0, sk = 0;
-      sgv = s_seg[w][0];
-      while (k >= sk + (sgv.y & 0xffff)) {
-        sk += sgv.y & 0xffff;
-        sgv = s_seg[w][++sg];
+      while (k >= cur.sk + (cur.v.y & 0xffff)) {
+        cur.sk += cur.v.y & 0xffff;
+        cur.v = s_seg[w][++cur.sg];
       }
-      e = s_list[sgv.x + k - sk];
+      e = s_list[cur.v.x + k - cur.sk];
     }
     const int rw = (e >> 5) & 31;
     const float mr = __shfl(m_list, rw);  // the max the distance is taken from
     uu = j < nl ? mr - (float)(e >> 10) * 4.76837158e-7f : -INFINITY;
-    kk = (uint32_t)(((w * 32 + rw) << SH) | ((sgv.y >> 16) * 32 + (e & 31)));
+    kk = (uint32_t)(((w * 32 + rw) << SH) | ((cur.v.y >> 16) * 32 + (e & 31)));
   };
   float eu[RUNMAX];
   uint32_t ek[RUNMAX];
+  {
+    SegCursor cur = cursor();
 #pragma unroll
-  for (int j = 0; j < RUNMAX; ++j) {
-    if (j >= run) break;
-    fetch(j, eu[j], ek[j]);
+    for (int j = 0; j < RUNMAX; ++j) {
+      if (j >= run) break;
+      fetch(cur, j, eu[j], ek[j]);
+    }
   }
   // fn(j, u, key) for every j < run: registers, then the list
   auto for_run = [&](auto&& fn) {
@@ -1104,11 +1111,14 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
       if (j >= run) break;
       fn(j, eu[j], ek[j]);
     }
-    for (int j = RUNMAX; j < run; ++j) {
-      float uu;
-      uint32_t kk;
-      fetch(j, uu, kk);
-      fn(j, uu, kk);
+    if (run > RUNMAX) {
+      SegCursor cur = cursor();
+      for (int j = RUNMAX; j < run; ++j) {
+        float uu;
+        uint32_t kk;
+        fetch(cur, j, uu, kk);
+        fn(j, uu, kk);
+      }
     }
   };
 
