@@ -1328,18 +1328,18 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   }
   __syncthreads();
   const long long toff = bh * a.per_head + prefill_tile_offset(tile, n_slots, causal);
-  if (tid < NW) {
-    uint32_t bits = s_union[tid];
-    int pos = s_pre[tid];
+  auto epos = [&](int c) { return s_pre[c >> 5] + __popc(s_union[c >> 5] & ((1u << (c & 31)) - 1u)); };
+  {
+    // every chunk slot of the union by its own thread, at its list position
     int* lst = (pooled ? a.clists : a.lists) + toff;
-    while (bits) {
-      const int c = tid * 32 + __ffs(bits) - 1;
-      s_cl[pos] = c;
-      lst[pos++] = c;
-      bits &= bits - 1u;
+    for (int c = tid; c < NW * 32; c += blockDim.x) {
+      if ((s_union[c >> 5] >> (c & 31)) & 1u) {
+        const int pos = epos(c);
+        s_cl[pos] = c;
+        lst[pos] = c;
+      }
     }
   }
-  auto epos = [&](int c) { return s_pre[c >> 5] + __popc(s_union[c >> 5] & ((1u << (c & 31)) - 1u)); };
   // rank of chunk c among the attended chunks of tile row rr
   auto rank_in_row = [&](int rr, int c) {
     int k = __popc(s_bits[rr][c >> 5] & ((1u << (c & 31)) - 1u));
