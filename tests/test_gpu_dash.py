@@ -274,6 +274,28 @@ def test_prefill_long_noncausal_sampled():
                   where="36k non-causal")
 
 
+def test_prefill_long_tile_union_over_1024_goes_general():
+    """A tile whose routed chunks number more than 1024 (the 2048-slot list
+    kernel's entry cap) although its candidate list is short: the keys of chunk
+    c are 6 e_(c mod 128) (e_j one-hot, so the summaries are exactly those
+    codes) and row i of the last tile queries 6 e_(i mod 128), so it routes the
+    ~10 chunks carrying its code with equal weight and the tile's 128 rows route
+    ~1240 chunks in all. The tile is routed by the general kernel (global
+    scratch form); sampled rows of it and of other tiles against the oracle."""
+    N = 80000
+    Q, K, V, cls = _inputs(1, 1, 1, N, 47, None)
+    eye = torch.zeros(128, 128, device="cuda")
+    eye[torch.arange(128), torch.arange(128)] = 6.0
+    codes = eye[torch.arange(N, device="cuda") // C % 128].to(K.dtype)
+    K[0, 0] = codes
+    last = torch.arange(N - N % 128 - 128, N - N % 128, device="cuda")
+    Q[0, 0, last] = eye[last % 128].to(Q.dtype)
+    rng = np.random.default_rng(47)
+    rows = np.unique(np.concatenate([last.cpu().numpy()[::9], [0, 64, 5000, 40000, N - 1], rng.integers(0, N, 6)]))
+    cnt = check_prefill(Q, K, V, cls, api.Params(), rows_of=lambda b, h: rows, where="union over 1024")
+    assert cnt["general_route_tiles"] > 0, cnt
+
+
 @pytest.mark.parametrize("name", ["routed_prefill_64k", "routed_prefill_128k"])
 def test_prefill_long_workload_sampled(name):
     """The 32K needle recipe at 64K and 128K tokens (1024 and 2048 chunk
