@@ -520,6 +520,62 @@ def sparsity_report(w, alphas=(1.333, 1.5, 2.0), scalings=(0.5, 1.0, 2.0, 4.0), 
     return {"workload": w.name, "depth_bins": depth_bins, "rows": rows}
 
 
+def union_density_report(names=("routed_prefill_4k", "routed_prefill_32k"), block_rows=(16, 32, 64, 128),
+                         thresholds=(0.25, 0.5, 0.75), depth_bins=8):
+    """How dense the routed past chunks of a block of consecutive rows of one
+    query head are: for blocks of R rows, the chunk union of the block (what a
+    row-major tile loop executes, R x 64 keys per chunk of the union) against the
+    rows' own routed past chunks (the chunk-major pairs). Per R: executed over
+    routed pairs overall and per depth bin, and the share of routed pairs (and of
+    blocks) in blocks at least `threshold` dense."""
+    out = []
+    for name in names:
+        w = WORKLOADS[name]
+        Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed, planted=w.planted, device="cuda")
+        del V
+        p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+        S = torch.empty(w.B, w.Hkv, -(-w.N // C), w.d, dtype=torch.float32, device="cuda")
+        api.summarize(K, cls, S, n_tokens=w.N, chunk_begin=0, chunk_end=w.N // C, params=p)
+        _, bits, ws = api.route(Q, K, cls, S, p, with_bits=True)
+        del ws, Q, K
+        B, H, N, W = bits.shape
+        # past chunks only: clear each row's own chunk
+        rows = torch.arange(N, device="cuda")
+        own = torch.zeros(N, W, dtype=torch.int64, device="cuda")
+        own[rows, (rows // C) // 32] = 1 << ((rows // C) % 32)
+        past = (bits.to(torch.int64) & 0xFFFFFFFF) & ~own  # [B, H, N, W], 32-bit words in int64
+        cnt = popcount32(past).sum(-1)  # [B, H, N]
+        total = float(cnt.sum())
+        rec = {"workload": name, "past_pairs": total, "rows": B * H * N, "past_chunks_per_row": total / (B * H * N),
+               "blocks": []}
+        for R in block_rows:
+            u = past.view(B, H, N // R, R, W)
+            while u.shape[3] > 1:
+                h = u.shape[3] // 2
+                u = u[:, :, :, :h] | u[:, :, :, h:2 * h]
+            union = popcount32(u[:, :, :, 0]).sum(-1)  # [B, H, N/R]
+            s = cnt.view(B, H, N // R, R).sum(-1)
+            eff = s.double() / (R * union.clamp(min=1)).double()
+            nb = N // R
+            entry = {"rows_per_block": R, "executed_over_pairs": float((union * R).sum()) / total,
+                     "executed_over_pairs_by_depth": [
+                         float((union[:, :, k * nb // depth_bins:(k + 1) * nb // depth_bins] * R).sum())
+                         / max(1.0, float(s[:, :, k * nb // depth_bins:(k + 1) * nb // depth_bins].sum()))
+                         for k in range(depth_bins)],
+                     "dense_blocks": []}
+            for th in thresholds:
+                sel = eff >= th
+                ps = float(s[sel].sum())
+                entry["dense_blocks"].append({"density_at_least": th, "pair_share": ps / total,
+                                              "block_share": float(sel.double().mean()),
+                                              "executed_over_pairs": float((union[sel] * R).sum()) / max(1.0, ps)})
+            rec["blocks"].append(entry)
+            log(f"union density {name} R={R}: executed/pairs {entry['executed_over_pairs']:.2f}")
+        out.append(rec)
+        del bits, past, cnt
+    return {"depth_bins": depth_bins, "workloads": out}
+
+
 # --------------------------------------------------------------------------- CPU oracle
 def cpu_baseline(w, budget_s=20.0):
     """The float64 oracle on host cores, on a random sample of query rows of the
@@ -648,6 +704,9 @@ def main():
                     help="skip the oracle timings of the other workloads (the cpu_baseline leg stays)")
     ap.add_argument("--sparsity", action="store_true",
                     help="only the measured-sparsity sweep (alpha x scaling_factor) on the 32K needle workload")
+    ap.add_argument("--union-density", action="store_true",
+                    help="only the density of the routed chunks of row blocks (row-major vs chunk-major work) "
+                         "on the 4K and 32K workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -658,6 +717,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.sparsity:
         print(json.dumps(sparsity_report(WORKLOADS["routed_prefill_32k"])), flush=True)
+        return
+    if args.union_density:
+        print(json.dumps(union_density_report()), flush=True)
         return
 
     if args.calibrate_copy:
