@@ -1482,10 +1482,14 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
 // Decode routing
 // ============================================================================
 // Scores of the complete chunks against the g query heads of one KV head:
-// eight lanes per summary row (four float4 each), 16 rows per wavefront.
+// eight lanes per summary row (four float4 each), 32 rows per wavefront, all of
+// a wavefront's summary loads in flight before any arithmetic.
+constexpr int kDecScorePasses = 4;                          // 8 rows per pass
+constexpr int kDecScoreRowsPerWg = 4 * 8 * kDecScorePasses;  // four wavefronts
 template <int G>
 __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
   constexpr int D = 128;
+  constexpr int NP = kDecScorePasses;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int grp_id = blockIdx.y;
@@ -1493,9 +1497,17 @@ __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
   const int hk = grp_id % a.Hkv;
   const int t = min(max(a.seqlens[b], 1), a.Lmax) - 1;  // clamp to the cache
   const int ncomp = t / kChunk;
-  const int c0 = blockIdx.x * 64 + w * 16;
+  const int c0 = blockIdx.x * kDecScoreRowsPerWg + w * 8 * NP;
   if (c0 >= ncomp) return;
   const int sub = lane & 7;
+  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap * D;
+  f32x4 sva[NP][4];
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    const int c = min(c0 + pass * 8 + (lane >> 3), ncomp - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sva[pass][k] = *reinterpret_cast<const f32x4*>(Sb + (size_t)c * D + 32 * k + 4 * sub);
+  }
   float q[G][16];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
@@ -1509,16 +1521,8 @@ __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
       q[hh][4 * k + 3] = bf16hi(v[1]);
     }
   }
-  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap * D;
-  f32x4 sva[2][4];  // both passes' loads issued before any arithmetic
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int c = min(c0 + pass * 8 + (lane >> 3), ncomp - 1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) sva[pass][k] = *reinterpret_cast<const f32x4*>(Sb + (size_t)c * D + 32 * k + 4 * sub);
-  }
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < NP; ++pass) {
     const int c = c0 + pass * 8 + (lane >> 3);
     const bool val = c < ncomp;
     const f32x4* sv = sva[pass];
@@ -1540,12 +1544,15 @@ __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
 }
 
 // tau, routed union and work list for the g query heads of one (b, kv head).
+// A wavefront per query head; the routed chunks travel as bitmask words built
+// from ballots (word j of a row in lane j % 64, register j / 64), and every
+// wavefront forms the group's union words and their prefix counts itself.
 template <int G, int KPL, int KIND>
 __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   constexpr int D = 128;
-  constexpr int NWD = 2 * KPL + 1;
-  __shared__ uint32_t s_union[NWD];
-  __shared__ int s_pre[NWD + 1];
+  constexpr int NWD = 2 * KPL + 1;           // bitmask words (the own chunk can sit in the last)
+  constexpr int NWL = (NWD + 63) / 64;       // words per lane
+  __shared__ uint32_t s_wb[G][64 * NWL];     // each head's words
   __shared__ float s_lc[G][64];
   __shared__ float s_qk[G][64];
 
@@ -1560,33 +1567,38 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   const int ncomp = ct;
   const bool est = a.est != 0;
   const int ncand = ncomp + (est ? 1 : 0);
-  for (int i = threadIdx.x; i < NWD; i += blockDim.x) s_union[i] = 0u;
 
   const size_t bh = (size_t)b * a.Hq + h;
   const float am1 = a.alpha - 1.f;
 
+  // ---- every load first: the estimate's query, head_cls and own-chunk keys,
+  // then the scores of complete chunks c = k*64 + lane (unconditional, keys
+  // past the sequence read its last key and are masked below)
+  const int sub = lane & 15, rg = lane >> 4;
+  const int nval = t - ct * kChunk + 1;
+  u32x4 qv = {0, 0, 0, 0}, cv = {0, 0, 0, 0}, kvs[16];
+  if (est) {
+    qv = ldg16(a.Q + bh * D + 8 * sub);
+    cv = ldg16(a.cls + (size_t)hk * D + 8 * sub);
+    const uint16_t* kp = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ct * kChunk) * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) kvs[r] = ldg16(kp + (size_t)min(r * 4 + rg, nval - 1) * D + 8 * sub);
+  }
+  float u[KPL];
+  const float* zrow = a.z + bh * a.n_slots;
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) u[k] = zrow[min(k * 64 + lane, max(ncomp - 1, 0))];
+
   // ---- own-chunk estimate from the tokens [ct*C, t]
   float ud = -INFINITY;
   if (est) {
-    const int sub = lane & 15, rg = lane >> 4;
     float wq[8], wc[8];
-    {
-      u32x4 qv = ldg16(a.Q + bh * D + 8 * sub);
-      u32x4 cv = ldg16(a.cls + (size_t)hk * D + 8 * sub);
-      for (int e = 0; e < 4; ++e) {
-        wq[2 * e] = bf16lo(qv[e]);
-        wq[2 * e + 1] = bf16hi(qv[e]);
-        wc[2 * e] = bf16lo(cv[e]);
-        wc[2 * e + 1] = bf16hi(cv[e]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      wq[2 * e] = bf16lo(qv[e]);
+      wq[2 * e + 1] = bf16hi(qv[e]);
+      wc[2 * e] = bf16lo(cv[e]);
+      wc[2 * e + 1] = bf16hi(cv[e]);
     }
-    const int nval = t - ct * kChunk + 1;
-    const uint16_t* kp = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ct * kChunk) * D;
-    // all 16 loads in flight together (keys past the sequence read its last
-    // key and are masked below)
-    u32x4 kvs[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) kvs[r] = ldg16(kp + (size_t)min(r * 4 + rg, nval - 1) * D + 8 * sub);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = r * 4 + rg;
@@ -1609,12 +1621,6 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
     ud = (num / den) * a.zscale * am1;
   }
 
-  // ---- scores of complete chunks c = k*64 + lane
-  float u[KPL];
-  const float* zrow = a.z + bh * a.n_slots;
-  // (unconditional loads, so that they are all in flight together)
-#pragma unroll
-  for (int k = 0; k < KPL; ++k) u[k] = zrow[min(k * 64 + lane, max(ncomp - 1, 0))];
 #pragma unroll
   for (int k = 0; k < KPL; ++k) u[k] = k * 64 + lane < ncomp ? u[k] * am1 : -INFINITY;
   float tau = INFINITY;
@@ -1645,61 +1651,105 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   const bool dact = est ? (tdg > 0.f) : true;
   const float lwd = est ? (tdg > 0.f ? log2_prior<KIND>(tdg, a.beta) : -INFINITY) : 0.f;
 
-  __syncthreads();  // s_union cleared; s_lc/s_qk no longer needed
-  uint32_t* bdst = a.bits ? a.bits + bh * (size_t)a.bits_words : nullptr;
+  // ---- this head's routed chunks as words: chunk k*64 + l is bit l % 32 of
+  // word 2k + l / 32; the own chunk ct (attended when dact) is bit ct % 32 of
+  // word ct / 32 (ct >= ncomp, so no score test covers it)
+  uint32_t myw[NWL];
+#pragma unroll
+  for (int i = 0; i < NWL; ++i) myw[i] = 0u;
 #pragma unroll
   for (int k = 0; k < KPL; ++k) {
     const unsigned long long m64 = __ballot(u[k] - tau > 0.f);
-    uint32_t w0 = (uint32_t)m64, w1 = (uint32_t)(m64 >> 32);
-    if (lane == 0 && w0) atomicOr(&s_union[2 * k], w0);
-    if (lane == 0 && w1) atomicOr(&s_union[2 * k + 1], w1);
-    if (dact && (ct >> 5) == 2 * k) w0 |= 1u << (ct & 31);
-    if (dact && (ct >> 5) == 2 * k + 1) w1 |= 1u << (ct & 31);
-    if (bdst && lane == 0 && 2 * k < a.bits_words) bdst[2 * k] = w0;
-    if (bdst && lane == 0 && 2 * k + 1 < a.bits_words) bdst[2 * k + 1] = w1;
+    const int j0 = 2 * k, j1 = 2 * k + 1;
+    myw[j0 / 64] = lane == (j0 & 63) ? (uint32_t)m64 : myw[j0 / 64];
+    myw[j1 / 64] = lane == (j1 & 63) ? (uint32_t)(m64 >> 32) : myw[j1 / 64];
   }
-  if (lane == 0 && dact) atomicOr(&s_union[ct >> 5], 1u << (ct & 31));
-  if (bdst && lane == 0)
-    for (int wd = 2 * KPL; wd < a.bits_words; ++wd)
-      bdst[wd] = (dact && (ct >> 5) == wd) ? (1u << (ct & 31)) : 0u;
+#pragma unroll
+  for (int i = 0; i < NWL; ++i)
+    if (dact && (ct >> 5) == i * 64 + lane) myw[i] |= 1u << (ct & 31);
+  uint32_t* bdst = a.bits ? a.bits + bh * (size_t)a.bits_words : nullptr;
+  if (bdst) {
+#pragma unroll
+    for (int i = 0; i < NWL; ++i)
+      if (i * 64 + lane < a.bits_words) bdst[i * 64 + lane] = myw[i];
+    for (int wd = 64 * NWL + lane; wd < a.bits_words; wd += 64) bdst[wd] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < NWL; ++i) s_wb[w][i * 64 + lane] = myw[i];
+  __syncthreads();
 
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int wd = 0; wd < NWD; ++wd) {
-      s_pre[wd] = acc;
-      acc += __popc(s_union[wd]);
+  // ---- the group's union words and their exclusive prefix counts, in every
+  // wavefront (word i*64 + lane in register i)
+  uint32_t uw[NWL];
+  int upre[NWL];
+  int acc = 0;
+#pragma unroll
+  for (int i = 0; i < NWL; ++i) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) x |= s_wb[hh][i * 64 + lane];
+    uw[i] = x;
+    const int c = __popc(x);
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      incl += lane >= off ? y : 0;
     }
-    s_pre[NWD] = acc;
-    a.counts[grp_id] = acc;
+    upre[i] = acc + incl - c;
+    acc += __shfl(incl, kWave - 1);
   }
-  __syncthreads();
   const size_t gbase = (size_t)grp_id * a.n_slots;
-  for (int wd = threadIdx.x; wd < NWD; wd += blockDim.x) {
-    uint32_t bits = s_union[wd];
-    int pos = s_pre[wd];
-    while (bits) {
-      const int bpos = __ffs(bits) - 1;
-      a.lists[gbase + pos++] = wd * 32 + bpos;
-      bits &= bits - 1u;
+  if (w == 0) {
+    if (lane == 0) a.counts[grp_id] = acc;
+    // the union list in ascending chunk order
+#pragma unroll
+    for (int i = 0; i < NWL; ++i) {
+      uint32_t bits = uw[i];
+      int pos = upre[i];
+      while (bits) {
+        const int bpos = __ffs(bits) - 1;
+        a.lists[gbase + pos++] = (i * 64 + lane) * 32 + bpos;
+        bits &= bits - 1u;
+      }
     }
+  }
+  // ---- this head's log2 weight at each union entry it routed (the other
+  // heads' entries are written by their wavefronts; an entry no head of the
+  // group routed does not exist)
+  uint32_t wk[KPL];
+  int pk[KPL];
+#pragma unroll
+  for (int k = 0; k < KPL; ++k) {
+    const int j = 2 * k + (lane >> 5);  // this lane's word for chunk k*64 + lane
+    wk[k] = __shfl(uw[(2 * k) / 64], j & 63);
+    pk[k] = __shfl(upre[(2 * k) / 64], j & 63);
   }
 #pragma unroll
   for (int k = 0; k < KPL; ++k) {
     const int c = k * 64 + lane;
-    const uint32_t word = s_union[c >> 5];
-    if (c != ct && ((word >> (c & 31)) & 1u)) {
-      const int pos = s_pre[c >> 5] + __popc(word & ((1u << (c & 31)) - 1u));
+    if (c != ct && ((wk[k] >> (c & 31)) & 1u)) {
+      const int pos = pk[k] + __popc(wk[k] & ((1u << (c & 31)) - 1u));
       const float tt = u[k] - tau;
       a.bias[(gbase + pos) * G + w] = tt > 0.f ? log2_prior<KIND>(tt, a.beta) : -INFINITY;
     }
   }
-  if (lane == 0) {
-    const uint32_t word = s_union[ct >> 5];
-    if ((word >> (ct & 31)) & 1u) {
-      const int pos = s_pre[ct >> 5] + __popc(word & ((1u << (ct & 31)) - 1u));
-      a.bias[(gbase + pos) * G + w] = lwd;
+  {
+    // the own chunk's entry (the shuffles with every lane active)
+    const int jc = ct >> 5;
+    uint32_t word = 0u;
+    int pre = 0;
+#pragma unroll
+    for (int i = 0; i < NWL; ++i) {
+      const uint32_t x = __shfl(uw[i], jc & 63);
+      const int y = __shfl(upre[i], jc & 63);
+      if (jc / 64 == i) {
+        word = x;
+        pre = y;
+      }
     }
+    if (lane == 0 && ((word >> (ct & 31)) & 1u))
+      a.bias[(gbase + pre + __popc(word & ((1u << (ct & 31)) - 1u))) * G + w] = lwd;
   }
 }
 
@@ -1744,7 +1794,8 @@ hipError_t launch_route_prefill(const RouteArgs& a, hipStream_t stream) {
 template <int G, int KIND>
 static hipError_t route_decode_g(const RouteArgs& a, hipStream_t stream) {
   const int ncomp_max = (a.Lmax - 1) / kChunk;
-  dim3 g1((ncomp_max + 63) / 64 > 0 ? (ncomp_max + 63) / 64 : 1, a.B * a.Hkv);
+  const int nwg = (ncomp_max + kDecScoreRowsPerWg - 1) / kDecScoreRowsPerWg;
+  dim3 g1(nwg > 0 ? nwg : 1, a.B * a.Hkv);
   if (ncomp_max > 0) hipLaunchKernelGGL((k_route_decode_scores<G>), g1, dim3(256), 0, stream, a);
   const int kpl = (ncomp_max + 63) / 64;
 #define DASH_RD(K)                                                                              \
