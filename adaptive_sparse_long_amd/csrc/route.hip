@@ -1633,11 +1633,32 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
     tau = lo;
     for (int it = 0; it < a.n_iter; ++it) {
       float f0 = 0.f, f1 = 0.f, f2 = 0.f;
+      if constexpr (KIND == 0) {
 #pragma unroll
-      for (int k = 0; k < KPL; ++k) tau_terms<KIND>(u[k], tau, a.beta, f0, f1, f2);
-      f0 = wave_sum(f0);
-      f1 = wave_sum(f1);
-      if (KIND != 1) f2 = wave_sum(f2);
+        for (int k = 0; k < KPL; ++k) tau_terms<KIND>(u[k], tau, a.beta, f0, f1, f2);
+        f0 = wave_sum(f0);
+        f1 = wave_sum(f1);
+        f2 = wave_sum(f2);
+      } else {
+        // beta = 2 or 1: the support size (f2, resp. f1) is a count, taken
+        // from the ballots of the tests (wave-uniform, no reduction)
+        int nsup = 0;
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+          const float t = u[k] - tau;
+          const float p = fmaxf(t, 0.f);
+          if constexpr (KIND == 2) f0 = fmaf(p, p, f0), f1 += p;
+          else f0 += p;
+          nsup += __popcll(__ballot(t > 0.f));
+        }
+        f0 = wave_sum(f0);
+        if constexpr (KIND == 2) {
+          f1 = wave_sum(f1);
+          f2 = (float)nsup;
+        } else {
+          f1 = (float)nsup;
+        }
+      }
       if (est) tau_terms<KIND>(ud, tau, a.beta, f0, f1, f2);
       const float nt = tau_step<KIND>(tau, f0, f1, f2, a.beta, lo, hi);
       const bool conv = tau_converged(tau, nt);
