@@ -820,7 +820,7 @@ def main():
         out["prefill_4k"] = {
             "workload": w2.name, "tokens_per_s": w2.N / (ms2 / 1e3), "ms_per_step": ms2,
             "ms_summarize": p2["ms_summarize"], "ms_route": p2["ms_route"], "ms_attention": p2["ms_attention"],
-            "routed_chunks_per_row": p2["routed_chunks_per_row"],
+            "routed_chunks_per_row": p2["routed_chunks_per_row"], "counters": p2["counters"],
             "alg_flops": p2["alg_flops"], "pair_flops": p2["pair_flops"], "dense_causal_flops": p2["dense_causal_flops"],
             "attention_alg_frac": p2["alg_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
             "attention_pair_frac": p2["pair_flops"] / (p2["ms_attention"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
