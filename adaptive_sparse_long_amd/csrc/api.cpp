@@ -100,7 +100,7 @@ dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_d
   if (!seqlens && (n_tokens <= 0 || n_tokens > Lmax)) return DASH_ERR_INVALID_ARG;
   if (p.chunk_size <= 0) return DASH_ERR_INVALID_ARG;
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
-  if (p.chunk_size != kChunk || dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if (p.chunk_size != kChunk || dt != DASH_BF16 || !dash_head_dim_ok(d)) return DASH_ERR_UNSUPPORTED;
   if ((long long)chunk_end * kChunk > (long long)Lmax + kChunk - 1) return DASH_ERR_INVALID_ARG;
   if (chunk_end == chunk_begin) return DASH_OK;
   SummarizeArgs a{K, head_cls, S, B, Hkv, Lmax, d, n_tokens, seqlens, chunk_begin, chunk_end,
@@ -127,16 +127,17 @@ dash_status dash_summarize_backward(const void* K, const void* head_cls, const f
 size_t dash_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, int decode,
                            dash_params p) {
   if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
-  if (decode) return decode_layout(B, Hq, Hkv, Lmax, d).total;
+  // the kernels' own arrays are kDashD wide whatever the head_dim
+  if (decode) return decode_layout(B, Hq, Hkv, Lmax, kDashD).total;
   if (Nq <= 0 || Nq > Lmax) return 0;
-  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, prefill_default_pairs(B, Hq, Nq)).total;
+  return prefill_layout(B, Hq, Hkv, Nq, kDashD, p.causal != 0, prefill_default_pairs(B, Hq, Nq)).total;
 }
 
 size_t dash_prefill_workspace_size(int B, int Hq, int Hkv, int Nq, int Lmax, int d, dash_params p,
                                    long long pool_pairs) {
   if (B <= 0 || !gqa_ok(Hq, Hkv) || Lmax <= 0 || d <= 0 || p.chunk_size != kChunk) return 0;
   if (Nq <= 0 || Nq > Lmax || pool_pairs < 0 || pool_pairs > kPoolMaxPairs) return 0;
-  return prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, pool_pairs).total;
+  return prefill_layout(B, Hq, Hkv, Nq, kDashD, p.causal != 0, pool_pairs).total;
 }
 
 dash_status dash_route(const void* Q, const void* K, const void* head_cls, const float* S,
@@ -149,7 +150,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
-  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if (dt != DASH_BF16 || !dash_head_dim_ok(d)) return DASH_ERR_UNSUPPORTED;
   const int g = Hq / Hkv;
   const bool decode = seqlens != nullptr;
   RouteArgs a{};
@@ -174,7 +175,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
     if (Nq != 1 || p.causal != 1) return DASH_ERR_INVALID_ARG;
     if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete || !g_supported(g)) return DASH_ERR_UNSUPPORTED;
     if (s_cap < (Lmax - 1) / kChunk) return DASH_ERR_INVALID_ARG;
-    const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, d);
+    const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, kDashD);
     if (active_bits && bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
     if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
     a.n_slots = L.n_slots;
@@ -189,9 +190,9 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   if (n_slots > kPrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
   if (s_cap < (p.causal ? Nq / kChunk : n_slots)) return DASH_ERR_INVALID_ARG;
   if (active_bits && bits_words < (n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
-  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, Nq, d, p.causal != 0, ws_bytes);
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, Nq, kDashD, p.causal != 0, ws_bytes);
   if (pool < 0) return DASH_ERR_WORKSPACE;
-  const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, d, p.causal != 0, pool);
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, Nq, kDashD, p.causal != 0, pool);
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   a.n_tiles = L.n_tiles;
   a.n_slots = L.n_slots;
@@ -219,7 +220,7 @@ dash_status dash_route(const void* Q, const void* K, const void* head_cls, const
   a.fb_count = reinterpret_cast<int*>(ws + L.off_fb_count);
   a.n_rm = a.fb_count + 1;
   a.s_hi = reinterpret_cast<uint16_t*>(ws + L.off_split);
-  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
+  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * kDashD;
   a.s_err = reinterpret_cast<float*>(ws + L.off_serr);
   a.gscr = reinterpret_cast<float*>(ws + L.off_gscr);
   return from_hip(launch_route_prefill(a, stream));
@@ -235,11 +236,11 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
-  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if (dt != DASH_BF16 || !dash_head_dim_ok(d)) return DASH_ERR_UNSUPPORTED;
   if ((N + kChunk - 1) / kChunk > kPrefillMaxSlots) return DASH_ERR_UNSUPPORTED;
-  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, d, p.causal != 0, ws_bytes);
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, kDashD, p.causal != 0, ws_bytes);
   if (pool < 0) return DASH_ERR_WORKSPACE;
-  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0, pool);
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, kDashD, p.causal != 0, pool);
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   PrefillAttnArgs a{};
@@ -249,6 +250,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.O = static_cast<uint16_t*>(O);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = Hq / Hkv; a.N = N; a.Lmax = Lmax;
   a.causal = p.causal;
+  a.d = d;
   a.scale_log2 = kLog2e / sqrtf((float)d);
   a.n_tiles = L.n_tiles;
   a.n_slots = L.n_slots;
@@ -259,7 +261,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
   a.rm_bits = reinterpret_cast<const uint32_t*>(ws + L.off_rmbits);
   a.rm_words = L.words;
   a.s_hi = reinterpret_cast<const uint16_t*>(ws + L.off_split);
-  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * d;
+  a.s_lo = a.s_hi + (size_t)B * Hkv * L.n_slots * kDashD;
   a.beta = 1.f / (p.alpha - 1.f);
   a.ccounts = reinterpret_cast<const int*>(ws + L.off_ccounts);
   a.clists = reinterpret_cast<const int*>(ws + L.off_clists);
@@ -292,9 +294,9 @@ dash_status dash_prefill_counters(const void* workspace, size_t ws_bytes, int B,
                                   int d, dash_params p, long long* out, hipStream_t stream) {
   if (!workspace || !out) return DASH_ERR_INVALID_ARG;
   if (B <= 0 || N <= 0 || d <= 0 || !gqa_ok(Hq, Hkv)) return DASH_ERR_INVALID_ARG;
-  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, d, p.causal != 0, ws_bytes);
+  const long long pool = prefill_pool_from_bytes(B, Hq, Hkv, N, kDashD, p.causal != 0, ws_bytes);
   if (pool < 0) return DASH_ERR_WORKSPACE;
-  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, d, p.causal != 0, pool);
+  const PrefillLayout L = prefill_layout(B, Hq, Hkv, N, kDashD, p.causal != 0, pool);
   const char* ws = static_cast<const char*>(workspace);
   std::vector<int> cmp((size_t)L.n_bhc);
   int fb[2] = {0, 0};
@@ -322,9 +324,9 @@ dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* V
   if (st != DASH_OK) return st;
   if (p.causal != 1) return DASH_ERR_INVALID_ARG;
   const int g = Hq / Hkv;
-  if (dt != DASH_BF16 || d != 128 || !g_supported(g)) return DASH_ERR_UNSUPPORTED;
+  if (dt != DASH_BF16 || !dash_head_dim_ok(d) || !g_supported(g)) return DASH_ERR_UNSUPPORTED;
   if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete) return DASH_ERR_UNSUPPORTED;
-  const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, d);
+  const DecodeLayout L = decode_layout(B, Hq, Hkv, Lmax, kDashD);
   if (ws_bytes < L.total) return DASH_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   DecodeAttnArgs a{};
@@ -333,6 +335,7 @@ dash_status dash_sparse_attn_decode(const void* Q, const void* Kc, const void* V
   a.V = static_cast<const uint16_t*>(Vc);
   a.O = static_cast<uint16_t*>(O);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = g; a.Lmax = Lmax;
+  a.d = d;
   a.seqlens = seqlens;
   a.scale_log2 = kLog2e / sqrtf((float)d);
   a.n_slots = L.n_slots;
@@ -427,10 +430,10 @@ dash_status dash_decode_step_noalloc(const void* Q, const void* Kc, const void* 
   if (st != DASH_OK) return st;
   if (p.causal != 1) return DASH_ERR_INVALID_ARG;
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
-  if (dt != DASH_BF16 || d != 128 || !g_supported(Hq / Hkv)) return DASH_ERR_UNSUPPORTED;
+  if (dt != DASH_BF16 || !dash_head_dim_ok(d) || !g_supported(Hq / Hkv)) return DASH_ERR_UNSUPPORTED;
   if ((Lmax - 1) / kChunk > kRouteDecodeMaxComplete) return DASH_ERR_UNSUPPORTED;
   if (s_cap < (Lmax - 1) / kChunk) return DASH_ERR_INVALID_ARG;
-  if (active_bits && bits_words < (decode_layout(B, Hq, Hkv, Lmax, d).n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
+  if (active_bits && bits_words < (decode_layout(B, Hq, Hkv, Lmax, kDashD).n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
   void* ws = nullptr;
   st = scratch_address(&ws);
   if (st != DASH_OK) return st;

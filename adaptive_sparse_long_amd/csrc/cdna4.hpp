@@ -82,6 +82,18 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// Sum over each group of 8 lanes; every lane of the group gets the result.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x;
+}
+// Pair reduction of lane l with lane l ^ 8 (row_ror:8 within each row of 16).
+constexpr int kDppRor8 = 0x128;
+__device__ __forceinline__ float sum_xor8(float x) { return x + dpp_f<kDppRor8>(x); }
+__device__ __forceinline__ float max_xor8(float x) { return fmaxf(x, dpp_f<kDppRor8>(x)); }
+
 // Sum / max over each row of 16 lanes; every lane of the row gets the result.
 __device__ __forceinline__ float sum16(float x) {
   x += dpp_f<kDppXor1>(x);

@@ -44,6 +44,54 @@ inline size_t route_glb_scratch_bytes(int n_slots) {
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------------------------
+// Head dimension. The DashAttention kernels are laid out for 128 dims; at
+// head_dim 64 they run the same layouts with dims 64..127 zero: the caller's
+// rows (Q, K, V, head_cls, the summary cache, O) are d elements wide, every
+// load of them goes through the helpers below (zeros at and past d, which leave
+// dot products, softmax sums and scores unchanged) and every store of O or S
+// writes dims below d only. The kernels' own arrays (split summaries, partial
+// results) stay 128 wide.
+// ---------------------------------------------------------------------------
+constexpr int kDashD = 128;
+inline bool dash_head_dim_ok(int d) { return d == 64 || d == 128; }
+// 8 bf16 at element col (a multiple of 8, below 128) of row `row` of d-wide
+// rows. The load itself always goes to col modulo d (inside the row: d is a
+// power of two) and is then zeroed past d, so that no load is predicated.
+__device__ __forceinline__ u32x4 ldg16_d(const uint16_t* base, size_t row, int col, int d) {
+  const u32x4 v = ldg16(base + row * (size_t)d + (col & (d - 1)));
+  return col < d ? v : u32x4{0, 0, 0, 0};
+}
+// The same with the head_dim a compile-time constant (no test at d = 128).
+template <int DC>
+__device__ __forceinline__ u32x4 ldg16_dc(const uint16_t* base, size_t row, int col) {
+  if constexpr (DC == kDashD) {
+    return ldg16(base + row * (size_t)DC + col);
+  } else {
+    const u32x4 v = ldg16(base + row * (size_t)DC + (col & (DC - 1)));
+    return col < DC ? v : u32x4{0, 0, 0, 0};
+  }
+}
+template <int DC>
+__device__ __forceinline__ f32x4 ldf4_dc(const float* base, size_t row, int col) {
+  if constexpr (DC == kDashD) {
+    return *reinterpret_cast<const f32x4*>(base + row * (size_t)DC + col);
+  } else {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(base + row * (size_t)DC + (col & (DC - 1)));
+    return col < DC ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+// 4 bf16 at element col (a multiple of 4)
+__device__ __forceinline__ u32x2 ldg8_d(const uint16_t* base, size_t row, int col, int d) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(base + row * (size_t)d + (col & (d - 1)));
+  return col < d ? v : u32x2{0, 0};
+}
+// 4 floats at element col (a multiple of 4)
+__device__ __forceinline__ f32x4 ldf4_d(const float* base, size_t row, int col, int d) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(base + row * (size_t)d + (col & (d - 1)));
+  return col < d ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---------------------------------------------------------------------------
 // Prefill work lists, per (b, query head) and 128-row tile, each an ascending
 // list of chunk ids:
 //   row-major list ("rm", tiles without pool slots): every attended chunk; the
@@ -280,6 +328,7 @@ struct PrefillAttnArgs {
   const uint16_t* V;
   uint16_t* O;
   int B, Hq, Hkv, g, N, Lmax, causal;
+  int d;  // the caller's head_dim (row width of Q, K, V, O): 64 or 128
   float scale_log2;
   int n_tiles, n_slots;
   long long per_head;
@@ -325,6 +374,7 @@ struct DecodeAttnArgs {
   const uint16_t* V;
   uint16_t* O;
   int B, Hq, Hkv, g, Lmax;
+  int d;  // the caller's head_dim: 64 or 128
   const int* seqlens;
   float scale_log2;
   int n_slots, n_splits;

@@ -132,9 +132,8 @@ __device__ __forceinline__ void route_general_tile(const RouteArgs& a, int q) {
   bf16x8 qa[NS];
   {
     const int qi = min(i0 + col, N - 1);
-    const uint16_t* qp = a.Q + (bh * N + qi) * (size_t)D + 8 * grp;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = as_bf16x8(ldg16(qp + 32 * s));
+    for (int s = 0; s < NS; ++s) qa[s] = as_bf16x8(ldg16_d(a.Q, bh * N + qi, 32 * s + 8 * grp, a.d));
   }
 
   // ---- routing scores in u units, u[blk][r]: chunk blk*16 + col, row grp*4 + r.
@@ -230,11 +229,11 @@ __device__ __forceinline__ void route_general_tile(const RouteArgs& a, int q) {
   // ---- own-chunk estimate: score against the summary of tokens [cw*C, i]
   float ud[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   if (est && wave_valid) {
-    const uint16_t* kp = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)cw * kChunk) * D;
+    const size_t krow0 = ((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)cw * kChunk;
     float wc[NS][8];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4 cv = ldg16(a.cls + (size_t)hk * D + 32 * s + 8 * grp);
+      u32x4 cv = ldg16_d(a.cls, hk, 32 * s + 8 * grp, a.d);
       for (int e = 0; e < 4; ++e) {
         wc[s][2 * e] = bf16lo(cv[e]);
         wc[s][2 * e + 1] = bf16hi(cv[e]);
@@ -249,7 +248,7 @@ __device__ __forceinline__ void route_general_tile(const RouteArgs& a, int q) {
       float part = 0.f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        u32x4 kv = ldg16(kp + (size_t)key * D + 32 * s + 8 * grp);
+        u32x4 kv = ldg16_d(a.K, krow0 + key, 32 * s + 8 * grp, a.d);
         acc = mfma16x16x32(qa[s], as_bf16x8(kv), acc);
         part += dot8_bf16(kv, wc[s]);
       }
@@ -734,7 +733,8 @@ __global__ __launch_bounds__(512) void k_route_prefill(RouteArgs a) {
 // row and its place among the pairs of its chunk follow without contended
 // atomics.
 // ============================================================================
-template <int KIND, int MS>
+// DC: the caller's head_dim (a template argument: no per-load test at 128)
+template <int KIND, int MS, int DC>
 __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 16;  // k-steps of the 32x32x16 MFMA
@@ -888,9 +888,8 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
 
   // ---- q^T as the B operand
   {
-    const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * hi32;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
+    for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16_dc<DC>(a.Q, bh * N + min(qi, N - 1), 16 * s + 8 * hi32));
   }
 
 
@@ -1002,16 +1001,14 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
   float ud = -INFINITY;
   const float uscale = (a.alpha - 1.f) * a.zscale;
   if (est && wave_valid) {
-    const uint16_t* kbase = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)cw * kChunk) * D;
+    const size_t krow0 = ((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)cw * kChunk;
     const int lim = N - 1 - cw * kChunk;  // last key of the chunk inside the sequence
     {
-      const uint16_t* kp = kbase + (size_t)min(lane, lim) * D;
-      const uint16_t* cp = a.cls + (size_t)hk * D;
       float l = 0.f;
 #pragma unroll
       for (int c8 = 0; c8 < D / 8; ++c8) {
-        const u32x4 kv = ldg16(kp + 8 * c8);
-        const u32x4 cv = ldg16(cp + 8 * c8);
+        const u32x4 kv = ldg16_dc<DC>(a.K, krow0 + min(lane, lim), 8 * c8);
+        const u32x4 cv = ldg16_dc<DC>(a.cls, hk, 8 * c8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           l = fmaf(bf16lo(kv[e]), bf16lo(cv[e]), l);
@@ -1026,12 +1023,11 @@ __global__ __launch_bounds__(256, MS <= 512 ? 4 : 2) void k_route_fast(RouteArgs
       e0[r] = 0.f;
       e1[r] = 0.f;
     }
-    const uint16_t* k0 = kbase + (size_t)min(row, lim) * D + 8 * hi32;
-    const uint16_t* k1 = kbase + (size_t)min(row + 32, lim) * D + 8 * hi32;
+    const size_t kr0 = krow0 + min(row, lim), kr1 = krow0 + min(row + 32, lim);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      e0 = mfma32x32x16(as_bf16x8(ldg16(k0 + 16 * s)), qb[s], e0);
-      e1 = mfma32x32x16(as_bf16x8(ldg16(k1 + 16 * s)), qb[s], e1);
+      e0 = mfma32x32x16(as_bf16x8(ldg16_dc<DC>(a.K, kr0, 16 * s + 8 * hi32)), qb[s], e0);
+      e1 = mfma32x32x16(as_bf16x8(ldg16_dc<DC>(a.K, kr1, 16 * s + 8 * hi32)), qb[s], e1);
     }
     wave_lds_fence();
     const int pi = qi - cw * kChunk;  // keys 0 .. pi of the chunk are the row's
@@ -1447,9 +1443,8 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
     const size_t rem = i % per_bh;
     const size_t c = rem / (D / 8);
     const int e8 = (int)(rem % (D / 8)) * 8;
-    const float* src = a.S + (bh * a.s_cap + c) * D + e8;
-    f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-    f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+    f32x4 x0 = ldf4_d(a.S, bh * a.s_cap + c, e8, a.d);
+    f32x4 x1 = ldf4_d(a.S, bh * a.s_cap + c, e8 + 4, a.d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x0[e] *= uscale;
@@ -1486,7 +1481,7 @@ __global__ __launch_bounds__(256) void k_split_summaries(RouteArgs a, int n_need
 // a wavefront's summary loads in flight before any arithmetic.
 constexpr int kDecScorePasses = 4;                          // 8 rows per pass
 constexpr int kDecScoreRowsPerWg = 4 * 8 * kDecScorePasses;  // four wavefronts
-template <int G>
+template <int G, int DC>
 __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
   constexpr int D = 128;
   constexpr int NP = kDecScorePasses;
@@ -1500,21 +1495,20 @@ __global__ __launch_bounds__(256) void k_route_decode_scores(RouteArgs a) {
   const int c0 = blockIdx.x * kDecScoreRowsPerWg + w * 8 * NP;
   if (c0 >= ncomp) return;
   const int sub = lane & 7;
-  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap * D;
+  const size_t srow0 = ((size_t)b * a.Hkv + hk) * (size_t)a.s_cap;
   f32x4 sva[NP][4];
 #pragma unroll
   for (int pass = 0; pass < NP; ++pass) {
     const int c = min(c0 + pass * 8 + (lane >> 3), ncomp - 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) sva[pass][k] = *reinterpret_cast<const f32x4*>(Sb + (size_t)c * D + 32 * k + 4 * sub);
+    for (int k = 0; k < 4; ++k) sva[pass][k] = ldf4_dc<DC>(a.S, srow0 + c, 32 * k + 4 * sub);
   }
   float q[G][16];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const uint16_t* qp = a.Q + ((size_t)b * a.Hq + hk * G + hh) * D;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      u32x2 v = *reinterpret_cast<const u32x2*>(qp + 32 * k + 4 * sub);
+      u32x2 v = ldg8_d(a.Q, (size_t)b * a.Hq + hk * G + hh, 32 * k + 4 * sub, a.d);
       q[hh][4 * k + 0] = bf16lo(v[0]);
       q[hh][4 * k + 1] = bf16hi(v[0]);
       q[hh][4 * k + 2] = bf16lo(v[1]);
@@ -1578,11 +1572,11 @@ __global__ __launch_bounds__(G * 64) void k_route_decode_tau(RouteArgs a) {
   const int nval = t - ct * kChunk + 1;
   u32x4 qv = {0, 0, 0, 0}, cv = {0, 0, 0, 0}, kvs[16];
   if (est) {
-    qv = ldg16(a.Q + bh * D + 8 * sub);
-    cv = ldg16(a.cls + (size_t)hk * D + 8 * sub);
-    const uint16_t* kp = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ct * kChunk) * D;
+    qv = ldg16_d(a.Q, bh, 8 * sub, a.d);
+    cv = ldg16_d(a.cls, hk, 8 * sub, a.d);
+    const size_t krow0 = ((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ct * kChunk;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) kvs[r] = ldg16(kp + (size_t)min(r * 4 + rg, nval - 1) * D + 8 * sub);
+    for (int r = 0; r < 16; ++r) kvs[r] = ldg16_d(a.K, krow0 + min(r * 4 + rg, nval - 1), 8 * sub, a.d);
   }
   float u[KPL];
   const float* zrow = a.z + bh * a.n_slots;
@@ -1789,9 +1783,11 @@ static hipError_t route_prefill_kind(const RouteArgs& a, hipStream_t stream) {
   const unsigned n_grid_tiles = (unsigned)a.n_tiles * a.Hq * a.B;
   // the list-based kernel, then the general kernel for the tiles it queued
   if (a.n_slots <= kRouteRegSlots) {
-    hipLaunchKernelGGL((k_route_fast<KIND, kRouteRegSlots>), grid, dim3(256), 0, stream, a);
+    if (a.d == 64) hipLaunchKernelGGL((k_route_fast<KIND, kRouteRegSlots, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_route_fast<KIND, kRouteRegSlots, 128>), grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_route_fast<KIND, kPrefillMaxSlots>), grid, dim3(256), 0, stream, a);
+    if (a.d == 64) hipLaunchKernelGGL((k_route_fast<KIND, kPrefillMaxSlots, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_route_fast<KIND, kPrefillMaxSlots, 128>), grid, dim3(256), 0, stream, a);
   }
   const int nb = (a.n_slots + 15) / 16;
 #define DASH_RP(NBV, GLB, GRID)                                                                  \
@@ -1817,7 +1813,10 @@ static hipError_t route_decode_g(const RouteArgs& a, hipStream_t stream) {
   const int ncomp_max = (a.Lmax - 1) / kChunk;
   const int nwg = (ncomp_max + kDecScoreRowsPerWg - 1) / kDecScoreRowsPerWg;
   dim3 g1(nwg > 0 ? nwg : 1, a.B * a.Hkv);
-  if (ncomp_max > 0) hipLaunchKernelGGL((k_route_decode_scores<G>), g1, dim3(256), 0, stream, a);
+  if (ncomp_max > 0) {
+    if (a.d == 64) hipLaunchKernelGGL((k_route_decode_scores<G, 64>), g1, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_route_decode_scores<G, 128>), g1, dim3(256), 0, stream, a);
+  }
   const int kpl = (ncomp_max + 63) / 64;
 #define DASH_RD(K)                                                                              \
   if (kpl <= K) {                                                                               \

@@ -22,7 +22,9 @@
 
 namespace dash {
 
-template <int G>
+// DC: the caller's head_dim (row width of q, K, V), a template argument so that
+// the 128-dim instance has no per-load head_dim test
+template <int G, int DC>
 __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
   constexpr int D = 128;
   constexpr int NS = D / 32;
@@ -52,9 +54,9 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
   bf16x8 qa[NS];
   {
     const bool has = (col % RSTEP) == 0 && col / RSTEP < G;
-    const uint16_t* qp = a.Q + ((size_t)b * a.Hq + hk * G + col / RSTEP) * D + 8 * rg;
+    const size_t qrow = (size_t)b * a.Hq + hk * G + col / RSTEP;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qa[s] = as_bf16x8(has ? ldg16(qp + 32 * s) : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < NS; ++s) qa[s] = as_bf16x8(has ? ldg16_dc<DC>(a.Q, qrow, 32 * s + 8 * rg) : u32x4{0, 0, 0, 0});
   }
   // heads held by this lane in the score layout: D row 4 rg + j is head (4 rg + j) / RSTEP
   int my_head[HPG];
@@ -78,8 +80,7 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
 
-  const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-  const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+  const size_t kvrow0 = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax;
   const float sc = a.scale_log2;
   const int pos_end = min(count, (split + 1) * kDecodeSplit);
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
       const bool val = key < n_keys;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        kv[kb][s] = val ? ldg16(Kb + (size_t)key * D + 32 * s + 8 * rg) : u32x4{0, 0, 0, 0};
+        kv[kb][s] = val ? ldg16_dc<DC>(a.K, kvrow0 + key, 32 * s + 8 * rg) : u32x4{0, 0, 0, 0};
     }
     float bias[HPG];
 #pragma unroll
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void k_sparse_decode(DecodeAttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = base + rg + 4 * r;
-      vv[r] = key < n_keys ? ldg16(Vb + (size_t)key * D + 8 * col) : u32x4{0, 0, 0, 0};
+      vv[r] = key < n_keys ? ldg16_dc<DC>(a.V, kvrow0 + key, 8 * col) : u32x4{0, 0, 0, 0};
     }
     __builtin_amdgcn_sched_barrier(0);
     float alpha_h[HPG];
@@ -254,12 +255,15 @@ __global__ __launch_bounds__(128) void k_decode_combine(DecodeAttnArgs a) {
     }
     M = Mn;
   }
-  a.O[((size_t)b * a.Hq + hk * G + hh) * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(o / L));
+  if (dd < a.d) a.O[((size_t)b * a.Hq + hk * G + hh) * a.d + dd] = __builtin_bit_cast(uint16_t, (__bf16)(o / L));
 }
 
 template <int G>
 static hipError_t decode_g(const DecodeAttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_sparse_decode<G>, dim3(a.n_splits, a.B * a.Hkv), dim3(256), 0, stream, a);
+  if (a.d == 64)
+    hipLaunchKernelGGL((k_sparse_decode<G, 64>), dim3(a.n_splits, a.B * a.Hkv), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_sparse_decode<G, 128>), dim3(a.n_splits, a.B * a.Hkv), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_decode_combine<G>, dim3(a.B * a.Hkv * G), dim3(128), 0, stream, a);
   return hipGetLastError();
 }

@@ -105,18 +105,25 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     // Q^T as the B operand: column qi, dims 16 s + 8 hi32 .. +7
     bf16x8 qb[NS];
     {
-      const uint16_t* qp = a.Q + (bh * N + qi) * (size_t)D + 8 * hi32;
+      // dims past the head_dim are zero
+      const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)a.d;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        qb[s] = as_bf16x8(qi < N ? ldg16(qp + 16 * s) : u32x4{0, 0, 0, 0});
+      for (int s = 0; s < NS; ++s) {
+        const int col = 16 * s + 8 * hi32;
+        qb[s] = as_bf16x8(qi < N && col < a.d ? ldg16(qp + col) : u32x4{0, 0, 0, 0});
+      }
     }
 
-    const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-    const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-    // staging roles: K rows t/16 + 16 r at dims (t%16)*8; V keys 4 (t%16) + r at dims 8 (t/16)
+    // staging roles: K rows t/16 + 16 r at dims (t%16)*8; V keys 4 (t%16) + r at
+    // dims 8 (t/16). A thread whose dims lie past the head_dim stages zeros.
     const int k_row = tid >> 4, k_col = (tid & 15) * 8;
     const int v_kg = tid & 15, v_dg = tid >> 4;
     const int n_keys = N;
+    const int dd = a.d;
+    const size_t kvrow0 = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax;
+    const uint16_t* Kt = a.K + kvrow0 * dd + k_col;
+    const uint16_t* Vt = a.V + kvrow0 * dd + 8 * v_dg;
+    const bool k_in = k_col < dd, v_in = 8 * v_dg < dd;
 
     u32x4 kr[4], vr[4], ur;
     // Keys past the sequence end are read from its last row instead (a valid
@@ -127,9 +134,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = min(base + k_row + 16 * r, n_keys - 1);
-        kr[r] = ldg16(Kb + (size_t)key * D + k_col);
+        kr[r] = k_in ? ldg16(Kt + (uint32_t)(key * dd)) : u32x4{0, 0, 0, 0};
         const int vkey = min(base + 4 * v_kg + r, n_keys - 1);
-        vr[r] = ldg16(Vb + (size_t)vkey * D + 8 * v_dg);
+        vr[r] = v_in ? ldg16(Vt + (uint32_t)(vkey * dd)) : u32x4{0, 0, 0, 0};
       }
       if (tid < 2 * D / 8) ur = ldg16(Ub + (tid >= D / 8 ? lo_off : 0) + (size_t)c * D + 8 * (tid % (D / 8)));
     };
@@ -301,14 +308,14 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
     const float l_tot = sum_xor32(l_run);
     if (qi < N) {
       const float inv = 1.f / l_tot;
-      uint16_t* op = a.O + (bh * N + qi) * (size_t)D + 4 * hi32;
+      uint16_t* op = a.O + (bh * N + qi) * (size_t)a.d + 4 * hi32;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           u32x2 v = {pack_bf16x2(o[db][4 * q4] * inv, o[db][4 * q4 + 1] * inv),
                      pack_bf16x2(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * q4) = v;
+          if (32 * db + 8 * q4 + 4 * hi32 < a.d) *reinterpret_cast<u32x2*>(op + 32 * db + 8 * q4) = v;
         }
     }
   }
@@ -415,7 +422,9 @@ __global__ __launch_bounds__(256) void k_cm_scatter(PrefillAttnArgs a) {
   }
 }
 
-template <int D>
+// DC: the caller's head_dim (the row width of Q, K, V), a template argument so
+// that the 128-dim instance has no per-load head_dim test
+template <int D, int DC>
 __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs a) {
   constexpr int NS = D / 16;
   constexpr int KROW = D + KPAD;
@@ -473,9 +482,8 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
       const int qh = valid_of(r, n) ? r.x : 0;
       const int row = qh / g;
       const size_t bh = (size_t)b * a.Hq + hk * g + (qh - row * g);
-      const uint16_t* qp = a.Q + (bh * N + row) * (size_t)D + 8 * hi32;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16(qp + 16 * s));
+      for (int s = 0; s < NS; ++s) qb[s] = as_bf16x8(ldg16_dc<DC>(a.Q, bh * N + row, 16 * s + 8 * hi32));
     };
 
     // ---- stage K (row-major) and V (transposed) of chunk c; keys past the
@@ -483,15 +491,14 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
     // rows are fetched meanwhile.
     bf16x8 qbuf[2][NS];
     {
-      const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-      const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+      const size_t kvrow0 = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax;
       const int k_row = tid >> 4, k_col = (tid & 15) * 8;
       const int v_kg = tid & 15, v_dg = tid >> 4;
       u32x4 kr[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        kr[r] = ldg16(Kb + (size_t)min(c * kChunk + k_row + 16 * r, N - 1) * D + k_col);
-        vr[r] = ldg16(Vb + (size_t)min(c * kChunk + 4 * v_kg + r, N - 1) * D + 8 * v_dg);
+        kr[r] = ldg16_dc<DC>(a.K, kvrow0 + min(c * kChunk + k_row + 16 * r, N - 1), k_col);
+        vr[r] = ldg16_dc<DC>(a.V, kvrow0 + min(c * kChunk + 4 * v_kg + r, N - 1), 8 * v_dg);
       }
       if (nb > 0) load_q(rec[0], cnt_of(0), qbuf[0]);
 #pragma unroll
@@ -670,9 +677,9 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   const int tid = threadIdx.x;
   if (*a.bad != 0) {
     // inconsistent workspace: every row of the unit reads NaN
-    for (int x = tid; x < kChunk * D / 2; x += blockDim.x) {
-      const int r = c * kChunk + x / (D / 2);
-      if (r < N) reinterpret_cast<uint32_t*>(a.O + (bh * N + r) * (size_t)D)[x % (D / 2)] = 0x7fc07fc0u;
+    for (int x = tid; x < kChunk * a.d / 2; x += blockDim.x) {
+      const int r = c * kChunk + x / (a.d / 2);
+      if (r < N) reinterpret_cast<uint32_t*>(a.O + (bh * N + r) * (size_t)a.d)[x % (a.d / 2)] = 0x7fc07fc0u;
     }
     return;
   }
@@ -696,8 +703,7 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   if constexpr (CAUSAL) {
     uint16_t* const sK = reinterpret_cast<uint16_t*>(s_raw);
     uint16_t* const sV = sK + kChunk * KROW;
-    const uint16_t* Kb = a.K + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
-    const uint16_t* Vb = a.V + ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+    const size_t kvrow0 = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax;
     // wavefront w: rows row0 + 16 w + lane % 16; lanes l, l^16, l^32, l^48 share a row
     const int rloc = 16 * w + (lane & 15);
     const int qi = row0 + rloc;
@@ -705,9 +711,8 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
     const float lw = qi < N ? a.own_lw[bh * (size_t)N + qi] : -INFINITY;
     bf16x8 qb[D / 32];  // Q^T as the B operand: column qi, dims 32 s + 8 q4 .. +7
     {
-      const uint16_t* qp = a.Q + (bh * N + min(qi, N - 1)) * (size_t)D + 8 * q4;
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(ldg16(qp + 32 * s));
+      for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(ldg16_d(a.Q, bh * N + min(qi, N - 1), 32 * s + 8 * q4, a.d));
     }
     {
       // K rows (row-major) and V (transposed) of chunk c; keys past the sequence
@@ -717,8 +722,8 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
       u32x4 kr[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        kr[r] = ldg16(Kb + (size_t)min(row0 + k_row + 16 * r, N - 1) * D + k_col);
-        vr[r] = ldg16(Vb + (size_t)min(row0 + 4 * v_kg + r, N - 1) * D + 8 * v_dg);
+        kr[r] = ldg16_d(a.K, kvrow0 + min(row0 + k_row + 16 * r, N - 1), k_col, a.d);
+        vr[r] = ldg16_d(a.V, kvrow0 + min(row0 + 4 * v_kg + r, N - 1), 8 * v_dg, a.d);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&sK[(k_row + 16 * r) * KROW + k_col]) = kr[r];
@@ -877,7 +882,7 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
       u32x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
-      __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(a.O + ri * D + 8 * p + 64 * hv));
+      if (8 * p + 64 * hv < a.d) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(a.O + ri * a.d + 8 * p + 64 * hv));
     }
   }
 }
@@ -886,7 +891,10 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(k_cm_plan, dim3((a.n_bhc + 255) / 256), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_cm_scatter, dim3(a.n_tiles, a.Hq, a.B), dim3(256), 0, stream, a);
   const long long cm_grid = std::min<long long>(a.max_items, (long long)a.n_cu * kCmWgPerCu);
-  hipLaunchKernelGGL(k_prefill_cm<128>, dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
+  if (a.d == 64)
+    hipLaunchKernelGGL((k_prefill_cm<128, 64>), dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_prefill_cm<128, 128>), dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
   const int m_units = a.B * a.Hkv * ((a.N + kChunk - 1) / kChunk);
   const unsigned merge_grid = (unsigned)((m_units + 7) / 8) * 8 * a.g;
   if (a.causal)

@@ -5,8 +5,9 @@
 //
 // One wavefront per (b, kv head, chunk). A 64 x 128 bf16 chunk is 16 KB of
 // contiguous memory; each load instruction of the wave reads 1 KB of it (four
-// rows, 16 lanes x 16 bytes per row), so every byte of K is read once with full
-// coalescing. The kernel is bound by HBM bandwidth.
+// rows, 16 lanes x 16 bytes per row; at head_dim 64, eight rows of 8 lanes), so
+// every byte of K is read once with full coalescing. The kernel is bound by HBM
+// bandwidth.
 #include "kernels.hpp"
 
 namespace dash {
@@ -20,7 +21,7 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
                                                    int C, float inv_sqrt_d) {
   constexpr int LPR = D / 8;          // lanes per key row (16 bytes each)
   constexpr int RPI = kWave / LPR;    // rows per load instruction
-  static_assert(LPR == 16, "summary kernel is laid out for head_dim 128");
+  static_assert(LPR == 16 || LPR == 8, "head_dim 128 or 64");
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int c = chunk_begin + blockIdx.x * (blockDim.x / kWave) + wave;
@@ -67,12 +68,14 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
       part = fmaf(bf16lo(kv[it][e]), w_cls[2 * e], part);
       part = fmaf(bf16hi(kv[it][e]), w_cls[2 * e + 1], part);
     }
-    float lg = sum16(part) * inv_sqrt_d;
+    float lg = (LPR == 16 ? sum16(part) : sum8(part)) * inv_sqrt_d;
     int row = it * RPI + rsub;
     lg = (it < n_it && row < n_valid) ? lg : -INFINITY;
     logit[it] = lg;
     mx = fmaxf(mx, lg);
   }
+  // across the row groups of a load instruction (lanes l ^ LPR, ...)
+  if (LPR == 8) mx = max_xor8(mx);
   mx = max_xor32(max_xor16(mx));
   float den = 0.f;
   float acc[8];
@@ -87,6 +90,10 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
     }
   }
   // every lane of a row group saw the same rows: den is per row group
+  if (LPR == 8) {
+    den = sum_xor8(den);
+    for (int e = 0; e < 8; ++e) acc[e] = sum_xor8(acc[e]);
+  }
   den = sum_xor32(sum_xor16(den));
   for (int e = 0; e < 8; ++e) acc[e] = sum_xor32(sum_xor16(acc[e]));
   if (lane < LPR) {
@@ -102,10 +109,16 @@ __global__ __launch_bounds__(256) void k_summarize(const uint16_t* __restrict__ 
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream) {
   const int n = a.chunk_end - a.chunk_begin;
   dim3 grid((n + 3) / 4, a.Hkv, a.B);
-  hipLaunchKernelGGL(k_summarize<128>, grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.cls), a.S,
-                     a.Hkv, a.Lmax, a.n_tokens, a.seqlens, a.chunk_begin, a.chunk_end, a.s_cap,
-                     a.C, a.inv_sqrt_d);
+  if (a.d == 64)
+    hipLaunchKernelGGL(k_summarize<64>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.cls), a.S,
+                       a.Hkv, a.Lmax, a.n_tokens, a.seqlens, a.chunk_begin, a.chunk_end, a.s_cap,
+                       a.C, a.inv_sqrt_d);
+  else
+    hipLaunchKernelGGL(k_summarize<128>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(a.K), static_cast<const uint16_t*>(a.cls), a.S,
+                       a.Hkv, a.Lmax, a.n_tokens, a.seqlens, a.chunk_begin, a.chunk_end, a.s_cap,
+                       a.C, a.inv_sqrt_d);
   return hipGetLastError();
 }
 

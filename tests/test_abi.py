@@ -78,6 +78,9 @@ def test_prefill_workspace_pool(lib):
     assert lib.dash_workspace_size(1, 32, 8, 32768, 32768, 128, 0, p) == lib.dash_prefill_workspace_size(
         1, 32, 8, 32768, 32768, 128, p, 5 * rows32)
     assert lib.dash_workspace_size(1, 32, 8, 32768, 32768, 128, 0, p) < 2 * 2 ** 30
+    # head_dim 64 runs the 128-wide layouts: the same workspace
+    assert lib.dash_workspace_size(1, 32, 8, 4096, 4096, 64, 0, p) == lib.dash_workspace_size(1, 32, 8, 4096, 4096, 128, 0, p)
+    assert lib.dash_workspace_size(2, 8, 2, 1, 8193, 64, 1, p) == lib.dash_workspace_size(2, 8, 2, 1, 8193, 128, 1, p)
     assert lib.dash_workspace_size(1, 32, 8, 4096, 4096, 128, 0, p) == lib.dash_prefill_workspace_size(
         1, 32, 8, 4096, 4096, 128, p, 16 * 32 * 4096)
     assert lib.dash_workspace_size(1, 32, 8, 16384, 16384, 128, 0, p) == lib.dash_prefill_workspace_size(
@@ -94,7 +97,7 @@ def test_summarize_validation(lib):
     assert _summ(lib, c1=3, cap=2) == INVALID       # chunk_end beyond the cache
     assert _summ(lib, n=0) == INVALID
     assert _summ(lib, n=200, Lmax=128) == INVALID
-    assert _summ(lib, d=64) == UNSUPPORTED
+    assert _summ(lib, d=96) == UNSUPPORTED   # head_dim 64 and 128 only
     assert _summ(lib, dt=0) == UNSUPPORTED
     assert _summ(lib, dt=7) == INVALID
     assert _summ(lib, p=_p(chunk_size=32)) == UNSUPPORTED
@@ -114,7 +117,8 @@ def test_route_validation(lib):
     assert _route(lib, p=_p(alpha=1.0)) == INVALID
     assert _route(lib, p=_p(alpha=float("nan"))) == INVALID
     assert _route(lib, p=_p(n_iter=0)) == INVALID
-    assert _route(lib, d=64) == UNSUPPORTED
+    assert _route(lib, d=96) == UNSUPPORTED
+    assert _route(lib, d=64, ws_bytes=16) == WORKSPACE  # head_dim 64 passes the checks
     assert _route(lib, dt=0) == UNSUPPORTED
     assert _route(lib, p=_p(chunk_size=128)) == UNSUPPORTED
     assert _route(lib, Nq=300, Lmax=256) == INVALID
@@ -135,13 +139,16 @@ def test_attention_validation(lib):
     f = lib.dash_sparse_attn_prefill
     assert f(NULL, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 128, p, FAKE, FAKE, 0, NULL) == INVALID
     assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 128, 128, p, FAKE, FAKE, 0, NULL) == INVALID
-    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 64, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 96, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 64, p, FAKE, FAKE, 8, NULL) == WORKSPACE
     assert f(FAKE, FAKE, FAKE, 1, 1, 4, 1, 256, 256, 128, p, FAKE, FAKE, 8, NULL) == WORKSPACE
     g = lib.dash_sparse_attn_decode
     assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, NULL, 256, 128, p, FAKE, FAKE, 0, NULL) == INVALID
     assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 128, _p(causal=False), FAKE, FAKE, 0, NULL) == INVALID
     assert g(FAKE, FAKE, FAKE, 1, 1, 48, 1, FAKE, 256, 128, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
     assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 128, p, FAKE, FAKE, 8, NULL) == WORKSPACE
+    assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 96, p, FAKE, FAKE, 0, NULL) == UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, 1, 1, 4, 1, FAKE, 256, 64, p, FAKE, FAKE, 8, NULL) == WORKSPACE
     e = lib.entmax_attn
     assert e(NULL, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.5, 10, 1, FAKE, FAKE, NULL, NULL) == INVALID
     assert e(FAKE, FAKE, FAKE, 1, 1, 1, 128, 64, NULL, 1.0, 10, 1, FAKE, FAKE, NULL, NULL) == INVALID
@@ -227,3 +234,16 @@ def test_decode_noalloc_validation(lib):
     # non-causal decode is refused
     assert lib.dash_decode_step_noalloc(P, P, P, P, P, 1, 2, 8, 2, P, 1024, 128, 16, _p(causal=False), P, P, None, 0,
                                         None) == 1
+
+
+def test_backward_head_dim_128_only(lib):
+    """The DashAttention backward and the summary backward are built for
+    head_dim 128: head_dim 64 is refused on the host (no launch)."""
+    p = _p()
+    f = lib.dash_sparse_attn_prefill_backward
+    F8 = [FAKE] * 8
+    # Q K V cls S dO tau bits words dt B Hq Hkv N Lmax d s_cap params dQ dK dV dcls ws ws_bytes stream
+    assert f(*F8, 8, 1, 1, 4, 1, 256, 256, 64, 4, p, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, NULL) == UNSUPPORTED
+    g = lib.dash_summarize_backward
+    F3 = [FAKE] * 3
+    assert g(*F3, 1, 1, 2, 256, 64, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED

@@ -102,6 +102,26 @@ def test_prefill_small(B, Hq, Hkv, N, p, planted):
 
 
 @pytest.mark.parametrize(
+    "B,Hq,Hkv,N,p,planted,pool",
+    [
+        (1, 4, 1, 1000, api.Params(causal=True, estimate_diagonal=True), "chunks", None),
+        (2, 4, 2, 700, api.Params(causal=False), "chunks", None),
+        (1, 8, 2, 2048, api.Params(alpha=2.0), "needles", None),
+        (1, 4, 4, 300, api.Params(scaling_factor=3.0), None, None),
+        (1, 1, 1, 37, api.Params(estimate_diagonal=False), None, None),
+        (1, 4, 1, 1000, api.Params(estimate_diagonal=True), "chunks", 0),  # every tile row-major
+    ],
+)
+def test_prefill_head_dim_64(B, Hq, Hkv, N, p, planted, pool):
+    """head_dim 64: the kernels run their 128-wide layouts with the upper dims
+    zero; summaries, tau, routed sets and O against the oracle at d = 64."""
+    Q, K, V, cls = routed_prefill_inputs(B, Hq, Hkv, N, 64, 11 + N, planted=planted, device="cuda")
+    cnt = check_prefill(Q, K, V, cls, p, where=f"d64 N={N} {p}", pool_pairs=pool)
+    if pool == 0:
+        assert cnt["row_major_tiles"] > 0, cnt
+
+
+@pytest.mark.parametrize(
     "B,Hq,Hkv,N,p,planted",
     [
         (1, 4, 1, 1000, api.Params(causal=True, estimate_diagonal=True), "chunks"),
@@ -358,6 +378,16 @@ def test_decode_small(est, g):
     q, Kc, Vc, cls, _ = decode_inputs(3, Hkv * g, Hkv, 1100, 128, seed=31 + g, device="cuda", Lmax=1160)
     seqlens = torch.tensor([1025, 1088, 700], dtype=torch.int32, device="cuda")
     check_decode(q, Kc, Vc, cls, seqlens, api.Params(estimate_diagonal=est), where=f"g{g} est{est}")
+
+
+@pytest.mark.parametrize("g,est", [(1, True), (4, True), (4, False), (8, True)])
+def test_decode_head_dim_64(g, est):
+    """Decode at head_dim 64 (caches, queries, head_cls and the summary cache
+    64 wide) against the oracle."""
+    Hkv = 2
+    q, Kc, Vc, cls, _ = decode_inputs(3, Hkv * g, Hkv, 1100, 64, seed=41 + g, device="cuda", Lmax=1160)
+    seqlens = torch.tensor([1025, 1088, 700], dtype=torch.int32, device="cuda")
+    check_decode(q, Kc, Vc, cls, seqlens, api.Params(estimate_diagonal=est), where=f"d64 g{g} est{est}")
 
 
 def test_decode_first_chunk_and_alpha2():
