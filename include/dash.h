@@ -19,6 +19,12 @@
  *     ordered by the caller (same stream).
  *   - Tensors are contiguous row-major. q/k/v use [batch, heads, seq, head_dim]
  *     ("Usage" of both pages); head_cls is [kv_heads, head_dim].
+ *   - head_dim: 64 or 128 for dash_summarize, dash_route,
+ *     dash_sparse_attn_prefill, dash_sparse_attn_decode,
+ *     dash_decode_step_noalloc, entmax_attn and entmax_attn_backward; 128 for
+ *     dash_summarize_backward and dash_sparse_attn_prefill_backward. The
+ *     DashAttention kernels keep their own arrays 128 wide, so a workspace
+ *     query gives the same size for head_dim 64 as for 128.
  *   - Work is enqueued on `stream` (NULL = the null stream); nothing
  *     synchronises the host. Outputs are valid once the stream reaches them.
  *   - All argument checks run on the host before any HIP call, so a bad call
@@ -160,7 +166,7 @@ dash_status dash_summarize_backward(const void* K, const void* head_cls, const f
  *               dash_sparse_attn_* call; size from dash_workspace_size().
  *               Prefill: the part beyond the fixed lists is the partial-result
  *               pool of dash_sparse_attn_prefill, one slot per (row, routed
- *               past chunk) pair (2 * d + 36 bytes each), so a larger workspace
+ *               past chunk) pair (292 bytes each, whatever the head_dim), so a larger workspace
  *               buys a larger pool (dash_prefill_workspace_size); the same
  *               ws_bytes must then be passed to dash_sparse_attn_prefill.
  * --------------------------------------------------------------------------- */
