@@ -245,6 +245,17 @@ def test_prefill_32k_workload_sampled():
     assert cnt["row_major_tiles"] == 0 and cnt["pool_pairs"] < 0.8 * cnt["pool_capacity"], cnt
 
 
+def test_prefill_32k_head_dim_64_sampled():
+    """The 32K needle recipe at head_dim 64 (sampled rows of two heads)."""
+    w = WORKLOADS["routed_prefill_32k"]
+    Q, K, V, cls = routed_prefill_inputs(w.B, w.Hq, w.Hkv, w.N, 64, w.seed + 64, planted=w.planted, device="cuda")
+    p = api.Params(alpha=w.alpha, causal=w.causal, estimate_diagonal=w.estimate_diagonal)
+    rng = np.random.default_rng(w.seed + 64)
+    heads = {3, 28}
+    check_prefill(Q, K, V, cls, p, rows_of=lambda b, h: _sample_rows(w.N, rng, 10) if h in heads else [],
+                  where="32k d64")
+
+
 def test_prefill_32k_workload_full_tiles():
     """Complete 128-row tiles of the 32K needle workload at depths 4K, 8K, 16K
     and 32K - 128, for all four query heads of KV head 0: every row of each

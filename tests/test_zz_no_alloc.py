@@ -19,10 +19,10 @@ pytestmark = pytest.mark.gpu
 C = 64
 
 
-def _case(B, Hq, Hkv, L, Lmax, seed, lens):
-    q, Kc, Vc, cls, _ = decode_inputs(B, Hq, Hkv, L, 128, seed, device="cuda", Lmax=Lmax)
+def _case(B, Hq, Hkv, L, Lmax, seed, lens, d=128):
+    q, Kc, Vc, cls, _ = decode_inputs(B, Hq, Hkv, L, d, seed, device="cuda", Lmax=Lmax)
     seqlens = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    S = torch.zeros(B, Hkv, -(-Lmax // C), 128, dtype=torch.float32, device="cuda")
+    S = torch.zeros(B, Hkv, -(-Lmax // C), d, dtype=torch.float32, device="cuda")
     p = api.Params()
     api.summarize(Kc, cls, S, seqlens=seqlens, chunk_begin=0, chunk_end=Lmax // C, params=p)
     return q, Kc, Vc, cls, S, seqlens, p
@@ -52,6 +52,15 @@ def test_noalloc_decode_matches_workspace_path_twice():
             o_ref, t_ref, _ = oracle.dash_rows(f64(q[b, h]), np.array([n - 1]), keys, vals, clsv, n, op, summ)
             tau_close(f64(tau[b, h, :1]), t_ref, f"noalloc b{b} h{h}")
             assert_close(f64(O[b, h, 0]), o_ref[0], TOL_BF16, f"noalloc O b{b} h{h}")
+
+
+def test_noalloc_decode_head_dim_64():
+    """head_dim 64 through the allocation-free step: equal to the workspace path."""
+    q, Kc, Vc, cls, S, seqlens, p = _case(2, 8, 2, 900, 1024, 13, [901, 700], d=64)
+    ref_O, ref_tau, ref_bits, _ = api.decode_step(q, Kc, Vc, cls, S, seqlens, p)
+    O, tau, bits = api.decode_step_noalloc(q, Kc, Vc, cls, S, seqlens, p)
+    torch.cuda.synchronize()
+    assert torch.equal(O, ref_O) and torch.equal(tau, ref_tau) and torch.equal(bits, ref_bits)
 
 
 def test_noalloc_refuses_sizes_beyond_the_scratch():
