@@ -117,7 +117,7 @@ dash_status dash_summarize_backward(const void* K, const void* head_cls, const f
   if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > s_cap) return DASH_ERR_INVALID_ARG;
   if (n_tokens <= 0 || n_tokens > Lmax || p.chunk_size <= 0) return DASH_ERR_INVALID_ARG;
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
-  if (p.chunk_size != kChunk || dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if (p.chunk_size != kChunk || dt != DASH_BF16 || !dash_head_dim_ok(d)) return DASH_ERR_UNSUPPORTED;
   if ((long long)chunk_end * kChunk > (long long)Lmax + kChunk - 1) return DASH_ERR_INVALID_ARG;
   SummarizeBwdArgs a{K, head_cls, dS, dK, dcls, partials, B, Hkv, Lmax, d, n_tokens,
                      chunk_begin, chunk_end, s_cap, kChunk, 1.f / sqrtf((float)d)};
@@ -366,7 +366,7 @@ dash_status dash_sparse_attn_prefill_backward(const void* Q, const void* K, cons
   if (dt != DASH_BF16 && dt != DASH_F32) return DASH_ERR_INVALID_ARG;
   dash_status st = check_params(p);
   if (st != DASH_OK) return st;
-  if (dt != DASH_BF16 || d != 128) return DASH_ERR_UNSUPPORTED;
+  if (dt != DASH_BF16 || !dash_head_dim_ok(d)) return DASH_ERR_UNSUPPORTED;
   const DashBwdLayout L = dash_bwd_layout(B, Hq, Hkv, N, Lmax, d, p.causal != 0);
   if (L.n_slots > kDashBwdMaxSlots) return DASH_ERR_UNSUPPORTED;
   if (bits_words < (L.n_slots + 31) / 32) return DASH_ERR_INVALID_ARG;
@@ -384,6 +384,7 @@ dash_status dash_sparse_attn_prefill_backward(const void* Q, const void* K, cons
   a.bits = active_bits;
   a.bits_words = bits_words;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.g = Hq / Hkv; a.N = N; a.Lmax = Lmax; a.s_cap = s_cap;
+  a.d = d;
   a.n_slots = L.n_slots;
   a.n_sum = L.n_sum;
   a.causal = p.causal;

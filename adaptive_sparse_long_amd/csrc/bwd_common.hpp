@@ -23,18 +23,21 @@ struct Frags {
 
 // Operand fragments of one row (row index valid < n_ok, else zeros): bf16 rows
 // give 8 elements per k-step at d = 16 s + 8 (lane / 32); float rows one
-// element at d = 2 s + lane / 32.
-template <bool BF, int D>
+// element at d = 2 s + lane / 32. DC: the rows' width in memory when it is
+// smaller than the fragments' D (head_dim 64 in a 128-wide layout): the dims
+// from DC on are zero.
+template <bool BF, int D, int DC = D>
 __device__ __forceinline__ void load_frags(Frags<BF, D>& fr, const void* base, int row, bool ok) {
   const int hi32 = lane_id() >> 5;
   if constexpr (BF) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + (size_t)row * D + 8 * hi32;
+    const uint16_t* p = static_cast<const uint16_t*>(base) + (size_t)row * DC + 8 * hi32;
 #pragma unroll
-    for (int s = 0; s < Frags<BF, D>::NS; ++s) fr.b[s] = as_bf16x8(ok ? ldg16(p + 16 * s) : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < Frags<BF, D>::NS; ++s)
+      fr.b[s] = as_bf16x8(ok && 16 * s < DC ? ldg16(p + 16 * s) : u32x4{0, 0, 0, 0});
   } else {
-    const float* p = static_cast<const float*>(base) + (size_t)row * D + hi32;
+    const float* p = static_cast<const float*>(base) + (size_t)row * DC + hi32;
 #pragma unroll
-    for (int s = 0; s < Frags<BF, D>::NS; ++s) fr.f[s] = ok ? p[2 * s] : 0.f;
+    for (int s = 0; s < Frags<BF, D>::NS; ++s) fr.f[s] = ok && 2 * s < DC ? p[2 * s] : 0.f;
   }
 }
 
@@ -102,14 +105,15 @@ __device__ __forceinline__ void acc_xt_w(f32x16 (&acc)[D / 32], const f32x16& w,
   }
 }
 
-// Write the lane's line of acc (dims 32 db + 8 q4 + 4 (l/32) + 0..3) times mul.
-template <bool BF, int D>
+// Write the lane's line of acc (dims 32 db + 8 q4 + 4 (l/32) + 0..3) times mul;
+// lines DC wide (dims from DC on are not written).
+template <bool BF, int D, int DC = D>
 __device__ __forceinline__ void store_line(void* out, size_t line, const f32x16 (&acc)[D / 32], float mul) {
   const int hi32 = lane_id() >> 5;
   if constexpr (BF) {
-    uint16_t* op = static_cast<uint16_t*>(out) + line * D + 4 * hi32;
+    uint16_t* op = static_cast<uint16_t*>(out) + line * DC + 4 * hi32;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DC / 32; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         u32x2 v = {pack_bf16x2(acc[db][4 * q4] * mul, acc[db][4 * q4 + 1] * mul),
@@ -117,9 +121,9 @@ __device__ __forceinline__ void store_line(void* out, size_t line, const f32x16 
         *reinterpret_cast<u32x2*>(op + 32 * db + 8 * q4) = v;
       }
   } else {
-    float* op = static_cast<float*>(out) + line * D + 4 * hi32;
+    float* op = static_cast<float*>(out) + line * DC + 4 * hi32;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DC / 32; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 v = {acc[db][4 * q4] * mul, acc[db][4 * q4 + 1] * mul, acc[db][4 * q4 + 2] * mul,

@@ -20,7 +20,7 @@
 //              [c_i C, i] passes its gradient to those keys and head_cls;
 //   summaries  the summary backward of every routed chunk (dash_summarize_backward's kernels).
 //
-// Kernels (bf16 inputs, head_dim 128, chunk 64):
+// Kernels (bf16 inputs, head_dim 64 or 128, chunk 64):
 //   k_dbwd_prep  per row: the log2 weight of every chunk (log2 pi recomputed
 //                from the float32 summaries, tau and the forward's routed-chunk
 //                bits; 0 for an own chunk attended with weight 1), stored
@@ -60,6 +60,11 @@ constexpr int kMaxListed = kDashBwdMaxSlots;  // chunk slots a row pass can list
 // ---------------------------------------------------------------------------
 // prep: one thread per row
 // ---------------------------------------------------------------------------
+// Every kernel below takes the caller's head_dim DC (the width of the rows of
+// Q, K, V, dO, head_cls, S, the outputs and this backward's own arrays) as a
+// template argument; at DC = 64 the 128-wide fragments and LDS layouts hold
+// zeros in dims 64..127 and nothing is stored there.
+template <int DC>
 __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const size_t bh = blockIdx.y;
@@ -69,14 +74,14 @@ __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
   const size_t row = bh * N + i;
   u32x4 q[D / 8];  // the query row, bf16
   {
-    const uint16_t* qp = a.Q + row * D;
+    const uint16_t* qp = a.Q + row * DC;
 #pragma unroll
-    for (int k = 0; k < D / 8; ++k) q[k] = ldg16(qp + 8 * k);
+    for (int k = 0; k < D / 8; ++k) q[k] = 8 * k < DC ? ldg16(qp + 8 * k) : u32x4{0, 0, 0, 0};
   }
   auto qdot_f32 = [&](const float* s) {  // <q_i, s> with s float32
     float z = 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 8; ++k) {
+    for (int k = 0; k < DC / 8; ++k) {
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + 8 * k);
       const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + 8 * k + 4);
       z = fmaf(bf16lo(q[k][0]), s0[0], z); z = fmaf(bf16hi(q[k][0]), s0[1], z);
@@ -89,7 +94,7 @@ __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
   auto bdot = [](const u32x4* x, const uint16_t* y) {  // <x, y>, both bf16
     float z = 0.f;
 #pragma unroll 4
-    for (int k = 0; k < D / 8; ++k) {
+    for (int k = 0; k < DC / 8; ++k) {
       const u32x4 v = ldg16(y + 8 * k);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -103,7 +108,7 @@ __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
   const uint32_t* bits = a.bits + row * a.bits_words;
   const int ci = i / kChunk;
   const int c_last = a.causal ? ci : a.n_slots - 1;
-  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * a.s_cap * D;
+  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * a.s_cap * DC;
   float* wt = a.WT + bh * (size_t)a.n_slots * N + i;
   auto weight = [&](float u) { return u > tau ? a.beta * __log2f(u - tau) : -INFINITY; };
   for (int c = 0; c < a.n_slots; ++c) {
@@ -115,23 +120,23 @@ __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
         } else {
           // score against the summary of tokens [ci*C, i]: sum_j a_j <q, k_j>
           // with a = softmax(<k_j, cls> / sqrt(d)) over those tokens
-          const uint16_t* kb = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ci * kChunk) * D;
+          const uint16_t* kb = a.K + (((size_t)b * a.Hkv + hk) * a.Lmax + (size_t)ci * kChunk) * DC;
           u32x4 cl[D / 8];
 #pragma unroll
-          for (int k = 0; k < D / 8; ++k) cl[k] = ldg16(a.cls + (size_t)hk * D + 8 * k);
+          for (int k = 0; k < D / 8; ++k) cl[k] = 8 * k < DC ? ldg16(a.cls + (size_t)hk * DC + 8 * k) : u32x4{0, 0, 0, 0};
           const int nj = i - ci * kChunk + 1;
           float m = -INFINITY;
-          for (int j = 0; j < nj; ++j) m = fmaxf(m, bdot(cl, kb + (size_t)j * D) * a.inv_sqrt_d);
+          for (int j = 0; j < nj; ++j) m = fmaxf(m, bdot(cl, kb + (size_t)j * DC) * a.inv_sqrt_d);
           float den = 0.f, num = 0.f;
           for (int j = 0; j < nj; ++j) {
-            const float e = __expf(bdot(cl, kb + (size_t)j * D) * a.inv_sqrt_d - m);
+            const float e = __expf(bdot(cl, kb + (size_t)j * DC) * a.inv_sqrt_d - m);
             den += e;
-            num = fmaf(e, bdot(q, kb + (size_t)j * D), num);
+            num = fmaf(e, bdot(q, kb + (size_t)j * DC), num);
           }
           w = weight(a.uscale * (num / den));
         }
       } else {
-        w = weight(a.uscale * qdot_f32(Sb + (size_t)c * D));
+        w = weight(a.uscale * qdot_f32(Sb + (size_t)c * DC));
       }
     }
     wt[(size_t)c * N] = w;
@@ -141,6 +146,7 @@ __global__ __launch_bounds__(256) void k_dbwd_prep(DashBwdArgs a) {
 // ---------------------------------------------------------------------------
 // row pass
 // ---------------------------------------------------------------------------
+template <int DC>
 __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   constexpr bool BF = true;
   __shared__ __attribute__((aligned(16))) uint16_t sKt[4][D * kTRow];
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   const bool row_ok = qi < N;
   const bool causal = a.causal != 0;
   const int ci = qi / kChunk;
-  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * DC;
   const uint16_t* Kp = a.K + kvb;
   const uint16_t* Vp = a.V + kvb;
   const float* wt = a.WT + bh * (size_t)a.n_slots * N;
@@ -166,8 +172,8 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   const float sc = a.scale_log2;
 
   Frags<BF, D> fq, fdo, fk, fv;
-  load_frags<BF, D>(fq, a.Q + bh * (size_t)N * D, qi, row_ok);
-  load_frags<BF, D>(fdo, a.dO + bh * (size_t)N * D, qi, row_ok);
+  load_frags<BF, D, DC>(fq, a.Q + bh * (size_t)N * DC, qi, row_ok);
+  load_frags<BF, D, DC>(fdo, a.dO + bh * (size_t)N * DC, qi, row_ok);
   auto wrow = [&](int c) { return row_ok ? wt[(size_t)c * N + qi] : -INFINITY; };
 
   // ---- the chunks some row of the wavefront attends: the OR of the rows'
@@ -220,8 +226,8 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   auto load_half = [&](Frags<BF, D>& k_, Frags<BF, D>& v_, float& wc_, int j) {  // half j % 2 of entry j / 2
     const int c = list[j >> 1];
     const int kr = (2 * c + (j & 1)) * 32 + (lane & 31);
-    load_frags<BF, D>(k_, Kp, kr, kr < N);
-    load_frags<BF, D>(v_, Vp, kr, kr < N);
+    load_frags<BF, D, DC>(k_, Kp, kr, kr < N);
+    load_frags<BF, D, DC>(v_, Vp, kr, kr < N);
     wc_ = wrow(c);
   };
   // fn(k fragments, v fragments, weight, half index j) over every half, prefetching
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
   }
   const float ratio = A2 > 0.f ? A1 / A2 : 0.f;
   // dQ = acc / sqrt(d) + rt * sum_c dz_c s_c: the routing term enters acc times sqrt(d) = sf / rt
-  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * a.s_cap * D;
+  const float* Sb = a.S + ((size_t)b * a.Hkv + hk) * a.s_cap * DC;
   float wn = -INFINITY, gn = 0.f;
   if (nl > 0) wg(0, wn, gn);
   for (int e = 0; e < nl; ++e) {
@@ -350,9 +356,9 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
     // the own chunk's estimate passes its gradient on in k_dbwd_est
     if (dz != 0.f && !(causal && c == ci)) {
       const float f = a.sf * dz;
-      const float* sr = Sb + (size_t)c * D + 4 * hi32;
+      const float* sr = Sb + (size_t)c * DC + 4 * hi32;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < DC / 32; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x4 v = *reinterpret_cast<const f32x4*>(sr + 32 * db + 8 * q4);
@@ -361,12 +367,13 @@ __global__ __launch_bounds__(256) void k_dbwd_rows(DashBwdArgs a) {
         }
     }
   }
-  if (row_ok) store_line<false, D>(a.dQf, bh * N + qi, acc, a.inv_sqrt_d);
+  if (row_ok) store_line<false, D, DC>(a.dQf, bh * N + qi, acc, a.inv_sqrt_d);
 }
 
 // ---------------------------------------------------------------------------
 // column pass
 // ---------------------------------------------------------------------------
+template <int DC>
 __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
   constexpr bool BF = true;
   constexpr int LC = 512;  // pair list entries per wavefront
@@ -388,12 +395,12 @@ __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
   const bool causal = a.causal != 0;
   const int c = k0 / kChunk;
   const bool first_half = (k0 % kChunk) == 0;  // this wavefront also sums the chunk's summary gradient
-  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * DC;
   const float sc = a.scale_log2;
 
   Frags<BF, D> fk, fv, fq, fdo;
-  load_frags<BF, D>(fk, a.K + kvb, kj, key_ok);
-  load_frags<BF, D>(fv, a.V + kvb, kj, key_ok);
+  load_frags<BF, D, DC>(fk, a.K + kvb, kj, key_ok);
+  load_frags<BF, D, DC>(fv, a.V + kvb, kj, key_ok);
   f32x16 dk[D / 32], dv[D / 32], dsum[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -422,8 +429,8 @@ __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
     const int ent = ok ? pairs[e0 + m] : 0;
     const int hh = ent >> 20, row = ent & 0xfffff;
     const size_t bh = bh0 + hh;
-    load_frags<BF, D>(fq, a.Q + bh * (size_t)N * D, row, ok);
-    load_frags<BF, D>(fdo, a.dO + bh * (size_t)N * D, row, ok);
+    load_frags<BF, D, DC>(fq, a.Q + bh * (size_t)N * DC, row, ok);
+    load_frags<BF, D, DC>(fdo, a.dO + bh * (size_t)N * DC, row, ok);
     const f32x16 s = dot32<BF, D>(fq, fk);    // S[pair][key]
     const f32x16 dp = dot32<BF, D>(fdo, fv);  // dP[pair][key]
     if (lane < 32) {
@@ -512,11 +519,11 @@ __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
   for (int e0 = 0; e0 < np; e0 += 32) process(e0, min(32, np - e0));
 
   if (key_ok) {
-    store_line<false, D>(a.dKf, ((size_t)b * a.Hkv + hk) * N + kj, dk, a.inv_sqrt_d);
-    store_line<true, D>(a.dV, ((size_t)b * a.Hkv + hk) * a.Lmax + kj, dv, 1.f);
+    store_line<false, D, DC>(a.dKf, ((size_t)b * a.Hkv + hk) * N + kj, dk, a.inv_sqrt_d);
+    store_line<true, D, DC>(a.dV, ((size_t)b * a.Hkv + hk) * a.Lmax + kj, dv, 1.f);
   }
   // every key column of dsum holds the same vector; lanes 0 and 32 store it
-  if (first_half && (lane & 31) == 0) store_line<false, D>(a.dSum, ((size_t)b * a.Hkv + hk) * a.n_slots + c, dsum, a.rt);
+  if (first_half && (lane & 31) == 0) store_line<false, D, DC>(a.dSum, ((size_t)b * a.Hkv + hk) * a.n_slots + c, dsum, a.rt);
 }
 
 // ---------------------------------------------------------------------------
@@ -528,6 +535,7 @@ __global__ __launch_bounds__(256) void k_dbwd_cols(DashBwdArgs a) {
 //   dK_j += a_ij ds^_i + de_ij cls / sqrt(d),  dcls += sum_j de_ij k_j / sqrt(d).
 // One workgroup per (b, kv head, chunk) over the g heads' rows of the chunk.
 // ---------------------------------------------------------------------------
+template <int DC>
 __global__ __launch_bounds__(256) void k_dbwd_est(DashBwdArgs a) {
   __shared__ float sK[kChunk][D + 1];
   __shared__ float sq[D], scl[D], se[kChunk], sa[kChunk], skq[kChunk], sde[kChunk];
@@ -535,12 +543,12 @@ __global__ __launch_bounds__(256) void k_dbwd_est(DashBwdArgs a) {
   const int N = a.N;
   const int t = threadIdx.x;
   const int nk = min(kChunk, N - c * kChunk);
-  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * D;
+  const size_t kvb = ((size_t)b * a.Hkv + hk) * (size_t)a.Lmax * DC;
   for (int x = t; x < kChunk * D; x += 256) {
     const int j = x / D, dd = x % D;
-    sK[j][dd] = j < nk ? __uint_as_float(((uint32_t)a.K[kvb + (size_t)(c * kChunk + j) * D + dd]) << 16) : 0.f;
+    sK[j][dd] = j < nk && dd < DC ? __uint_as_float(((uint32_t)a.K[kvb + (size_t)(c * kChunk + j) * DC + dd]) << 16) : 0.f;
   }
-  if (t < D) scl[t] = __uint_as_float(((uint32_t)a.cls[(size_t)hk * D + t]) << 16);
+  if (t < D) scl[t] = t < DC ? __uint_as_float(((uint32_t)a.cls[(size_t)hk * DC + t]) << 16) : 0.f;
   __syncthreads();
   if (t < kChunk) {
     float e = 0.f;
@@ -563,7 +571,7 @@ __global__ __launch_bounds__(256) void k_dbwd_est(DashBwdArgs a) {
       const float kappa = wtc[i] > -INFINITY ? a.rt * dztc[i] : 0.f;
       if (kappa == 0.f) continue;
       __syncthreads();  // the previous row's shared values are no longer read
-      if (t < D) sq[t] = __uint_as_float(((uint32_t)a.Q[(bh * N + i) * D + t]) << 16);
+      if (t < D) sq[t] = t < DC ? __uint_as_float(((uint32_t)a.Q[(bh * N + i) * DC + t]) << 16) : 0.f;
       __syncthreads();
       if (t < kChunk) {  // wavefront 0: prefix softmax weights and <k_j, q_i>
         const bool on = t <= il;
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(256) void k_dbwd_est(DashBwdArgs a) {
           shat = fmaf(sa[j], sK[j][t], shat);
           dc = fmaf(sde[j], sK[j][t], dc);
         }
-        a.dQf[(bh * N + i) * D + t] += kappa * shat;
+        if (t < DC) a.dQf[(bh * N + i) * DC + t] += kappa * shat;
         dcl = fmaf(dc, a.inv_sqrt_d, dcl);
       }
       if (jt <= il) {
@@ -596,20 +604,21 @@ __global__ __launch_bounds__(256) void k_dbwd_est(DashBwdArgs a) {
       }
     }
   }
-  if (jt < nk) {
-    float* dst = a.dKf + (((size_t)b * a.Hkv + hk) * N + (size_t)c * kChunk + jt) * D + d0;
+  if (jt < nk && d0 < DC) {
+    float* dst = a.dKf + (((size_t)b * a.Hkv + hk) * N + (size_t)c * kChunk + jt) * DC + d0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) dst[k] += dk[k];
   }
-  if (t < D) a.dcls_p[(((size_t)b * a.Hkv + hk) * a.n_slots + c) * D + t] = dcl;
+  if (t < DC) a.dcls_p[(((size_t)b * a.Hkv + hk) * a.n_slots + c) * DC + t] = dcl;
 }
 
 // ---------------------------------------------------------------------------
 // combine: dQ, dK to the output dtype; dcls = summary part + estimate parts (fixed order)
 // ---------------------------------------------------------------------------
+template <int DC>
 __global__ __launch_bounds__(256) void k_dbwd_combine(DashBwdArgs a) {
-  const size_t nq = (size_t)a.B * a.Hq * a.N * D;
-  const size_t nk = (size_t)a.B * a.Hkv * a.N * D;
+  const size_t nq = (size_t)a.B * a.Hq * a.N * DC;
+  const size_t nk = (size_t)a.B * a.Hkv * a.N * DC;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   uint16_t* dQ = static_cast<uint16_t*>(a.dQ);
   uint16_t* dK = static_cast<uint16_t*>(a.dK);
@@ -617,38 +626,43 @@ __global__ __launch_bounds__(256) void k_dbwd_combine(DashBwdArgs a) {
     dQ[x] = __builtin_bit_cast(uint16_t, (__bf16)a.dQf[x]);
   const int n_sum_rows = a.n_sum * kChunk;
   for (size_t x = blockIdx.x * (size_t)blockDim.x + threadIdx.x; x < nk; x += stride) {
-    const size_t line = x / D;
-    const int dd = (int)(x % D);
+    const size_t line = x / DC;
+    const int dd = (int)(x % DC);
     const int j = (int)(line % a.N);
     const size_t bhk = line / a.N;
     float v = a.dKf[x];
-    if (j < n_sum_rows) v += a.dKs[(bhk * a.Lmax + j) * D + dd];
-    dK[(bhk * a.Lmax + j) * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    if (j < n_sum_rows) v += a.dKs[(bhk * a.Lmax + j) * DC + dd];
+    dK[(bhk * a.Lmax + j) * DC + dd] = __builtin_bit_cast(uint16_t, (__bf16)v);
   }
-  if (blockIdx.x < (unsigned)a.Hkv && threadIdx.x < D) {
+  if (blockIdx.x < (unsigned)a.Hkv && threadIdx.x < DC) {
     const int hk = blockIdx.x;
-    float v = a.dcls_s[(size_t)hk * D + threadIdx.x];
+    float v = a.dcls_s[(size_t)hk * DC + threadIdx.x];
     if (a.causal && a.est)
       for (int b = 0; b < a.B; ++b)
-        for (int c = 0; c < a.n_slots; ++c) v += a.dcls_p[(((size_t)b * a.Hkv + hk) * a.n_slots + c) * D + threadIdx.x];
-    a.dcls[(size_t)hk * D + threadIdx.x] = v;
+        for (int c = 0; c < a.n_slots; ++c) v += a.dcls_p[(((size_t)b * a.Hkv + hk) * a.n_slots + c) * DC + threadIdx.x];
+    a.dcls[(size_t)hk * DC + threadIdx.x] = v;
   }
 }
 
-hipError_t launch_dash_bwd(const DashBwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k_dbwd_prep, dim3((a.N + 255) / 256, a.B * a.Hq), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(k_dbwd_rows, dim3((a.N + 127) / 128, a.B * a.Hq), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(k_dbwd_cols, dim3((a.N + 127) / 128, a.Hkv, a.B), dim3(256), 0, stream, a);
-  if (a.causal && a.est) hipLaunchKernelGGL(k_dbwd_est, dim3(a.n_slots, a.Hkv, a.B), dim3(256), 0, stream, a);
+template <int DC>
+static hipError_t dash_bwd_dc(const DashBwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_dbwd_prep<DC>, dim3((a.N + 255) / 256, a.B * a.Hq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_dbwd_rows<DC>, dim3((a.N + 127) / 128, a.B * a.Hq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_dbwd_cols<DC>, dim3((a.N + 127) / 128, a.Hkv, a.B), dim3(256), 0, stream, a);
+  if (a.causal && a.est) hipLaunchKernelGGL(k_dbwd_est<DC>, dim3(a.n_slots, a.Hkv, a.B), dim3(256), 0, stream, a);
   // the summaries' backward for dS = dSum
-  SummarizeBwdArgs sb{a.K, a.cls, a.dSum, a.dKs, a.dcls_s, a.sb_part, a.B, a.Hkv, a.Lmax, D, a.N,
+  SummarizeBwdArgs sb{a.K, a.cls, a.dSum, a.dKs, a.dcls_s, a.sb_part, a.B, a.Hkv, a.Lmax, DC, a.N,
                       0, a.n_sum, a.n_slots, kChunk, a.inv_sqrt_d};
   hipError_t e = launch_summarize_bwd(sb, stream);
   if (e != hipSuccess) return e;
-  const size_t nq = (size_t)a.B * a.Hq * a.N * D;
+  const size_t nq = (size_t)a.B * a.Hq * a.N * DC;
   const unsigned grid = (unsigned)std::min<size_t>((nq + 255) / 256, 8192);
-  hipLaunchKernelGGL(k_dbwd_combine, dim3(std::max<unsigned>(grid, (unsigned)a.Hkv)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_dbwd_combine<DC>, dim3(std::max<unsigned>(grid, (unsigned)a.Hkv)), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_dash_bwd(const DashBwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? dash_bwd_dc<64>(a, stream) : dash_bwd_dc<128>(a, stream);
 }
 
 }  // namespace dash

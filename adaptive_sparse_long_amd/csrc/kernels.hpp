@@ -426,6 +426,7 @@ struct DashBwdArgs {
   const uint32_t* bits;    // [B, Hq, N, bits_words] attended chunks
   int bits_words;
   int B, Hq, Hkv, g, N, Lmax, s_cap, n_slots, n_sum;
+  int d;             // head_dim (64 or 128): the width of every row above and below
   int causal, est;
   float alpha, beta;
   float uscale;      // (alpha - 1) * scaling_factor / sqrt(d): u per <q, s>

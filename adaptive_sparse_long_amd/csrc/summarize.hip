@@ -140,7 +140,13 @@ template <int D>
 __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
   constexpr int LPR = D / 8;
   constexpr int RPI = kWave / LPR;
-  static_assert(LPR == 16, "summary kernel is laid out for head_dim 128");
+  static_assert(LPR == 16 || LPR == 8, "head_dim 128 or 64");
+  // sums over a row's LPR lanes, and over the row groups of a load instruction
+  auto rsum = [](float x) { return LPR == 16 ? sum16(x) : sum8(x); };
+  auto gsum = [](float x) {
+    if (LPR == 8) x = sum_xor8(x);
+    return sum_xor32(sum_xor16(x));
+  };
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int c = a.chunk_begin + blockIdx.x * (blockDim.x / kWave) + wave;
@@ -200,10 +206,11 @@ __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
     }
     const int row = it * RPI + rsub;
     const bool ok = it < n_it && row < n_valid;
-    logit[it] = ok ? sum16(pl) * a.inv_sqrt_d : -INFINITY;
-    dot[it] = sum16(pd);  // <k_j, ds>
+    logit[it] = ok ? rsum(pl) * a.inv_sqrt_d : -INFINITY;
+    dot[it] = rsum(pd);  // <k_j, ds>
     mx = fmaxf(mx, logit[it]);
   }
+  if (LPR == 8) mx = max_xor8(mx);
   mx = max_xor32(max_xor16(mx));
   float den = 0.f, sacc[8];
   for (int e = 0; e < 8; ++e) sacc[e] = 0.f;
@@ -216,11 +223,11 @@ __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
       sacc[2 * e + 1] = fmaf(logit[it], bf16hi(kv[it][e]), sacc[2 * e + 1]);
     }
   }
-  den = sum_xor32(sum_xor16(den));
+  den = gsum(den);
   const float inv = 1.f / den;
   float sd = 0.f;  // <s_c, ds> over this lane's dims, then over the row
-  for (int e = 0; e < 8; ++e) sd = fmaf(sum_xor32(sum_xor16(sacc[e])) * inv, g[e], sd);
-  sd = sum16(sd);
+  for (int e = 0; e < 8; ++e) sd = fmaf(gsum(sacc[e]) * inv, g[e], sd);
+  sd = rsum(sd);
 
   float pc[8];
   for (int e = 0; e < 8; ++e) pc[e] = 0.f;
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) void k_summarize_bwd(SummarizeBwdArgs a) {
       *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
     }
   }
-  for (int e = 0; e < 8; ++e) pc[e] = sum_xor32(sum_xor16(pc[e])) * a.inv_sqrt_d;
+  for (int e = 0; e < 8; ++e) pc[e] = gsum(pc[e]) * a.inv_sqrt_d;
   if (lane < LPR) {
     *reinterpret_cast<f32x4*>(part) = f32x4{pc[0], pc[1], pc[2], pc[3]};
     *reinterpret_cast<f32x4*>(part + 4) = f32x4{pc[4], pc[5], pc[6], pc[7]};
@@ -296,16 +303,21 @@ __global__ __launch_bounds__(D) void k_summarize_bwd_reduce2(SummarizeBwdArgs a)
   a.dcls[(size_t)h * D + threadIdx.x] = t;
 }
 
-hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream) {
+template <int D>
+static hipError_t summarize_bwd_d(const SummarizeBwdArgs& a, hipStream_t stream) {
   const int n = a.chunk_end - a.chunk_begin;
   if (n > 0) {
     dim3 grid((n + 3) / 4, a.Hkv, a.B);
-    hipLaunchKernelGGL(k_summarize_bwd<128>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_summarize_bwd<D>, grid, dim3(256), 0, stream, a);
     dim3 g1((n + kRedRows - 1) / kRedRows, a.Hkv, a.B);
-    hipLaunchKernelGGL(k_summarize_bwd_reduce1<128>, g1, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_summarize_bwd_reduce1<D>, g1, dim3(256), 0, stream, a);
   }
-  hipLaunchKernelGGL(k_summarize_bwd_reduce2<128>, dim3(a.Hkv), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(k_summarize_bwd_reduce2<D>, dim3(a.Hkv), dim3(D), 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_summarize_bwd(const SummarizeBwdArgs& a, hipStream_t stream) {
+  return a.d == 64 ? summarize_bwd_d<64>(a, stream) : summarize_bwd_d<128>(a, stream);
 }
 
 }  // namespace dash

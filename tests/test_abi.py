@@ -210,7 +210,7 @@ def test_summarize_backward_validation(lib):
     assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 5, 4, p, *F3, NULL) == INVALID
     assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 6, 8, p, *F3, NULL) == INVALID
     assert f(*F3, 0, 1, 2, 256, 128, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
-    assert f(*F3, 1, 1, 2, 256, 64, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
+    assert f(*F3, 1, 1, 2, 256, 96, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
     assert f(*F3, 1, 1, 2, 256, 128, 256, 0, 4, 4, _lib.params(chunk_size=32), *F3, NULL) == UNSUPPORTED
 
 
@@ -236,14 +236,15 @@ def test_decode_noalloc_validation(lib):
                                         None) == 1
 
 
-def test_backward_head_dim_128_only(lib):
-    """The DashAttention backward and the summary backward are built for
-    head_dim 128: head_dim 64 is refused on the host (no launch)."""
+def test_backward_head_dim(lib):
+    """The backward entry points take head_dim 64 and 128 and refuse others on
+    the host (no launch)."""
     p = _p()
     f = lib.dash_sparse_attn_prefill_backward
     F8 = [FAKE] * 8
     # Q K V cls S dO tau bits words dt B Hq Hkv N Lmax d s_cap params dQ dK dV dcls ws ws_bytes stream
-    assert f(*F8, 8, 1, 1, 4, 1, 256, 256, 64, 4, p, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, NULL) == UNSUPPORTED
+    assert f(*F8, 8, 1, 1, 4, 1, 256, 256, 96, 4, p, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, NULL) == UNSUPPORTED
+    assert f(*F8, 8, 1, 1, 4, 1, 256, 256, 64, 4, p, FAKE, FAKE, FAKE, FAKE, FAKE, 16, NULL) == WORKSPACE
     g = lib.dash_summarize_backward
     F3 = [FAKE] * 3
-    assert g(*F3, 1, 1, 2, 256, 64, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED
+    assert g(*F3, 1, 1, 2, 256, 96, 256, 0, 4, 4, p, *F3, NULL) == UNSUPPORTED

@@ -35,9 +35,9 @@ def _check(name, got, ref, tol):
     assert not bad.any(), f"{name}: {int(bad.sum())} entries off, max err {float(err.max()):.3e} at {np.unravel_index(np.argmax(err - tol), err.shape)}"
 
 
-def _run(B, Hq, Hkv, N, p: api.Params, seed, planted="chunks"):
-    Q, K, V, cls = routed_prefill_inputs(B, Hq, Hkv, N, 128, seed, planted=planted, device="cuda")
-    dO = cotangent((B, Hq, N, 128), seed + 1, dtype="bf16", device="cuda")
+def _run(B, Hq, Hkv, N, p: api.Params, seed, planted="chunks", d=128):
+    Q, K, V, cls = routed_prefill_inputs(B, Hq, Hkv, N, d, seed, planted=planted, device="cuda")
+    dO = cotangent((B, Hq, N, d), seed + 1, dtype="bf16", device="cuda")
     O, tau, bits, S, _ = api.prefill(Q, K, V, cls, p, with_bits=True)
     dQ, dK, dV, dcls = api.prefill_backward(Q, K, V, cls, S, dO, tau, bits, p)
     torch.cuda.synchronize()
@@ -65,6 +65,20 @@ def _run(B, Hq, Hkv, N, p: api.Params, seed, planted="chunks"):
 )
 def test_prefill_backward_small(B, Hq, Hkv, N, p, planted):
     _run(B, Hq, Hkv, N, p, seed=100 + N, planted=planted)
+
+
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,N,p,planted",
+    [
+        (1, 4, 2, 260, api.Params(estimate_diagonal=True), "chunks"),
+        (1, 4, 1, 300, api.Params(estimate_diagonal=False), "needles"),
+        (2, 2, 1, 200, api.Params(causal=False), "chunks"),
+        (1, 2, 1, 330, api.Params(alpha=2.0), "chunks"),
+    ],
+)
+def test_prefill_backward_head_dim_64(B, Hq, Hkv, N, p, planted):
+    """The DashAttention backward at head_dim 64 against the oracle."""
+    _run(B, Hq, Hkv, N, p, seed=300 + N, planted=planted, d=64)
 
 
 def test_prefill_backward_deterministic():

@@ -69,6 +69,21 @@ def test_summarize_backward_small(B, Hkv, Lmax, n_tokens, c0, c1, cls_scale):
     assert bool((dK[:, :, : c0 * C] == 0).all()) and bool((dK[:, :, min(c1 * C, Lmax):] == 0).all())
 
 
+@pytest.mark.parametrize("B,Hkv,Lmax,n_tokens,c0,c1", [(2, 2, 320, 300, 0, 5), (1, 1, 128, 65, 0, 2)])
+def test_summarize_backward_head_dim_64(B, Hkv, Lmax, n_tokens, c0, c1):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(700 + Lmax)
+    K = torch.randn(B, Hkv, Lmax, 64, generator=gen, device="cuda").to(torch.bfloat16)
+    cls = torch.randn(Hkv, 64, generator=gen, device="cuda").to(torch.bfloat16)
+    dS = cotangent((B, Hkv, c1 + 1, 64), 800 + Lmax, dtype="f32", device="cuda")
+    dK, dcls = api.summarize_backward(K, cls, dS, n_tokens=n_tokens, chunk_begin=c0, chunk_end=c1,
+                                      params=api.Params())
+    torch.cuda.synchronize()
+    rK, rc = _reference(f64(K), f64(cls), f64(dS), n_tokens, c0, c1)
+    assert_close(f64(dK), rK, TOL_F32, "dK d64")
+    assert_close(f64(dcls), rc, TOL_F32, "dcls d64")
+
+
 def test_summarize_backward_deterministic_and_empty_range():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(7)
