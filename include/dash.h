@@ -19,12 +19,9 @@
  *     ordered by the caller (same stream).
  *   - Tensors are contiguous row-major. q/k/v use [batch, heads, seq, head_dim]
  *     ("Usage" of both pages); head_cls is [kv_heads, head_dim].
- *   - head_dim: 64 or 128 for dash_summarize, dash_route,
- *     dash_sparse_attn_prefill, dash_sparse_attn_decode,
- *     dash_decode_step_noalloc, entmax_attn and entmax_attn_backward; 128 for
- *     dash_summarize_backward and dash_sparse_attn_prefill_backward. The
- *     DashAttention kernels keep their own arrays 128 wide, so a workspace
- *     query gives the same size for head_dim 64 as for 128.
+ *   - head_dim: 64 or 128 for every entry point. The forward DashAttention
+ *     kernels keep their own arrays 128 wide, so dash_workspace_size gives the
+ *     same size for head_dim 64 as for 128.
  *   - Work is enqueued on `stream` (NULL = the null stream); nothing
  *     synchronises the host. Outputs are valid once the stream reaches them.
  *   - All argument checks run on the host before any HIP call, so a bad call
@@ -126,8 +123,8 @@ dash_status dash_summarize(const void* K, const void* head_cls, float* S, dash_d
  * dcls is reduced in a fixed order (deterministic). Device memory is the
  * caller's; nothing is allocated; no host sync. Errors: NULL pointers, sizes
  * <= 0, a chunk range outside [0, s_cap] or past Lmax, n_tokens outside
- * [1, Lmax] -> DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d != 128 or
- * chunk_size != 64 -> DASH_ERR_UNSUPPORTED; a launch failure -> DASH_ERR_HIP.
+ * [1, Lmax] -> DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d not 64 or 128
+ * or chunk_size != 64 -> DASH_ERR_UNSUPPORTED; a launch failure -> DASH_ERR_HIP.
  * --------------------------------------------------------------------------- */
 dash_status dash_summarize_backward(const void* K, const void* head_cls, const float* dS,
                                     dash_dtype dt, int B, int Hkv, int Lmax, int d, int n_tokens,
@@ -263,7 +260,7 @@ dash_status dash_sparse_attn_prefill(const void* Q, const void* K, const void* V
  * ceil(N/64) * 4 + 3 * B * Hq * N * d * 4 bytes), nothing is allocated, no
  * host sync. Errors: NULL pointers, sizes <= 0, N > Lmax, Hq % Hkv != 0, bad
  * params, bits_words too small, s_cap below the summarised chunks ->
- * DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d != 128, chunk_size != 64,
+ * DASH_ERR_INVALID_ARG; dt other than DASH_BF16, d not 64 or 128, chunk_size != 64,
  * N > 65536 -> DASH_ERR_UNSUPPORTED; ws_bytes too small -> DASH_ERR_WORKSPACE;
  * a launch failure -> DASH_ERR_HIP.
  * --------------------------------------------------------------------------- */
