@@ -648,7 +648,8 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
 // chunks that the caches can still serve. The g heads of one (b, kv head, chunk) get work ids
 // that are equal modulo 8 (one XCD), so their K/V reads share that L2.
 // ---------------------------------------------------------------------------
-template <bool CAUSAL>
+// DC: the caller's head_dim (row width of Q, K, V, O), a template argument
+template <bool CAUSAL, int DC>
 __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   constexpr int D = 128;
   constexpr int NP = 4;           // partials loaded together
@@ -677,9 +678,9 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
   const int tid = threadIdx.x;
   if (*a.bad != 0) {
     // inconsistent workspace: every row of the unit reads NaN
-    for (int x = tid; x < kChunk * a.d / 2; x += blockDim.x) {
-      const int r = c * kChunk + x / (a.d / 2);
-      if (r < N) reinterpret_cast<uint32_t*>(a.O + (bh * N + r) * (size_t)a.d)[x % (a.d / 2)] = 0x7fc07fc0u;
+    for (int x = tid; x < kChunk * DC / 2; x += blockDim.x) {
+      const int r = c * kChunk + x / (DC / 2);
+      if (r < N) reinterpret_cast<uint32_t*>(a.O + (bh * N + r) * (size_t)DC)[x % (DC / 2)] = 0x7fc07fc0u;
     }
     return;
   }
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
     bf16x8 qb[D / 32];  // Q^T as the B operand: column qi, dims 32 s + 8 q4 .. +7
     {
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(ldg16_d(a.Q, bh * N + min(qi, N - 1), 32 * s + 8 * q4, a.d));
+      for (int s = 0; s < D / 32; ++s) qb[s] = as_bf16x8(ldg16_dc<DC>(a.Q, bh * N + min(qi, N - 1), 32 * s + 8 * q4));
     }
     {
       // K rows (row-major) and V (transposed) of chunk c; keys past the sequence
@@ -722,8 +723,8 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
       u32x4 kr[4], vr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        kr[r] = ldg16_d(a.K, kvrow0 + min(row0 + k_row + 16 * r, N - 1), k_col, a.d);
-        vr[r] = ldg16_d(a.V, kvrow0 + min(row0 + 4 * v_kg + r, N - 1), 8 * v_dg, a.d);
+        kr[r] = ldg16_dc<DC>(a.K, kvrow0 + min(row0 + k_row + 16 * r, N - 1), k_col);
+        vr[r] = ldg16_dc<DC>(a.V, kvrow0 + min(row0 + 4 * v_kg + r, N - 1), 8 * v_dg);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&sK[(k_row + 16 * r) * KROW + k_col]) = kr[r];
@@ -882,7 +883,7 @@ __global__ __launch_bounds__(256) void k_prefill_merge(PrefillAttnArgs a) {
       u32x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[8 * hv + 2 * e], acc[8 * hv + 2 * e + 1]);
-      if (8 * p + 64 * hv < a.d) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(a.O + ri * a.d + 8 * p + 64 * hv));
+      if (8 * p + 64 * hv < DC) __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(a.O + ri * DC + 8 * p + 64 * hv));
     }
   }
 }
@@ -897,10 +898,13 @@ hipError_t launch_sparse_prefill(const PrefillAttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((k_prefill_cm<128, 128>), dim3((unsigned)cm_grid), dim3(256), 0, stream, a);
   const int m_units = a.B * a.Hkv * ((a.N + kChunk - 1) / kChunk);
   const unsigned merge_grid = (unsigned)((m_units + 7) / 8) * 8 * a.g;
-  if (a.causal)
-    hipLaunchKernelGGL(k_prefill_merge<true>, dim3(merge_grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_prefill_merge<false>, dim3(merge_grid), dim3(256), 0, stream, a);
+  if (a.causal) {
+    if (a.d == 64) hipLaunchKernelGGL((k_prefill_merge<true, 64>), dim3(merge_grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_prefill_merge<true, 128>), dim3(merge_grid), dim3(256), 0, stream, a);
+  } else {
+    if (a.d == 64) hipLaunchKernelGGL((k_prefill_merge<false, 64>), dim3(merge_grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((k_prefill_merge<false, 128>), dim3(merge_grid), dim3(256), 0, stream, a);
+  }
   // row-major fallback for tiles without pool slots (a persistent grid that
   // skips every other tile)
   const int n_units = a.n_tiles * a.B * a.Hkv;

@@ -73,8 +73,8 @@ KERNEL_SOURCES = {
     "k_cm_plan": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_sparse_prefill": ["sparse_prefill.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
     "k_summarize_bwd": ["summarize.hip", "kernels.hpp", "cdna4.hpp"],
-    "k_entmax_bwd_dq": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
-    "k_entmax_bwd_dkdv": ["entmax_attn_bwd.hip", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_bwd_dq": ["entmax_attn_bwd.hip", "bwd_common.hpp", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
+    "k_entmax_bwd_dkdv": ["entmax_attn_bwd.hip", "bwd_common.hpp", "kernels.hpp", "cdna4.hpp", "tau_solve.hpp"],
 }
 # the kernels of one dash_sparse_attn_prefill call
 ATTN_KERNELS = ["k_cm_plan", "k_cm_scatter", "k_prefill_cm", "k_prefill_merge", "k_sparse_prefill"]
