@@ -122,6 +122,25 @@ def test_prefill_head_dim_64(B, Hq, Hkv, N, p, planted, pool):
 
 
 @pytest.mark.parametrize(
+    "B,Hq,Hkv,N,p",
+    [
+        (1, 2, 1, 1, api.Params()),                                # one token
+        (1, 2, 1, 2, api.Params(estimate_diagonal=False)),
+        (1, 4, 2, 63, api.Params()),                               # no complete chunk
+        (1, 4, 2, 65, api.Params(estimate_diagonal=False)),        # one complete chunk + 1 token
+        (2, 4, 1, 65, api.Params(alpha=2.0)),
+        (1, 2, 2, 129, api.Params()),                              # one row past a 128-row tile
+        (1, 2, 1, 1, api.Params(causal=False)),
+        (1, 4, 4, 65, api.Params(causal=False, alpha=1.333)),
+    ],
+)
+def test_prefill_tiny_edges(B, Hq, Hkv, N, p):
+    """Tiny and ragged lengths around the chunk (64) and tile (128) sizes."""
+    Q, K, V, cls = _inputs(B, Hq, Hkv, N, 900 + N, None)
+    check_prefill(Q, K, V, cls, p, where=f"tiny N={N} {p}")
+
+
+@pytest.mark.parametrize(
     "B,Hq,Hkv,N,p,planted",
     [
         (1, 4, 1, 1000, api.Params(causal=True, estimate_diagonal=True), "chunks"),
