@@ -81,6 +81,20 @@ def test_prefill_backward_head_dim_64(B, Hq, Hkv, N, p, planted):
     _run(B, Hq, Hkv, N, p, seed=300 + N, planted=planted, d=64)
 
 
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,N,p",
+    [
+        (1, 2, 1, 1, api.Params()),
+        (1, 2, 1, 2, api.Params(estimate_diagonal=False)),
+        (1, 2, 2, 65, api.Params()),
+        (1, 2, 1, 129, api.Params(causal=False)),
+    ],
+)
+def test_prefill_backward_tiny_edges(B, Hq, Hkv, N, p):
+    """The backward at tiny and ragged lengths around the chunk and tile sizes."""
+    _run(B, Hq, Hkv, N, p, seed=400 + N, planted=None)
+
+
 def test_prefill_backward_deterministic():
     Q, K, V, cls = routed_prefill_inputs(1, 4, 1, 400, 128, 5, planted="chunks", device="cuda")
     dO = cotangent((1, 4, 400, 128), 6, dtype="bf16", device="cuda")
