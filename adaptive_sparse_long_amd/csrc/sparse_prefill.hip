@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_prefill(PrefillAttnArgs a) {
   constexpr int NDB = D / 32; // 32-dim blocks of O^T
   constexpr int KROW = D + KPAD;
   constexpr int VROW = kChunk + VPAD;
-  static_assert(D == 128, "staging is laid out 128 dims wide (head_dim 64 runs it with zero upper dims)");
+  static_assert(D == 128, "staging is laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VROW];
   __shared__ __attribute__((aligned(16))) uint16_t sU[2][2 * D];  // the chunk's summary: high parts, low parts
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256, kCmWgPerCu) void k_prefill_cm(PrefillAttnArgs 
   constexpr int VROW = kChunk + VPAD;
   constexpr int NBW = kCmBlocks / 4;  // blocks of an item per wavefront
   constexpr int OROW = 64 + 8;        // output staging: 64 dims of a row, padded
-  static_assert(D == 128, "staging is laid out 128 dims wide (head_dim 64 runs it with zero upper dims)");
+  static_assert(D == 128, "staging is laid out for head_dim 128");
   __shared__ __attribute__((aligned(16))) uint16_t sK[kChunk * KROW];
   __shared__ __attribute__((aligned(16))) uint16_t sV[D * VROW];
   __shared__ __attribute__((aligned(16))) uint16_t sO[4][32 * OROW];  // per wavefront
