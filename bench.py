@@ -337,20 +337,24 @@ def bench_decode(w, steps, warmup):
     flush = CacheEvictor(dev)
     t_route, t_attn, t_step = Timer(), Timer(), Timer()
 
+    # timed=True: events around the routing and the attention (the parts);
+    # timed="step": events around the whole step only, so that the step time
+    # carries no instrumentation between its kernels
     def step(timed):
-        e = t_step.start() if timed else None
-        e1 = t_route.start() if timed else None
+        parts = timed is True
+        e = t_step.start() if timed == "step" else None
+        e1 = t_route.start() if parts else None
         api.route(q, Kc, cls, S, p, seqlens=seqlens, with_bits=False, workspace=ws)
-        if timed:
+        if parts:
             t_route.stop(e1)
             e1 = t_attn.start()
         api.sparse_attn_decode(q, Kc, Vc, seqlens, ws, p, out=O)
-        if timed:
+        if parts:
             t_attn.stop(e1)
         done = sorted({n // C - 1 for n in lengths if n % C == 0})
         for c in done:
             api.summarize(Kc, cls, S, seqlens=seqlens, chunk_begin=c, chunk_end=c + 1, params=p)
-        if timed:
+        if e is not None:
             t_step.stop(e)
 
     for _ in range(warmup):
@@ -359,6 +363,9 @@ def bench_decode(w, steps, warmup):
     for _ in range(steps):
         flush()
         step(True)
+    for _ in range(steps):
+        flush()
+        step("step")
     torch.cuda.synchronize()
     # chunks each (b, kv head) group read: union of its g heads' routed chunks
     _, bits, _ = api.route(q, Kc, cls, S, p, seqlens=seqlens, with_bits=True, workspace=ws)
